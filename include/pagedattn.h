@@ -1,0 +1,177 @@
+/*
+ * pagedattn.h -- C ABI of libpagedattn.so: attention over a block-paged KV
+ * cache on AMD Instinct MI355X (gfx950).
+ *
+ * The operation. The mini-vllm page ("mini-vllm：基于 NanoGPT 的
+ * PagedAttention 风格 KV 缓存管理实现", section "mini-vllm 的架构设计",
+ * item 2 "KVCache") keeps every sequence's K/V rows in fixed-size physical
+ * blocks of one preallocated device tensor and finds them, for reads and
+ * writes alike, through a per-sequence block table; the nano-vllm page
+ * ("nano vllm：轻量级大模型推理框架的KV Cache优化实践", §3.1 and §3.2) gives a
+ * sequence its list of physical block ids and lets blocks be shared between
+ * sequences through prefix hashing and reference counts. Attention through
+ * the table equals ordinary scaled dot-product attention over the sequence's
+ * rows in logical order:
+ *
+ *     out[h] = softmax(scale * K[g(h)] q[h]) V[g(h)],   g(h) = h / (Hq / Hkv)
+ *
+ * Layouts (all row-major, contiguous unless a stride is given):
+ *   k_cache, v_cache   [num_blocks][block_size][num_kv_heads][head_dim]
+ *   q, out             [tokens][num_heads][head_dim]
+ *   key, value         [num_tokens][num_kv_heads][head_dim], token stride given
+ *   block_tables       int32 [num_seqs][max_blocks_per_seq]; logical token j
+ *                      of sequence i is row j % block_size of physical block
+ *                      block_tables[i][j / block_size]
+ *   context_lens       int32 [num_seqs]; number of context tokens, INCLUDING
+ *                      the newest one (store it first, then attend)
+ *   slot_mapping       int32 [num_tokens]; slot s = block * block_size + row
+ *   query_start_loc    int32 [num_seqs + 1]; prefill rows of sequence i are
+ *                      query_start_loc[i] .. query_start_loc[i+1]-1
+ *
+ * Element type: PA_F32 or PA_BF16 for every floating-point buffer of one
+ * call; out has the type of q. Accumulation is always fp32.
+ *
+ * Ownership and streams. The caller owns every buffer (device pointers; the
+ * library allocates no device memory in these calls). Each call enqueues its
+ * kernels on the given hipStream_t (passed as void*, NULL = default stream)
+ * and returns without synchronising; it never reads device memory on the
+ * host, which is why the maxima (max_context_len, max_query_len) are
+ * arguments.
+ *
+ * Errors. Arguments are checked on the host before anything is enqueued; a
+ * bad argument returns a code and enqueues nothing. A failed launch returns
+ * PA_ERR_HIP. No C++ exception crosses this interface. pa_last_error()
+ * returns a description of the calling thread's last failure. A call with
+ * num_seqs == 0 or num_tokens == 0 is a no-op returning PA_OK.
+ *
+ * Supported shapes: head_dim 64 or 128; block_size a power of two in
+ * [8, 1024]; num_heads a multiple of num_kv_heads; pointers 16-byte aligned.
+ *
+ * Device-content preconditions (documented, not checked on the host; the
+ * kernels clamp indices so a violation gives wrong numbers, not a fault):
+ *   - 1 <= context_lens[i] <= max_context_len <= max_blocks_per_seq*block_size
+ *   - block table entries used by a context lie in [0, num_blocks)
+ *   - slots >= 0 are unique; a slot never lies in a block that another
+ *     sequence's table also references (no store into a shared block)
+ *   - prefill: 1 <= n_i <= max_query_len and n_i <= context_lens[i]
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARG = 1,  /* null pointer, negative size, inconsistent sizes */
+  PA_ERR_UNSUPPORTED = 2,  /* valid but not implemented (head_dim, block_size, alignment) */
+  PA_ERR_WORKSPACE = 3,    /* split decode without a large enough workspace */
+  PA_ERR_HIP = 4           /* a HIP runtime call or launch failed */
+} pa_status;
+
+typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/*
+ * pa_store_kvcache -- scatter new K/V rows into the pools.
+ *
+ * For each token t with s = slot_mapping[t] in [0, num_blocks*block_size):
+ *   k_cache[s / block_size][s % block_size][:][:] = key[t][:][:]
+ *   v_cache[s / block_size][s % block_size][:][:] = value[t][:][:]
+ * (mini-vllm page, item 2 "KVCache": the block table locates writes).
+ * A negative slot is padding and writes nothing; a slot past the pool is
+ * skipped too. The copy is bit-exact.
+ *
+ * key_tok_stride / value_tok_stride: elements between consecutive tokens of
+ * key / value (>= num_kv_heads*head_dim, a multiple of 16 bytes), so that
+ * slices of a fused QKV tensor can be passed directly.
+ */
+pa_status pa_store_kvcache(const void* key, const void* value,
+                           int64_t key_tok_stride, int64_t value_tok_stride,
+                           void* k_cache, void* v_cache,
+                           const int32_t* slot_mapping, int32_t num_tokens,
+                           int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t num_blocks,
+                           pa_dtype dtype, void* stream);
+
+/*
+ * pa_decode_workspace_size -- bytes of workspace pa_decode needs when the
+ * context is split into partitions of partition_size tokens; 0 when no
+ * sequence can need more than one partition (partition_size == 0 or
+ * partition_size >= max_context_len). Returns 0 for invalid arguments too.
+ */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
+                                int32_t num_kv_heads, int32_t head_dim,
+                                int32_t max_context_len, int32_t partition_size);
+
+/*
+ * pa_decode -- one query token per sequence.
+ *
+ * For every sequence i and query head h:
+ *   out[i][h] = softmax(scale * K_i[g] q[i][h]) V_i[g]
+ * over the context_lens[i] tokens of sequence i gathered through
+ * block_tables[i], g = h / (num_heads / num_kv_heads).
+ *
+ * partition_size > 0 splits each context into slices of that many tokens
+ * (a multiple of 16); every slice yields an fp32 (max, sum, weighted values)
+ * state in the workspace and the last slice of a (sequence, head group) to
+ * finish merges them into out, all in one launch. partition_size == 0
+ * attends over whole contexts. The result does not depend on the split
+ * beyond fp32 rounding.
+ *
+ * workspace: device memory of at least pa_decode_workspace_size(...) bytes,
+ * 256-byte aligned, ZERO-FILLED before its first use; every completed call
+ * leaves it zero-filled again, so it can be reused by later calls of any
+ * shape without clearing. Calls sharing a workspace must not overlap in
+ * time (same stream, or synchronised). May be NULL when the size is 0.
+ */
+pa_status pa_decode(void* out, const void* q,
+                    const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens,
+                    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                    int32_t max_blocks_per_seq, int32_t max_context_len,
+                    float scale, int32_t partition_size,
+                    void* workspace, size_t workspace_bytes,
+                    pa_dtype dtype, void* stream);
+
+/*
+ * pa_prefill_chunk -- causal attention of a chunk of new tokens over the
+ * cached-plus-new paged context (the prefill pass of the mini-vllm page's
+ * inference engine, run chunk by chunk).
+ *
+ * Sequence i has n_i = query_start_loc[i+1] - query_start_loc[i] new rows
+ * and c_i = context_lens[i] - n_i cached tokens; the new tokens' K/V must
+ * already be stored (pa_store_kvcache). Row t (0 <= t < n_i) sits at
+ * position c_i + t and attends to keys 0 .. c_i + t:
+ *   out[r][h] = softmax(scale * K_i[g][0..c_i+t] q[r][h]) V_i[g][0..c_i+t],
+ *   r = query_start_loc[i] + t.
+ * Only PA_BF16 is implemented (bf16 MFMA, fp32 accumulation; the
+ * probabilities are rounded to bf16 before the PV product).
+ */
+pa_status pa_prefill_chunk(void* out, const void* q,
+                           const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables,
+                           const int32_t* query_start_loc,
+                           const int32_t* context_lens,
+                           int32_t num_seqs, int32_t num_heads,
+                           int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t num_blocks,
+                           int32_t max_blocks_per_seq, int32_t max_query_len,
+                           int32_t max_context_len, float scale,
+                           pa_dtype dtype, void* stream);
+
+/* Static description of a status code. */
+const char* pa_status_string(pa_status s);
+
+/* Description of the calling thread's last failed call ("" if none). */
+const char* pa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

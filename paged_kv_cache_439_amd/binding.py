@@ -1,0 +1,198 @@
+"""ctypes binding of libpagedattn.so (argument marshalling only).
+
+Each function takes torch tensors, checks what the C side cannot see (device,
+dtype, contiguity, shape agreement), passes raw pointers and sizes to the C
+entry point of the same name, and raises PagedAttnError on a non-zero status.
+All compute runs in the library's HIP kernels; there is no fallback path:
+if the library is missing, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libpagedattn.so"
+
+PA_F32, PA_BF16 = 0, 1
+_STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED",
+           3: "PA_ERR_WORKSPACE", 4: "PA_ERR_HIP"}
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, func, status, message):
+        self.status = status
+        super().__init__(f"{func}: {_STATUS.get(status, status)}: {message}")
+
+
+def library_path() -> str:
+    return os.environ.get("PAGEDATTN_LIB", os.path.join(_HERE, _LIB_NAME))
+
+
+_lib = None
+
+_c_void_p, _i32, _i64, _f32, _size = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                      ctypes.c_float, ctypes.c_size_t)
+
+_SIGNATURES = {
+    "pa_store_kvcache": ([_c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
+                          _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _c_void_p], ctypes.c_int),
+    "pa_decode_workspace_size": ([_i32, _i32, _i32, _i32, _i32, _i32], _size),
+    "pa_decode": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                   _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                   _c_void_p, _size, ctypes.c_int, _c_void_p], ctypes.c_int),
+    "pa_prefill_chunk": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                          _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                          _f32, ctypes.c_int, _c_void_p], ctypes.c_int),
+    "pa_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "pa_last_error": ([], ctypes.c_char_p),
+}
+
+
+def load_library():
+    """Load the built library once; raise if it is not there."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} not found: build the HIP library first "
+            f"(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(path)
+    for name, (args, res) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(func, status):
+    if status != 0:
+        msg = load_library().pa_last_error().decode(errors="replace")
+        raise PagedAttnError(func, status, msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return PA_F32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(cond, what):
+    if not cond:
+        raise ValueError(what)
+
+
+def _int32_device(t, name, device):
+    _need(t.dtype == torch.int32, f"{name} must be int32")
+    _need(t.device == device, f"{name} must be on {device}")
+    _need(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def pa_status_string(status: int) -> str:
+    return load_library().pa_status_string(int(status)).decode()
+
+
+def pa_store_kvcache(key, value, k_cache, v_cache, slot_mapping, stream=None):
+    """Scatter key/value rows [T][Hkv][D] into the pools by slot_mapping."""
+    lib = load_library()
+    T, Hkv, D = key.shape
+    _need(value.shape == key.shape, "key and value shapes differ")
+    _need(k_cache.dim() == 4 and k_cache.shape == v_cache.shape, "pools must be [NB][bs][Hkv][D]")
+    NB, bs, Hkv2, D2 = k_cache.shape
+    _need((Hkv2, D2) == (Hkv, D), "pool head shape does not match key")
+    _need(k_cache.is_contiguous() and v_cache.is_contiguous(), "pools must be contiguous")
+    for t in (key, value):
+        _need(t.stride(2) == 1 and t.stride(1) == D, "key/value rows must be dense [Hkv][D]")
+    _need(key.dtype == value.dtype == k_cache.dtype == v_cache.dtype, "dtypes differ")
+    _int32_device(slot_mapping, "slot_mapping", k_cache.device)
+    _need(slot_mapping.numel() == T, "slot_mapping length differs from key")
+    st = lib.pa_store_kvcache(_ptr(key), _ptr(value), key.stride(0), value.stride(0),
+                              _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), T, Hkv, D, bs, NB,
+                              _dtype_code(key), _stream(stream))
+    _check("pa_store_kvcache", st)
+
+
+def pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
+                             partition_size) -> int:
+    return int(load_library().pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                       max_context_len, partition_size))
+
+
+def decode_workspace(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
+                     partition_size, device):
+    """A zero-filled workspace of the size pa_decode needs (None if 0)."""
+    n = pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
+                                 partition_size)
+    if n == 0:
+        return None
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+              partition_size=0, workspace=None, stream=None):
+    """Single-token decode; out and q are [B][Hq][D]."""
+    lib = load_library()
+    B, Hq, D = q.shape
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    _need(q.is_contiguous() and out.is_contiguous(), "q and out must be contiguous")
+    _need(k_cache.dim() == 4 and k_cache.shape == v_cache.shape, "pools must be [NB][bs][Hkv][D]")
+    _need(k_cache.is_contiguous() and v_cache.is_contiguous(), "pools must be contiguous")
+    NB, bs, Hkv, D2 = k_cache.shape
+    _need(D2 == D, "head_dim of pools and q differ")
+    _need(q.dtype == k_cache.dtype == v_cache.dtype, "dtypes differ")
+    _int32_device(block_tables, "block_tables", q.device)
+    _int32_device(context_lens, "context_lens", q.device)
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == B, "block_tables must be [B][max_blocks]")
+    _need(context_lens.numel() == B, "context_lens must have B entries")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _need(workspace.device == q.device and workspace.is_contiguous(), "bad workspace")
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    st = lib.pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                       _ptr(context_lens), B, Hq, Hkv, D, bs, NB, block_tables.shape[1],
+                       int(max_context_len), float(scale), int(partition_size), ws_ptr, ws_bytes,
+                       _dtype_code(q), _stream(stream))
+    _check("pa_decode", st)
+
+
+def pa_prefill_chunk(out, q, k_cache, v_cache, block_tables, query_start_loc, context_lens,
+                     max_query_len, max_context_len, scale, stream=None):
+    """Chunked causal prefill; out and q are [sum n_i][Hq][D]."""
+    lib = load_library()
+    T, Hq, D = q.shape
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    _need(q.is_contiguous() and out.is_contiguous(), "q and out must be contiguous")
+    _need(k_cache.dim() == 4 and k_cache.shape == v_cache.shape, "pools must be [NB][bs][Hkv][D]")
+    _need(k_cache.is_contiguous() and v_cache.is_contiguous(), "pools must be contiguous")
+    NB, bs, Hkv, D2 = k_cache.shape
+    _need(D2 == D, "head_dim of pools and q differ")
+    _need(q.dtype == k_cache.dtype == v_cache.dtype, "dtypes differ")
+    for name, t in (("block_tables", block_tables), ("query_start_loc", query_start_loc),
+                    ("context_lens", context_lens)):
+        _int32_device(t, name, q.device)
+    B = context_lens.numel()
+    _need(query_start_loc.numel() == B + 1, "query_start_loc must have B+1 entries")
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == B, "block_tables must be [B][max_blocks]")
+    st = lib.pa_prefill_chunk(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                              _ptr(query_start_loc), _ptr(context_lens), B, Hq, Hkv, D, bs, NB,
+                              block_tables.shape[1], int(max_query_len), int(max_context_len),
+                              float(scale), _dtype_code(q), _stream(stream))
+    _check("pa_prefill_chunk", st)

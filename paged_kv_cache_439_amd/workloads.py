@@ -1,0 +1,411 @@
+"""Seeded synthetic inputs for paged-KV attention.
+
+This module only draws inputs; it holds none of the attention arithmetic and
+none of the prefix-hash arithmetic, and it serves both the library's tests and
+benchmark and the CPU oracle's checks.
+
+Structure (context lengths, token ids, block tables, slot mapping) is drawn
+with numpy's PCG64 from seed ``439000 + config id`` in this order:
+
+  1. for prefix-sharing workloads, the subset of sequences that share;
+  2. context lengths (decode) or cached lengths (prefill);
+  3. token ids, uniform in [0, 50257) (the GPT-2 vocabulary the NanoGPT model
+     of the mini-vllm page uses), with one common prefix for sharers;
+  4. a random permutation of the pool's block ids, used as the free list;
+     sequences take blocks from its front in order, and a sharing sequence
+     reuses the blocks of the common prefix that the first sharer took.
+
+Dense values (pool K/V, the new K/V rows, Q) are N(0, 1) float32 from a
+seeded torch generator on the target device, rounded to nearest-even when the
+workload is bf16. Drawing them on the device keeps multi-GB pools fast to
+build; the oracle receives host copies of exactly these values.
+
+Block-table entries past a sequence's last block are -1.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+VOCAB = 50257
+SEED_BASE = 439000
+
+# The five workloads. Lengths include the newest token.
+CONFIGS = {
+    1: dict(name="tiny_fp32_mha_decode", kind="decode", dtype="f32", num_seqs=4,
+            num_heads=8, num_kv_heads=8, head_dim=64, block_size=16,
+            lens=("fixed", [17, 33, 64, 100]), pool=("blocks", 64),
+            max_context=100, partition_size=0),
+    2: dict(name="bf16_mha_decode_b64", kind="decode", dtype="bf16", num_seqs=64,
+            num_heads=12, num_kv_heads=12, head_dim=64, block_size=256,
+            lens=("uniform", 512, 4096), pool=("factor", 1.25),
+            max_context=4096, partition_size=256),
+    3: dict(name="bf16_gqa_decode_b256_shared_prefix", kind="decode", dtype="bf16",
+            num_seqs=256, num_heads=16, num_kv_heads=8, head_dim=128, block_size=256,
+            lens=("uniform", 1024, 4096), pool=("factor", 1.25),
+            share=dict(num_sharers=128, prefix_tokens=1024),
+            max_context=4096, partition_size=512),
+    4: dict(name="bf16_gqa_chunked_prefill", kind="prefill", dtype="bf16", num_seqs=8,
+            num_heads=32, num_kv_heads=8, head_dim=128, block_size=256,
+            cached=("uniform", 0, 3584), chunk=512, pool=("factor", 1.25),
+            max_context=4096),
+    5: dict(name="bf16_gqa_decode_b512_lognormal", kind="decode", dtype="bf16",
+            num_seqs=512, num_heads=32, num_kv_heads=8, head_dim=128, block_size=64,
+            lens=("lognormal", 1500.0, 1.0, 64, 4096), pool=("factor", 1.25),
+            max_context=4096, partition_size=512),
+}
+
+
+def torch_dtype(dtype: str):
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[dtype]
+
+
+def elem_bytes(dtype: str) -> int:
+    return {"f32": 4, "bf16": 2}[dtype]
+
+
+@dataclass
+class Batch:
+    """One batch of paged-attention inputs."""
+    spec: dict
+    kind: str                      # "decode" | "prefill"
+    dtype: str                     # "f32" | "bf16"
+    num_seqs: int
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    scale: float
+    context_lens: np.ndarray       # int32 [B]
+    block_tables: np.ndarray       # int32 [B][max_blocks_per_seq]
+    slot_mapping: np.ndarray       # int32 [T]
+    token_ids: list
+    query_start_loc: np.ndarray | None = None   # prefill: int32 [B+1]
+    shared_blocks: list = field(default_factory=list)
+    k_cache: torch.Tensor | None = None   # [NB][bs][Hkv][D]
+    v_cache: torch.Tensor | None = None
+    key: torch.Tensor | None = None       # new rows [T][Hkv][D]
+    value: torch.Tensor | None = None
+    q: torch.Tensor | None = None         # [T_q][Hq][D]
+    device: str = "cpu"
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return int(self.block_tables.shape[1])
+
+    @property
+    def max_context_len(self) -> int:
+        return int(self.context_lens.max()) if len(self.context_lens) else 0
+
+    @property
+    def max_query_len(self) -> int:
+        if self.query_start_loc is None:
+            return 1
+        return int(np.diff(self.query_start_loc).max())
+
+    @property
+    def logical_blocks(self) -> int:
+        return int(sum(math.ceil(int(L) / self.block_size) for L in self.context_lens))
+
+    @property
+    def unique_blocks(self) -> int:
+        used = set()
+        for i, L in enumerate(self.context_lens):
+            used.update(self.block_tables[i, :math.ceil(int(L) / self.block_size)].tolist())
+        return len(used)
+
+    def kv_bytes(self, unique: bool = True) -> int:
+        """K+V bytes a decode pass must read: one row per distinct
+        (physical block, row) that some context covers when unique (a block
+        shared by several sequences counts once), else one per
+        (sequence, token)."""
+        row = self.num_kv_heads * self.head_dim * elem_bytes(self.dtype) * 2
+        if not unique:
+            return int(self.context_lens.astype(np.int64).sum()) * row
+        return int(covered_rows(self).sum()) * row
+
+
+# ---------------------------------------------------------------------------
+# structure
+# ---------------------------------------------------------------------------
+
+def _draw_lengths(rng, spec, n, lo_override=None):
+    kind = spec[0]
+    if kind == "fixed":
+        return np.asarray(spec[1], dtype=np.int64)
+    if kind == "uniform":
+        lo, hi = spec[1], spec[2]
+        if lo_override is not None:
+            lo = np.maximum(lo, lo_override)
+        return rng.integers(lo, hi + 1, size=n, dtype=np.int64)
+    if kind == "lognormal":
+        median, sigma, lo, hi = spec[1:5]
+        z = rng.standard_normal(n)
+        return np.clip(np.rint(median * np.exp(sigma * z)), lo, hi).astype(np.int64)
+    raise ValueError(spec)
+
+
+def _allocate(rng, lens, bs, pool_spec, sharers, prefix_blocks, max_blocks):
+    """Tables from a shuffled free list; sharers reuse the prefix blocks."""
+    need_logical = [math.ceil(int(L) / bs) for L in lens]
+    n_shared_users = sum(1 for i in range(len(lens)) if sharers[i])
+    need_unique = sum(need_logical) - max(0, n_shared_users - 1) * prefix_blocks
+    if pool_spec[0] == "blocks":
+        num_blocks = int(pool_spec[1])
+    else:
+        num_blocks = int(math.ceil(pool_spec[1] * need_unique))
+    if num_blocks < need_unique:
+        raise ValueError("pool too small for the drawn lengths")
+    free = rng.permutation(num_blocks).astype(np.int64)
+    free_list = free.copy()
+    pos = 0
+    tables = np.full((len(lens), max_blocks), -1, dtype=np.int32)
+    shared_ids = [None] * prefix_blocks
+    for i, nb in enumerate(need_logical):
+        for k in range(nb):
+            if sharers[i] and k < prefix_blocks:
+                if shared_ids[k] is None:
+                    shared_ids[k] = int(free[pos])
+                    pos += 1
+                tables[i, k] = shared_ids[k]
+            else:
+                tables[i, k] = int(free[pos])
+                pos += 1
+    return num_blocks, tables, [b for b in shared_ids if b is not None], free_list
+
+
+def draw_structure(spec, seed=None):
+    """Structure only (no dense values): a dict with context_lens, chunks
+    (prefill), token_ids, num_blocks, block_tables, shared_blocks and the
+    free list the tables were taken from."""
+    if seed is None:
+        seed = SEED_BASE + int(spec.get("id", 0))
+    lens, chunks, token_ids, num_blocks, tables, shared, free = _structure(spec, seed)
+    return dict(context_lens=lens, chunks=chunks, token_ids=token_ids, num_blocks=num_blocks,
+                block_tables=tables, shared_blocks=shared, free_list=free)
+
+
+def _structure(spec, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    B = spec["num_seqs"]
+    bs = spec["block_size"]
+    share = spec.get("share")
+    sharers = np.zeros(B, dtype=bool)
+    prefix_tokens = 0
+    if share:
+        sharers[rng.choice(B, size=share["num_sharers"], replace=False)] = True
+        prefix_tokens = share["prefix_tokens"]
+        if prefix_tokens % bs:
+            raise ValueError("shared prefix must be whole blocks")
+    if spec["kind"] == "decode":
+        lens = _draw_lengths(rng, spec["lens"], B)
+        if share:
+            # a sharer's newest token must land past the shared blocks, so
+            # that storing it never writes into a block other tables use
+            lo = prefix_tokens + 1
+            redo = sharers & (lens < lo)
+            while redo.any():
+                lens[redo] = _draw_lengths(rng, spec["lens"], int(redo.sum()), lo_override=lo)
+                redo = sharers & (lens < lo)
+        chunks = None
+    else:
+        cached = _draw_lengths(rng, spec["cached"], B)
+        chunk = spec["chunk"]
+        chunks = np.full(B, chunk, dtype=np.int64) if np.isscalar(chunk) else np.asarray(chunk, np.int64)
+        lens = cached + chunks
+    common = rng.integers(0, VOCAB, size=prefix_tokens, dtype=np.int64)
+    token_ids = []
+    for i in range(B):
+        ids = rng.integers(0, VOCAB, size=int(lens[i]), dtype=np.int64)
+        if sharers[i]:
+            ids[:prefix_tokens] = common
+        token_ids.append(ids)
+    max_blocks = math.ceil(spec["max_context"] / bs)
+    if int(lens.max()) > spec["max_context"]:
+        raise ValueError("a drawn length exceeds max_context")
+    num_blocks, tables, shared, free = _allocate(rng, lens, bs, spec["pool"], sharers,
+                                                 prefix_tokens // bs, max_blocks)
+    return lens.astype(np.int32), chunks, token_ids, num_blocks, tables, shared, free
+
+
+def _slot(tables, i, pos, bs):
+    return int(tables[i, pos // bs]) * bs + pos % bs
+
+
+# ---------------------------------------------------------------------------
+# dense values
+# ---------------------------------------------------------------------------
+
+def _randn(shape, dtype, device, seed, chunk_rows=None):
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    td = torch_dtype(dtype)
+    out = torch.empty(shape, dtype=td, device=device)
+    rows = shape[0]
+    step = chunk_rows or rows or 1
+    for r0 in range(0, rows, step):
+        r1 = min(rows, r0 + step)
+        out[r0:r1] = torch.randn((r1 - r0,) + tuple(shape[1:]), generator=g,
+                                 device=device, dtype=torch.float32).to(td)
+    return out
+
+
+def make_batch(spec, device="cpu", seed=None, poison=False):
+    """Draw a full batch for ``spec`` (an entry of CONFIGS or a variant).
+
+    poison=True fills every pool row that no context covers, and the rows the
+    new tokens are about to be stored into, with NaN; a kernel that reads
+    outside the context then shows NaN in its output.
+    """
+    if seed is None:
+        seed = SEED_BASE + int(spec.get("id", 0))
+    lens, chunks, token_ids, num_blocks, tables, shared, _ = _structure(spec, seed)
+    B = spec["num_seqs"]
+    Hq, Hkv, D, bs = spec["num_heads"], spec["num_kv_heads"], spec["head_dim"], spec["block_size"]
+    if spec["kind"] == "decode":
+        slots = np.array([_slot(tables, i, int(lens[i]) - 1, bs) for i in range(B)], dtype=np.int32)
+        qsl = None
+        n_new = B
+        n_q = B
+    else:
+        slots = []
+        for i in range(B):
+            c = int(lens[i] - chunks[i])
+            slots.extend(_slot(tables, i, p, bs) for p in range(c, int(lens[i])))
+        slots = np.asarray(slots, dtype=np.int32)
+        qsl = np.zeros(B + 1, dtype=np.int32)
+        qsl[1:] = np.cumsum(chunks)
+        n_new = int(qsl[-1])
+        n_q = n_new
+    dtype = spec["dtype"]
+    base = int(seed) * 16
+    row_elems = bs * Hkv * D
+    chunk_rows = max(1, (1 << 26) // row_elems)    # ~64M elements per draw
+    k_cache = _randn((num_blocks, bs, Hkv, D), dtype, device, base + 1, chunk_rows)
+    v_cache = _randn((num_blocks, bs, Hkv, D), dtype, device, base + 2, chunk_rows)
+    key = _randn((n_new, Hkv, D), dtype, device, base + 3)
+    value = _randn((n_new, Hkv, D), dtype, device, base + 4)
+    q = _randn((n_q, Hq, D), dtype, device, base + 5)
+    batch = Batch(spec=spec, kind=spec["kind"], dtype=dtype, num_seqs=B, num_heads=Hq,
+                  num_kv_heads=Hkv, head_dim=D, block_size=bs, num_blocks=num_blocks,
+                  scale=1.0 / math.sqrt(D), context_lens=lens, block_tables=tables,
+                  slot_mapping=slots, token_ids=token_ids, query_start_loc=qsl,
+                  shared_blocks=shared, k_cache=k_cache, v_cache=v_cache, key=key,
+                  value=value, q=q, device=str(device))
+    if poison:
+        poison_unused_rows(batch)
+    return batch
+
+
+def covered_rows(batch):
+    """Boolean [num_blocks][block_size]: rows some context covers."""
+    bs = batch.block_size
+    mask = np.zeros((batch.num_blocks, bs), dtype=bool)
+    for i, L in enumerate(batch.context_lens):
+        j = np.arange(int(L))
+        mask[batch.block_tables[i, j // bs], j % bs] = True
+    return mask
+
+
+def poison_unused_rows(batch):
+    mask = covered_rows(batch)
+    bs = batch.block_size
+    for s in batch.slot_mapping.tolist():
+        if s >= 0:
+            mask[s // bs, s % bs] = False
+    dead = torch.from_numpy(~mask).to(batch.k_cache.device)
+    batch.k_cache[dead] = float("nan")
+    batch.v_cache[dead] = float("nan")
+
+
+# ---------------------------------------------------------------------------
+# host copies for the oracle
+# ---------------------------------------------------------------------------
+
+def to_numpy(t: torch.Tensor):
+    """Host copy; bf16 tensors come back as uint16 bit patterns."""
+    t = t.detach().to("cpu").contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+@dataclass
+class HostBatch:
+    """Host (numpy) copy of the inputs of a subset of sequences."""
+    dtype: str
+    block_size: int
+    scale: float
+    seqs: list
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    block_tables: np.ndarray
+    context_lens: np.ndarray
+    slot_mapping: np.ndarray
+    key: np.ndarray
+    value: np.ndarray
+    q: np.ndarray
+    query_start_loc: np.ndarray | None
+    new_rows: list            # index of each sequence's new rows in the full batch
+
+
+def host_subset(batch: Batch, seqs=None):
+    """Copy the inputs the given sequences depend on to the host.
+
+    Only the blocks those sequences reference are copied; they are renumbered
+    0..n-1 in order of first use, and the tables and slots are rewritten to
+    match. A renumbering of physical blocks does not change any result.
+    """
+    if seqs is None:
+        seqs = list(range(batch.num_seqs))
+    seqs = [int(s) for s in seqs]
+    bs = batch.block_size
+    remap = {}
+    for i in seqs:
+        nb = math.ceil(int(batch.context_lens[i]) / bs)
+        for b in batch.block_tables[i, :nb].tolist():
+            if b not in remap:
+                remap[b] = len(remap)
+    order = torch.tensor(list(remap.keys()), dtype=torch.long, device=batch.k_cache.device)
+    k = to_numpy(batch.k_cache.index_select(0, order)) if len(remap) else None
+    v = to_numpy(batch.v_cache.index_select(0, order)) if len(remap) else None
+    tables = np.full((len(seqs), batch.max_blocks_per_seq), -1, dtype=np.int32)
+    for r, i in enumerate(seqs):
+        nb = math.ceil(int(batch.context_lens[i]) / bs)
+        tables[r, :nb] = [remap[b] for b in batch.block_tables[i, :nb].tolist()]
+    lens = batch.context_lens[seqs].copy()
+    key_all, value_all, q_all = to_numpy(batch.key), to_numpy(batch.value), to_numpy(batch.q)
+    if batch.kind == "decode":
+        rows = [[i] for i in seqs]
+        qsl = None
+        q_rows = seqs
+    else:
+        qsl_full = batch.query_start_loc
+        rows = [list(range(int(qsl_full[i]), int(qsl_full[i + 1]))) for i in seqs]
+        qsl = np.zeros(len(seqs) + 1, dtype=np.int32)
+        qsl[1:] = np.cumsum([len(r) for r in rows])
+        q_rows = [t for r in rows for t in r]
+    flat = [t for r in rows for t in r]
+    slots = []
+    for r, i in enumerate(seqs):
+        for t in rows[r]:
+            s = int(batch.slot_mapping[t])
+            slots.append(remap[s // bs] * bs + s % bs if s >= 0 else -1)
+    return HostBatch(dtype=batch.dtype, block_size=bs, scale=batch.scale, seqs=seqs,
+                     k_cache=k, v_cache=v, block_tables=tables, context_lens=lens,
+                     slot_mapping=np.asarray(slots, dtype=np.int32),
+                     key=key_all[flat], value=value_all[flat], q=q_all[q_rows],
+                     query_start_loc=qsl, new_rows=rows)
+
+
+def spec(config_id, **overrides):
+    """A copy of CONFIGS[config_id] with overrides, tagged with its id."""
+    s = dict(CONFIGS[config_id])
+    s["id"] = config_id
+    s.update(overrides)
+    return s

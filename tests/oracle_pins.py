@@ -1,0 +1,419 @@
+"""Checks that tie the CPU oracle to facts outside itself.
+
+Each pin_* function raises AssertionError when the oracle disagrees with what
+the pages or the mathematics fix: closed forms, a library attention routine,
+invariances of paging (block renumbering, sharing vs duplication), the
+grouped-query/multi-head equivalence, slicing invariance of the split merge,
+the prefill/decode identity, and the rolling hash's closed-form vectors.
+
+The functions look the oracle up through its modules at call time, so a test
+can plant a mistake in the oracle (monkeypatch) and see which pins catch it.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import oracle.attention as oa
+import oracle.prefix_cache as opc
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _paged_from_contiguous(rows_per_seq, block_size, num_blocks, rng, fill=np.nan):
+    """Lay contiguous per-sequence rows into a block pool, block by block
+    (slice copies; no slot arithmetic), with a random block order."""
+    shape = rows_per_seq[0].shape[1:]
+    pool = np.full((num_blocks, block_size) + shape, fill, dtype=rows_per_seq[0].dtype)
+    perm = rng.permutation(num_blocks)
+    nmax = max(math.ceil(len(r) / block_size) for r in rows_per_seq)
+    tables = np.full((len(rows_per_seq), nmax), -1, dtype=np.int64)
+    nxt = 0
+    for i, rows in enumerate(rows_per_seq):
+        for k in range(math.ceil(len(rows) / block_size)):
+            b = int(perm[nxt])
+            nxt += 1
+            part = rows[k * block_size:(k + 1) * block_size]
+            pool[b, :len(part)] = part
+            tables[i, k] = b
+    return pool, tables
+
+
+def _sdpa(q, k, v, scale, causal=False):
+    """torch's attention routine on CPU in fp64. q [H][Lq][D], k/v [H][L][D]."""
+    out = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None],
+        scale=scale, is_causal=causal)
+    return out[0].numpy()
+
+
+def _decode_case(seed=1, lens=(1, 5, 13, 32), Hq=6, Hkv=2, D=16, bs=4, dtype="f32"):
+    rng = _rng(seed)
+    kc = [rng.standard_normal((L, Hkv, D)).astype(np.float32) for L in lens]
+    vc = [rng.standard_normal((L, Hkv, D)).astype(np.float32) for L in lens]
+    nb = sum(math.ceil(L / bs) for L in lens) + 3
+    r2 = _rng(seed + 100)
+    kp, tables = _paged_from_contiguous(kc, bs, nb, r2)
+    vp, tables_v = _paged_from_contiguous(vc, bs, nb, _rng(seed + 100))
+    assert np.array_equal(tables, tables_v)
+    q = rng.standard_normal((len(lens), Hq, D)).astype(np.float32)
+    return dict(q=q, kp=kp, vp=vp, tables=tables, lens=np.array(lens), kc=kc, vc=vc,
+                bs=bs, scale=1.0 / math.sqrt(D), Hq=Hq, Hkv=Hkv, D=D)
+
+
+# ---------------------------------------------------------------------------
+# store / gather
+# ---------------------------------------------------------------------------
+
+def pin_store_bytes():
+    """Stored rows land at slot = flat row index of the [NB*bs] row view;
+    every other byte is untouched; negative slots write nothing."""
+    rng = _rng(2)
+    NB, bs, Hkv, D = 6, 8, 2, 4
+    for dt in (np.uint16, np.float32):
+        if dt is np.uint16:
+            kp = rng.integers(0, 1 << 16, size=(NB, bs, Hkv, D), dtype=np.uint16)
+            vp = rng.integers(0, 1 << 16, size=(NB, bs, Hkv, D), dtype=np.uint16)
+            key = rng.integers(0, 1 << 16, size=(5, Hkv, D), dtype=np.uint16)
+            val = rng.integers(0, 1 << 16, size=(5, Hkv, D), dtype=np.uint16)
+        else:
+            kp = rng.standard_normal((NB, bs, Hkv, D)).astype(np.float32)
+            vp = rng.standard_normal((NB, bs, Hkv, D)).astype(np.float32)
+            key = rng.standard_normal((5, Hkv, D)).astype(np.float32)
+            val = rng.standard_normal((5, Hkv, D)).astype(np.float32)
+        slots = np.array([7, -1, 40, 0, 47], dtype=np.int32)
+        k2, v2 = oa.store_kvcache(kp, vp, key, val, slots, bs)
+        ek = kp.reshape(NB * bs, Hkv, D).copy()
+        ev = vp.reshape(NB * bs, Hkv, D).copy()
+        for t, s in enumerate(slots):
+            if s >= 0:
+                ek[s] = key[t]
+                ev[s] = val[t]
+        assert k2.tobytes() == ek.reshape(kp.shape).tobytes()
+        assert v2.tobytes() == ev.reshape(vp.shape).tobytes()
+        assert kp.tobytes() != k2.tobytes()
+
+
+def pin_gather_inverts_layout():
+    """Gathering through the table returns the contiguous rows that were laid
+    out block by block."""
+    c = _decode_case(seed=3, lens=(1, 4, 9, 17), bs=4)
+    for i, L in enumerate(c["lens"]):
+        got = oa.gather_context(c["kp"], c["tables"][i], L, c["bs"])
+        assert np.array_equal(got, c["kc"][i])
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+
+def pin_decode_vs_sdpa():
+    """Paged decode equals torch's attention over the contiguous rows."""
+    c = _decode_case(seed=4)
+    out = oa.decode(c["q"], c["kp"], c["vp"], c["tables"], c["lens"], c["scale"], c["bs"], "f32")
+    G = c["Hq"] // c["Hkv"]
+    for i, L in enumerate(c["lens"]):
+        k = np.repeat(c["kc"][i].astype(np.float64), G, axis=1).transpose(1, 0, 2)
+        v = np.repeat(c["vc"][i].astype(np.float64), G, axis=1).transpose(1, 0, 2)
+        q = c["q"][i].astype(np.float64)[:, None, :]
+        ref = _sdpa(q, np.ascontiguousarray(k), np.ascontiguousarray(v), c["scale"])[:, 0, :]
+        assert np.max(np.abs(out[i] - ref)) < 1e-12
+
+
+def pin_decode_closed_forms():
+    """L=1 returns v_0 exactly; q=0 or equal keys give the mean value row;
+    a logit raised by 1e3 over the rest returns that row's value."""
+    rng = _rng(5)
+    D, bs = 8, 4
+    # L = 1
+    kp = rng.standard_normal((3, bs, 1, D)).astype(np.float32)
+    vp = rng.standard_normal((3, bs, 1, D)).astype(np.float32)
+    q = rng.standard_normal((1, 1, D)).astype(np.float32)
+    out = oa.decode(q, kp, vp, np.array([[2]]), np.array([1]), 0.3, bs, "f32")
+    assert np.array_equal(out[0, 0], vp[2, 0, 0].astype(np.float64))
+    # q = 0 -> uniform weights over the L rows
+    L = 11
+    rows_k = rng.standard_normal((L, 1, D)).astype(np.float32)
+    rows_v = rng.standard_normal((L, 1, D)).astype(np.float32)
+    kp, tb = _paged_from_contiguous([rows_k], bs, 5, _rng(6))
+    vp, _ = _paged_from_contiguous([rows_v], bs, 5, _rng(6))
+    out = oa.decode(np.zeros((1, 1, D), np.float32), kp, vp, tb, np.array([L]), 0.5, bs, "f32")
+    assert np.max(np.abs(out[0, 0] - rows_v[:, 0].astype(np.float64).mean(0))) < 1e-14
+    # equal keys -> uniform weights as well
+    same = np.repeat(rows_k[:1], L, axis=0)
+    kp2, _ = _paged_from_contiguous([same], bs, 5, _rng(6))
+    qn = rng.standard_normal((1, 1, D)).astype(np.float32)
+    out = oa.decode(qn, kp2, vp, tb, np.array([L]), 0.5, bs, "f32")
+    assert np.max(np.abs(out[0, 0] - rows_v[:, 0].astype(np.float64).mean(0))) < 1e-14
+    # one dominant logit: key 7 = q * c with scale*c*|q|^2 = 1e3 + others
+    qd = np.zeros((1, 1, D), np.float32)
+    qd[0, 0, 0] = 1.0
+    ks = np.zeros((L, 1, D), np.float32)
+    ks[:, 0, 0] = rng.standard_normal(L).astype(np.float32)
+    ks[7, 0, 0] = 2000.0
+    kp3, _ = _paged_from_contiguous([ks], bs, 5, _rng(6))
+    out = oa.decode(qd, kp3, vp, tb, np.array([L]), 1.0, bs, "f32")
+    assert np.max(np.abs(out[0, 0] - rows_v[7, 0].astype(np.float64))) < 1e-12
+
+
+def pin_decode_block_permutation():
+    """Renumbering physical blocks (and rewriting the tables) changes nothing,
+    bit for bit."""
+    c = _decode_case(seed=7)
+    out = oa.decode(c["q"], c["kp"], c["vp"], c["tables"], c["lens"], c["scale"], c["bs"], "f32")
+    nb = c["kp"].shape[0]
+    perm = _rng(8).permutation(nb)           # new id of old block b is perm[b]
+    kp2 = np.empty_like(c["kp"])
+    vp2 = np.empty_like(c["vp"])
+    kp2[perm] = c["kp"]
+    vp2[perm] = c["vp"]
+    t2 = np.where(c["tables"] >= 0, perm[np.maximum(c["tables"], 0)], -1)
+    out2 = oa.decode(c["q"], kp2, vp2, t2, c["lens"], c["scale"], c["bs"], "f32")
+    assert out.tobytes() == out2.tobytes()
+
+
+def pin_decode_sharing_equals_duplication():
+    """Two sequences reading one shared prefix block give the same result as
+    when each owns a copy of it."""
+    rng = _rng(9)
+    bs, Hkv, D = 4, 2, 8
+    prefix_k = rng.standard_normal((bs, Hkv, D)).astype(np.float32)
+    prefix_v = rng.standard_normal((bs, Hkv, D)).astype(np.float32)
+    tails_k = [rng.standard_normal((n, Hkv, D)).astype(np.float32) for n in (3, 6)]
+    tails_v = [rng.standard_normal((n, Hkv, D)).astype(np.float32) for n in (3, 6)]
+    nb = 8
+    kp = np.full((nb, bs, Hkv, D), np.nan, np.float32)
+    vp = np.full((nb, bs, Hkv, D), np.nan, np.float32)
+    kp[5], vp[5] = prefix_k, prefix_v
+    kp[1, :3], vp[1, :3] = tails_k[0], tails_v[0]
+    kp[6], vp[6] = tails_k[1][:4], tails_v[1][:4]
+    kp[2, :2], vp[2, :2] = tails_k[1][4:], tails_v[1][4:]
+    shared = np.array([[5, 1, -1], [5, 6, 2]])
+    kd, vd = kp.copy(), vp.copy()
+    kd[0], vd[0] = prefix_k, prefix_v       # private copy for sequence 1
+    dup = np.array([[5, 1, -1], [0, 6, 2]])
+    lens = np.array([bs + 3, bs + 6])
+    q = rng.standard_normal((2, 4, D)).astype(np.float32)
+    a = oa.decode(q, kp, vp, shared, lens, 0.35, bs, "f32")
+    b = oa.decode(q, kd, vd, dup, lens, 0.35, bs, "f32")
+    assert a.tobytes() == b.tobytes()
+    assert np.isfinite(a).all()
+
+
+def pin_gqa_equals_expanded_mha():
+    """Grouped-query decode equals multi-head decode with each KV head
+    repeated for the query heads of its group (heads h*G .. h*G+G-1)."""
+    c = _decode_case(seed=10, Hq=6, Hkv=2)
+    G = 3
+    out = oa.decode(c["q"], c["kp"], c["vp"], c["tables"], c["lens"], c["scale"], c["bs"], "f32")
+    kp = np.repeat(c["kp"], G, axis=2)
+    vp = np.repeat(c["vp"], G, axis=2)
+    out2 = oa.decode(c["q"], kp, vp, c["tables"], c["lens"], c["scale"], c["bs"], "f32")
+    assert out.tobytes() == out2.tobytes()
+    # and the groups really differ (a mapping h % Hkv would read other heads)
+    assert np.max(np.abs(out[:, 1] - out[:, 3])) > 1e-3
+
+
+def pin_partition_invariance():
+    """Slicing the context and merging slice states gives the unsliced
+    result to fp64 rounding, for any slice length."""
+    c = _decode_case(seed=11, lens=(1, 7, 16, 33))
+    ref = oa.decode(c["q"], c["kp"], c["vp"], c["tables"], c["lens"], c["scale"], c["bs"], "f32")
+    for P in (1, 3, 4, 7, 16, 1000):
+        got = oa.decode_partitioned(c["q"], c["kp"], c["vp"], c["tables"], c["lens"],
+                                    c["scale"], c["bs"], "f32", P)
+        assert np.max(np.abs(got - ref)) < 1e-12, P
+
+
+def pin_merge_of_disjoint_states():
+    """merge_states of two slices equals attention over their union (also
+    when one slice's maximum is far below the other's)."""
+    rng = _rng(12)
+    D = 6
+    q = rng.standard_normal(D)
+    k1, k2 = rng.standard_normal((5, D)), rng.standard_normal((4, D)) + 3 * q
+    v1, v2 = rng.standard_normal((5, D)), rng.standard_normal((4, D))
+    s1 = oa.partition_state(q, k1, v1, 0.9)
+    s2 = oa.partition_state(q, k2, v2, 0.9)
+    got = oa.merge_states([s1, s2])
+    ref = _sdpa(q[None, None], np.concatenate([k1, k2])[None], np.concatenate([v1, v2])[None], 0.9)[0, 0]
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def pin_bf16_widening():
+    """bf16 bit patterns widen to the float32 values with the same top 16
+    bits (0x3F80 is 1.0, 0xC000 is -2.0, 0x0001 the smallest subnormal)."""
+    bits = np.array([0x3F80, 0xC000, 0x0001, 0x7F7F, 0x0000, 0x8000], dtype=np.uint16)
+    got = oa.widen(bits, "bf16")
+    ref = np.array([1.0, -2.0, 2.0 ** -133, (2 - 2 ** -7) * 2.0 ** 127, 0.0, -0.0])
+    assert np.array_equal(got, ref)
+    assert np.signbit(got[5])
+    t = torch.tensor([0.1, -3.7, 1e-3, 65504.0], dtype=torch.float32).to(torch.bfloat16)
+    via_torch = t.to(torch.float64).numpy()
+    assert np.array_equal(oa.widen(t.view(torch.int16).numpy().view(np.uint16), "bf16"), via_torch)
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+
+def _prefill_case(seed, cached, chunk, Hq=4, Hkv=2, D=8, bs=4):
+    rng = _rng(seed)
+    lens = [c + n for c, n in zip(cached, chunk)]
+    kc = [rng.standard_normal((L, Hkv, D)).astype(np.float32) for L in lens]
+    vc = [rng.standard_normal((L, Hkv, D)).astype(np.float32) for L in lens]
+    nb = sum(math.ceil(L / bs) for L in lens) + 2
+    kp, tables = _paged_from_contiguous(kc, bs, nb, _rng(seed + 1))
+    vp, _ = _paged_from_contiguous(vc, bs, nb, _rng(seed + 1))
+    qsl = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int64)
+    q = rng.standard_normal((int(qsl[-1]), Hq, D)).astype(np.float32)
+    return dict(q=q, kp=kp, vp=vp, tables=tables, lens=np.array(lens), qsl=qsl, kc=kc, vc=vc,
+                bs=bs, scale=1.0 / math.sqrt(D), Hq=Hq, Hkv=Hkv, D=D, cached=cached, chunk=chunk)
+
+
+def pin_prefill_row_is_decode():
+    """Prefill row t of a sequence equals decode of that row's query over
+    the first c + t + 1 tokens, bit for bit."""
+    c = _prefill_case(13, cached=[0, 5, 9], chunk=[3, 4, 6])
+    out = oa.prefill(c["q"], c["kp"], c["vp"], c["tables"], c["qsl"], c["lens"], c["scale"], c["bs"], "f32")
+    for i in range(3):
+        for t in range(c["chunk"][i]):
+            r = int(c["qsl"][i]) + t
+            one = oa.decode(c["q"][r:r + 1], c["kp"], c["vp"], c["tables"][i:i + 1],
+                            np.array([c["cached"][i] + t + 1]), c["scale"], c["bs"], "f32")
+            assert out[r].tobytes() == one[0].tobytes()
+
+
+def pin_prefill_c0_is_causal_sdpa():
+    """With nothing cached, prefill is ordinary causal attention."""
+    c = _prefill_case(14, cached=[0, 0], chunk=[7, 12])
+    out = oa.prefill(c["q"], c["kp"], c["vp"], c["tables"], c["qsl"], c["lens"], c["scale"], c["bs"], "f32")
+    G = c["Hq"] // c["Hkv"]
+    for i in range(2):
+        rows = slice(int(c["qsl"][i]), int(c["qsl"][i + 1]))
+        q = c["q"][rows].astype(np.float64).transpose(1, 0, 2)
+        k = np.repeat(c["kc"][i].astype(np.float64), G, axis=1).transpose(1, 0, 2)
+        v = np.repeat(c["vc"][i].astype(np.float64), G, axis=1).transpose(1, 0, 2)
+        ref = _sdpa(np.ascontiguousarray(q), np.ascontiguousarray(k), np.ascontiguousarray(v),
+                    c["scale"], causal=True).transpose(1, 0, 2)
+        assert np.max(np.abs(out[rows] - ref)) < 1e-12
+
+
+def pin_prefill_chunk_split():
+    """Running a chunk as two smaller chunks (the second with the first one
+    counted as cached) gives the same rows, bit for bit."""
+    c = _prefill_case(15, cached=[6], chunk=[9])
+    full = oa.prefill(c["q"], c["kp"], c["vp"], c["tables"], c["qsl"], c["lens"], c["scale"], c["bs"], "f32")
+    n1 = 4
+    first = oa.prefill(c["q"][:n1], c["kp"], c["vp"], c["tables"], np.array([0, n1]),
+                       np.array([6 + n1]), c["scale"], c["bs"], "f32")
+    second = oa.prefill(c["q"][n1:], c["kp"], c["vp"], c["tables"], np.array([0, 9 - n1]),
+                        np.array([15]), c["scale"], c["bs"], "f32")
+    assert np.concatenate([first, second]).tobytes() == full.tobytes()
+
+
+def pin_prefill_rows_subset():
+    """The sampled-row form returns the same values as the full chunk."""
+    c = _prefill_case(16, cached=[2, 7], chunk=[5, 3])
+    full = oa.prefill(c["q"], c["kp"], c["vp"], c["tables"], c["qsl"], c["lens"], c["scale"], c["bs"], "f32")
+    rows = [(0, 0), (4, 3), (5, 1), (7, 2)]
+    got = oa.prefill_rows(c["q"], c["kp"], c["vp"], c["tables"], c["qsl"], c["lens"], c["scale"],
+                          c["bs"], "f32", rows)
+    for r, (tok, h) in enumerate(rows):
+        assert got[r].tobytes() == full[tok, h].tobytes()
+    d = _decode_case(seed=17)
+    fulld = oa.decode(d["q"], d["kp"], d["vp"], d["tables"], d["lens"], d["scale"], d["bs"], "f32")
+    rows = [(0, 0), (3, 5), (2, 2)]
+    got = oa.decode_rows(d["q"], d["kp"], d["vp"], d["tables"], d["lens"], d["scale"], d["bs"], "f32", rows)
+    for r, (i, h) in enumerate(rows):
+        assert got[r].tobytes() == fulld[i, h].tobytes()
+
+
+# ---------------------------------------------------------------------------
+# rolling hash and allocation
+# ---------------------------------------------------------------------------
+
+def pin_hash_vectors():
+    """Closed-form values of h <- (31*h + t) mod 2**32."""
+    for h in (0, 1, 12345, 0xFFFFFFFF):
+        assert opc.compute_hash([], h) == h
+    assert opc.compute_hash([1, 2, 3], 0) == 1 * 31 ** 2 + 2 * 31 + 3 == 1026
+    assert opc.compute_hash([0], 0xFFFFFFFF) == (2 ** 32 - 31) == 4294967265
+    ref = sum(t * pow(31, 255 - t, 2 ** 32) for t in range(256)) % 2 ** 32
+    assert opc.compute_hash(range(256), 0) == ref == 452919424
+
+
+def pin_hash_polynomial_and_chaining():
+    """The fold equals the polynomial h*31^n + sum_k t_k 31^(n-1-k) mod 2^32,
+    and hashing a+b equals hashing b from the hash of a."""
+    rng = _rng(18)
+    for n in (1, 2, 17, 256):
+        toks = rng.integers(0, 50257, size=n).tolist()
+        h0 = int(rng.integers(0, 2 ** 32))
+        poly = (h0 * pow(31, n, 2 ** 32) + sum(t * pow(31, n - 1 - k, 2 ** 32)
+                                               for k, t in enumerate(toks))) % 2 ** 32
+        assert opc.compute_hash(toks, h0) == poly
+        cut = n // 2
+        assert opc.compute_hash(toks[cut:], opc.compute_hash(toks[:cut], h0)) == opc.compute_hash(toks, h0)
+
+
+def pin_allocator_sharing_small():
+    """Three sequences, two with a common two-block prefix: the prefix blocks
+    are shared with two references; partial blocks are never shared; freeing
+    returns every block and forgets every hash."""
+    bs = 4
+    common = [5, 6, 7, 8, 9, 10, 11, 12]
+    seqs = [common + [1, 2], [40, 41, 42, 43, 44], common + [1, 2]]
+    alloc = opc.PrefixBlockAllocator(list(range(10)), bs)
+    tables = [alloc.allocate(s) for s in seqs]
+    assert tables[0] == [0, 1, 2]
+    assert tables[1] == [3, 4]
+    assert tables[2] == [0, 1, 5]            # same partial tail, still private
+    rc = alloc.ref_counts()
+    assert rc[0] == 2 and rc[1] == 2 and rc[2] == 1 and rc[5] == 1
+    assert sum(rc.values()) == sum(len(t) for t in tables)
+    # a block of equal tokens after a different prefix is not shared
+    t4 = alloc.allocate([50, 51, 52, 53] + common[4:8])
+    assert t4[1] != 1
+    for t in tables + [t4]:
+        alloc.free_table(t)
+    assert alloc.ref_counts() == {} and not alloc.hash_to_block_id
+    assert sorted(alloc.free) == list(range(10))
+
+
+def pin_allocator_matches_structure(structure, block_size, num_sharers, prefix_tokens):
+    """The hash-sharing allocator, fed the drawn token ids and free list,
+    reproduces the drawn block tables; reference counts add up."""
+    alloc = opc.PrefixBlockAllocator(structure["free_list"].tolist(), block_size)
+    lens = structure["context_lens"]
+    logical = 0
+    for i, ids in enumerate(structure["token_ids"]):
+        t = alloc.allocate(ids.tolist())
+        nb = math.ceil(int(lens[i]) / block_size)
+        assert t == structure["block_tables"][i, :nb].tolist(), i
+        logical += nb
+    rc = alloc.ref_counts()
+    assert sum(rc.values()) == logical
+    pb = prefix_tokens // block_size
+    shared = [b for b, n in rc.items() if n > 1]
+    if num_sharers > 1:
+        assert sorted(shared) == sorted(structure["shared_blocks"])
+        assert all(rc[b] == num_sharers for b in shared) and len(shared) == pb
+    else:
+        assert not shared
+    assert len(rc) == logical - max(0, num_sharers - 1) * pb
+
+
+ALL_PINS = [
+    pin_store_bytes, pin_gather_inverts_layout, pin_decode_vs_sdpa, pin_decode_closed_forms,
+    pin_decode_block_permutation, pin_decode_sharing_equals_duplication,
+    pin_gqa_equals_expanded_mha, pin_partition_invariance, pin_merge_of_disjoint_states,
+    pin_bf16_widening, pin_prefill_row_is_decode, pin_prefill_c0_is_causal_sdpa,
+    pin_prefill_chunk_split, pin_prefill_rows_subset, pin_hash_vectors,
+    pin_hash_polynomial_and_chaining, pin_allocator_sharing_small,
+]
