@@ -1,0 +1,244 @@
+"""Benchmark: paged decode on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--no-extra]
+
+A step is one pass of the decode hot path over one batch: pa_store_kvcache
+writes the new token's K/V row of every sequence, then pa_decode attends over
+the whole paged context (split into partitions, merged in the same launch).
+The default workload is the bf16 MHA decode batch (64 sequences, 12 heads,
+head_dim 64, block 256, context lengths uniform in [512, 4096]). Several
+independently drawn batches (each with its own pool) are resident in HBM and
+the steps cycle through them, so consecutive steps never find their K/V in the
+256 MB last-level cache.
+
+Prints ONE JSON line. `value` is decode tokens/s (sequences x steps / timed
+seconds). `roofline` covers the decode kernel: algorithmic K+V bytes per launch
+over its average duration, from HIP events recorded on the launch stream
+around each timed launch. `cpu_baseline` is the CPU oracle on a bounded sample
+of the same workload, single-threaded. `extra` reports the other workloads
+(GQA decode with shared prefix, GQA decode at 512 sequences, chunked prefill)
+measured the same way.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from paged_kv_cache_439_amd import binding as pa  # noqa: E402
+from paged_kv_cache_439_amd import workloads as wl  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+class DecodeSet:
+    """R resident batches of one decode workload, with device-side arrays."""
+
+    def __init__(self, cfg, rotations, device):
+        self.spec = wl.spec(cfg)
+        self.P = self.spec.get("partition_size", 0)
+        self.batches = []
+        for r in range(rotations):
+            b = wl.make_batch(self.spec, device=device, seed=wl.SEED_BASE + cfg + 1000 * r)
+            arrs = dict(slots=torch.from_numpy(b.slot_mapping).to(device),
+                        tables=torch.from_numpy(b.block_tables).to(device),
+                        lens=torch.from_numpy(b.context_lens).to(device),
+                        out=torch.empty_like(b.q))
+            self.batches.append((b, arrs))
+        b0 = self.batches[0][0]
+        maxL = max(b.max_context_len for b, _ in self.batches)
+        self.max_context = maxL
+        self.ws = pa.decode_workspace(b0.num_seqs, b0.num_heads, b0.num_kv_heads, b0.head_dim,
+                                      maxL, self.P, device)
+        self.kv_bytes = [b.kv_bytes(unique=True) for b, _ in self.batches]
+        self.kv_bytes_logical = [b.kv_bytes(unique=False) for b, _ in self.batches]
+
+    def step(self, i, ev=None):
+        b, a = self.batches[i % len(self.batches)]
+        pa.pa_store_kvcache(b.key, b.value, b.k_cache, b.v_cache, a["slots"])
+        if ev is not None:
+            ev[0].record()
+        pa.pa_decode(a["out"], b.q, b.k_cache, b.v_cache, a["tables"], a["lens"],
+                     b.max_context_len, b.scale, self.P, self.ws)
+        if ev is not None:
+            ev[1].record()
+
+
+def time_decode(ds, steps, warmup):
+    """Returns (seconds for `steps` steps, mean decode-kernel ms, bytes/launch)."""
+    for i in range(warmup):
+        ds.step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ds.step(i, evs[i])
+    torch.cuda.synchronize()
+    secs = time.perf_counter() - t0
+    kms = [s.elapsed_time(e) for s, e in evs]
+    nbytes = [ds.kv_bytes[i % len(ds.batches)] for i in range(steps)]
+    return secs, float(np.mean(kms)), float(np.mean(nbytes)), kms
+
+
+def bench_prefill(steps, warmup, device):
+    sp = wl.spec(4)
+    b = wl.make_batch(sp, device=device)
+    slots = torch.from_numpy(b.slot_mapping).to(device)
+    tables = torch.from_numpy(b.block_tables).to(device)
+    qsl = torch.from_numpy(b.query_start_loc).to(device)
+    lens = torch.from_numpy(b.context_lens).to(device)
+    out = torch.empty_like(b.q)
+    flops = 0
+    for i in range(b.num_seqs):
+        n = int(b.query_start_loc[i + 1] - b.query_start_loc[i])
+        c = int(b.context_lens[i]) - n
+        flops += 4 * b.head_dim * b.num_heads * (n * c + n * (n + 1) // 2)
+    pa.pa_store_kvcache(b.key, b.value, b.k_cache, b.v_cache, slots)
+
+    def run():
+        pa.pa_prefill_chunk(out, b.q, b.k_cache, b.v_cache, tables, qsl, lens, b.max_query_len,
+                            b.max_context_len, b.scale)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for s, e in evs:
+        s.record()
+        run()
+        e.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([s.elapsed_time(e) for s, e in evs]))
+    tflops = flops / (ms * 1e-3) / 1e12
+    return dict(workload=sp["name"], kernel_ms=round(ms, 4), gflop=round(flops / 1e9, 2),
+                tflops=round(tflops, 1), frac_of_bf16_mfma_peak=round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+                tokens_per_s=round(int(b.query_start_loc[-1]) / (ms * 1e-3), 1))
+
+
+def cpu_baseline(ds, budget_s=12.0):
+    """The CPU oracle (store + decode, fp64), single-threaded, on whole
+    sequences of the first batch until about budget_s seconds have passed."""
+    import oracle.attention as oa
+    from threadpoolctl import threadpool_limits
+    b = ds.batches[0][0]
+    hb = wl.host_subset(b)
+    done = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s:
+            kp, vp = oa.store_kvcache(hb.k_cache, hb.v_cache, hb.key, hb.value, hb.slot_mapping,
+                                      b.block_size)
+            for i in range(b.num_seqs):
+                oa.decode(hb.q[i:i + 1], kp, vp, hb.block_tables[i:i + 1], hb.context_lens[i:i + 1],
+                          b.scale, b.block_size, b.dtype)
+                done += 1
+                if time.perf_counter() - t0 >= budget_s:
+                    break
+    secs = time.perf_counter() - t0
+    return dict(value=round(done / secs, 2), unit="tokens/s", cores=1, kind="oracle",
+                sample=f"{done} sequences of the first batch (mean context "
+                       f"{float(b.context_lens.mean()):.0f} tokens), store+decode in fp64, "
+                       f"{secs:.1f} s on 1 thread")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 5])
+    ap.add_argument("--rotations", type=int, default=4)
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    pa.load_library()
+
+    log(f"building workload {args.workload} x{args.rotations}")
+    ds = DecodeSet(args.workload, args.rotations, dev)
+    b0 = ds.batches[0][0]
+    log("timing")
+    secs, kms, kbytes, _ = time_decode(ds, args.steps, args.warmup)
+    tokens = b0.num_seqs * args.steps
+    achieved = kbytes / (kms * 1e-3) / 1e9
+    line = {
+        "metric": "paged-decode tokens/s + achieved KV GB/s as % of MI355X HBM peak",
+        "value": round(tokens / secs, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(secs * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": b0.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": ds.spec["name"],
+            "num_seqs": b0.num_seqs, "num_heads": b0.num_heads, "num_kv_heads": b0.num_kv_heads,
+            "head_dim": b0.head_dim, "block_size": b0.block_size,
+            "context_lens": "uniform[512,4096]" if args.workload == 2 else str(ds.spec["lens"]),
+            "partition_size": ds.P, "rotating_batches": args.rotations,
+            "step": "store_kvcache(new rows) + decode",
+        },
+        "roofline": {
+            "bound": "hbm", "kernel": "paged_decode_kernel",
+            "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel_ms": round(kms, 4), "bytes_per_launch": int(kbytes),
+        },
+    }
+    if not args.no_extra:
+        extra = {}
+        for cfg in (2, 3, 5):
+            if cfg == args.workload:
+                continue
+            log(f"extra workload {cfg}")
+            d = DecodeSet(cfg, 2, dev)
+            s, ms, nb, _ = time_decode(d, 30, 5)
+            bb = d.batches[0][0]
+            extra[d.spec["name"]] = dict(
+                tokens_per_s=round(bb.num_seqs * 30 / s, 1), kernel_ms=round(ms, 4),
+                kv_gbs=round(nb / (ms * 1e-3) / 1e9, 1),
+                frac_of_hbm_peak=round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                bytes_per_launch=int(nb), partition_size=d.P,
+                logical_bytes_per_launch=int(np.mean(d.kv_bytes_logical)))
+            del d
+            torch.cuda.empty_cache()
+        log("extra prefill")
+        extra["prefill"] = bench_prefill(20, 3, dev)
+        line["extra"] = extra
+    if not args.no_cpu:
+        log("cpu baseline")
+        line["cpu_baseline"] = cpu_baseline(ds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

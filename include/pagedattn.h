@@ -117,16 +117,15 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
  *
  * partition_size > 0 splits each context into slices of that many tokens
  * (a multiple of 16); every slice yields an fp32 (max, sum, weighted values)
- * state in the workspace and the last slice of a (sequence, head group) to
- * finish merges them into out, all in one launch. partition_size == 0
- * attends over whole contexts. The result does not depend on the split
+ * state in the workspace, and a second kernel on the same stream merges the
+ * states of each (sequence, head) into out. partition_size == 0 attends over
+ * whole contexts in one kernel. The result does not depend on the split
  * beyond fp32 rounding.
  *
  * workspace: device memory of at least pa_decode_workspace_size(...) bytes,
- * 256-byte aligned, ZERO-FILLED before its first use; every completed call
- * leaves it zero-filled again, so it can be reused by later calls of any
- * shape without clearing. Calls sharing a workspace must not overlap in
- * time (same stream, or synchronised). May be NULL when the size is 0.
+ * 256-byte aligned; its contents on entry do not matter and are scratch
+ * afterwards. Calls sharing a workspace must not overlap in time (same
+ * stream, or synchronised). May be NULL when the size is 0.
  */
 pa_status pa_decode(void* out, const void* q,
                     const void* k_cache, const void* v_cache,

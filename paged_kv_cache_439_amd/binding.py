@@ -138,12 +138,13 @@ def pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, max_co
 
 def decode_workspace(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
                      partition_size, device):
-    """A zero-filled workspace of the size pa_decode needs (None if 0)."""
+    """A workspace of the size pa_decode needs (None if 0); its contents do
+    not matter."""
     n = pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
                                  partition_size)
     if n == 0:
         return None
-    return torch.zeros(n, dtype=torch.uint8, device=device)
+    return torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,

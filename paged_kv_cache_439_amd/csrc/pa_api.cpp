@@ -1,0 +1,219 @@
+// C-ABI entry points of libpagedattn: argument validation on the host, then
+// the kernel launchers. No exception crosses the interface; every failure is
+// a pa_status plus a per-thread message (pa_last_error).
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/pagedattn.h"
+#include "pa_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+pa_status fail(pa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+pa_status ok() {
+  g_last_error[0] = '\0';
+  return PA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool pow2(int32_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int elem_size(pa_dtype d) { return d == PA_BF16 ? 2 : 4; }
+
+pa_status check_dtype(pa_dtype d) {
+  if (d != PA_F32 && d != PA_BF16) return fail(PA_ERR_INVALID_ARG, "unknown dtype %d", (int)d);
+  return PA_OK;
+}
+
+// Shape checks shared by decode and prefill.
+pa_status check_attention_shapes(int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t num_blocks,
+                                 int32_t max_blocks_per_seq, int32_t max_context_len) {
+  if (num_heads <= 0 || num_kv_heads <= 0)
+    return fail(PA_ERR_INVALID_ARG, "num_heads=%d num_kv_heads=%d must be positive", num_heads,
+                num_kv_heads);
+  if (num_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID_ARG, "num_heads=%d is not a multiple of num_kv_heads=%d",
+                num_heads, num_kv_heads);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "head_dim=%d (supported: 64, 128)", head_dim);
+  if (!pow2(block_size) || block_size < 8 || block_size > 1024)
+    return fail(PA_ERR_UNSUPPORTED, "block_size=%d (supported: powers of two in [8, 1024])",
+                block_size);
+  if (num_blocks <= 0) return fail(PA_ERR_INVALID_ARG, "num_blocks=%d must be positive", num_blocks);
+  if (max_blocks_per_seq <= 0)
+    return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq=%d must be positive", max_blocks_per_seq);
+  if (max_context_len <= 0)
+    return fail(PA_ERR_INVALID_ARG, "max_context_len=%d must be positive", max_context_len);
+  if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
+    return fail(PA_ERR_INVALID_ARG, "max_context_len=%d exceeds max_blocks_per_seq*block_size=%lld",
+                max_context_len, (long long)max_blocks_per_seq * block_size);
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
+    case PA_ERR_HIP: return "PA_ERR_HIP";
+  }
+  return "PA_UNKNOWN_STATUS";
+}
+
+const char* pa_last_error(void) { return g_last_error; }
+
+pa_status pa_store_kvcache(const void* key, const void* value, int64_t key_tok_stride,
+                           int64_t value_tok_stride, void* k_cache, void* v_cache,
+                           const int32_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                           pa_dtype dtype, void* stream) {
+  try {
+    if (pa_status st = check_dtype(dtype)) return st;
+    if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens=%d is negative", num_tokens);
+    if (num_tokens == 0) return ok();
+    if (!key || !value || !k_cache || !v_cache || !slot_mapping)
+      return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+    if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+      return fail(PA_ERR_INVALID_ARG, "num_kv_heads, head_dim, block_size, num_blocks must be positive");
+    const int e = elem_size(dtype);
+    const int64_t row_elems = (int64_t)num_kv_heads * head_dim;
+    const int64_t row_bytes = row_elems * e;
+    if (row_bytes % 16 != 0 || row_bytes > (1 << 20))
+      return fail(PA_ERR_UNSUPPORTED, "row of %lld bytes (needs a multiple of 16, at most 1 MiB)",
+                  (long long)row_bytes);
+    if (key_tok_stride < row_elems || value_tok_stride < row_elems)
+      return fail(PA_ERR_INVALID_ARG, "token strides (%lld, %lld) below a row of %lld elements",
+                  (long long)key_tok_stride, (long long)value_tok_stride, (long long)row_elems);
+    if ((key_tok_stride * e) % 16 || (value_tok_stride * e) % 16)
+      return fail(PA_ERR_UNSUPPORTED, "token strides must be multiples of 16 bytes");
+    if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(slot_mapping, 4))
+      return fail(PA_ERR_UNSUPPORTED, "pointers must be 16-byte aligned (slot_mapping 4-byte)");
+    const int64_t num_slots = (int64_t)num_blocks * block_size;
+    if (num_slots > INT32_MAX)
+      return fail(PA_ERR_INVALID_ARG, "num_blocks*block_size=%lld exceeds int32 slots",
+                  (long long)num_slots);
+    if ((int64_t)num_tokens * (row_bytes / 16) > (int64_t)INT32_MAX)
+      return fail(PA_ERR_UNSUPPORTED, "too many tokens in one call");
+    pa::StoreArgs a{key, value, key_tok_stride * e, value_tok_stride * e, k_cache, v_cache,
+                    slot_mapping, num_tokens, (int32_t)row_bytes, num_slots};
+    const hipError_t err = pa::launch_store(a, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(PA_ERR_HIP, "store launch: %s", hipGetErrorString(err));
+    return ok();
+  } catch (...) {
+    return fail(PA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads ||
+      head_dim <= 0 || max_context_len <= 0 || partition_size < 0)
+    return 0;
+  return pa::plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
+                         partition_size)
+      .total_bytes;
+}
+
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                    int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                    float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+                    pa_dtype dtype, void* stream) {
+  try {
+    if (pa_status st = check_dtype(dtype)) return st;
+    if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs=%d is negative", num_seqs);
+    if (num_seqs == 0) return ok();
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+      return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+    if (pa_status st = check_attention_shapes(num_heads, num_kv_heads, head_dim, block_size,
+                                              num_blocks, max_blocks_per_seq, max_context_len))
+      return st;
+    if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs=%d above 65535", num_seqs);
+    if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+    if (partition_size < 0 || partition_size % 16 != 0)
+      return fail(PA_ERR_INVALID_ARG, "partition_size=%d must be 0 or a positive multiple of 16",
+                  partition_size);
+    if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(block_tables, 4) || !aligned(context_lens, 4))
+      return fail(PA_ERR_UNSUPPORTED, "pointers must be 16-byte aligned (int arrays 4-byte)");
+    const pa::DecodePlan plan = pa::plan_decode(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                max_context_len, partition_size);
+    if ((plan.units + 3) / 4 > 65535) return fail(PA_ERR_UNSUPPORTED, "too many heads");
+    if (plan.total_bytes) {
+      if (!workspace)
+        return fail(PA_ERR_WORKSPACE, "split decode needs a workspace of %zu bytes",
+                    plan.total_bytes);
+      if (workspace_bytes < plan.total_bytes)
+        return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes,
+                    plan.total_bytes);
+      if (!aligned(workspace, 256)) return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    }
+    pa::DecodeArgs a{out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
+                     num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                     max_context_len, scale, partition_size, workspace, dtype == PA_BF16};
+    const hipError_t err = pa::launch_decode(a, plan, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(PA_ERR_HIP, "decode launch: %s", hipGetErrorString(err));
+    return ok();
+  } catch (...) {
+    return fail(PA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+pa_status pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* query_start_loc,
+                           const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_query_len,
+                           int32_t max_context_len, float scale, pa_dtype dtype, void* stream) {
+  try {
+    if (pa_status st = check_dtype(dtype)) return st;
+    if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs=%d is negative", num_seqs);
+    if (num_seqs == 0) return ok();
+    if (dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "prefill is implemented for bf16 only");
+    if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start_loc || !context_lens)
+      return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+    if (pa_status st = check_attention_shapes(num_heads, num_kv_heads, head_dim, block_size,
+                                              num_blocks, max_blocks_per_seq, max_context_len))
+      return st;
+    if (max_query_len <= 0 || max_query_len > max_context_len)
+      return fail(PA_ERR_INVALID_ARG, "max_query_len=%d must be in [1, max_context_len=%d]",
+                  max_query_len, max_context_len);
+    if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs=%d above 65535", num_seqs);
+    if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+    if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(block_tables, 4) || !aligned(query_start_loc, 4) || !aligned(context_lens, 4))
+      return fail(PA_ERR_UNSUPPORTED, "pointers must be 16-byte aligned (int arrays 4-byte)");
+    if ((int64_t)num_heads > 65535) return fail(PA_ERR_UNSUPPORTED, "too many heads");
+    pa::PrefillArgs a{out, q, k_cache, v_cache, block_tables, query_start_loc, context_lens,
+                      num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                      max_blocks_per_seq, max_query_len, max_context_len, scale};
+    const hipError_t err = pa::launch_prefill(a, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(PA_ERR_HIP, "prefill launch: %s", hipGetErrorString(err));
+    return ok();
+  } catch (...) {
+    return fail(PA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+}  // extern "C"

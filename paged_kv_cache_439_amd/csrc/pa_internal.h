@@ -1,0 +1,69 @@
+// Launch interface between the C-ABI layer (pa_api.cpp) and the kernels.
+// Every argument here has already been validated on the host.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+struct StoreArgs {
+  const void* key;
+  const void* value;
+  int64_t key_stride_bytes;
+  int64_t value_stride_bytes;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* slot_mapping;
+  int32_t num_tokens;
+  int32_t row_bytes;       // num_kv_heads * head_dim * element size
+  int64_t num_slots;       // num_blocks * block_size
+};
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int32_t num_seqs, num_heads, num_kv_heads, head_dim;
+  int32_t block_size, num_blocks, max_blocks_per_seq, max_context_len;
+  float scale;
+  int32_t partition_size;  // 0: no split
+  void* workspace;
+  bool bf16;
+};
+
+struct PrefillArgs {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* query_start_loc;
+  const int32_t* context_lens;
+  int32_t num_seqs, num_heads, num_kv_heads, head_dim;
+  int32_t block_size, num_blocks, max_blocks_per_seq, max_query_len, max_context_len;
+  float scale;
+};
+
+// Decode work split, shared by the workspace-size query and the launcher.
+struct DecodePlan {
+  int32_t group;           // query heads per KV head
+  int32_t heads_per_unit;  // query heads one wave handles (divides group)
+  int32_t units;           // waves per (sequence, partition) = Hkv * group / heads_per_unit
+  int32_t partition;       // tokens per partition (> 0)
+  int32_t max_parts;       // partitions of the longest context
+  size_t acc_bytes, ml_bytes, total_bytes;  // workspace regions (0 if unsplit)
+};
+
+DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t max_context_len, int32_t partition_size);
+
+hipError_t launch_store(const StoreArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace pa

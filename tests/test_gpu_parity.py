@@ -1,0 +1,305 @@
+"""GPU parity: the HIP library through its C ABI against the CPU oracle.
+
+Bars: store bit-exact over the whole pool; attention within max-abs 2e-2 and
+mean-abs 2e-3 for bf16, max-abs 1e-5 for fp32 (absolute errors against the
+fp64 oracle). Pools are NaN-poisoned outside every context, so a read past a
+context or a missed store shows up as NaN.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.attention as oa
+from paged_kv_cache_439_amd import binding as pa
+from paged_kv_cache_439_amd import workloads as wl
+from tests import gpu_support as gs
+
+pytestmark = pytest.mark.gpu
+
+
+# ---------------------------------------------------------------------------
+# store
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg,over", [
+    (1, {}),
+    (4, dict(num_seqs=8)),                       # bf16, 4096 rows, chunks start mid-block
+    (5, dict(num_seqs=64)),                      # bf16, block 64
+])
+def test_store_bit_exact_whole_pool(gpu, cfg, over):
+    b = wl.make_batch(wl.spec(cfg, **over), device=gpu, poison=True)
+    gs.say(f"store cfg{cfg} rows={len(b.slot_mapping)}")
+    kp0, vp0 = wl.to_numpy(b.k_cache), wl.to_numpy(b.v_cache)
+    key, value = wl.to_numpy(b.key), wl.to_numpy(b.value)
+    ek, ev = oa.store_kvcache(kp0, vp0, key, value, b.slot_mapping, b.block_size)
+    gs.gpu_store(b)
+    torch.cuda.synchronize()
+    assert wl.to_numpy(b.k_cache).tobytes() == ek.tobytes()
+    assert wl.to_numpy(b.v_cache).tobytes() == ev.tobytes()
+
+
+def test_store_skips_negative_and_out_of_pool_slots(gpu):
+    b = wl.make_batch(wl.spec(1), device=gpu)
+    slots = b.slot_mapping.copy()
+    slots[1] = -1
+    slots[2] = b.num_blocks * b.block_size + 5      # past the pool: skipped
+    kp0, vp0 = wl.to_numpy(b.k_cache), wl.to_numpy(b.v_cache)
+    ek, ev = oa.store_kvcache(kp0, vp0, wl.to_numpy(b.key)[[0, 3]], wl.to_numpy(b.value)[[0, 3]],
+                              slots[[0, 3]], b.block_size)
+    pa.pa_store_kvcache(b.key, b.value, b.k_cache, b.v_cache, torch.from_numpy(slots).to(gpu))
+    torch.cuda.synchronize()
+    assert wl.to_numpy(b.k_cache).tobytes() == ek.tobytes()
+    assert wl.to_numpy(b.v_cache).tobytes() == ev.tobytes()
+
+
+def test_store_strided_key(gpu):
+    """key/value as slices of a fused [T][3][Hkv][D] tensor."""
+    b = wl.make_batch(wl.spec(4, num_seqs=2, cached=("uniform", 0, 200), chunk=40, max_context=512),
+                      device=gpu)
+    T, Hkv, D = b.key.shape
+    fused = torch.randn(T, 3, Hkv, D, device=gpu).to(b.key.dtype)
+    fused[:, 1] = b.key
+    fused[:, 2] = b.value
+    kp0, vp0 = wl.to_numpy(b.k_cache), wl.to_numpy(b.v_cache)
+    ek, ev = oa.store_kvcache(kp0, vp0, wl.to_numpy(b.key), wl.to_numpy(b.value), b.slot_mapping,
+                              b.block_size)
+    pa.pa_store_kvcache(fused[:, 1], fused[:, 2], b.k_cache, b.v_cache,
+                        torch.from_numpy(b.slot_mapping).to(gpu))
+    torch.cuda.synchronize()
+    assert wl.to_numpy(b.k_cache).tobytes() == ek.tobytes()
+    assert wl.to_numpy(b.v_cache).tobytes() == ev.tobytes()
+
+
+# ---------------------------------------------------------------------------
+# decode: small configs compared in full
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("P", [0, 16, 32, 48, 64])
+def test_decode_tiny_fp32(gpu, P):
+    b = wl.make_batch(wl.spec(1), device=gpu, poison=True)
+    gs.say(f"decode cfg1 P={P}")
+    gs.decode_parity(b, P)
+
+
+DECODE_VARIANTS = {
+    # bf16 MHA D=64, block 256, several partitions and ragged tails
+    "mha64_bs256": (2, dict(num_seqs=8, lens=("uniform", 1, 1500), max_context=1536), [0, 256, 512]),
+    # bf16 GQA 16/8 D=128 with a shared prefix
+    "gqa2_shared": (3, dict(num_seqs=12, lens=("uniform", 300, 1800), max_context=2048,
+                            share=dict(num_sharers=6, prefix_tokens=256)), [0, 512, 128]),
+    # bf16 GQA 32/8 D=128, block 64, lognormal lengths
+    "gqa4_bs64": (5, dict(num_seqs=16, lens=("lognormal", 300.0, 1.0, 1, 2048), max_context=2048),
+                  [0, 512, 64]),
+    # fp32 GQA 16/8 D=128
+    "f32_gqa2_d128": (3, dict(dtype="f32", num_seqs=6, lens=("uniform", 1, 700), max_context=768,
+                              share=None, block_size=32), [0, 96]),
+    # bf16 GQA group 8 (one wave per 8 heads)
+    "gqa8": (5, dict(num_seqs=6, num_heads=32, num_kv_heads=4, lens=("uniform", 1, 900),
+                     max_context=1024, block_size=16), [0, 128]),
+    # group 3 (waves of 1 head), D=64
+    "group3_d64": (2, dict(num_seqs=5, num_heads=12, num_kv_heads=4, lens=("uniform", 1, 600),
+                           max_context=640, block_size=8), [0, 32]),
+    # fp32 D=128, block 1024
+    "f32_bs1024": (3, dict(dtype="f32", num_seqs=3, lens=("uniform", 500, 2048), max_context=2048,
+                           share=None, block_size=1024), [0, 1024, 144]),
+    # bf16 D=64 with 6 query heads per KV head (waves of 2 heads)
+    "group6_d64": (2, dict(num_seqs=4, num_heads=12, num_kv_heads=2, lens=("uniform", 1, 400),
+                           max_context=512, block_size=32), [0, 64]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DECODE_VARIANTS))
+def test_decode_variants(gpu, name):
+    cfg, over, parts = DECODE_VARIANTS[name]
+    for P in parts:
+        b = wl.make_batch(wl.spec(cfg, **over), device=gpu, poison=True)
+        gs.say(f"decode {name} P={P} lens={b.context_lens.tolist()}")
+        gs.decode_parity(b, P)
+
+
+def test_decode_edge_lengths(gpu):
+    """Lengths 1, one block, one partition, partition+1, full table."""
+    bs, P = 16, 32
+    lens = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128]
+    sp = wl.spec(5, num_seqs=len(lens), lens=("fixed", lens), block_size=bs, max_context=128,
+                 pool=("factor", 1.5))
+    for part in (0, P, 16, 112):
+        b = wl.make_batch(sp, device=gpu, poison=True)
+        gs.say(f"decode edge lengths P={part}")
+        gs.decode_parity(b, part)
+
+
+def test_decode_zero_length_gives_zeros(gpu):
+    b = wl.make_batch(wl.spec(1), device=gpu)
+    arrs = gs.device_arrays(b)
+    arrs["lens"][2] = 0
+    out = gs.gpu_decode(b, 16, arrs)
+    torch.cuda.synchronize()
+    assert (out[2] == 0).all()
+    assert torch.isfinite(out).all()
+
+
+def test_decode_workspace_reuse_across_shapes(gpu):
+    """One workspace, filled with NaN bytes first, reused by calls of
+    different shapes back to back: its prior contents never matter."""
+    ws = torch.full((64 << 20,), 0xFF, dtype=torch.uint8, device=gpu)
+    specs = [wl.spec(5, num_seqs=16, lens=("uniform", 1, 2048), max_context=2048),
+             wl.spec(2, num_seqs=5, lens=("uniform", 1, 1024), max_context=1024),
+             wl.spec(5, num_seqs=9, lens=("uniform", 600, 2048), max_context=2048)]
+    for i, sp in enumerate(specs * 2):
+        b = wl.make_batch(sp, device=gpu, seed=1000 + i, poison=True)
+        hb, kp, vp = gs.oracle_inputs(b)
+        arrs = gs.device_arrays(b)
+        gs.gpu_store(b, arrs)
+        out = gs.gpu_decode(b, 64, arrs, workspace=ws)
+        torch.cuda.synchronize()
+        ref = oa.decode(hb.q, kp, vp, hb.block_tables, hb.context_lens, b.scale, b.block_size, b.dtype)
+        gs.check_close(gs.as_f64(out), ref, b.dtype, f"reuse call {i}")
+
+
+def test_decode_split_agrees_with_unsplit(gpu):
+    b = wl.make_batch(wl.spec(5, num_seqs=32, lens=("uniform", 1, 4096)), device=gpu)
+    arrs = gs.device_arrays(b)
+    gs.gpu_store(b, arrs)
+    base = gs.as_f64(gs.gpu_decode(b, 0, arrs))
+    for P in (64, 256, 512, 2048):
+        got = gs.as_f64(gs.gpu_decode(b, P, arrs))
+        assert np.abs(got - base).max() <= 8e-3, P      # two bf16 roundings apart at most
+
+
+def test_decode_block_permutation_bit_identical(gpu):
+    """Renumbering physical blocks leaves the GPU result bit-identical (its
+    reduction order depends only on logical positions)."""
+    b = wl.make_batch(wl.spec(3, num_seqs=10, lens=("uniform", 100, 1500), max_context=1536,
+                              share=dict(num_sharers=4, prefix_tokens=256)), device=gpu)
+    arrs = gs.device_arrays(b)
+    gs.gpu_store(b, arrs)
+    for P in (0, 256):
+        out1 = gs.gpu_decode(b, P, arrs).cpu()
+        perm = torch.randperm(b.num_blocks, generator=torch.Generator().manual_seed(5))
+        k2 = torch.empty_like(b.k_cache)
+        v2 = torch.empty_like(b.v_cache)
+        k2[perm.to(gpu)] = b.k_cache
+        v2[perm.to(gpu)] = b.v_cache
+        t = torch.from_numpy(b.block_tables).long()
+        t2 = torch.where(t >= 0, perm[t.clamp(min=0)], t).to(torch.int32).to(gpu)
+        out2 = torch.empty_like(b.q)
+        ws = pa.decode_workspace(b.num_seqs, b.num_heads, b.num_kv_heads, b.head_dim,
+                                 b.max_context_len, P, gpu)
+        pa.pa_decode(out2, b.q, k2, v2, t2, arrs["lens"], b.max_context_len, b.scale, P, ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out1.view(torch.int16), out2.cpu().view(torch.int16))
+
+
+def test_decode_sharing_equals_duplication(gpu):
+    """Sequences reading shared prefix blocks match the same sequences reading
+    private copies, bit for bit."""
+    sp = wl.spec(3, num_seqs=8, lens=("uniform", 600, 1500), max_context=1536,
+                 share=dict(num_sharers=5, prefix_tokens=512))
+    b = wl.make_batch(sp, device=gpu)
+    arrs = gs.device_arrays(b)
+    gs.gpu_store(b, arrs)
+    out1 = gs.gpu_decode(b, 256, arrs).cpu()
+    # give every sharer but the first its own copy of the shared blocks
+    shared = b.shared_blocks
+    users = [i for i in range(b.num_seqs) if b.block_tables[i, 0] == shared[0]]
+    extra = len(shared) * (len(users) - 1)
+    k2 = torch.cat([b.k_cache, torch.empty((extra,) + tuple(b.k_cache.shape[1:]), dtype=b.k_cache.dtype,
+                                           device=gpu)])
+    v2 = torch.cat([b.v_cache, torch.empty_like(k2[b.num_blocks:])])
+    tables = b.block_tables.copy()
+    nxt = b.num_blocks
+    for i in users[1:]:
+        for k, blk in enumerate(shared):
+            k2[nxt] = b.k_cache[blk]
+            v2[nxt] = b.v_cache[blk]
+            tables[i, k] = nxt
+            nxt += 1
+    out2 = torch.empty_like(b.q)
+    ws = pa.decode_workspace(b.num_seqs, b.num_heads, b.num_kv_heads, b.head_dim, b.max_context_len,
+                             256, gpu)
+    pa.pa_decode(out2, b.q, k2, v2, torch.from_numpy(tables).to(gpu), arrs["lens"], b.max_context_len,
+                 b.scale, 256, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.int16), out2.cpu().view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
+# decode: full-size configs, sampled outputs, in the benchmark's launch form
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("cfg,nseq", [(2, 8), (3, 6), (5, 6)])
+def test_decode_full_config_sampled(gpu, cfg, nseq):
+    b = wl.make_batch(wl.spec(cfg), device=gpu, poison=True)
+    seqs = gs.sample_seqs(b, nseq, seed=cfg)
+    if cfg == 3:   # include two sequences that read the shared prefix
+        sharers = [i for i in range(b.num_seqs) if b.block_tables[i, 0] == b.shared_blocks[0]]
+        seqs = sorted(set(seqs) | set(sharers[:2]))
+    gs.say(f"decode full cfg{cfg} seqs={seqs} P={gs.full_config_parts(cfg)}")
+    gs.decode_parity(b, gs.full_config_parts(cfg), seqs=seqs)
+
+
+def test_decode_full_config_properties(gpu):
+    """Every output of the largest decode workload is finite and, being a
+    convex combination of value rows, lies within the range of its head's
+    values."""
+    b = wl.make_batch(wl.spec(5), device=gpu, poison=True)
+    arrs = gs.device_arrays(b)
+    gs.gpu_store(b, arrs)
+    out = gs.gpu_decode(b, 512, arrs)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    vmax = torch.nan_to_num(b.v_cache.float(), nan=0.0).abs().amax().item()
+    assert out.float().abs().max().item() <= vmax * (1 + 2 ** -7)
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+
+PREFILL_VARIANTS = {
+    "gqa4_small": dict(num_seqs=3, cached=("uniform", 0, 700), chunk=[100, 257, 31], max_context=1024),
+    "cached_zero": dict(num_seqs=2, cached=("fixed", [0, 0]), chunk=[130, 64], max_context=256),
+    "mha_d64": dict(num_seqs=2, num_heads=8, num_kv_heads=8, head_dim=64, block_size=16,
+                    cached=("uniform", 0, 300), chunk=[77, 140], max_context=512),
+    "gqa2_bs64": dict(num_seqs=3, num_heads=16, num_kv_heads=8, block_size=64,
+                      cached=("uniform", 1, 400), chunk=[1, 65, 200], max_context=640),
+    "group8": dict(num_seqs=2, num_heads=32, num_kv_heads=4, block_size=32,
+                   cached=("uniform", 0, 500), chunk=[96, 33], max_context=640),
+    "group3": dict(num_seqs=2, num_heads=12, num_kv_heads=4, head_dim=64, block_size=128,
+                   cached=("uniform", 0, 500), chunk=[50, 129], max_context=768),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PREFILL_VARIANTS))
+def test_prefill_variants(gpu, name):
+    b = wl.make_batch(wl.spec(4, **PREFILL_VARIANTS[name]), device=gpu, poison=True)
+    gs.say(f"prefill {name} lens={b.context_lens.tolist()} qsl={b.query_start_loc.tolist()}")
+    gs.prefill_parity(b)
+
+
+def test_prefill_full_config_sampled(gpu):
+    b = wl.make_batch(wl.spec(4), device=gpu, poison=True)
+    gs.say(f"prefill full cfg4 lens={b.context_lens.tolist()}")
+    gs.prefill_parity(b, sample_rows=96, seed=4)
+
+
+def test_prefill_last_row_matches_decode(gpu):
+    """The last row of each chunk attends to the whole context, as a decode
+    of that query does."""
+    b = wl.make_batch(wl.spec(4, num_seqs=4, cached=("uniform", 0, 900), chunk=64, max_context=1024),
+                      device=gpu)
+    arrs = gs.device_arrays(b)
+    gs.gpu_store(b, arrs)
+    pre = gs.gpu_prefill(b, arrs)
+    last = torch.from_numpy(b.query_start_loc[1:] - 1).long().to(gpu)
+    q_last = b.q.index_select(0, last).contiguous()
+    dec = torch.empty_like(q_last)
+    pa.pa_decode(dec, q_last, b.k_cache, b.v_cache, arrs["tables"], arrs["lens"], b.max_context_len,
+                 b.scale, 0, None)
+    torch.cuda.synchronize()
+    diff = (pre.index_select(0, last).float() - dec.float()).abs().max().item()
+    assert diff <= 2e-2
