@@ -38,8 +38,10 @@ if ROOT not in sys.path:
 
 from paged_kv_cache_439_amd import binding as pa  # noqa: E402
 from paged_kv_cache_439_amd import workloads as wl  # noqa: E402
+from paged_kv_cache_439_amd.rocprof_summary import decode_source_hash  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_hbm_traffic.json")
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 
 
@@ -133,6 +135,33 @@ def bench_prefill(steps, warmup, device):
                 tokens_per_s=round(int(b.query_start_loc[-1]) / (ms * 1e-3), 1))
 
 
+def measured_traffic(workload_name):
+    """HBM bytes per decode launch from the committed counter runs, or None
+    when there are none or the decode kernel sources changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as fh:
+        rec = json.load(fh)
+    if rec.get("kernel_source_sha256") != decode_source_hash():
+        return None
+    w = rec.get("workloads", {}).get(workload_name)
+    if not w:
+        return None
+    return int(w["hbm_bytes_per_launch"])
+
+
+def copy_probe(nbytes, device, reps=3):
+    """A plain device-to-device copy of a known size, for scaling the HBM
+    byte counters (FETCH_SIZE / WRITE_SIZE) of a profiling run."""
+    x = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    y = torch.empty_like(x)
+    x.fill_(1)
+    for _ in range(reps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    del x, y
+
+
 def cpu_baseline(ds, budget_s=12.0):
     """The CPU oracle (store + decode, fp64), single-threaded, on whole
     sequences of the first batch until about budget_s seconds have passed."""
@@ -168,6 +197,8 @@ def main():
     ap.add_argument("--rotations", type=int, default=4)
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="also run a device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -210,7 +241,8 @@ def main():
         "roofline": {
             "bound": "hbm", "kernel": "paged_decode_kernel",
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(ds.spec["name"]),
             "kernel_ms": round(kms, 4), "bytes_per_launch": int(kbytes),
         },
     }
@@ -234,6 +266,9 @@ def main():
         log("extra prefill")
         extra["prefill"] = bench_prefill(20, 3, dev)
         line["extra"] = extra
+    if args.copy_probe:
+        log(f"copy probe {args.copy_probe} bytes")
+        copy_probe(args.copy_probe, dev)
     if not args.no_cpu:
         log("cpu baseline")
         line["cpu_baseline"] = cpu_baseline(ds)

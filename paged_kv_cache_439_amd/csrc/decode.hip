@@ -35,6 +35,10 @@
 #include "pa_device.h"
 #include "pa_internal.h"
 
+#ifndef DECODE_U
+#define DECODE_U 8
+#endif
+
 namespace pa {
 
 struct DecodeParams {
@@ -49,8 +53,18 @@ struct DecodeParams {
   int32_t num_heads, num_kv_heads, group, n_sub, units;
   int32_t bs_log2, num_blocks, max_blocks_per_seq, max_context_len;
   int32_t partition, max_parts;
-  float scale_log2;  // scale * log2(e): logits are kept in log2 units
+  int32_t row_bytes;    // Hkv * D * e: bytes between consecutive tokens of a block
+  int64_t block_bytes;  // block_size * row_bytes
+  float scale_log2;     // scale * log2(e): logits are kept in log2 units
 };
+
+// 16-byte streaming load of pool data: every K/V byte is read once per call,
+// so the loads carry the nontemporal hint and do not displace reusable lines.
+__device__ __forceinline__ uint4 stream_load(const char* ptr) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 template <typename T>
 struct ElemTraits;
@@ -131,7 +145,10 @@ __device__ __forceinline__ void merge_row_groups(float (&m)[GT], float (&l)[GT],
   }
 }
 
-template <typename T, int D, int GT, int U>
+// UNIFORM_BLOCK: every chunk lies inside one block (block_size >= CT and
+// partitions start at multiples of CT), so one scalar table lookup serves the
+// whole chunk; otherwise each lane looks up its own token's block.
+template <typename T, int D, int GT, int U, bool UNIFORM_BLOCK>
 __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams p) {
   constexpr int E = ElemTraits<T>::E;
   constexpr int EPL = 16 / E;     // elements per 16-byte lane slice
@@ -141,10 +158,10 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams p) {
   static_assert(LPT >= 1 && LPT <= 32 && (64 % LPT) == 0, "unsupported head_dim");
 
   const int lane = threadIdx.x & 63;
-  const int unit = blockIdx.z * 4 + (threadIdx.x >> 6);
+  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (unit >= p.units) return;
-  const int seq = blockIdx.y;
-  const int part = blockIdx.x;
+  const int seq = blockIdx.z;
+  const int part = blockIdx.y;
   const int L = min(p.context_lens[seq], p.max_context_len);
   const int P = p.partition;
   const int nparts = L > 0 ? (L + P - 1) / P : 0;
@@ -173,8 +190,8 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams p) {
   const int tok_end = min(L, tok_begin + P);
   const int bs_log2 = p.bs_log2;
   const int bs_mask = (1 << bs_log2) - 1;
-  const int64_t row_bytes = (int64_t)p.num_kv_heads * D * E;
-  const int64_t lane_off = (int64_t)kvh * D * E + dc * 16;
+  const int row_bytes = p.row_bytes;
+  const int lane_off = kvh * D * E + dc * 16;
   const int32_t* bt = p.block_tables + (int64_t)seq * p.max_blocks_per_seq;
 
   // q slices of the GT heads, as stored (bf16 pairs feed v_dot2 directly).
@@ -207,18 +224,41 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams p) {
       wbase = j0 >> bs_log2;
       tbl = (wbase + lane <= last_blk) ? clamp_block(bt[wbase + lane], p.num_blocks) : 0;
     }
-    uint4 kr[U], vr[U];
+    // Addresses first, then every K and V load of the chunk, then compute:
+    // the whole chunk's bytes are in flight before any of them is waited on.
     bool valid[U];
+    int64_t off[U];
+    if constexpr (UNIFORM_BLOCK) {
+      const int phys = __builtin_amdgcn_readlane(tbl, (j0 >> bs_log2) - wbase);
+      const int64_t base = (int64_t)phys * p.block_bytes;
+      const int row0 = (j0 & bs_mask) + tr;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = j0 + u * TPW + tr;
-      valid[u] = j < tok_end;
-      const int jj = valid[u] ? j : j0;  // in-bounds stand-in for tail lanes
-      const int phys = __shfl(tbl, (jj >> bs_log2) - wbase);
-      const int64_t off = (((int64_t)phys << bs_log2) + (jj & bs_mask)) * row_bytes + lane_off;
-      kr[u] = *reinterpret_cast<const uint4*>(p.k_cache + off);
-      vr[u] = *reinterpret_cast<const uint4*>(p.v_cache + off);
+      for (int u = 0; u < U; ++u) {
+        const int j = j0 + u * TPW + tr;
+        valid[u] = j < tok_end;
+        const int row = valid[u] ? row0 + u * TPW : (j0 & bs_mask);
+        off[u] = base + (row * row_bytes + lane_off);
+      }
+    } else {
+      int phys[U], row[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = j0 + u * TPW + tr;
+        valid[u] = j < tok_end;
+        const int jj = valid[u] ? j : j0;  // in-bounds stand-in for tail lanes
+        phys[u] = __shfl(tbl, (jj >> bs_log2) - wbase);
+        row[u] = jj & bs_mask;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < U; ++u) off[u] = (int64_t)phys[u] * p.block_bytes + (row[u] * row_bytes + lane_off);
     }
+    uint4 kr[U], vr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) kr[u] = stream_load(p.k_cache + off[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) vr[u] = stream_load(p.v_cache + off[u]);
+    __builtin_amdgcn_sched_barrier(0);
 
     float s[U][GT];
 #pragma unroll
@@ -388,13 +428,23 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
   return pl;
 }
 
+template <typename T, int D, int GT, int U>
+static void launch_u(const DecodeParams& prm, dim3 grid, bool split, hipStream_t stream) {
+  constexpr int TPW = 64 / (D * (int)sizeof(T) / 16);
+  constexpr int CT = U * TPW;
+  const bool uniform = (1 << prm.bs_log2) >= CT && (prm.max_parts == 1 || prm.partition % CT == 0);
+  if (uniform)
+    hipLaunchKernelGGL((paged_decode_kernel<T, D, GT, U, true>), grid, dim3(256), 0, stream, prm);
+  else
+    hipLaunchKernelGGL((paged_decode_kernel<T, D, GT, U, false>), grid, dim3(256), 0, stream, prm);
+  if (split)
+    hipLaunchKernelGGL((paged_decode_merge_kernel<T, D, GT>), dim3(grid.z, (grid.x)), dim3(256), 0,
+                       stream, prm);
+}
+
 template <typename T, int D, int GT>
 static void launch_one(const DecodeParams& prm, dim3 grid, bool split, hipStream_t stream) {
-  constexpr int U = 8;
-  hipLaunchKernelGGL((paged_decode_kernel<T, D, GT, U>), grid, dim3(256), 0, stream, prm);
-  if (split)
-    hipLaunchKernelGGL((paged_decode_merge_kernel<T, D, GT>), dim3(grid.y, grid.z), dim3(256), 0,
-                       stream, prm);
+  launch_u<T, D, GT, DECODE_U>(prm, grid, split, stream);
 }
 
 template <typename T, int D>
@@ -432,7 +482,11 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   prm.partition = pl.partition;
   prm.max_parts = pl.max_parts;
   prm.scale_log2 = a.scale * 1.4426950408889634f;
-  const dim3 grid((unsigned)pl.max_parts, (unsigned)a.num_seqs, (unsigned)((pl.units + 3) / 4));
+  prm.row_bytes = a.num_kv_heads * a.head_dim * (a.bf16 ? 2 : 4);
+  prm.block_bytes = (int64_t)a.block_size * prm.row_bytes;
+  // x: head group (fastest, so one token's rows of all heads are read by
+  // neighbouring workgroups), y: partition, z: sequence.
+  const dim3 grid((unsigned)((pl.units + 3) / 4), (unsigned)pl.max_parts, (unsigned)a.num_seqs);
   const bool split = pl.max_parts > 1;
   if (a.bf16) {
     if (a.head_dim == 64) launch_gt<uint16_t, 64>(pl.heads_per_unit, prm, grid, split, stream);

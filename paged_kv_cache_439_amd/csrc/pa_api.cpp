@@ -58,6 +58,9 @@ pa_status check_attention_shapes(int32_t num_heads, int32_t num_kv_heads, int32_
     return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq=%d must be positive", max_blocks_per_seq);
   if (max_context_len <= 0)
     return fail(PA_ERR_INVALID_ARG, "max_context_len=%d must be positive", max_context_len);
+  if ((int64_t)block_size * num_kv_heads * head_dim * 4 > INT32_MAX)
+    return fail(PA_ERR_UNSUPPORTED, "a block of %lld elements per pool is too large",
+                (long long)block_size * num_kv_heads * head_dim);
   if ((int64_t)max_context_len > (int64_t)max_blocks_per_seq * block_size)
     return fail(PA_ERR_INVALID_ARG, "max_context_len=%d exceeds max_blocks_per_seq*block_size=%lld",
                 max_context_len, (long long)max_blocks_per_seq * block_size);

@@ -1,0 +1,146 @@
+"""Summaries of rocprofv3 output for the profiles/ folder.
+
+    python -m paged_kv_cache_439_amd.rocprof_summary trace STATS_CSV OUT_MD --cmd "..."
+    python -m paged_kv_cache_439_amd.rocprof_summary traffic FETCH_CSV WRITE_CSV OUT_JSON OUT_MD \
+        --copy-bytes N --cmd-fetch "..." --cmd-write "..."
+
+trace:   kernel-trace statistics of this library's kernels as a table.
+traffic: HBM bytes per dispatch from the FETCH_SIZE and WRITE_SIZE counter
+         passes (KiB per dispatch), each scaled by what the same counter
+         reads for a plain device copy of a known size in the same run (the
+         last three copy dispatches whose WRITE_SIZE equals that size). The
+         JSON carries the sha256 of the decode sources it was measured on;
+         bench.py reports the traffic only while the sources still match.
+"""
+
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import os
+import re
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_439_amd", "csrc", f)
+                  for f in ("decode.hip", "pa_device.h")]
+
+
+def decode_source_hash():
+    h = hashlib.sha256()
+    for f in DECODE_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _ours(name):
+    return "pa::" in name
+
+
+def _short(name):
+    name = re.sub(r"\(pa::\w+\)$", "", name.replace("void ", ""))
+    return re.sub(r"\(char const\*.*$", "", name)
+
+
+def trace(stats_csv, out_md, cmd):
+    rows = [r for r in csv.DictReader(open(stats_csv)) if _ours(r["Name"])]
+    lines = ["# Kernel trace: libpagedattn kernels", "", "Command:", "", "```", cmd, "```", "",
+             "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
+# kernel template arguments -> workload name (dtype bf16, head_dim, heads per wave)
+KERNEL_WORKLOAD = {
+    ("64", "1"): "bf16_mha_decode_b64",
+    ("128", "2"): "bf16_gqa_decode_b256_shared_prefix",
+    ("128", "4"): "bf16_gqa_decode_b512_lognormal",
+}
+
+
+def _per_kernel(path, counter):
+    rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in rows if r["Counter_Name"] == counter]
+
+
+def traffic(fetch_csv, write_csv, out_json, out_md, copy_bytes, cmd_fetch, cmd_write):
+    fetch = _per_kernel(fetch_csv, "FETCH_SIZE")
+    write = _per_kernel(write_csv, "WRITE_SIZE")
+    # the copy-probe dispatches are found in the write pass (WRITE_SIZE equals
+    # the probe size); the fetch pass dispatches the same kernels in order
+    wnames = [n for n, _ in write]
+    probe_kib = copy_bytes / 1024
+    probe_idx = [i for i, (n, v) in enumerate(write) if "copyBuffer" in n and abs(v - probe_kib) < 1][-3:]
+    fs = probe_kib / (sum(fetch[i][1] for i in probe_idx) / len(probe_idx))
+    ws = probe_kib / (sum(write[i][1] for i in probe_idx) / len(probe_idx))
+    assert [fetch[i][0] for i in probe_idx] == [wnames[i] for i in probe_idx]
+    per = collections.defaultdict(lambda: dict(fetch=[], write=[]))
+    for (n, v), (n2, w) in zip(fetch, write):
+        assert n == n2, "the two passes dispatched different kernels"
+        if _ours(n):
+            per[_short(n)]["fetch"].append(v * fs * 1024)
+            per[_short(n)]["write"].append(w * ws * 1024)
+    kernels = {k: dict(dispatches=len(v["fetch"]), fetch_bytes=sum(v["fetch"]) / len(v["fetch"]),
+                       write_bytes=sum(v["write"]) / len(v["write"])) for k, v in per.items()}
+    workloads = {}
+    for k, v in kernels.items():
+        m = re.search(r"paged_decode(_merge)?_kernel<unsigned short, (\d+), (\d+)", k)
+        if not m:
+            continue
+        wname = KERNEL_WORKLOAD.get((m.group(2), m.group(3)))
+        if not wname:
+            continue
+        w = workloads.setdefault(wname, dict(hbm_bytes_per_launch=0.0, kernels=[]))
+        w["hbm_bytes_per_launch"] += v["fetch_bytes"] + v["write_bytes"]
+        w["kernels"].append(k)
+    for w in workloads.values():
+        w["hbm_bytes_per_launch"] = int(w["hbm_bytes_per_launch"])
+    rec = dict(kernel_source_sha256=decode_source_hash(), fetch_scale=fs, write_scale=ws,
+               copy_probe_bytes=copy_bytes, cmd_fetch=cmd_fetch, cmd_write=cmd_write,
+               kernels={k: {kk: (int(vv) if "bytes" in kk else vv) for kk, vv in v.items()}
+                        for k, v in kernels.items()},
+               workloads=workloads)
+    json.dump(rec, open(out_json, "w"), indent=1)
+    lines = ["# HBM traffic per dispatch (rocprofv3 FETCH_SIZE / WRITE_SIZE)", "",
+             f"Calibration: a {copy_bytes} B device copy reads as FETCH_SIZE x{fs:.4f} and "
+             f"WRITE_SIZE x{ws:.4f} of its true size; every value below is scaled by those factors.",
+             "", "Commands:", "", "```", cmd_fetch, cmd_write, "```", "",
+             "| kernel | dispatches | fetch MB | write MB |", "|---|---|---|---|"]
+    for k, v in sorted(kernels.items(), key=lambda kv: -kv[1]["fetch_bytes"]):
+        lines.append(f"| `{k}` | {v['dispatches']} | {v['fetch_bytes'] / 1e6:.1f} | {v['write_bytes'] / 1e6:.2f} |")
+    lines += ["", "Per decode call (main + merge kernels):", ""]
+    for wname, w in workloads.items():
+        lines.append(f"- {wname}: {w['hbm_bytes_per_launch'] / 1e6:.1f} MB")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="mode", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("stats_csv")
+    t.add_argument("out_md")
+    t.add_argument("--cmd", required=True)
+    f = sub.add_parser("traffic")
+    f.add_argument("fetch_csv")
+    f.add_argument("write_csv")
+    f.add_argument("out_json")
+    f.add_argument("out_md")
+    f.add_argument("--copy-bytes", type=int, required=True)
+    f.add_argument("--cmd-fetch", required=True)
+    f.add_argument("--cmd-write", required=True)
+    a = ap.parse_args()
+    if a.mode == "trace":
+        trace(a.stats_csv, a.out_md, a.cmd)
+    else:
+        traffic(a.fetch_csv, a.write_csv, a.out_json, a.out_md, a.copy_bytes, a.cmd_fetch, a.cmd_write)
+
+
+if __name__ == "__main__":
+    main()

@@ -43,12 +43,12 @@ CONFIGS = {
     2: dict(name="bf16_mha_decode_b64", kind="decode", dtype="bf16", num_seqs=64,
             num_heads=12, num_kv_heads=12, head_dim=64, block_size=256,
             lens=("uniform", 512, 4096), pool=("factor", 1.25),
-            max_context=4096, partition_size=256),
+            max_context=4096, partition_size=256),   # split: 64 sequences alone underfill the chip
     3: dict(name="bf16_gqa_decode_b256_shared_prefix", kind="decode", dtype="bf16",
             num_seqs=256, num_heads=16, num_kv_heads=8, head_dim=128, block_size=256,
             lens=("uniform", 1024, 4096), pool=("factor", 1.25),
             share=dict(num_sharers=128, prefix_tokens=1024),
-            max_context=4096, partition_size=512),
+            max_context=4096, partition_size=0),     # 256 x 8 waves fill the chip unsplit
     4: dict(name="bf16_gqa_chunked_prefill", kind="prefill", dtype="bf16", num_seqs=8,
             num_heads=32, num_kv_heads=8, head_dim=128, block_size=256,
             cached=("uniform", 0, 3584), chunk=512, pool=("factor", 1.25),
