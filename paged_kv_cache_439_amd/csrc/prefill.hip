@@ -8,14 +8,20 @@
 // attends to keys 0 .. c_i + t (causal, aligned to the end of the context).
 //
 // Work decomposition: a workgroup of 4 waves handles one KV head and 32*RG
-// query rows of one sequence; HW = 4/RG query heads of that KV head's group
-// share the workgroup, so every K/V tile staged in LDS serves HW heads x 32*RG
-// rows. Wave w takes head (w % HW) and rows 32*(w / HW) .. +32 (two 16-row
-// MFMA tiles).
+// query positions of one sequence; HW = 4/RG query heads of that KV head's
+// group share the workgroup, so every K/V tile staged in LDS serves
+// HW heads x 32*RG rows. Wave w takes head (w % HW) and positions
+// 32*(w / HW) .. +32 (two 16-row MFMA tiles). The grid's slowest dimension
+// walks the row blocks from the end of the chunk, so the workgroups with the
+// longest key ranges are dispatched first.
 //
-// Per 64-key tile:
-//   * stage K as [key][d] and V transposed as [d][key] in LDS (rows padded by
-//     16 bytes), reading 16-byte slices of paged rows through the table;
+// Per 64-key tile (software-pipelined: the K/V rows of tile i+1 are loaded
+// into registers while tile i is computed from LDS):
+//   * the physical block ids come from a window of the block table held in
+//     LDS, loaded once (and again only if a context outgrows the window);
+//   * K is staged as [key][d] and V transposed as [d][key]; 16-byte granules
+//     are XOR-swizzled within a row so that the MFMA operand reads and the
+//     staging writes spread over the LDS banks;
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = 16 keys x 32 d from LDS,
 //     B = Q^T slice held in registers for the whole kernel). The C layout puts
 //     one query row in each lane (column = lane % 16) and 4 keys per register
@@ -27,7 +33,12 @@
 //     transpose;
 //   * O^T += V^T P^T with the same MFMA (A = 16 d x 32 keys from the
 //     transposed V tile); O^T's column is again the lane's query row, so the
-//     online-softmax rescale is a per-lane multiply.
+//     online-softmax rescale is a per-lane multiply;
+//   * the running maximum is only raised (and O rescaled) when a tile's
+//     maximum exceeds it by more than 2^8 in probability, so most tiles skip
+//     the rescale; the result is the same softmax, with probabilities below
+//     2^8 relative to the kept maximum;
+//   * only tiles that straddle a wave's causal diagonal are masked.
 //
 // Bound: MFMA (bf16 dense). Algorithmic flops = 4 * D * Hq * (visible
 // query-key pairs).
@@ -47,48 +58,110 @@ struct PrefillParams {
   const int32_t* context_lens;
   int32_t num_heads, num_kv_heads, group, n_sub;
   int32_t bs_log2, num_blocks, max_blocks_per_seq, max_query_len, max_context_len;
+  int32_t row_blocks;  // gridDim.z: ceil(max_query_len / ROWS)
   float scale_log2;
 };
 
-__device__ __forceinline__ uint32_t bf16_elem(const uint4& v, int d) {
-  const uint32_t w = (d < 2) ? v.x : (d < 4) ? v.y : (d < 6) ? v.z : v.w;
-  return (d & 1) ? (w >> 16) : (w & 0xFFFFu);
+// Lazy-rescale threshold in log2 units: probabilities stay below 2^8.
+constexpr float RESCALE_SLACK = 8.0f;
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// 16 bytes from global memory straight into LDS: lane l of the wave writes
+// lds_base + 16*l (lds_base must be the same for every lane).
+__device__ __forceinline__ void load_lds16(const void* gptr, void* lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)gptr,
+                                   (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+// Transposing LDS read of 4 bf16. Within each group of 16 lanes, lane i
+// receives element i % 4 of the 8 bytes addressed by lanes 4j + i/4,
+// j = 0..3: when lane s of the group points at row r0 + s/4, columns
+// c0 + 4*(s%4) .. +3 of a row-major tile, lane i gets column c0 + i of rows
+// r0 .. r0+3.
+__device__ __forceinline__ uint2 lds_read_tr4(const uint16_t* ptr) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)ptr);
+  return __builtin_bit_cast(uint2, v);
 }
 
 template <int D, int HW>
-__global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillParams p) {
+__global__ __launch_bounds__(256, 2) void prefill_chunk_kernel(PrefillParams p) {
   constexpr int RG = 4 / HW;      // row groups of 32 rows
-  constexpr int ROWS = 32 * RG;   // query rows per workgroup
+  constexpr int ROWS = 32 * RG;   // query positions per workgroup
   constexpr int KT = 64;          // keys per tile
   constexpr int KS = D / 32;      // MFMA k-steps over head_dim for S
   constexpr int DT = D / 16;      // 16-wide d tiles of O^T
-  constexpr int DCH = D / 8;      // 16-byte slices per row
-  constexpr int KROW = D + 8;     // LDS row pitch of the K tile (elements)
-  constexpr int VROW = KT + 8;    // LDS row pitch of the V^T tile (elements)
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * KROW];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VROW];
+  constexpr int GPR = D / 8;      // 16-byte granules per K/V row of one head
+  constexpr int KPI = 64 / GPR;   // keys one wave-wide 16-byte load covers
+  constexpr int NIW = KT / KPI / 4;  // such loads per wave per tile, per tensor
+  constexpr int TE = KT * D;      // elements of one staged tile
+  constexpr int TBL = 512;        // block-table window (entries)
+  static_assert(NIW >= 1, "tile shape");
+
+  // Two stages, each [0 = K, 1 = V][key][granule] with granules XOR-swizzled
+  // per key. Separate arrays, so the compiler can tell that a load into one
+  // stage does not feed the reads of the other.
+  __shared__ __attribute__((aligned(16))) uint16_t kv0[2][TE];
+  __shared__ __attribute__((aligned(16))) uint16_t kv1[2][TE];
+  __shared__ int32_t tbl[TBL];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qgrp = lane >> 4;     // 0..3
   const int lrow = lane & 15;
   const int seq = blockIdx.y;
   const int qs = p.query_start_loc[seq];
   const int n = min(p.query_start_loc[seq + 1] - qs, p.max_query_len);
-  const int t0 = blockIdx.x * ROWS;
+  const int t0 = (p.row_blocks - 1 - (int)blockIdx.z) * ROWS;  // longest ranges first
   if (t0 >= n) return;  // whole workgroup
   const int L = min(p.context_lens[seq], p.max_context_len);
   const int c = L - n;
-  const int kvh = blockIdx.z / p.n_sub;
-  const int head = kvh * p.group + (blockIdx.z - kvh * p.n_sub) * HW + (wave % HW);
+  const int kvh = blockIdx.x / p.n_sub;
+  const int head = kvh * p.group + (blockIdx.x - kvh * p.n_sub) * HW + (wave % HW);
   const int wrow0 = t0 + (wave / HW) * 32;
   const int kv_end = min(L, c + min(t0 + ROWS, n));  // keys this workgroup needs
+  if (kv_end <= 0) return;  // only when a precondition is violated (n > L)
+  const int wave_last_key = c + wrow0 + 31;          // last key any row of this wave sees
   const int bs_log2 = p.bs_log2;
   const int bs_mask = (1 << bs_log2) - 1;
   const int64_t row_bytes = (int64_t)p.num_kv_heads * D * 2;
   const int64_t head_off = (int64_t)kvh * D * 2;
   const int32_t* bt = p.block_tables + (int64_t)seq * p.max_blocks_per_seq;
+  const int nblk = (kv_end + bs_mask) >> bs_log2;
+
+  // Granule swizzles (key = index within the tile). K rows are read 16 keys
+  // at a time at one granule: key bits 0,1,3,4 pick distinct granules. V rows
+  // are read by the transposing load, 8 keys x 2 granules at a time: even
+  // swizzles from key bits 0,1,3.
+  auto swz_k = [](int key) { return ((key & 3) | ((key >> 1) & 12)) & (GPR - 1); };
+  auto swz_v = [](int key) { return (2 * ((key & 3) | ((key >> 1) & 4))) & (GPR - 1); };
+
+  // ---- block-table window ----
+  int wb = 0;
+  auto load_window = [&](int base) {
+    for (int i = tid; i < TBL; i += 256)
+      tbl[i] = (base + i < nblk) ? clamp_block(bt[base + i], p.num_blocks) : 0;
+  };
+  load_window(0);
+
+  // Issue the global->LDS loads of tile kt0 into stage st. Keys past the
+  // workgroup's range read the last needed row instead (finite data whose
+  // probability is zero), so no NaN from outside the context reaches V.
+  auto issue = [&](int kt0, uint16_t (&stage)[2][TE]) {
+#pragma unroll
+    for (int i = 0; i < NIW; ++i) {
+      const int ins = wave * NIW + i;
+      const int key = ins * KPI + lane / GPR;
+      const int j = min(kt0 + key, kv_end - 1);
+      const int phys = tbl[(j >> bs_log2) - wb];
+      const int64_t row = (((int64_t)phys << bs_log2) + (j & bs_mask)) * row_bytes + head_off;
+      const int gl = lane % GPR;
+      load_lds16(p.k_cache + row + ((gl ^ swz_k(key)) * 16), &stage[0][ins * KPI * D]);
+      load_lds16(p.v_cache + row + ((gl ^ swz_v(key)) * 16), &stage[1][ins * KPI * D]);
+    }
+  };
 
   // Q^T B operands: lane holds Q[row lrow][32*ks + 8*qgrp .. +8] per tile.
   bf16x8 qreg[2][KS];
@@ -114,96 +187,107 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillParams p) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  const float sl2 = p.scale_log2;
 
-  for (int kt0 = 0; kt0 < kv_end; kt0 += KT) {
-    __syncthreads();  // the previous tile's LDS reads are done
-    // ---- stage K [key][d] ----
-#pragma unroll
-    for (int it = tid; it < KT * DCH; it += 256) {
-      const int key = it / DCH, dch = it % DCH;
-      const int j = kt0 + key;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (j < kv_end) {
-        const int phys = clamp_block(bt[j >> bs_log2], p.num_blocks);
-        v = *reinterpret_cast<const uint4*>(
-            p.k_cache + (((int64_t)phys << bs_log2) + (j & bs_mask)) * row_bytes + head_off + dch * 16);
+  __syncthreads();  // table window visible
+  issue(0, kv0);
+
+  // One 64-key tile: wait for its loads, start the next tile's loads into
+  // the other stage, then compute from this stage.
+  auto step = [&](int kt0, uint16_t (&cur)[2][TE], uint16_t (&nxt_stage)[2][TE]) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of tile kt0 landed
+    __syncthreads();  // the whole tile is in LDS; every wave is done with the other stage
+    const int nxt = kt0 + KT;
+    if (nxt < kv_end) {
+      const int last_blk = (min(nxt + KT, kv_end) - 1) >> bs_log2;
+      if (last_blk >= wb + TBL) {  // uniform and rare: slide the window
+        wb = nxt >> bs_log2;
+        load_window(wb);
+        __syncthreads();
       }
-      *reinterpret_cast<uint4*>(&Ks[key * KROW + dch * 8]) = v;
+      issue(nxt, nxt_stage);  // in flight while this tile is computed
     }
-    // ---- stage V transposed [d][key]: a thread moves 4 keys x 8 d ----
-    for (int it = tid; it < (KT / 4) * DCH; it += 256) {
-      const int kq = it / DCH, dch = it % DCH;
-      uint4 v[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = kt0 + 4 * kq + e;
-        v[e] = make_uint4(0, 0, 0, 0);
-        if (j < kv_end) {
-          const int phys = clamp_block(bt[j >> bs_log2], p.num_blocks);
-          v[e] = *reinterpret_cast<const uint4*>(
-              p.v_cache + (((int64_t)phys << bs_log2) + (j & bs_mask)) * row_bytes + head_off + dch * 16);
-        }
-      }
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        uint2 w;
-        w.x = bf16_elem(v[0], d) | (bf16_elem(v[1], d) << 16);
-        w.y = bf16_elem(v[2], d) | (bf16_elem(v[3], d) << 16);
-        *reinterpret_cast<uint2*>(&Vt[(dch * 8 + d) * VROW + 4 * kq]) = w;
-      }
-    }
-    __syncthreads();
+    if (kt0 > wave_last_key) return;  // every key of this tile is masked for this wave
+    const uint16_t* Kt = cur[0];
+    const uint16_t* Vt = cur[1];
 
     // ---- S^T = K Q^T: tiles [step c2][half hf][row tile rt] ----
     f32x4 s[2][2][2];
 #pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2)
+    for (int c2 = 0; c2 < 2; ++c2) {
+      bf16x8 a[2][KS];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const int key = 32 * c2 + 8 * (lrow >> 2) + 4 * hf + (lrow & 3);
+        const int sk = swz_k(key);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          a[hf][ks] = *reinterpret_cast<const bf16x8*>(&Kt[key * D + (((4 * ks + qgrp) ^ sk) * 8)]);
+      }
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
         s[c2][hf][0] = f32x4{0.f, 0.f, 0.f, 0.f};
         s[c2][hf][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[key * KROW + 32 * ks + 8 * qgrp]);
-          s[c2][hf][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[0][ks], s[c2][hf][0], 0, 0, 0);
-          s[c2][hf][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qreg[1][ks], s[c2][hf][1], 0, 0, 0);
+          s[c2][hf][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[hf][ks], qreg[0][ks], s[c2][hf][0], 0, 0, 0);
+          s[c2][hf][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[hf][ks], qreg[1][ks], s[c2][hf][1], 0, 0, 0);
         }
       }
+    }
 
     // ---- online softmax per query row (lane row lrow of tile rt) ----
-    bf16x8 pb[2][2];
+    const bool masked = kt0 + KT - 1 > c + wrow0;  // some key is past some row's diagonal
+    float mt[2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
       const int tpos = c + wrow0 + rt * 16 + lrow;  // absolute position of the row
-      float mt = NEG_BIG;
+      float mx = -INFINITY;
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int key = kt0 + 32 * c2 + 8 * qgrp + 4 * hf + i;
-            float v = s[c2][hf][rt][i] * p.scale_log2;
-            v = (key <= tpos && key < kv_end) ? v : -INFINITY;
+            float v = s[c2][hf][rt][i] * sl2;
+            if (masked) {
+              const int key = kt0 + 32 * c2 + 8 * qgrp + 4 * hf + i;
+              v = (key <= tpos) ? v : -INFINITY;
+            }
             s[c2][hf][rt][i] = v;
-            mt = fmaxf(mt, v);
+            mx = fmaxf(mx, v);
           }
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float mn = fmaxf(m[rt], mt);
-      const float alpha = fast_exp2(m[rt] - mn);
-      m[rt] = mn;
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mt[rt] = fmaxf(mx, __shfl_xor(mx, 32));
+    }
+    // Raise the running maxima only when some row's tile maximum exceeds its
+    // kept maximum by more than the slack (wave-uniform decision).
+    const bool grow = (mt[0] > m[0] + RESCALE_SLACK) || (mt[1] > m[1] + RESCALE_SLACK);
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const float mn = fmaxf(m[rt], mt[rt]);
+        const float alpha = fast_exp2(m[rt] - mn);
+        m[rt] = mn;
+        lsum[rt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) o[dt][rt] *= alpha;
+      }
+    }
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      const float mr = m[rt];
       float ps = 0.0f;
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
         uint32_t w[4];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          const float p0 = fast_exp2(s[c2][hf][rt][0] - mn);
-          const float p1 = fast_exp2(s[c2][hf][rt][1] - mn);
-          const float p2 = fast_exp2(s[c2][hf][rt][2] - mn);
-          const float p3 = fast_exp2(s[c2][hf][rt][3] - mn);
+          const float p0 = fast_exp2(s[c2][hf][rt][0] - mr);
+          const float p1 = fast_exp2(s[c2][hf][rt][1] - mr);
+          const float p2 = fast_exp2(s[c2][hf][rt][2] - mr);
+          const float p3 = fast_exp2(s[c2][hf][rt][3] - mr);
           w[2 * hf] = pack_bf16x2(p0, p1);
           w[2 * hf + 1] = pack_bf16x2(p2, p3);
           // sum the rounded weights, the ones the PV product uses
@@ -211,20 +295,37 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillParams p) {
         }
         pb[rt][c2] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
       }
-      lsum[rt] = lsum[rt] * alpha + ps;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) o[dt][rt] *= alpha;
+      lsum[rt] += ps;
     }
 
-    // ---- O^T += V^T P^T ----
+    // ---- O^T += V^T P^T; V^T fragments come from the transposing read ----
+    const int src_key = 8 * qgrp + (lrow >> 2);  // + 32*c2 + 4*h
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DT; ++dt) {
+      const int gran = 2 * dt + ((lrow & 3) >> 1);
+      const int half = (lrow & 1) * 4;
+      bf16x8 a[2];
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Vt[(16 * dt + lrow) * VROW + 32 * c2 + 8 * qgrp]);
-        o[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[0][c2], o[dt][0], 0, 0, 0);
-        o[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[1][c2], o[dt][1], 0, 0, 0);
+        uint2 r[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int key = 32 * c2 + 4 * h + src_key;
+          r[h] = lds_read_tr4(&Vt[key * D + ((gran ^ swz_v(key)) * 8) + half]);
+        }
+        a[c2] = __builtin_bit_cast(bf16x8, make_uint4(r[0].x, r[0].y, r[1].x, r[1].y));
       }
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        o[dt][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c2], pb[0][c2], o[dt][0], 0, 0, 0);
+        o[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c2], pb[1][c2], o[dt][1], 0, 0, 0);
+      }
+    }
+  };
+
+  for (int kt0 = 0; kt0 < kv_end; kt0 += 2 * KT) {
+    step(kt0, kv0, kv1);
+    if (kt0 + KT < kv_end) step(kt0 + KT, kv1, kv0);
   }
 
   // ---- normalise and write: lane holds O[row][16*dt + 4*qgrp + 0..3] ----
@@ -255,11 +356,12 @@ static int32_t prefill_heads_per_wg(int32_t group) {
 }
 
 template <int D, int HW>
-static void launch_prefill_t(const PrefillParams& prm, int32_t max_query_len, int32_t num_seqs,
+static void launch_prefill_t(PrefillParams prm, int32_t max_query_len, int32_t num_seqs,
                              int32_t num_kv_heads, hipStream_t stream) {
   constexpr int ROWS = 32 * (4 / HW);
-  const dim3 grid((unsigned)((max_query_len + ROWS - 1) / ROWS), (unsigned)num_seqs,
-                  (unsigned)(num_kv_heads * prm.n_sub));
+  prm.row_blocks = (max_query_len + ROWS - 1) / ROWS;
+  // x: head group, y: sequence, z: row block (from the end of the chunk).
+  const dim3 grid((unsigned)(num_kv_heads * prm.n_sub), (unsigned)num_seqs, (unsigned)prm.row_blocks);
   hipLaunchKernelGGL((prefill_chunk_kernel<D, HW>), grid, dim3(256), 0, stream, prm);
 }
 

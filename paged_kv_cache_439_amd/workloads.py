@@ -293,7 +293,7 @@ def make_batch(spec, device="cpu", seed=None, poison=False):
     q = _randn((n_q, Hq, D), dtype, device, base + 5)
     batch = Batch(spec=spec, kind=spec["kind"], dtype=dtype, num_seqs=B, num_heads=Hq,
                   num_kv_heads=Hkv, head_dim=D, block_size=bs, num_blocks=num_blocks,
-                  scale=1.0 / math.sqrt(D), context_lens=lens, block_tables=tables,
+                  scale=float(spec.get("scale", 1.0 / math.sqrt(D))), context_lens=lens, block_tables=tables,
                   slot_mapping=slots, token_ids=token_ids, query_start_loc=qsl,
                   shared_blocks=shared, k_cache=k_cache, v_cache=v_cache, key=key,
                   value=value, q=q, device=str(device))

@@ -271,6 +271,16 @@ PREFILL_VARIANTS = {
                    cached=("uniform", 0, 500), chunk=[96, 33], max_context=640),
     "group3": dict(num_seqs=2, num_heads=12, num_kv_heads=4, head_dim=64, block_size=128,
                    cached=("uniform", 0, 500), chunk=[50, 129], max_context=768),
+    # 568 blocks of 8 tokens: more than the kernel's block-table window holds at once
+    "bs8_long_context": dict(num_seqs=2, num_heads=8, num_kv_heads=2, block_size=8,
+                             cached=("fixed", [4500, 70]), chunk=[40, 90], max_context=4608),
+    # scale 1: logits with std ~11, so the running maximum moves by large steps
+    "peaked_scores": dict(num_seqs=3, cached=("uniform", 0, 700), chunk=[100, 64, 31],
+                          max_context=1024, scale=1.0),
+    # negative scale: the softmax favours the smallest dot products
+    "negative_scale": dict(num_seqs=2, num_heads=8, num_kv_heads=8, head_dim=64, block_size=32,
+                           cached=("uniform", 0, 300), chunk=[45, 70], max_context=512,
+                           scale=-0.125),
 }
 
 
