@@ -43,6 +43,8 @@
 // Bound: MFMA (bf16 dense). Algorithmic flops = 4 * D * Hq * (visible
 // query-key pairs).
 
+#include <type_traits>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -58,9 +60,15 @@ struct PrefillParams {
   const int32_t* context_lens;
   int32_t num_heads, num_kv_heads, group, n_sub;
   int32_t bs_log2, num_blocks, max_blocks_per_seq, max_query_len, max_context_len;
+  int32_t num_seqs;
   int32_t row_blocks;  // gridDim.z: ceil(max_query_len / ROWS)
   float scale_log2;
 };
+
+// Work items (sequence, row block) are ranked by their number of key tiles
+// when there are at most this many of them; larger launches keep the grid
+// order (row blocks from the end of the chunk first).
+constexpr int RANK_MAX_ITEMS = 512;
 
 // Lazy-rescale threshold in log2 units: probabilities stay below 2^8.
 constexpr float RESCALE_SLACK = 8.0f;
@@ -111,10 +119,49 @@ __global__ __launch_bounds__(256, 2) void prefill_chunk_kernel(PrefillParams p) 
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qgrp = lane >> 4;     // 0..3
   const int lrow = lane & 15;
-  const int seq = blockIdx.y;
+
+  // ---- which (sequence, row block) this workgroup takes ----
+  // Workgroups are dispatched in order of (blockIdx.z, blockIdx.y); the k-th
+  // one takes the work item with the k-th most key tiles, so the longest
+  // items start first and short ones fill in at the end.
+  auto item_tiles = [&](int s, int rb) {
+    const int q0 = p.query_start_loc[s];
+    const int nn = min(p.query_start_loc[s + 1] - q0, p.max_query_len);
+    const int tt = rb * ROWS;
+    if (tt >= nn) return 0;
+    const int LL = min(p.context_lens[s], p.max_context_len);
+    const int ke = min(LL, LL - nn + min(tt + ROWS, nn));
+    return ke > 0 ? (ke + KT - 1) / KT : 0;
+  };
+  const int R = p.row_blocks;
+  const int n_items = p.num_seqs * R;
+  const int k_rank = (int)blockIdx.z * p.num_seqs + (int)blockIdx.y;
+  int seq, rb;
+  if (n_items <= RANK_MAX_ITEMS) {
+    int* cost = reinterpret_cast<int*>(&kv0[0][0]);  // LDS, free until the main loop
+    for (int x = tid; x < n_items; x += 256) cost[x] = item_tiles(x / R, x % R);
+    __syncthreads();
+    for (int x = tid; x < n_items; x += 256) {
+      const int cx = cost[x];
+      int r = 0;
+      for (int y = 0; y < n_items; ++y) {
+        const int cy = cost[y];
+        r += (cy > cx) || (cy == cx && y < x);
+      }
+      if (r == k_rank) tbl[0] = x;
+    }
+    __syncthreads();
+    const int x = tbl[0];
+    __syncthreads();  // tbl is reused for the block table below
+    seq = x / R;
+    rb = x % R;
+  } else {
+    seq = blockIdx.y;
+    rb = R - 1 - (int)blockIdx.z;
+  }
   const int qs = p.query_start_loc[seq];
   const int n = min(p.query_start_loc[seq + 1] - qs, p.max_query_len);
-  const int t0 = (p.row_blocks - 1 - (int)blockIdx.z) * ROWS;  // longest ranges first
+  const int t0 = rb * ROWS;
   if (t0 >= n) return;  // whole workgroup
   const int L = min(p.context_lens[seq], p.max_context_len);
   const int c = L - n;
@@ -164,6 +211,10 @@ __global__ __launch_bounds__(256, 2) void prefill_chunk_kernel(PrefillParams p) 
   };
 
   // Q^T B operands: lane holds Q[row lrow][32*ks + 8*qgrp .. +8] per tile.
+  // A negative scale is applied as an (exact) sign flip of Q, so that the
+  // logit scale sl2 below is never negative.
+  const uint32_t qsign = p.scale_log2 < 0.0f ? 0x80008000u : 0u;
+  const float sl2 = fabsf(p.scale_log2);
   bf16x8 qreg[2][KS];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
@@ -174,6 +225,7 @@ __global__ __launch_bounds__(256, 2) void prefill_chunk_kernel(PrefillParams p) 
       if (t < n)
         v = *reinterpret_cast<const uint4*>(
             p.q + ((int64_t)(qs + t) * p.num_heads + head) * D + 32 * ks + 8 * qgrp);
+      v.x ^= qsign; v.y ^= qsign; v.z ^= qsign; v.w ^= qsign;
       qreg[rt][ks] = __builtin_bit_cast(bf16x8, v);
     }
   }
@@ -187,7 +239,6 @@ __global__ __launch_bounds__(256, 2) void prefill_chunk_kernel(PrefillParams p) 
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[dt][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const float sl2 = p.scale_log2;
 
   __syncthreads();  // table window visible
   issue(0, kv0);
@@ -237,66 +288,78 @@ __global__ __launch_bounds__(256, 2) void prefill_chunk_kernel(PrefillParams p) 
     }
 
     // ---- online softmax per query row (lane row lrow of tile rt) ----
-    const bool masked = kt0 + KT - 1 > c + wrow0;  // some key is past some row's diagonal
-    float mt[2];
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const int tpos = c + wrow0 + rt * 16 + lrow;  // absolute position of the row
-      float mx = -INFINITY;
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float v = s[c2][hf][rt][i] * sl2;
-            if (masked) {
-              const int key = kt0 + 32 * c2 + 8 * qgrp + 4 * hf + i;
-              v = (key <= tpos) ? v : -INFINITY;
-            }
-            s[c2][hf][rt][i] = v;
-            mx = fmaxf(mx, v);
-          }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mt[rt] = fmaxf(mx, __shfl_xor(mx, 32));
-    }
-    // Raise the running maxima only when some row's tile maximum exceeds its
-    // kept maximum by more than the slack (wave-uniform decision).
-    const bool grow = (mt[0] > m[0] + RESCALE_SLACK) || (mt[1] > m[1] + RESCALE_SLACK);
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+    // Logits are s * sl2 with sl2 >= 0 (a negative scale was moved into the
+    // sign of Q), so a row's largest logit comes from its largest raw score.
+    // Only tiles that cross this wave's causal diagonal take the masked path.
+    bf16x8 pb[2][2];
+    auto softmax = [&](auto masked_tag) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
+      float mt[2];
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
-        const float mn = fmaxf(m[rt], mt[rt]);
-        const float alpha = fast_exp2(m[rt] - mn);
-        m[rt] = mn;
-        lsum[rt] *= alpha;
+        const int tpos = c + wrow0 + rt * 16 + lrow;  // absolute position of the row
+        float mx = -INFINITY;
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) o[dt][rt] *= alpha;
+        for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              float v = s[c2][hf][rt][i];
+              if constexpr (MASKED) {
+                const int key = kt0 + 32 * c2 + 8 * qgrp + 4 * hf + i;
+                v = (key <= tpos) ? v : -INFINITY;
+                s[c2][hf][rt][i] = v;
+              }
+              mx = fmaxf(mx, v);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mt[rt] = (MASKED && mx == -INFINITY) ? -INFINITY : mx * sl2;
       }
-    }
-    bf16x8 pb[2][2];
+      // Raise a row's running maximum only when the tile's maximum exceeds it
+      // by more than the slack. The four lanes that hold a row agree on the
+      // decision; the branch is skipped when no lane needs it.
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      const float mr = m[rt];
-      float ps = 0.0f;
+      for (int rt = 0; rt < 2; ++rt) {
+        if (mt[rt] > m[rt] + RESCALE_SLACK) {
+          asm volatile("" ::: "memory");  // keep it a branch, not selects
+          const float alpha = fast_exp2(m[rt] - mt[rt]);
+          m[rt] = mt[rt];
+          lsum[rt] *= alpha;
 #pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2) {
-        uint32_t w[4];
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const float p0 = fast_exp2(s[c2][hf][rt][0] - mr);
-          const float p1 = fast_exp2(s[c2][hf][rt][1] - mr);
-          const float p2 = fast_exp2(s[c2][hf][rt][2] - mr);
-          const float p3 = fast_exp2(s[c2][hf][rt][3] - mr);
-          w[2 * hf] = pack_bf16x2(p0, p1);
-          w[2 * hf + 1] = pack_bf16x2(p2, p3);
-          // sum the rounded weights, the ones the PV product uses
-          ps += bf16lo(w[2 * hf]) + bf16hi(w[2 * hf]) + bf16lo(w[2 * hf + 1]) + bf16hi(w[2 * hf + 1]);
+          for (int dt = 0; dt < DT; ++dt) o[dt][rt] *= alpha;
         }
-        pb[rt][c2] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
       }
-      lsum[rt] += ps;
-    }
+      const uint32_t ones = 0x3F803F80u;  // two bf16 1.0
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const float nm = -m[rt];
+        float ps = lsum[rt];
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2) {
+          uint32_t w[4];
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+            for (int i2 = 0; i2 < 2; ++i2) {
+              float p0 = fast_exp2(fmaf(s[c2][hf][rt][2 * i2], sl2, nm));
+              float p1 = fast_exp2(fmaf(s[c2][hf][rt][2 * i2 + 1], sl2, nm));
+              if constexpr (MASKED) {
+                p0 = (s[c2][hf][rt][2 * i2] == -INFINITY) ? 0.0f : p0;
+                p1 = (s[c2][hf][rt][2 * i2 + 1] == -INFINITY) ? 0.0f : p1;
+              }
+              const uint32_t pk = pack2_bf16(p0, p1);
+              w[2 * hf + i2] = pk;
+              ps = dot2_bf16(pk, ones, ps);  // the rounded weights the PV product uses
+            }
+          pb[rt][c2] = __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+        }
+        lsum[rt] = ps;
+      }
+    };
+    if (kt0 + KT - 1 > c + wrow0) softmax(std::true_type{});
+    else softmax(std::false_type{});
 
     // ---- O^T += V^T P^T; V^T fragments come from the transposing read ----
     const int src_key = 8 * qgrp + (lrow >> 2);  // + 32*c2 + 4*h
@@ -360,6 +423,7 @@ static void launch_prefill_t(PrefillParams prm, int32_t max_query_len, int32_t n
                              int32_t num_kv_heads, hipStream_t stream) {
   constexpr int ROWS = 32 * (4 / HW);
   prm.row_blocks = (max_query_len + ROWS - 1) / ROWS;
+  prm.num_seqs = num_seqs;
   // x: head group, y: sequence, z: row block (from the end of the chunk).
   const dim3 grid((unsigned)(num_kv_heads * prm.n_sub), (unsigned)num_seqs, (unsigned)prm.row_blocks);
   hipLaunchKernelGGL((prefill_chunk_kernel<D, HW>), grid, dim3(256), 0, stream, prm);
