@@ -4,7 +4,8 @@
 
 A step is one pass of the decode hot path over one batch: pa_store_kvcache
 writes the new token's K/V row of every sequence, then pa_decode attends over
-the whole paged context (split into partitions, merged in the same launch).
+the whole paged context (balanced split: equal K/V ranges per resident wave,
+then a merge kernel for the sequences the ranges cut).
 The default workload is the bf16 MHA decode batch (64 sequences, 12 heads,
 head_dim 64, block 256, context lengths uniform in [512, 4096]). Several
 independently drawn batches (each with its own pool) are resident in HBM and
@@ -12,12 +13,13 @@ the steps cycle through them, so consecutive steps never find their K/V in the
 256 MB last-level cache.
 
 Prints ONE JSON line. `value` is decode tokens/s (sequences x steps / timed
-seconds). `roofline` covers the decode kernel: algorithmic K+V bytes per launch
-over its average duration, from HIP events recorded on the launch stream
-around each timed launch. `cpu_baseline` is the CPU oracle on a bounded sample
-of the same workload, single-threaded. `extra` reports the other workloads
-(GQA decode with shared prefix, GQA decode at 512 sequences, chunked prefill)
-measured the same way.
+seconds). `roofline` covers the decode call (its main and merge kernels):
+algorithmic K+V bytes per launch over its average duration, from HIP events
+recorded on the launch stream around each timed launch. `cpu_baseline` is the
+CPU oracle on a bounded sample of the same workload, single-threaded. `extra`
+reports the other workloads (GQA decode with shared prefix, GQA decode at 512
+sequences, each with the balanced split and with its fixed-slice split, and
+chunked prefill) measured the same way.
 """
 
 from __future__ import annotations
@@ -52,9 +54,9 @@ def log(msg):
 class DecodeSet:
     """R resident batches of one decode workload, with device-side arrays."""
 
-    def __init__(self, cfg, rotations, device):
+    def __init__(self, cfg, rotations, device, partition=None):
         self.spec = wl.spec(cfg)
-        self.P = self.spec.get("partition_size", 0)
+        self.P = self.spec.get("partition_size", 0) if partition is None else partition
         self.batches = []
         for r in range(rotations):
             b = wl.make_batch(self.spec, device=device, seed=wl.SEED_BASE + cfg + 1000 * r)
@@ -135,19 +137,24 @@ def bench_prefill(steps, warmup, device):
                 tokens_per_s=round(int(b.query_start_loc[-1]) / (ms * 1e-3), 1))
 
 
-def measured_traffic(workload_name):
-    """HBM bytes per decode launch from the committed counter runs, or None
-    when there are none or the decode kernel sources changed since."""
+def measured_traffic(workload_name, split):
+    """HBM bytes per decode launch (split "balanced" or "fixed") from the
+    committed counter runs, or None when there are none or the decode kernel
+    sources changed since."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     with open(TRAFFIC_FILE) as fh:
         rec = json.load(fh)
     if rec.get("kernel_source_sha256") != decode_source_hash():
         return None
-    w = rec.get("workloads", {}).get(workload_name)
+    w = rec.get("workloads", {}).get(workload_name, {}).get(split)
     if not w:
         return None
     return int(w["hbm_bytes_per_launch"])
+
+
+def split_name(P):
+    return "balanced" if P == pa.PA_PARTITION_BALANCED else "fixed"
 
 
 def copy_probe(nbytes, device, reps=3):
@@ -235,34 +242,39 @@ def main():
             "num_seqs": b0.num_seqs, "num_heads": b0.num_heads, "num_kv_heads": b0.num_kv_heads,
             "head_dim": b0.head_dim, "block_size": b0.block_size,
             "context_lens": "uniform[512,4096]" if args.workload == 2 else str(ds.spec["lens"]),
-            "partition_size": ds.P, "rotating_batches": args.rotations,
+            "split": split_name(ds.P), "partition_size": ds.P, "rotating_batches": args.rotations,
             "step": "store_kvcache(new rows) + decode",
         },
         "roofline": {
-            "bound": "hbm", "kernel": "paged_decode_kernel",
+            "bound": "hbm",
+            "kernel": ("pa_decode: paged_decode_balanced_kernel + paged_decode_balanced_merge_kernel"
+                       if ds.P == pa.PA_PARTITION_BALANCED else "pa_decode: paged_decode_kernel (+ merge)"),
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(ds.spec["name"]),
+            "traffic": measured_traffic(ds.spec["name"], split_name(ds.P)),
             "kernel_ms": round(kms, 4), "bytes_per_launch": int(kbytes),
         },
     }
     if not args.no_extra:
         extra = {}
         for cfg in (2, 3, 5):
-            if cfg == args.workload:
-                continue
-            log(f"extra workload {cfg}")
-            d = DecodeSet(cfg, 2, dev)
-            s, ms, nb, _ = time_decode(d, 30, 5)
-            bb = d.batches[0][0]
-            extra[d.spec["name"]] = dict(
-                tokens_per_s=round(bb.num_seqs * 30 / s, 1), kernel_ms=round(ms, 4),
-                kv_gbs=round(nb / (ms * 1e-3) / 1e9, 1),
-                frac_of_hbm_peak=round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                bytes_per_launch=int(nb), partition_size=d.P,
-                logical_bytes_per_launch=int(np.mean(d.kv_bytes_logical)))
-            del d
-            torch.cuda.empty_cache()
+            for P in (wl.CONFIGS[cfg]["partition_size"], wl.CONFIGS[cfg]["fixed_partition_size"]):
+                if cfg == args.workload and P == ds.P:
+                    continue
+                log(f"extra workload {cfg} partition_size={P}")
+                d = DecodeSet(cfg, 2, dev, partition=P)
+                s, ms, nb, _ = time_decode(d, 30, 5)
+                bb = d.batches[0][0]
+                key = d.spec["name"] + ("" if P == pa.PA_PARTITION_BALANCED else f"_fixed_p{P}")
+                extra[key] = dict(
+                    tokens_per_s=round(bb.num_seqs * 30 / s, 1), kernel_ms=round(ms, 4),
+                    kv_gbs=round(nb / (ms * 1e-3) / 1e9, 1),
+                    frac_of_hbm_peak=round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    bytes_per_launch=int(nb), split=split_name(P), partition_size=P,
+                    traffic=measured_traffic(d.spec["name"], split_name(P)),
+                    logical_bytes_per_launch=int(np.mean(d.kv_bytes_logical)))
+                del d
+                torch.cuda.empty_cache()
         log("extra prefill")
         extra["prefill"] = bench_prefill(20, 3, dev)
         line["extra"] = extra

@@ -75,6 +75,9 @@ typedef enum pa_status {
 
 typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
 
+/* partition_size value of pa_decode that selects the balanced split. */
+#define PA_PARTITION_BALANCED (-1)
+
 /*
  * pa_store_kvcache -- scatter new K/V rows into the pools.
  *
@@ -98,10 +101,12 @@ pa_status pa_store_kvcache(const void* key, const void* value,
                            pa_dtype dtype, void* stream);
 
 /*
- * pa_decode_workspace_size -- bytes of workspace pa_decode needs when the
- * context is split into partitions of partition_size tokens; 0 when no
- * sequence can need more than one partition (partition_size == 0 or
- * partition_size >= max_context_len). Returns 0 for invalid arguments too.
+ * pa_decode_workspace_size -- bytes of workspace pa_decode needs for the
+ * given split: partitions of partition_size tokens (0 when no sequence can
+ * need more than one partition, i.e. partition_size == 0 or partition_size
+ * >= max_context_len), or the balanced split (PA_PARTITION_BALANCED; the
+ * size depends on the current device's compute-unit count, 256 assumed when
+ * no device is visible). Returns 0 for invalid arguments too.
  */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
                                 int32_t num_kv_heads, int32_t head_dim,
@@ -115,12 +120,18 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
  * over the context_lens[i] tokens of sequence i gathered through
  * block_tables[i], g = h / (num_heads / num_kv_heads).
  *
- * partition_size > 0 splits each context into slices of that many tokens
- * (a multiple of 16); every slice yields an fp32 (max, sum, weighted values)
- * state in the workspace, and a second kernel on the same stream merges the
- * states of each (sequence, head) into out. partition_size == 0 attends over
- * whole contexts in one kernel. The result does not depend on the split
- * beyond fp32 rounding.
+ * partition_size selects how contexts are split across waves:
+ *   0                      whole contexts, one kernel;
+ *   > 0 (multiple of 16)   slices of that many tokens; every slice yields an
+ *                          fp32 (max, sum, weighted values) state in the
+ *                          workspace, and a second kernel on the same stream
+ *                          merges the states of each (sequence, head);
+ *   PA_PARTITION_BALANCED  the contexts laid end to end are cut into equal
+ *                          ranges, one per resident wave, so that every wave
+ *                          streams the same number of K/V bytes whatever the
+ *                          length mix; sequences cut by a range boundary are
+ *                          merged by a second kernel. At most 4096 sequences.
+ * The result does not depend on the split beyond fp32 rounding.
  *
  * workspace: device memory of at least pa_decode_workspace_size(...) bytes,
  * 256-byte aligned; its contents on entry do not matter and are scratch

@@ -18,6 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_NAME = "libpagedattn.so"
 
 PA_F32, PA_BF16 = 0, 1
+PA_PARTITION_BALANCED = -1  # pa_decode partition_size: equal work per resident wave
 _STATUS = {0: "PA_OK", 1: "PA_ERR_INVALID_ARG", 2: "PA_ERR_UNSUPPORTED",
            3: "PA_ERR_WORKSPACE", 4: "PA_ERR_HIP"}
 

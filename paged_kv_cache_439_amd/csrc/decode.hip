@@ -35,8 +35,14 @@
 #include "pa_device.h"
 #include "pa_internal.h"
 
+#include <algorithm>
+
 #ifndef DECODE_U
 #define DECODE_U 8
+#endif
+// Resident waves per SIMD the balanced split plans for.
+#ifndef DECODE_BAL_WAVES_PER_SIMD
+#define DECODE_BAL_WAVES_PER_SIMD 2
 #endif
 
 namespace pa {
@@ -48,8 +54,12 @@ struct DecodeParams {
   const char* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
-  float* ws_acc;     // [B][Hq][max_parts][D]
-  float* ws_ml;      // [B][Hq][max_parts][2]
+  float* ws_acc;     // fixed split: [B][Hq][max_parts][D]
+  float* ws_ml;      // fixed split: [B][Hq][max_parts][2]
+  float* part_acc;   // balanced split: [workers][2 slots][Hq][D]
+  float* part_ml;    // balanced split: [workers][2 slots][Hq][2]
+  int32_t* ws_pfx;   // balanced split: chunk prefix sums [B + 1]
+  int32_t num_seqs, workers;  // balanced split: workers per unit
   int32_t num_heads, num_kv_heads, group, n_sub, units;
   int32_t bs_log2, num_blocks, max_blocks_per_seq, max_context_len;
   int32_t partition, max_parts;
@@ -145,78 +155,58 @@ __device__ __forceinline__ void merge_row_groups(float (&m)[GT], float (&l)[GT],
   }
 }
 
-// UNIFORM_BLOCK: every chunk lies inside one block (block_size >= CT and
-// partitions start at multiples of CT), so one scalar table lookup serves the
-// whole chunk; otherwise each lane looks up its own token's block.
+// The online-softmax state of one wave: per head of its group, the running
+// maximum m (log2 units), the running sum l and the weighted value sum acc
+// over this lane's d-slice, kept separately per token-row group tr.
+template <int GT, int EPL>
+struct WaveState {
+  float m[GT], l[GT], acc[GT][EPL];
+  __device__ __forceinline__ void reset() {
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+      m[h] = NEG_BIG;
+      l[h] = 0.0f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] = 0.0f;
+    }
+  }
+};
+
+// Load this lane's 16-byte q slices of heads h0 .. h0+GT-1 of sequence seq.
+template <typename T, int D, int GT>
+__device__ __forceinline__ void load_q(const DecodeParams& p, int seq, int h0, int dc, uint4 (&qv)[GT]) {
+  constexpr int E = ElemTraits<T>::E;
+  const char* qb = static_cast<const char*>(p.q);
+#pragma unroll
+  for (int h = 0; h < GT; ++h)
+    qv[h] = *reinterpret_cast<const uint4*>(qb + (((int64_t)seq * p.num_heads + h0 + h) * D) * E + dc * 16);
+}
+
+// Stream tokens [tok_begin, tok_end) of sequence seq (KV head kvh) through
+// the online softmax of st. UNIFORM_BLOCK: every chunk lies inside one block
+// (block_size >= CT and tok_begin a multiple of CT), so one table lookup per
+// chunk serves all lanes; otherwise each lane looks up its own token's block.
 template <typename T, int D, int GT, int U, bool UNIFORM_BLOCK>
-__global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams p) {
+__device__ __forceinline__ void attend_range(const DecodeParams& p, int seq, int kvh, int lane,
+                                             int tok_begin, int tok_end, const uint4 (&qv)[GT],
+                                             WaveState<GT, 16 / ElemTraits<T>::E>& st) {
   constexpr int E = ElemTraits<T>::E;
   constexpr int EPL = 16 / E;     // elements per 16-byte lane slice
   constexpr int LPT = D / EPL;    // lanes per token row of one head
   constexpr int TPW = 64 / LPT;   // token rows per wave-wide load
   constexpr int CT = U * TPW;     // tokens per chunk
-  static_assert(LPT >= 1 && LPT <= 32 && (64 % LPT) == 0, "unsupported head_dim");
-
-  const int lane = threadIdx.x & 63;
-  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (unit >= p.units) return;
-  const int seq = blockIdx.z;
-  const int part = blockIdx.y;
-  const int L = min(p.context_lens[seq], p.max_context_len);
-  const int P = p.partition;
-  const int nparts = L > 0 ? (L + P - 1) / P : 0;
-
-  const int kvh = unit / p.n_sub;
-  const int h0 = kvh * p.group + (unit - kvh * p.n_sub) * GT;
   const int dc = lane % LPT;
   const int tr = lane / LPT;
-  const int64_t head_stride = D;
-  char* const out_base = static_cast<char*>(p.out);
-
-  if (nparts == 0) {  // empty context: defined output of zeros
-    if (part == 0 && tr == 0) {
-      float z[EPL];
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) z[e] = 0.0f;
-#pragma unroll
-      for (int h = 0; h < GT; ++h)
-        store_slice<T, EPL>(out_base + (((int64_t)seq * p.num_heads + h0 + h) * head_stride + dc * EPL) * E, z);
-    }
-    return;
-  }
-  if (part >= nparts) return;
-
-  const int tok_begin = part * P;
-  const int tok_end = min(L, tok_begin + P);
   const int bs_log2 = p.bs_log2;
   const int bs_mask = (1 << bs_log2) - 1;
   const int row_bytes = p.row_bytes;
   const int lane_off = kvh * D * E + dc * 16;
   const int32_t* bt = p.block_tables + (int64_t)seq * p.max_blocks_per_seq;
 
-  // q slices of the GT heads, as stored (bf16 pairs feed v_dot2 directly).
-  uint4 qv[GT];
-  {
-    const char* qb = static_cast<const char*>(p.q);
-#pragma unroll
-    for (int h = 0; h < GT; ++h)
-      qv[h] = *reinterpret_cast<const uint4*>(
-          qb + (((int64_t)seq * p.num_heads + h0 + h) * head_stride) * E + dc * 16);
-  }
-
   // Block-table window: lane i holds the physical id of block wbase + i.
   const int last_blk = (tok_end - 1) >> bs_log2;
   int wbase = tok_begin >> bs_log2;
   int tbl = (wbase + lane <= last_blk) ? clamp_block(bt[wbase + lane], p.num_blocks) : 0;
-
-  float m[GT], l[GT], acc[GT][EPL];
-#pragma unroll
-  for (int h = 0; h < GT; ++h) {
-    m[h] = NEG_BIG;
-    l[h] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.0f;
-  }
 
   for (int j0 = tok_begin; j0 < tok_end; j0 += CT) {
     const int chunk_last = (min(j0 + CT, tok_end) - 1) >> bs_log2;
@@ -274,16 +264,16 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams p) {
         s[u][h] = valid[u] ? s[u][h] * p.scale_log2 : -INFINITY;
         cm = fmaxf(cm, s[u][h]);
       }
-      const float mn = fmaxf(m[h], cm);
-      const float alpha = fast_exp2(m[h] - mn);
-      m[h] = mn;
-      l[h] *= alpha;
+      const float mn = fmaxf(st.m[h], cm);
+      const float alpha = fast_exp2(st.m[h] - mn);
+      st.m[h] = mn;
+      st.l[h] *= alpha;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] *= alpha;
+      for (int e = 0; e < EPL; ++e) st.acc[h][e] *= alpha;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         s[u][h] = fast_exp2(s[u][h] - mn);
-        l[h] += s[u][h];
+        st.l[h] += s[u][h];
       }
     }
 
@@ -294,23 +284,85 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams p) {
 #pragma unroll
       for (int h = 0; h < GT; ++h)
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(s[u][h], vf[e], acc[h][e]);
+        for (int e = 0; e < EPL; ++e) st.acc[h][e] = fmaf(s[u][h], vf[e], st.acc[h][e]);
     }
   }
+}
 
-  merge_row_groups<LPT, GT, EPL>(m, l, acc);
+// Write the (merged) state of heads h0.. of sequence seq as the final output.
+template <typename T, int D, int GT, int EPL>
+__device__ __forceinline__ void store_output(const DecodeParams& p, int seq, int h0, int dc,
+                                             const WaveState<GT, EPL>& st) {
+  constexpr int E = ElemTraits<T>::E;
+  char* const out_base = static_cast<char*>(p.out);
+#pragma unroll
+  for (int h = 0; h < GT; ++h) {
+    float o[EPL];
+    const float inv = 1.0f / st.l[h];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[e] = st.acc[h][e] * inv;
+    store_slice<T, EPL>(out_base + (((int64_t)seq * p.num_heads + h0 + h) * D + dc * EPL) * E, o);
+  }
+}
+
+// Zeros for heads h0.. of sequence seq (the defined output of an empty context).
+template <typename T, int D, int GT>
+__device__ __forceinline__ void store_zeros(const DecodeParams& p, int seq, int h0, int dc) {
+  constexpr int E = ElemTraits<T>::E;
+  constexpr int EPL = 16 / E;
+  char* const out_base = static_cast<char*>(p.out);
+  float z[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) z[e] = 0.0f;
+#pragma unroll
+  for (int h = 0; h < GT; ++h)
+    store_slice<T, EPL>(out_base + (((int64_t)seq * p.num_heads + h0 + h) * D + dc * EPL) * E, z);
+}
+
+// Workgroups per CU the decode kernels are compiled for: 3 (12 waves) keeps
+// enough loads in flight; eight heads per wave need the registers of 2.
+template <int GT>
+constexpr int decode_min_wgs() { return GT >= 8 ? 2 : 3; }
+
+// One wave = (sequence, KV head, group of GT query heads, partition).
+template <typename T, int D, int GT, int U, bool UNIFORM_BLOCK>
+__global__ __launch_bounds__(256, decode_min_wgs<GT>()) void paged_decode_kernel(DecodeParams p) {
+  constexpr int E = ElemTraits<T>::E;
+  constexpr int EPL = 16 / E;     // elements per 16-byte lane slice
+  constexpr int LPT = D / EPL;    // lanes per token row of one head
+  static_assert(LPT >= 1 && LPT <= 32 && (64 % LPT) == 0, "unsupported head_dim");
+
+  const int lane = threadIdx.x & 63;
+  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (unit >= p.units) return;
+  const int seq = blockIdx.z;
+  const int part = blockIdx.y;
+  const int L = min(p.context_lens[seq], p.max_context_len);
+  const int P = p.partition;
+  const int nparts = L > 0 ? (L + P - 1) / P : 0;
+
+  const int kvh = unit / p.n_sub;
+  const int h0 = kvh * p.group + (unit - kvh * p.n_sub) * GT;
+  const int dc = lane % LPT;
+  const int tr = lane / LPT;
+
+  if (nparts == 0) {  // empty context: defined output of zeros
+    if (part == 0 && tr == 0) store_zeros<T, D, GT>(p, seq, h0, dc);
+    return;
+  }
+  if (part >= nparts) return;
+
+  const int tok_begin = part * P;
+  const int tok_end = min(L, tok_begin + P);
+  uint4 qv[GT];
+  load_q<T, D, GT>(p, seq, h0, dc, qv);
+  WaveState<GT, EPL> st;
+  st.reset();
+  attend_range<T, D, GT, U, UNIFORM_BLOCK>(p, seq, kvh, lane, tok_begin, tok_end, qv, st);
+  merge_row_groups<LPT, GT, EPL>(st.m, st.l, st.acc);
 
   if (nparts == 1) {
-    if (tr == 0) {
-#pragma unroll
-      for (int h = 0; h < GT; ++h) {
-        float o[EPL];
-        const float inv = 1.0f / l[h];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) o[e] = acc[h][e] * inv;
-        store_slice<T, EPL>(out_base + (((int64_t)seq * p.num_heads + h0 + h) * head_stride + dc * EPL) * E, o);
-      }
-    }
+    if (tr == 0) store_output<T, D, GT, EPL>(p, seq, h0, dc, st);
     return;
   }
 
@@ -323,8 +375,9 @@ __global__ __launch_bounds__(256) void paged_decode_kernel(DecodeParams p) {
       float* dst = p.ws_acc + (sh * mp + part) * D + dc * EPL;
 #pragma unroll
       for (int e = 0; e < EPL; e += 4)
-        *reinterpret_cast<float4*>(dst + e) = make_float4(acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]);
-      if (dc == 0) *reinterpret_cast<float2*>(p.ws_ml + (sh * mp + part) * 2) = make_float2(m[h], l[h]);
+        *reinterpret_cast<float4*>(dst + e) =
+            make_float4(st.acc[h][e], st.acc[h][e + 1], st.acc[h][e + 2], st.acc[h][e + 3]);
+      if (dc == 0) *reinterpret_cast<float2*>(p.ws_ml + (sh * mp + part) * 2) = make_float2(st.m[h], st.l[h]);
     }
   }
 }
@@ -398,17 +451,218 @@ __global__ __launch_bounds__(256) void paged_decode_merge_kernel(DecodeParams p)
 }
 
 // ---------------------------------------------------------------------------
+// balanced split
+// ---------------------------------------------------------------------------
+//
+// The contexts of all sequences, cut into chunks of CT tokens, are laid end
+// to end; the W workers of each unit (one wave each, all resident at once)
+// take equal contiguous ranges of that chunk sequence. A worker streams its
+// range without a break, crossing from one sequence into another: a
+// sequence wholly inside one range is written out directly, and a sequence
+// cut by a range boundary leaves a partial (m, l, acc) state in one of the
+// worker's two slots (slot 0: the piece the range starts in, slot 1: the
+// piece it ends in), which paged_decode_balanced_merge_kernel combines.
+// Every worker does the same amount of work whatever the length mix, and
+// each wave pays its start-up (prefix sums, q, table window) once.
+
+// Sequences the balanced split supports (their chunk prefix sums live in LDS).
+constexpr int BAL_MAX_SEQS = 4096;
+
+// pfx[0] = 0, pfx[k+1] = pfx[k] + ceil(L_k / CT): chunk prefix sums of the
+// clamped context lengths, computed by the whole workgroup.
+template <int CT>
+__device__ __forceinline__ void chunk_prefix(const DecodeParams& p, int32_t* pfx) {
+  __shared__ int32_t wave_total[4];
+  const int B = p.num_seqs;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int per = (B + 255) / 256;
+  const int k0 = min(B, tid * per);
+  const int k1 = min(B, k0 + per);
+  auto chunks = [&](int k) {
+    const int L = min(p.context_lens[k], p.max_context_len);
+    return L > 0 ? (L + CT - 1) / CT : 0;
+  };
+  int local = 0;
+  for (int k = k0; k < k1; ++k) local += chunks(k);
+  int x = local;  // inclusive scan over the wave
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wave_total[wv] = x;
+  __syncthreads();
+  int run = x - local;
+  for (int w = 0; w < wv; ++w) run += wave_total[w];
+  if (tid == 0) pfx[0] = 0;
+  for (int k = k0; k < k1; ++k) {
+    run += chunks(k);
+    pfx[k + 1] = run;
+  }
+  __syncthreads();
+}
+
+template <typename T, int D, int GT, int U, bool UNIFORM_BLOCK>
+__global__ __launch_bounds__(256, 2) void paged_decode_balanced_kernel(DecodeParams p) {
+  constexpr int E = ElemTraits<T>::E;
+  constexpr int EPL = 16 / E;
+  constexpr int LPT = D / EPL;
+  constexpr int TPW = 64 / LPT;
+  constexpr int CT = U * TPW;
+  __shared__ int32_t pfx[BAL_MAX_SEQS + 1];
+  chunk_prefix<CT>(p, pfx);
+  const int B = p.num_seqs;
+  if (blockIdx.x == 0)
+    for (int k = threadIdx.x; k <= B; k += 256) p.ws_pfx[k] = pfx[k];
+  const int C = pfx[B];
+
+  const int lane = threadIdx.x & 63;
+  const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int unit = g % p.units;  // the waves of a workgroup share a range
+  const int w = g / p.units;
+  if (w >= p.workers) return;
+  const int c0 = (int)((int64_t)w * C / p.workers);
+  const int c1 = (int)((int64_t)(w + 1) * C / p.workers);
+  if (c0 >= c1) return;
+  const int kvh = unit / p.n_sub;
+  const int h0 = kvh * p.group + (unit - kvh * p.n_sub) * GT;
+  const int dc = lane % LPT;
+  const int tr = lane / LPT;
+
+  // Pieces are taken from the end of the range backwards. The last piece
+  // begins at a context's first token (unless the range lies inside one
+  // context), so the first blocks of contexts, which prefix sharing makes
+  // common to many sequences, are read by all workers near the start of the
+  // kernel, while the shared lines are still cached.
+  // The sequence holding chunk c1 - 1: the last i with pfx[i] <= c1 - 1.
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pfx[mid] <= c1 - 1) lo = mid;
+    else hi = mid - 1;
+  }
+  int i = lo;
+  for (;;) {
+    const int cb = pfx[i], ce = pfx[i + 1];
+    const int ps = max(c0, cb), pe = min(c1, ce);
+    const int L = min(p.context_lens[i], p.max_context_len);
+    uint4 qv[GT];
+    load_q<T, D, GT>(p, i, h0, dc, qv);
+    WaveState<GT, EPL> st;
+    st.reset();
+    attend_range<T, D, GT, U, UNIFORM_BLOCK>(p, i, kvh, lane, (ps - cb) * CT, min((pe - cb) * CT, L), qv, st);
+    merge_row_groups<LPT, GT, EPL>(st.m, st.l, st.acc);
+    if (tr == 0) {
+      if (ps == cb && pe == ce) {
+        store_output<T, D, GT, EPL>(p, i, h0, dc, st);
+      } else {
+        // slot 0: the piece holding c0; slot 1: the piece holding c1 - 1
+        const int64_t slot = (int64_t)w * 2 + (ps == c0 ? 0 : 1);
+#pragma unroll
+        for (int h = 0; h < GT; ++h) {
+          const int64_t sh = slot * p.num_heads + h0 + h;
+          float* dst = p.part_acc + sh * D + dc * EPL;
+#pragma unroll
+          for (int e = 0; e < EPL; e += 4)
+            *reinterpret_cast<float4*>(dst + e) =
+                make_float4(st.acc[h][e], st.acc[h][e + 1], st.acc[h][e + 2], st.acc[h][e + 3]);
+          if (dc == 0) *reinterpret_cast<float2*>(p.part_ml + sh * 2) = make_float2(st.m[h], st.l[h]);
+        }
+      }
+    }
+    if (ps <= c0) break;
+    do {
+      --i;
+    } while (pfx[i] == pfx[i + 1]);  // skip empty contexts
+  }
+}
+
+// One wave per (sequence, unit): combine the partial states the workers
+// left for a sequence their ranges cut, and write zeros for an empty
+// context. Sequences inside one range were written by the main kernel.
+template <typename T, int D, int GT>
+__global__ __launch_bounds__(256) void paged_decode_balanced_merge_kernel(DecodeParams p) {
+  constexpr int E = ElemTraits<T>::E;
+  constexpr int EPL = 16 / E;
+  constexpr int LPT = D / EPL;
+  constexpr int TPW = 64 / LPT;
+  const int lane = threadIdx.x & 63;
+  const int unit = blockIdx.y * 4 + (threadIdx.x >> 6);
+  if (unit >= p.units) return;
+  const int seq = blockIdx.x;
+  const int kvh = unit / p.n_sub;
+  const int h0 = kvh * p.group + (unit - kvh * p.n_sub) * GT;
+  const int dc = lane % LPT;
+  const int tr = lane / LPT;
+  const int L = min(p.context_lens[seq], p.max_context_len);
+  if (L <= 0) {
+    if (tr == 0) store_zeros<T, D, GT>(p, seq, h0, dc);
+    return;
+  }
+  const int cb = p.ws_pfx[seq], ce = p.ws_pfx[seq + 1], C = p.ws_pfx[p.num_seqs];
+  const int W = p.workers;
+  auto worker_of = [&](int ch) { return (int)((((int64_t)ch + 1) * W - 1) / C); };
+  auto start_of = [&](int wk) { return (int)((int64_t)wk * C / W); };
+  const int wf = worker_of(cb), wl = worker_of(ce - 1);
+  if (wf == wl) return;
+
+  WaveState<GT, EPL> st;
+  st.reset();
+  for (int wk = wf + tr; wk <= wl; wk += TPW) {
+    const int s0 = start_of(wk);
+    if (s0 == start_of(wk + 1)) continue;  // an empty range left nothing
+    const int64_t slot = (int64_t)wk * 2 + ((wk == wf && s0 != cb) ? 1 : 0);
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+      const int64_t sh = slot * p.num_heads + h0 + h;
+      const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + sh * 2);
+      const float* src = p.part_acc + sh * D + dc * EPL;
+      const float mn = fmaxf(st.m[h], ml.x);
+      const float a = fast_exp2(st.m[h] - mn);
+      const float b = fast_exp2(ml.x - mn);
+      st.l[h] = st.l[h] * a + ml.y * b;
+#pragma unroll
+      for (int e = 0; e < EPL; e += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(src + e);
+        st.acc[h][e] = st.acc[h][e] * a + v.x * b;
+        st.acc[h][e + 1] = st.acc[h][e + 1] * a + v.y * b;
+        st.acc[h][e + 2] = st.acc[h][e + 2] * a + v.z * b;
+        st.acc[h][e + 3] = st.acc[h][e + 3] * a + v.w * b;
+      }
+      st.m[h] = mn;
+    }
+  }
+  merge_row_groups<LPT, GT, EPL>(st.m, st.l, st.acc);
+  if (tr == 0) store_output<T, D, GT, EPL>(p, seq, h0, dc, st);
+}
+
+// ---------------------------------------------------------------------------
 // planning and launch
 // ---------------------------------------------------------------------------
 
+// Query heads one wave handles: at most 4 (a group of 8 becomes two waves
+// of the same workgroup, which read the same K/V rows through the caches).
 static int32_t heads_per_unit(int32_t group) {
-  for (int32_t g : {8, 4, 2}) {
-    if (group % g == 0) return g;
-  }
+  if (group % 4 == 0) return 4;
+  if (group % 2 == 0) return 2;
   return 1;
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Compute units of the current device (256 on MI355X when none is visible,
+// so that workspace sizes can be computed without a GPU).
+static int32_t device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  return n;
+}
 
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                        int32_t head_dim, int32_t max_context_len, int32_t partition_size) {
@@ -416,6 +670,19 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
   pl.group = num_heads / num_kv_heads;
   pl.heads_per_unit = heads_per_unit(pl.group);
   pl.units = num_kv_heads * (pl.group / pl.heads_per_unit);
+  if (partition_size == PA_PARTITION_BALANCED_VALUE) {
+    pl.balanced = true;
+    pl.partition = max_context_len > 0 ? max_context_len : 1;
+    pl.max_parts = 1;
+    const int64_t waves = (int64_t)DECODE_BAL_WAVES_PER_SIMD * 4 * device_cus();
+    pl.workers = (int32_t)std::max<int64_t>(1, waves / pl.units);
+    const size_t slots = (size_t)pl.workers * 2 * num_heads;
+    pl.acc_bytes = align256(slots * head_dim * sizeof(float));
+    pl.ml_bytes = align256(slots * 2 * sizeof(float));
+    pl.pfx_bytes = align256(((size_t)num_seqs + 1) * sizeof(int32_t));
+    pl.total_bytes = pl.acc_bytes + pl.ml_bytes + pl.pfx_bytes;
+    return pl;
+  }
   const bool split = partition_size > 0 && partition_size < max_context_len;
   pl.partition = split ? partition_size : (max_context_len > 0 ? max_context_len : 1);
   pl.max_parts = split ? (max_context_len + partition_size - 1) / partition_size : 1;
@@ -429,31 +696,37 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
 }
 
 template <typename T, int D, int GT, int U>
-static void launch_u(const DecodeParams& prm, dim3 grid, bool split, hipStream_t stream) {
+static void launch_u(const DecodeParams& prm, const DecodePlan& pl, dim3 grid, hipStream_t stream) {
   constexpr int TPW = 64 / (D * (int)sizeof(T) / 16);
   constexpr int CT = U * TPW;
-  const bool uniform = (1 << prm.bs_log2) >= CT && (prm.max_parts == 1 || prm.partition % CT == 0);
+  const bool big_blocks = (1 << prm.bs_log2) >= CT;
+  if (pl.balanced) {
+    const int64_t waves = (int64_t)pl.workers * pl.units;
+    const dim3 bgrid((unsigned)((waves + 3) / 4));
+    if (big_blocks)
+      hipLaunchKernelGGL((paged_decode_balanced_kernel<T, D, GT, U, true>), bgrid, dim3(256), 0, stream, prm);
+    else
+      hipLaunchKernelGGL((paged_decode_balanced_kernel<T, D, GT, U, false>), bgrid, dim3(256), 0, stream, prm);
+    hipLaunchKernelGGL((paged_decode_balanced_merge_kernel<T, D, GT>), dim3(grid.z, grid.x), dim3(256), 0,
+                       stream, prm);
+    return;
+  }
+  const bool uniform = big_blocks && (prm.max_parts == 1 || prm.partition % CT == 0);
   if (uniform)
     hipLaunchKernelGGL((paged_decode_kernel<T, D, GT, U, true>), grid, dim3(256), 0, stream, prm);
   else
     hipLaunchKernelGGL((paged_decode_kernel<T, D, GT, U, false>), grid, dim3(256), 0, stream, prm);
-  if (split)
-    hipLaunchKernelGGL((paged_decode_merge_kernel<T, D, GT>), dim3(grid.z, (grid.x)), dim3(256), 0,
+  if (pl.max_parts > 1)
+    hipLaunchKernelGGL((paged_decode_merge_kernel<T, D, GT>), dim3(grid.z, grid.x), dim3(256), 0,
                        stream, prm);
 }
 
-template <typename T, int D, int GT>
-static void launch_one(const DecodeParams& prm, dim3 grid, bool split, hipStream_t stream) {
-  launch_u<T, D, GT, DECODE_U>(prm, grid, split, stream);
-}
-
 template <typename T, int D>
-static void launch_gt(int gt, const DecodeParams& prm, dim3 grid, bool split, hipStream_t stream) {
-  switch (gt) {
-    case 1: launch_one<T, D, 1>(prm, grid, split, stream); break;
-    case 2: launch_one<T, D, 2>(prm, grid, split, stream); break;
-    case 4: launch_one<T, D, 4>(prm, grid, split, stream); break;
-    default: launch_one<T, D, 8>(prm, grid, split, stream); break;
+static void launch_gt(const DecodeParams& prm, const DecodePlan& pl, dim3 grid, hipStream_t stream) {
+  switch (pl.heads_per_unit) {
+    case 1: launch_u<T, D, 1, DECODE_U>(prm, pl, grid, stream); break;
+    case 2: launch_u<T, D, 2, DECODE_U>(prm, pl, grid, stream); break;
+    default: launch_u<T, D, 4, DECODE_U>(prm, pl, grid, stream); break;
   }
 }
 
@@ -467,9 +740,17 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   prm.context_lens = a.context_lens;
   if (pl.total_bytes) {
     char* ws = static_cast<char*>(a.workspace);
-    prm.ws_acc = reinterpret_cast<float*>(ws);
-    prm.ws_ml = reinterpret_cast<float*>(ws + pl.acc_bytes);
+    if (pl.balanced) {
+      prm.part_acc = reinterpret_cast<float*>(ws);
+      prm.part_ml = reinterpret_cast<float*>(ws + pl.acc_bytes);
+      prm.ws_pfx = reinterpret_cast<int32_t*>(ws + pl.acc_bytes + pl.ml_bytes);
+    } else {
+      prm.ws_acc = reinterpret_cast<float*>(ws);
+      prm.ws_ml = reinterpret_cast<float*>(ws + pl.acc_bytes);
+    }
   }
+  prm.num_seqs = a.num_seqs;
+  prm.workers = pl.workers;
   prm.num_heads = a.num_heads;
   prm.num_kv_heads = a.num_kv_heads;
   prm.group = pl.group;
@@ -487,13 +768,12 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   // x: head group (fastest, so one token's rows of all heads are read by
   // neighbouring workgroups), y: partition, z: sequence.
   const dim3 grid((unsigned)((pl.units + 3) / 4), (unsigned)pl.max_parts, (unsigned)a.num_seqs);
-  const bool split = pl.max_parts > 1;
   if (a.bf16) {
-    if (a.head_dim == 64) launch_gt<uint16_t, 64>(pl.heads_per_unit, prm, grid, split, stream);
-    else launch_gt<uint16_t, 128>(pl.heads_per_unit, prm, grid, split, stream);
+    if (a.head_dim == 64) launch_gt<uint16_t, 64>(prm, pl, grid, stream);
+    else launch_gt<uint16_t, 128>(prm, pl, grid, stream);
   } else {
-    if (a.head_dim == 64) launch_gt<float, 64>(pl.heads_per_unit, prm, grid, split, stream);
-    else launch_gt<float, 128>(pl.heads_per_unit, prm, grid, split, stream);
+    if (a.head_dim == 64) launch_gt<float, 64>(prm, pl, grid, stream);
+    else launch_gt<float, 128>(prm, pl, grid, stream);
   }
   return hipGetLastError();
 }

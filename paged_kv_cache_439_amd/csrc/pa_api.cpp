@@ -10,6 +10,8 @@
 #include "../../include/pagedattn.h"
 #include "pa_internal.h"
 
+static_assert(PA_PARTITION_BALANCED == pa::PA_PARTITION_BALANCED_VALUE, "balanced split constant");
+
 namespace {
 
 thread_local char g_last_error[512] = "";
@@ -130,7 +132,8 @@ pa_status pa_store_kvcache(const void* key, const void* value, int64_t key_tok_s
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t max_context_len, int32_t partition_size) {
   if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads ||
-      head_dim <= 0 || max_context_len <= 0 || partition_size < 0)
+      head_dim <= 0 || max_context_len <= 0 ||
+      (partition_size < 0 && partition_size != PA_PARTITION_BALANCED))
     return 0;
   return pa::plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
                          partition_size)
@@ -154,9 +157,13 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
       return st;
     if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs=%d above 65535", num_seqs);
     if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
-    if (partition_size < 0 || partition_size % 16 != 0)
-      return fail(PA_ERR_INVALID_ARG, "partition_size=%d must be 0 or a positive multiple of 16",
+    if (partition_size != PA_PARTITION_BALANCED && (partition_size < 0 || partition_size % 16 != 0))
+      return fail(PA_ERR_INVALID_ARG,
+                  "partition_size=%d must be 0, a positive multiple of 16 or PA_PARTITION_BALANCED",
                   partition_size);
+    if (partition_size == PA_PARTITION_BALANCED && num_seqs > 4096)
+      return fail(PA_ERR_UNSUPPORTED, "the balanced split supports at most 4096 sequences (got %d)",
+                  num_seqs);
     if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
         !aligned(block_tables, 4) || !aligned(context_lens, 4))
       return fail(PA_ERR_UNSUPPORTED, "pointers must be 16-byte aligned (int arrays 4-byte)");

@@ -49,6 +49,9 @@ struct PrefillArgs {
   float scale;
 };
 
+// partition_size value that selects the balanced split (pagedattn.h).
+constexpr int32_t PA_PARTITION_BALANCED_VALUE = -1;
+
 // Decode work split, shared by the workspace-size query and the launcher.
 struct DecodePlan {
   int32_t group;           // query heads per KV head
@@ -56,7 +59,9 @@ struct DecodePlan {
   int32_t units;           // waves per (sequence, partition) = Hkv * group / heads_per_unit
   int32_t partition;       // tokens per partition (> 0)
   int32_t max_parts;       // partitions of the longest context
-  size_t acc_bytes, ml_bytes, total_bytes;  // workspace regions (0 if unsplit)
+  bool balanced;           // balanced split: equal chunk ranges per worker
+  int32_t workers;         // balanced split: workers (waves) per unit
+  size_t acc_bytes, ml_bytes, pfx_bytes, total_bytes;  // workspace regions (0 if unsplit)
 };
 
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,

@@ -15,13 +15,14 @@
 // walks the row blocks from the end of the chunk, so the workgroups with the
 // longest key ranges are dispatched first.
 //
-// Per 64-key tile (software-pipelined: the K/V rows of tile i+1 are loaded
-// into registers while tile i is computed from LDS):
+// Per 64-key tile (software-pipelined: the K/V rows of tile i+1 move from
+// global memory straight into the other of two LDS stages while tile i is
+// computed):
 //   * the physical block ids come from a window of the block table held in
 //     LDS, loaded once (and again only if a context outgrows the window);
-//   * K is staged as [key][d] and V transposed as [d][key]; 16-byte granules
-//     are XOR-swizzled within a row so that the MFMA operand reads and the
-//     staging writes spread over the LDS banks;
+//   * K and V are staged as [key][d]; 16-byte granules are XOR-swizzled
+//     within a row (the swizzle is applied to the global addresses of the
+//     loads) so that the MFMA operand reads spread over the LDS banks;
 //   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = 16 keys x 32 d from LDS,
 //     B = Q^T slice held in registers for the whole kernel). The C layout puts
 //     one query row in each lane (column = lane % 16) and 4 keys per register
@@ -31,13 +32,14 @@
 //     group q ends up holding keys 8q .. 8q+7 contiguously: the probabilities
 //     then ARE the B operand (P^T) of the next product without a register
 //     transpose;
-//   * O^T += V^T P^T with the same MFMA (A = 16 d x 32 keys from the
-//     transposed V tile); O^T's column is again the lane's query row, so the
-//     online-softmax rescale is a per-lane multiply;
+//   * O^T += V^T P^T with the same MFMA; its A operand (16 d x 32 keys) is
+//     read from the untransposed V tile with ds_read_b64_tr_b16; O^T's column
+//     is again the lane's query row, so the online-softmax rescale is a
+//     per-lane multiply;
 //   * the running maximum is only raised (and O rescaled) when a tile's
-//     maximum exceeds it by more than 2^8 in probability, so most tiles skip
-//     the rescale; the result is the same softmax, with probabilities below
-//     2^8 relative to the kept maximum;
+//     maximum exceeds it by more than 2^32 in probability, so almost every
+//     tile after the first skips the rescale; the result is the same
+//     softmax, with probabilities below 2^32 relative to the kept maximum;
 //   * only tiles that straddle a wave's causal diagonal are masked.
 //
 // Bound: MFMA (bf16 dense). Algorithmic flops = 4 * D * Hq * (visible
@@ -70,8 +72,11 @@ struct PrefillParams {
 // order (row blocks from the end of the chunk first).
 constexpr int RANK_MAX_ITEMS = 512;
 
-// Lazy-rescale threshold in log2 units: probabilities stay below 2^8.
-constexpr float RESCALE_SLACK = 8.0f;
+// Lazy-rescale threshold in log2 units: probabilities stay below 2^32. bf16
+// and fp32 keep their relative precision at that size, and a row sum of at
+// most 2^32 per key cannot overflow fp32, so after the first tile a rescale
+// of the accumulators is needed only when a row's maximum jumps by 2^32.
+constexpr float RESCALE_SLACK = 32.0f;
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -193,16 +198,20 @@ __global__ __launch_bounds__(256, 2) void prefill_chunk_kernel(PrefillParams p) 
   };
   load_window(0);
 
-  // Issue the global->LDS loads of tile kt0 into stage st. Keys past the
+  // Issue the global->LDS loads of tile kt0 into a stage. Keys past the
   // workgroup's range read the last needed row instead (finite data whose
   // probability is zero), so no NaN from outside the context reaches V.
   auto issue = [&](int kt0, uint16_t (&stage)[2][TE]) {
+    // When the tile lies inside one block (block_size >= KT) one table entry
+    // serves every lane.
+    const bool one_block = KT <= (1 << bs_log2);
+    const int phys0 = __builtin_amdgcn_readfirstlane(tbl[(kt0 >> bs_log2) - wb]);
 #pragma unroll
     for (int i = 0; i < NIW; ++i) {
       const int ins = wave * NIW + i;
       const int key = ins * KPI + lane / GPR;
       const int j = min(kt0 + key, kv_end - 1);
-      const int phys = tbl[(j >> bs_log2) - wb];
+      const int phys = one_block ? phys0 : tbl[(j >> bs_log2) - wb];
       const int64_t row = (((int64_t)phys << bs_log2) + (j & bs_mask)) * row_bytes + head_off;
       const int gl = lane % GPR;
       load_lds16(p.k_cache + row + ((gl ^ swz_k(key)) * 16), &stage[0][ins * KPI * D]);
@@ -265,27 +274,23 @@ __global__ __launch_bounds__(256, 2) void prefill_chunk_kernel(PrefillParams p) 
     // ---- S^T = K Q^T: tiles [step c2][half hf][row tile rt] ----
     f32x4 s[2][2][2];
 #pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-      bf16x8 a[2][KS];
+    for (int c2 = 0; c2 < 2; ++c2)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const int key = 32 * c2 + 8 * (lrow >> 2) + 4 * hf + (lrow & 3);
         const int sk = swz_k(key);
+        bf16x8 a[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-          a[hf][ks] = *reinterpret_cast<const bf16x8*>(&Kt[key * D + (((4 * ks + qgrp) ^ sk) * 8)]);
-      }
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
+          a[ks] = *reinterpret_cast<const bf16x8*>(&Kt[key * D + (((4 * ks + qgrp) ^ sk) * 8)]);
         s[c2][hf][0] = f32x4{0.f, 0.f, 0.f, 0.f};
         s[c2][hf][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          s[c2][hf][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[hf][ks], qreg[0][ks], s[c2][hf][0], 0, 0, 0);
-          s[c2][hf][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[hf][ks], qreg[1][ks], s[c2][hf][1], 0, 0, 0);
+          s[c2][hf][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], qreg[0][ks], s[c2][hf][0], 0, 0, 0);
+          s[c2][hf][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], qreg[1][ks], s[c2][hf][1], 0, 0, 0);
         }
       }
-    }
 
     // ---- online softmax per query row (lane row lrow of tile rt) ----
     // Logits are s * sl2 with sl2 >= 0 (a negative scale was moved into the
@@ -311,10 +316,10 @@ __global__ __launch_bounds__(256, 2) void prefill_chunk_kernel(PrefillParams p) 
                 v = (key <= tpos) ? v : -INFINITY;
                 s[c2][hf][rt][i] = v;
               }
-              mx = fmaxf(mx, v);
+              mx = __builtin_elementwise_maximum(mx, v);
             }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 16));
+        mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32));
         mt[rt] = (MASKED && mx == -INFINITY) ? -INFINITY : mx * sl2;
       }
       // Raise a row's running maximum only when the tile's maximum exceeds it

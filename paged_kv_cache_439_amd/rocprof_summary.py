@@ -88,19 +88,23 @@ def traffic(fetch_csv, write_csv, out_json, out_md, copy_bytes, cmd_fetch, cmd_w
             per[_short(n)]["write"].append(w * ws * 1024)
     kernels = {k: dict(dispatches=len(v["fetch"]), fetch_bytes=sum(v["fetch"]) / len(v["fetch"]),
                        write_bytes=sum(v["write"]) / len(v["write"])) for k, v in per.items()}
+    # per workload and split: the balanced split's two kernels, or the
+    # fixed-slice split's main and merge kernels
     workloads = {}
     for k, v in kernels.items():
-        m = re.search(r"paged_decode(_merge)?_kernel<unsigned short, (\d+), (\d+)", k)
+        m = re.search(r"paged_decode(_balanced)?(_merge)?_kernel<unsigned short, (\d+), (\d+)", k)
         if not m:
             continue
-        wname = KERNEL_WORKLOAD.get((m.group(2), m.group(3)))
+        wname = KERNEL_WORKLOAD.get((m.group(3), m.group(4)))
         if not wname:
             continue
-        w = workloads.setdefault(wname, dict(hbm_bytes_per_launch=0.0, kernels=[]))
+        split = "balanced" if m.group(1) else "fixed"
+        w = workloads.setdefault(wname, {}).setdefault(split, dict(hbm_bytes_per_launch=0.0, kernels=[]))
         w["hbm_bytes_per_launch"] += v["fetch_bytes"] + v["write_bytes"]
         w["kernels"].append(k)
-    for w in workloads.values():
-        w["hbm_bytes_per_launch"] = int(w["hbm_bytes_per_launch"])
+    for ws_ in workloads.values():
+        for w in ws_.values():
+            w["hbm_bytes_per_launch"] = int(w["hbm_bytes_per_launch"])
     rec = dict(kernel_source_sha256=decode_source_hash(), fetch_scale=fs, write_scale=ws,
                copy_probe_bytes=copy_bytes, cmd_fetch=cmd_fetch, cmd_write=cmd_write,
                kernels={k: {kk: (int(vv) if "bytes" in kk else vv) for kk, vv in v.items()}
@@ -115,8 +119,9 @@ def traffic(fetch_csv, write_csv, out_json, out_md, copy_bytes, cmd_fetch, cmd_w
     for k, v in sorted(kernels.items(), key=lambda kv: -kv[1]["fetch_bytes"]):
         lines.append(f"| `{k}` | {v['dispatches']} | {v['fetch_bytes'] / 1e6:.1f} | {v['write_bytes'] / 1e6:.2f} |")
     lines += ["", "Per decode call (main + merge kernels):", ""]
-    for wname, w in workloads.items():
-        lines.append(f"- {wname}: {w['hbm_bytes_per_launch'] / 1e6:.1f} MB")
+    for wname, ws_ in workloads.items():
+        for split, w in ws_.items():
+            lines.append(f"- {wname}, {split} split: {w['hbm_bytes_per_launch'] / 1e6:.1f} MB")
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 

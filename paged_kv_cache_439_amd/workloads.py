@@ -34,7 +34,10 @@ import torch
 VOCAB = 50257
 SEED_BASE = 439000
 
-# The five workloads. Lengths include the newest token.
+# The five workloads. Lengths include the newest token. partition_size is the
+# decode split the benchmark times (-1: the library's balanced split);
+# fixed_partition_size is the fixed-slice split measured beside it (0: whole
+# contexts), the 512-token slices the b512 workload names among them.
 CONFIGS = {
     1: dict(name="tiny_fp32_mha_decode", kind="decode", dtype="f32", num_seqs=4,
             num_heads=8, num_kv_heads=8, head_dim=64, block_size=16,
@@ -43,12 +46,12 @@ CONFIGS = {
     2: dict(name="bf16_mha_decode_b64", kind="decode", dtype="bf16", num_seqs=64,
             num_heads=12, num_kv_heads=12, head_dim=64, block_size=256,
             lens=("uniform", 512, 4096), pool=("factor", 1.25),
-            max_context=4096, partition_size=256),   # split: 64 sequences alone underfill the chip
+            max_context=4096, partition_size=-1, fixed_partition_size=256),
     3: dict(name="bf16_gqa_decode_b256_shared_prefix", kind="decode", dtype="bf16",
             num_seqs=256, num_heads=16, num_kv_heads=8, head_dim=128, block_size=256,
             lens=("uniform", 1024, 4096), pool=("factor", 1.25),
             share=dict(num_sharers=128, prefix_tokens=1024),
-            max_context=4096, partition_size=0),     # 256 x 8 waves fill the chip unsplit
+            max_context=4096, partition_size=-1, fixed_partition_size=0),
     4: dict(name="bf16_gqa_chunked_prefill", kind="prefill", dtype="bf16", num_seqs=8,
             num_heads=32, num_kv_heads=8, head_dim=128, block_size=256,
             cached=("uniform", 0, 3584), chunk=512, pool=("factor", 1.25),
@@ -56,7 +59,7 @@ CONFIGS = {
     5: dict(name="bf16_gqa_decode_b512_lognormal", kind="decode", dtype="bf16",
             num_seqs=512, num_heads=32, num_kv_heads=8, head_dim=128, block_size=64,
             lens=("lognormal", 1500.0, 1.0, 64, 4096), pool=("factor", 1.25),
-            max_context=4096, partition_size=512),
+            max_context=4096, partition_size=-1, fixed_partition_size=512),
 }
 
 

@@ -136,5 +136,8 @@ def sample_seqs(batch, k, seed=0):
     return sorted(pick | set(rest[:max(0, k - len(pick))]))
 
 
-def full_config_parts(cfg):
-    return wl.CONFIGS[cfg].get("partition_size", 0)
+def full_config_parts(cfg, split="balanced"):
+    """The decode split the benchmark times for a workload: its balanced
+    split, or the fixed one measured beside it."""
+    key = "partition_size" if split == "balanced" else "fixed_partition_size"
+    return wl.CONFIGS[cfg].get(key, 0)

@@ -79,6 +79,14 @@ def test_decode_rejections(lib):
     assert "workspace" in binding.load_library().pa_last_error().decode()
 
 
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
 def test_workspace_sizes(lib):
     assert lib.pa_decode_workspace_size(4, 8, 8, 64, 100, 0) == 0
     assert lib.pa_decode_workspace_size(4, 8, 8, 64, 100, 112) == 0    # one partition suffices
@@ -87,6 +95,33 @@ def test_workspace_sizes(lib):
     r = lambda x: (x + 255) // 256 * 256
     assert n == r(4 * 8 * 4 * 64 * 4) + r(4 * 8 * 4 * 2 * 4)
     assert lib.pa_decode_workspace_size(4, 8, 3, 64, 100, 32) == 0      # invalid grouping
+    assert lib.pa_decode_workspace_size(4, 8, 8, 64, 100, -2) == 0      # not a split mode
+
+
+def test_balanced_workspace_size(lib):
+    """Balanced split: 2 waves per SIMD of a 256-CU device (assumed when no
+    device is visible), each wave with two (acc[D], m, l) slots per head of
+    its unit, plus the chunk prefix sums."""
+    if _gpu_visible():
+        pytest.skip("the size depends on the visible device")
+    r = lambda x: (x + 255) // 256 * 256
+    for (B, Hq, Hkv, D) in [(4, 8, 8, 64), (512, 32, 8, 128), (7, 12, 4, 64)]:
+        G = Hq // Hkv
+        gt = 4 if G % 4 == 0 else 2 if G % 2 == 0 else 1
+        units = Hkv * (G // gt)
+        workers = (2 * 4 * 256) // units
+        slots = workers * 2 * Hq
+        want = r(slots * D * 4) + r(slots * 2 * 4) + r((B + 1) * 4)
+        assert lib.pa_decode_workspace_size(B, Hq, Hkv, D, 4096, -1) == want
+
+
+def test_balanced_rejections(lib):
+    need = lib.pa_decode_workspace_size(4, 8, 8, 64, 100, -1)
+    assert need > 0
+    assert _decode(lib, P=-1) == PA_ERR_WORKSPACE
+    assert _decode(lib, P=-1, ws=FAKE, wsb=need - 1) == PA_ERR_WORKSPACE
+    assert _decode(lib, P=-2, ws=FAKE, wsb=need) == PA_ERR_INVALID_ARG
+    assert _decode(lib, P=-1, B=4097, ws=FAKE, wsb=1 << 40) == PA_ERR_UNSUPPORTED
 
 
 def _store(lib, **kw):

@@ -77,7 +77,7 @@ def test_store_strided_key(gpu):
 # decode: small configs compared in full
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("P", [0, 16, 32, 48, 64])
+@pytest.mark.parametrize("P", [0, 16, 32, 48, 64, -1])
 def test_decode_tiny_fp32(gpu, P):
     b = wl.make_batch(wl.spec(1), device=gpu, poison=True)
     gs.say(f"decode cfg1 P={P}")
@@ -86,28 +86,28 @@ def test_decode_tiny_fp32(gpu, P):
 
 DECODE_VARIANTS = {
     # bf16 MHA D=64, block 256, several partitions and ragged tails
-    "mha64_bs256": (2, dict(num_seqs=8, lens=("uniform", 1, 1500), max_context=1536), [0, 256, 512]),
+    "mha64_bs256": (2, dict(num_seqs=8, lens=("uniform", 1, 1500), max_context=1536), [0, 256, 512, -1]),
     # bf16 GQA 16/8 D=128 with a shared prefix
     "gqa2_shared": (3, dict(num_seqs=12, lens=("uniform", 300, 1800), max_context=2048,
-                            share=dict(num_sharers=6, prefix_tokens=256)), [0, 512, 128]),
+                            share=dict(num_sharers=6, prefix_tokens=256)), [0, 512, 128, -1]),
     # bf16 GQA 32/8 D=128, block 64, lognormal lengths
     "gqa4_bs64": (5, dict(num_seqs=16, lens=("lognormal", 300.0, 1.0, 1, 2048), max_context=2048),
-                  [0, 512, 64]),
+                  [0, 512, 64, -1]),
     # fp32 GQA 16/8 D=128
     "f32_gqa2_d128": (3, dict(dtype="f32", num_seqs=6, lens=("uniform", 1, 700), max_context=768,
-                              share=None, block_size=32), [0, 96]),
+                              share=None, block_size=32), [0, 96, -1]),
     # bf16 GQA group 8 (one wave per 8 heads)
     "gqa8": (5, dict(num_seqs=6, num_heads=32, num_kv_heads=4, lens=("uniform", 1, 900),
-                     max_context=1024, block_size=16), [0, 128]),
+                     max_context=1024, block_size=16), [0, 128, -1]),
     # group 3 (waves of 1 head), D=64
     "group3_d64": (2, dict(num_seqs=5, num_heads=12, num_kv_heads=4, lens=("uniform", 1, 600),
-                           max_context=640, block_size=8), [0, 32]),
+                           max_context=640, block_size=8), [0, 32, -1]),
     # fp32 D=128, block 1024
     "f32_bs1024": (3, dict(dtype="f32", num_seqs=3, lens=("uniform", 500, 2048), max_context=2048,
-                           share=None, block_size=1024), [0, 1024, 144]),
+                           share=None, block_size=1024), [0, 1024, 144, -1]),
     # bf16 D=64 with 6 query heads per KV head (waves of 2 heads)
     "group6_d64": (2, dict(num_seqs=4, num_heads=12, num_kv_heads=2, lens=("uniform", 1, 400),
-                           max_context=512, block_size=32), [0, 64]),
+                           max_context=512, block_size=32), [0, 64, -1]),
 }
 
 
@@ -126,17 +126,18 @@ def test_decode_edge_lengths(gpu):
     lens = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128]
     sp = wl.spec(5, num_seqs=len(lens), lens=("fixed", lens), block_size=bs, max_context=128,
                  pool=("factor", 1.5))
-    for part in (0, P, 16, 112):
+    for part in (0, P, 16, 112, -1):
         b = wl.make_batch(sp, device=gpu, poison=True)
         gs.say(f"decode edge lengths P={part}")
         gs.decode_parity(b, part)
 
 
-def test_decode_zero_length_gives_zeros(gpu):
+@pytest.mark.parametrize("P", [0, 16, -1])
+def test_decode_zero_length_gives_zeros(gpu, P):
     b = wl.make_batch(wl.spec(1), device=gpu)
     arrs = gs.device_arrays(b)
     arrs["lens"][2] = 0
-    out = gs.gpu_decode(b, 16, arrs)
+    out = gs.gpu_decode(b, P, arrs)
     torch.cuda.synchronize()
     assert (out[2] == 0).all()
     assert torch.isfinite(out).all()
@@ -165,9 +166,46 @@ def test_decode_split_agrees_with_unsplit(gpu):
     arrs = gs.device_arrays(b)
     gs.gpu_store(b, arrs)
     base = gs.as_f64(gs.gpu_decode(b, 0, arrs))
-    for P in (64, 256, 512, 2048):
+    for P in (64, 256, 512, 2048, pa.PA_PARTITION_BALANCED):
         got = gs.as_f64(gs.gpu_decode(b, P, arrs))
         assert np.abs(got - base).max() <= 8e-3, P      # two bf16 roundings apart at most
+
+
+def test_decode_balanced_many_short_and_empty(gpu):
+    """Balanced split over 600 contexts of 0..40 tokens: ranges cover many
+    whole sequences each, and empty contexts give zeros."""
+    rng = np.random.Generator(np.random.PCG64(77))
+    lens = rng.integers(1, 41, size=600)
+    sp = wl.spec(5, num_seqs=600, lens=("fixed", lens.tolist()), block_size=16, max_context=48,
+                 pool=("factor", 1.25))
+    b = wl.make_batch(sp, device=gpu, poison=True)
+    gs.say("decode balanced: 600 short contexts")
+    gs.decode_parity(b, pa.PA_PARTITION_BALANCED)
+    arrs = gs.device_arrays(b)
+    gs.gpu_store(b, arrs)
+    zero = [3, 4, 5, 599]
+    arrs["lens"][zero] = 0
+    out = gs.gpu_decode(b, pa.PA_PARTITION_BALANCED, arrs)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    assert (out[zero] == 0).all()
+
+
+def test_decode_balanced_few_long(gpu):
+    """Two long contexts cut across hundreds of ranges each."""
+    sp = wl.spec(5, num_seqs=2, lens=("fixed", [4096, 3001]), max_context=4096)
+    b = wl.make_batch(sp, device=gpu, poison=True)
+    gs.say("decode balanced: 2 long contexts")
+    gs.decode_parity(b, pa.PA_PARTITION_BALANCED)
+
+
+def test_decode_balanced_at_sequence_limit(gpu):
+    """4096 sequences, the most the balanced split takes."""
+    sp = wl.spec(2, num_seqs=4096, lens=("uniform", 1, 64), block_size=16, max_context=64)
+    b = wl.make_batch(sp, device=gpu, poison=True)
+    seqs = gs.sample_seqs(b, 24, seed=9) + [4095]
+    gs.say("decode balanced: 4096 sequences")
+    gs.decode_parity(b, pa.PA_PARTITION_BALANCED, seqs=sorted(set(seqs)))
 
 
 def test_decode_block_permutation_bit_identical(gpu):
@@ -177,7 +215,7 @@ def test_decode_block_permutation_bit_identical(gpu):
                               share=dict(num_sharers=4, prefix_tokens=256)), device=gpu)
     arrs = gs.device_arrays(b)
     gs.gpu_store(b, arrs)
-    for P in (0, 256):
+    for P in (0, 256, pa.PA_PARTITION_BALANCED):
         out1 = gs.gpu_decode(b, P, arrs).cpu()
         perm = torch.randperm(b.num_blocks, generator=torch.Generator().manual_seed(5))
         k2 = torch.empty_like(b.k_cache)
@@ -232,14 +270,16 @@ def test_decode_sharing_equals_duplication(gpu):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("cfg,nseq", [(2, 8), (3, 6), (5, 6)])
-def test_decode_full_config_sampled(gpu, cfg, nseq):
+@pytest.mark.parametrize("split", ["fixed", "balanced"])
+def test_decode_full_config_sampled(gpu, cfg, nseq, split):
     b = wl.make_batch(wl.spec(cfg), device=gpu, poison=True)
     seqs = gs.sample_seqs(b, nseq, seed=cfg)
     if cfg == 3:   # include two sequences that read the shared prefix
         sharers = [i for i in range(b.num_seqs) if b.block_tables[i, 0] == b.shared_blocks[0]]
         seqs = sorted(set(seqs) | set(sharers[:2]))
-    gs.say(f"decode full cfg{cfg} seqs={seqs} P={gs.full_config_parts(cfg)}")
-    gs.decode_parity(b, gs.full_config_parts(cfg), seqs=seqs)
+    P = gs.full_config_parts(cfg, split)
+    gs.say(f"decode full cfg{cfg} seqs={seqs} P={P}")
+    gs.decode_parity(b, P, seqs=seqs)
 
 
 def test_decode_full_config_properties(gpu):
