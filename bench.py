@@ -2,10 +2,11 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--no-extra]
 
-A step is one pass of the decode hot path over one batch: pa_store_kvcache
-writes the new token's K/V row of every sequence, then pa_decode attends over
-the whole paged context (balanced split: equal K/V ranges per resident wave,
-then a merge kernel for the sequences the ranges cut).
+A step is one pass of the decode hot path over one batch: pa_store_decode
+writes the new token's K/V row of every sequence into the pool and attends
+over the whole paged context in the same launch (balanced split: equal K/V
+ranges per resident wave, then a merge kernel for the sequences the ranges
+cut).
 The default workload is the bf16 MHA decode batch (64 sequences, 12 heads,
 head_dim 64, block 256, context lengths uniform in [512, 4096]). Several
 independently drawn batches (each with its own pool) are resident in HBM and
@@ -54,8 +55,9 @@ def log(msg):
 class DecodeSet:
     """R resident batches of one decode workload, with device-side arrays."""
 
-    def __init__(self, cfg, rotations, device, partition=None):
+    def __init__(self, cfg, rotations, device, partition=None, fused=True):
         self.spec = wl.spec(cfg)
+        self.fused = fused
         self.P = self.spec.get("partition_size", 0) if partition is None else partition
         self.batches = []
         for r in range(rotations):
@@ -74,12 +76,20 @@ class DecodeSet:
         self.kv_bytes_logical = [b.kv_bytes(unique=False) for b, _ in self.batches]
 
     def step(self, i, ev=None):
+        """Store the new rows and decode: one pa_store_decode call (its main
+        kernel writes the rows while it attends), or, with fused=False, the
+        two calls pa_store_kvcache and pa_decode."""
         b, a = self.batches[i % len(self.batches)]
-        pa.pa_store_kvcache(b.key, b.value, b.k_cache, b.v_cache, a["slots"])
+        if not self.fused:
+            pa.pa_store_kvcache(b.key, b.value, b.k_cache, b.v_cache, a["slots"])
         if ev is not None:
             ev[0].record()
-        pa.pa_decode(a["out"], b.q, b.k_cache, b.v_cache, a["tables"], a["lens"],
-                     b.max_context_len, b.scale, self.P, self.ws)
+        if self.fused:
+            pa.pa_store_decode(a["out"], b.q, b.key, b.value, b.k_cache, b.v_cache, a["slots"],
+                               a["tables"], a["lens"], b.max_context_len, b.scale, self.P, self.ws)
+        else:
+            pa.pa_decode(a["out"], b.q, b.k_cache, b.v_cache, a["tables"], a["lens"],
+                         b.max_context_len, b.scale, self.P, self.ws)
         if ev is not None:
             ev[1].record()
 
@@ -243,7 +253,7 @@ def main():
             "head_dim": b0.head_dim, "block_size": b0.block_size,
             "context_lens": "uniform[512,4096]" if args.workload == 2 else str(ds.spec["lens"]),
             "split": split_name(ds.P), "partition_size": ds.P, "rotating_batches": args.rotations,
-            "step": "store_kvcache(new rows) + decode",
+            "step": "pa_store_decode: store the new rows + decode, one launch (+ merge)",
         },
         "roofline": {
             "bound": "hbm",
@@ -258,19 +268,23 @@ def main():
     if not args.no_extra:
         extra = {}
         for cfg in (2, 3, 5):
-            for P in (wl.CONFIGS[cfg]["partition_size"], wl.CONFIGS[cfg]["fixed_partition_size"]):
-                if cfg == args.workload and P == ds.P:
+            runs = [(wl.CONFIGS[cfg]["partition_size"], True), (wl.CONFIGS[cfg]["fixed_partition_size"], True)]
+            if cfg == args.workload:
+                runs.append((ds.P, False))
+            for P, fused in runs:
+                if cfg == args.workload and P == ds.P and fused:
                     continue
-                log(f"extra workload {cfg} partition_size={P}")
-                d = DecodeSet(cfg, 2, dev, partition=P)
+                log(f"extra workload {cfg} partition_size={P} fused={fused}")
+                d = DecodeSet(cfg, 2, dev, partition=P, fused=fused)
                 s, ms, nb, _ = time_decode(d, 30, 5)
                 bb = d.batches[0][0]
                 key = d.spec["name"] + ("" if P == pa.PA_PARTITION_BALANCED else f"_fixed_p{P}")
+                key += "" if fused else "_separate_store"
                 extra[key] = dict(
                     tokens_per_s=round(bb.num_seqs * 30 / s, 1), kernel_ms=round(ms, 4),
                     kv_gbs=round(nb / (ms * 1e-3) / 1e9, 1),
                     frac_of_hbm_peak=round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                    bytes_per_launch=int(nb), split=split_name(P), partition_size=P,
+                    bytes_per_launch=int(nb), split=split_name(P), partition_size=P, fused_store=fused,
                     traffic=measured_traffic(d.spec["name"], split_name(P)),
                     logical_bytes_per_launch=int(np.mean(d.kv_bytes_logical)))
                 del d

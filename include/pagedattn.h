@@ -149,6 +149,36 @@ pa_status pa_decode(void* out, const void* q,
                     pa_dtype dtype, void* stream);
 
 /*
+ * pa_store_decode -- pa_store_kvcache of each sequence's newest token fused
+ * with pa_decode, in one launch (plus the merge kernel of a split).
+ *
+ * Row i of key/value ([num_seqs][num_kv_heads][head_dim], token strides in
+ * elements as for pa_store_kvcache) is sequence i's newest token, at
+ * position context_lens[i] - 1, and slot_mapping[i] is that position's slot
+ * (block_tables[i][(L-1)/block_size] * block_size + (L-1) % block_size) or
+ * negative. The result equals pa_store_kvcache(key, value, slot_mapping)
+ * followed by pa_decode with the same arguments, up to fp32 rounding: the
+ * rows are written into the pools, and the attention takes the newest token
+ * from key/value directly instead of reading back the slot it writes (the
+ * mini-vllm page's engine, whose decode step appends one token's K/V through
+ * the block table and attends over the whole cached context). A sequence
+ * with a negative slot is not stored and attends over the pool as it is.
+ * All other arguments, errors and the workspace are those of pa_decode.
+ */
+pa_status pa_store_decode(void* out, const void* q,
+                          const void* key, const void* value,
+                          int64_t key_tok_stride, int64_t value_tok_stride,
+                          void* k_cache, void* v_cache,
+                          const int32_t* slot_mapping,
+                          const int32_t* block_tables, const int32_t* context_lens,
+                          int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                          int32_t max_blocks_per_seq, int32_t max_context_len,
+                          float scale, int32_t partition_size,
+                          void* workspace, size_t workspace_bytes,
+                          pa_dtype dtype, void* stream);
+
+/*
  * pa_prefill_chunk -- causal attention of a chunk of new tokens over the
  * cached-plus-new paged context (the prefill pass of the mini-vllm page's
  * inference engine, run chunk by chunk).

@@ -45,6 +45,9 @@ _SIGNATURES = {
     "pa_decode": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                    _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                    _c_void_p, _size, ctypes.c_int, _c_void_p], ctypes.c_int),
+    "pa_store_decode": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p,
+                         _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                         _i32, _f32, _i32, _c_void_p, _size, ctypes.c_int, _c_void_p], ctypes.c_int),
     "pa_prefill_chunk": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                           _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                           _f32, ctypes.c_int, _c_void_p], ctypes.c_int),
@@ -173,6 +176,40 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_
                        int(max_context_len), float(scale), int(partition_size), ws_ptr, ws_bytes,
                        _dtype_code(q), _stream(stream))
     _check("pa_decode", st)
+
+
+def pa_store_decode(out, q, key, value, k_cache, v_cache, slot_mapping, block_tables, context_lens,
+                    max_context_len, scale, partition_size=0, workspace=None, stream=None):
+    """Store each sequence's newest K/V row [B][Hkv][D] and decode, in one
+    launch; the same as pa_store_kvcache followed by pa_decode."""
+    lib = load_library()
+    B, Hq, D = q.shape
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    _need(q.is_contiguous() and out.is_contiguous(), "q and out must be contiguous")
+    _need(k_cache.dim() == 4 and k_cache.shape == v_cache.shape, "pools must be [NB][bs][Hkv][D]")
+    _need(k_cache.is_contiguous() and v_cache.is_contiguous(), "pools must be contiguous")
+    NB, bs, Hkv, D2 = k_cache.shape
+    _need(D2 == D, "head_dim of pools and q differ")
+    _need(key.shape == value.shape == (B, Hkv, D), "key/value must be [B][Hkv][D]")
+    for t in (key, value):
+        _need(t.stride(2) == 1 and t.stride(1) == D, "key/value rows must be dense [Hkv][D]")
+    _need(q.dtype == k_cache.dtype == v_cache.dtype == key.dtype == value.dtype, "dtypes differ")
+    for name, t in (("slot_mapping", slot_mapping), ("block_tables", block_tables),
+                    ("context_lens", context_lens)):
+        _int32_device(t, name, q.device)
+    _need(slot_mapping.numel() == B, "slot_mapping must have B entries")
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == B, "block_tables must be [B][max_blocks]")
+    _need(context_lens.numel() == B, "context_lens must have B entries")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _need(workspace.device == q.device and workspace.is_contiguous(), "bad workspace")
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    st = lib.pa_store_decode(_ptr(out), _ptr(q), _ptr(key), _ptr(value), key.stride(0), value.stride(0),
+                             _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), _ptr(block_tables),
+                             _ptr(context_lens), B, Hq, Hkv, D, bs, NB, block_tables.shape[1],
+                             int(max_context_len), float(scale), int(partition_size), ws_ptr, ws_bytes,
+                             _dtype_code(q), _stream(stream))
+    _check("pa_store_decode", st)
 
 
 def pa_prefill_chunk(out, q, k_cache, v_cache, block_tables, query_start_loc, context_lens,

@@ -66,7 +66,41 @@ struct DecodeParams {
   int32_t row_bytes;    // Hkv * D * e: bytes between consecutive tokens of a block
   int64_t block_bytes;  // block_size * row_bytes
   float scale_log2;     // scale * log2(e): logits are kept in log2 units
+  // Fused store (pa_store_decode), else null: sequence i's newest K/V row
+  // [Hkv][D] at new_k + i*new_k_stride, to be written at slot_mapping[i].
+  const char* new_k;
+  const char* new_v;
+  int64_t new_k_stride, new_v_stride;  // bytes
+  const int32_t* slot_mapping;
+  int64_t num_slots;  // num_blocks * block_size
 };
+
+// Fused store: does this call write sequence seq's newest row into the pool
+// (the same test pa_store_kvcache applies to a slot)?
+__device__ __forceinline__ bool stores_new_row(const DecodeParams& p, int seq) {
+  if (p.new_k == nullptr) return false;
+  const int32_t s = p.slot_mapping[seq];
+  return s >= 0 && (int64_t)s < p.num_slots;
+}
+
+// Fused store: copy the newest rows of sequences into the pools, 16 bytes
+// per thread: (sequence, granule) pairs first, first + stride, ... below end
+// (pairs numbered sequence-major, row_bytes / 16 granules per sequence).
+__device__ __forceinline__ void store_new_rows(const DecodeParams& p, int64_t first, int64_t stride,
+                                               int64_t end) {
+  const int32_t cpr = p.row_bytes / 16;
+  end = min(end, (int64_t)p.num_seqs * cpr);
+  for (int64_t idx = first; idx < end; idx += stride) {
+    const int64_t t = idx / cpr;
+    const int32_t c = (int32_t)(idx - t * cpr);
+    if (!stores_new_row(p, (int)t)) continue;
+    const int64_t dst = (int64_t)p.slot_mapping[t] * p.row_bytes + (int64_t)c * 16;
+    const uint4 kv = *reinterpret_cast<const uint4*>(p.new_k + t * p.new_k_stride + (int64_t)c * 16);
+    const uint4 vv = *reinterpret_cast<const uint4*>(p.new_v + t * p.new_v_stride + (int64_t)c * 16);
+    *reinterpret_cast<uint4*>(const_cast<char*>(p.k_cache) + dst) = kv;
+    *reinterpret_cast<uint4*>(const_cast<char*>(p.v_cache) + dst) = vv;
+  }
+}
 
 // 16-byte streaming load of pool data: every K/V byte is read once per call,
 // so the loads carry the nontemporal hint and do not displace reusable lines.
@@ -190,6 +224,12 @@ template <typename T, int D, int GT, int U, bool UNIFORM_BLOCK>
 __device__ __forceinline__ void attend_range(const DecodeParams& p, int seq, int kvh, int lane,
                                              int tok_begin, int tok_end, const uint4 (&qv)[GT],
                                              WaveState<GT, 16 / ElemTraits<T>::E>& st) {
+  // With a fused store, the newest token (position L-1, L = the context
+  // length) comes from the new row itself, not from the pool slot this same
+  // launch is writing.
+  const bool new_row = tok_end > tok_begin && stores_new_row(p, seq) &&
+                       tok_end == min(p.context_lens[seq], p.max_context_len);
+  if (new_row) --tok_end;
   constexpr int E = ElemTraits<T>::E;
   constexpr int EPL = 16 / E;     // elements per 16-byte lane slice
   constexpr int LPT = D / EPL;    // lanes per token row of one head
@@ -287,6 +327,28 @@ __device__ __forceinline__ void attend_range(const DecodeParams& p, int seq, int
         for (int e = 0; e < EPL; ++e) st.acc[h][e] = fmaf(s[u][h], vf[e], st.acc[h][e]);
     }
   }
+
+  if (new_row) {
+    // one more token, held by token-row group 0 (every lane loads the same
+    // row so that the butterfly over the row's lanes stays uniform)
+    const int64_t off = (int64_t)kvh * D * E + dc * 16;
+    const uint4 kr = *reinterpret_cast<const uint4*>(p.new_k + seq * p.new_k_stride + off);
+    const uint4 vr = *reinterpret_cast<const uint4*>(p.new_v + seq * p.new_v_stride + off);
+    float vf[EPL];
+    widen_slice<T, EPL>(vr, vf);
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+      float sc = group_sum<LPT>(slice_dot<T>(qv[h], kr)) * p.scale_log2;
+      sc = (tr == 0) ? sc : -INFINITY;
+      const float mn = fmaxf(st.m[h], sc);
+      const float alpha = fast_exp2(st.m[h] - mn);
+      const float pr = fast_exp2(sc - mn);
+      st.m[h] = mn;
+      st.l[h] = st.l[h] * alpha + pr;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) st.acc[h][e] = fmaf(pr, vf[e], st.acc[h][e] * alpha);
+    }
+  }
 }
 
 // Write the (merged) state of heads h0.. of sequence seq as the final output.
@@ -334,9 +396,13 @@ __global__ __launch_bounds__(256, decode_min_wgs<GT>()) void paged_decode_kernel
 
   const int lane = threadIdx.x & 63;
   const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (unit >= p.units) return;
   const int seq = blockIdx.z;
   const int part = blockIdx.y;
+  if (p.new_k != nullptr && blockIdx.x == 0 && part == 0) {  // fused store of seq's row
+    const int64_t cpr = p.row_bytes / 16;
+    store_new_rows(p, (int64_t)seq * cpr + threadIdx.x, 256, (int64_t)(seq + 1) * cpr);
+  }
+  if (unit >= p.units) return;
   const int L = min(p.context_lens[seq], p.max_context_len);
   const int P = p.partition;
   const int nparts = L > 0 ? (L + P - 1) / P : 0;
@@ -512,6 +578,8 @@ __global__ __launch_bounds__(256, 2) void paged_decode_balanced_kernel(DecodePar
   constexpr int TPW = 64 / LPT;
   constexpr int CT = U * TPW;
   __shared__ int32_t pfx[BAL_MAX_SEQS + 1];
+  if (p.new_k != nullptr)  // fused store: every thread of the grid copies a share of the rows
+    store_new_rows(p, (int64_t)blockIdx.x * 256 + threadIdx.x, (int64_t)gridDim.x * 256, INT64_MAX);
   chunk_prefix<CT>(p, pfx);
   const int B = p.num_seqs;
   if (blockIdx.x == 0)
@@ -765,6 +833,14 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   prm.scale_log2 = a.scale * 1.4426950408889634f;
   prm.row_bytes = a.num_kv_heads * a.head_dim * (a.bf16 ? 2 : 4);
   prm.block_bytes = (int64_t)a.block_size * prm.row_bytes;
+  if (a.key != nullptr) {
+    prm.new_k = static_cast<const char*>(a.key);
+    prm.new_v = static_cast<const char*>(a.value);
+    prm.new_k_stride = a.key_stride_bytes;
+    prm.new_v_stride = a.value_stride_bytes;
+    prm.slot_mapping = a.slot_mapping;
+    prm.num_slots = (int64_t)a.num_blocks * a.block_size;
+  }
   // x: head group (fastest, so one token's rows of all heads are read by
   // neighbouring workgroups), y: partition, z: sequence.
   const dim3 grid((unsigned)((pl.units + 3) / 4), (unsigned)pl.max_parts, (unsigned)a.num_seqs);

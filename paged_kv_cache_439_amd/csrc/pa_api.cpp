@@ -140,6 +140,95 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num
       .total_bytes;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Shared by pa_decode and pa_store_decode: validation, planning, launch.
+// fused == nullptr for a plain decode.
+struct Fusion {
+  const void* key;
+  const void* value;
+  int64_t key_tok_stride, value_tok_stride;  // elements
+  const int32_t* slot_mapping;
+};
+
+pa_status decode_impl(const char* fn, void* out, const void* q, const void* k_cache,
+                      const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                      int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                      int32_t max_context_len, float scale, int32_t partition_size, void* workspace,
+                      size_t workspace_bytes, pa_dtype dtype, void* stream, const Fusion* fused) {
+  if (pa_status st = check_dtype(dtype)) return st;
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_seqs=%d is negative", fn, num_seqs);
+  if (num_seqs == 0) return ok();
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PA_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  if (pa_status st = check_attention_shapes(num_heads, num_kv_heads, head_dim, block_size,
+                                            num_blocks, max_blocks_per_seq, max_context_len))
+    return st;
+  if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "%s: num_seqs=%d above 65535", fn, num_seqs);
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "%s: scale is not finite", fn);
+  if (partition_size != PA_PARTITION_BALANCED && (partition_size < 0 || partition_size % 16 != 0))
+    return fail(PA_ERR_INVALID_ARG,
+                "%s: partition_size=%d must be 0, a positive multiple of 16 or PA_PARTITION_BALANCED",
+                fn, partition_size);
+  if (partition_size == PA_PARTITION_BALANCED && num_seqs > 4096)
+    return fail(PA_ERR_UNSUPPORTED, "%s: the balanced split supports at most 4096 sequences (got %d)",
+                fn, num_seqs);
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4))
+    return fail(PA_ERR_UNSUPPORTED, "%s: pointers must be 16-byte aligned (int arrays 4-byte)", fn);
+  const int e = elem_size(dtype);
+  if (fused) {
+    const int64_t row_elems = (int64_t)num_kv_heads * head_dim;
+    if (!fused->key || !fused->value || !fused->slot_mapping)
+      return fail(PA_ERR_INVALID_ARG, "%s: null key, value or slot_mapping", fn);
+    if (fused->key_tok_stride < row_elems || fused->value_tok_stride < row_elems)
+      return fail(PA_ERR_INVALID_ARG, "%s: token strides (%lld, %lld) below a row of %lld elements", fn,
+                  (long long)fused->key_tok_stride, (long long)fused->value_tok_stride,
+                  (long long)row_elems);
+    if ((fused->key_tok_stride * e) % 16 || (fused->value_tok_stride * e) % 16)
+      return fail(PA_ERR_UNSUPPORTED, "%s: token strides must be multiples of 16 bytes", fn);
+    if (!aligned(fused->key, 16) || !aligned(fused->value, 16) || !aligned(fused->slot_mapping, 4))
+      return fail(PA_ERR_UNSUPPORTED, "%s: key/value must be 16-byte aligned, slot_mapping 4-byte", fn);
+    if ((int64_t)num_blocks * block_size > INT32_MAX)
+      return fail(PA_ERR_INVALID_ARG, "%s: num_blocks*block_size=%lld exceeds int32 slots", fn,
+                  (long long)num_blocks * block_size);
+  }
+  const pa::DecodePlan plan = pa::plan_decode(num_seqs, num_heads, num_kv_heads, head_dim,
+                                              max_context_len, partition_size);
+  if ((plan.units + 3) / 4 > 65535) return fail(PA_ERR_UNSUPPORTED, "%s: too many heads", fn);
+  if (plan.total_bytes) {
+    if (!workspace)
+      return fail(PA_ERR_WORKSPACE, "%s: this split needs a workspace of %zu bytes", fn,
+                  plan.total_bytes);
+    if (workspace_bytes < plan.total_bytes)
+      return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes,
+                  plan.total_bytes);
+    if (!aligned(workspace, 256))
+      return fail(PA_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+  }
+  pa::DecodeArgs a{out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
+                   num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                   max_context_len, scale, partition_size, workspace, dtype == PA_BF16,
+                   nullptr, nullptr, 0, 0, nullptr};
+  if (fused) {
+    a.key = fused->key;
+    a.value = fused->value;
+    a.key_stride_bytes = fused->key_tok_stride * e;
+    a.value_stride_bytes = fused->value_tok_stride * e;
+    a.slot_mapping = fused->slot_mapping;
+  }
+  const hipError_t err = pa::launch_decode(a, plan, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(PA_ERR_HIP, "%s launch: %s", fn, hipGetErrorString(err));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
 pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
                     int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
@@ -147,44 +236,29 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
                     pa_dtype dtype, void* stream) {
   try {
-    if (pa_status st = check_dtype(dtype)) return st;
-    if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs=%d is negative", num_seqs);
-    if (num_seqs == 0) return ok();
-    if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens)
-      return fail(PA_ERR_INVALID_ARG, "null pointer argument");
-    if (pa_status st = check_attention_shapes(num_heads, num_kv_heads, head_dim, block_size,
-                                              num_blocks, max_blocks_per_seq, max_context_len))
-      return st;
-    if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs=%d above 65535", num_seqs);
-    if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
-    if (partition_size != PA_PARTITION_BALANCED && (partition_size < 0 || partition_size % 16 != 0))
-      return fail(PA_ERR_INVALID_ARG,
-                  "partition_size=%d must be 0, a positive multiple of 16 or PA_PARTITION_BALANCED",
-                  partition_size);
-    if (partition_size == PA_PARTITION_BALANCED && num_seqs > 4096)
-      return fail(PA_ERR_UNSUPPORTED, "the balanced split supports at most 4096 sequences (got %d)",
-                  num_seqs);
-    if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
-        !aligned(block_tables, 4) || !aligned(context_lens, 4))
-      return fail(PA_ERR_UNSUPPORTED, "pointers must be 16-byte aligned (int arrays 4-byte)");
-    const pa::DecodePlan plan = pa::plan_decode(num_seqs, num_heads, num_kv_heads, head_dim,
-                                                max_context_len, partition_size);
-    if ((plan.units + 3) / 4 > 65535) return fail(PA_ERR_UNSUPPORTED, "too many heads");
-    if (plan.total_bytes) {
-      if (!workspace)
-        return fail(PA_ERR_WORKSPACE, "split decode needs a workspace of %zu bytes",
-                    plan.total_bytes);
-      if (workspace_bytes < plan.total_bytes)
-        return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes,
-                    plan.total_bytes);
-      if (!aligned(workspace, 256)) return fail(PA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-    }
-    pa::DecodeArgs a{out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
-                     num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
-                     max_context_len, scale, partition_size, workspace, dtype == PA_BF16};
-    const hipError_t err = pa::launch_decode(a, plan, static_cast<hipStream_t>(stream));
-    if (err != hipSuccess) return fail(PA_ERR_HIP, "decode launch: %s", hipGetErrorString(err));
-    return ok();
+    return decode_impl("pa_decode", out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+                       num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                       max_context_len, scale, partition_size, workspace, workspace_bytes, dtype,
+                       stream, nullptr);
+  } catch (...) {
+    return fail(PA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+pa_status pa_store_decode(void* out, const void* q, const void* key, const void* value,
+                          int64_t key_tok_stride, int64_t value_tok_stride, void* k_cache,
+                          void* v_cache, const int32_t* slot_mapping, const int32_t* block_tables,
+                          const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                          int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                          float scale, int32_t partition_size, void* workspace,
+                          size_t workspace_bytes, pa_dtype dtype, void* stream) {
+  try {
+    const Fusion f{key, value, key_tok_stride, value_tok_stride, slot_mapping};
+    return decode_impl("pa_store_decode", out, q, k_cache, v_cache, block_tables, context_lens,
+                       num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                       max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
+                       workspace_bytes, dtype, stream, &f);
   } catch (...) {
     return fail(PA_ERR_HIP, "unexpected C++ exception");
   }

@@ -34,6 +34,11 @@ struct DecodeArgs {
   int32_t partition_size;  // 0: no split
   void* workspace;
   bool bf16;
+  // fused store (pa_store_decode); key == nullptr otherwise
+  const void* key;
+  const void* value;
+  int64_t key_stride_bytes, value_stride_bytes;
+  const int32_t* slot_mapping;
 };
 
 struct PrefillArgs {

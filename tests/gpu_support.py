@@ -49,6 +49,20 @@ def gpu_decode(batch, partition_size, arrs=None, workspace=None):
     return out
 
 
+def gpu_store_decode(batch, partition_size, arrs=None, workspace=None):
+    """The fused store + decode call."""
+    arrs = arrs or device_arrays(batch)
+    dev = batch.q.device
+    if workspace is None:
+        workspace = pa.decode_workspace(batch.num_seqs, batch.num_heads, batch.num_kv_heads,
+                                        batch.head_dim, batch.max_context_len, partition_size, dev)
+    out = torch.full_like(batch.q, float("nan"))
+    pa.pa_store_decode(out, batch.q, batch.key, batch.value, batch.k_cache, batch.v_cache, arrs["slots"],
+                       arrs["tables"], arrs["lens"], batch.max_context_len, batch.scale, partition_size,
+                       workspace)
+    return out
+
+
 def gpu_prefill(batch, arrs=None):
     arrs = arrs or device_arrays(batch)
     out = torch.full_like(batch.q, float("nan"))
@@ -99,6 +113,33 @@ def decode_parity(batch, partition_size, seqs=None, heads=None):
                          batch.block_size, batch.dtype, rows)
     sel = np.stack([got[seqs[r], h] for r, h in rows])
     return check_close(sel, ref, batch.dtype, "decode (sampled)")
+
+
+def store_decode_parity(batch, partition_size):
+    """Fused store + decode on the GPU against the oracle's store followed by
+    its decode; the pools must also equal the oracle's stored pools byte for
+    byte."""
+    hb, kp, vp = oracle_inputs(batch)
+    arrs = device_arrays(batch)
+    out = gpu_store_decode(batch, partition_size, arrs)
+    torch.cuda.synchronize()
+    ref = oa.decode(hb.q, kp, vp, hb.block_tables, hb.context_lens, batch.scale, batch.block_size,
+                    batch.dtype)
+    res = check_close(as_f64(out), ref, batch.dtype, "store+decode")
+    ek, ev = oa.store_kvcache(wl_full_pool(batch, "k"), wl_full_pool(batch, "v"), wl.to_numpy(batch.key),
+                              wl.to_numpy(batch.value), batch.slot_mapping, batch.block_size)
+    return res, ek, ev
+
+
+def wl_full_pool(batch, which):
+    """Host copy of a whole pool as it was before the call under test (kept
+    on the batch by snapshot_pools)."""
+    return batch._pool_snapshot[which]
+
+
+def snapshot_pools(batch):
+    batch._pool_snapshot = dict(k=wl.to_numpy(batch.k_cache), v=wl.to_numpy(batch.v_cache))
+    return batch
 
 
 def prefill_parity(batch, sample_rows=None, seed=0):

@@ -124,6 +124,29 @@ def test_balanced_rejections(lib):
     assert _decode(lib, P=-1, B=4097, ws=FAKE, wsb=1 << 40) == PA_ERR_UNSUPPORTED
 
 
+def _store_decode(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, key=FAKE, value=FAKE, ks=512, vs=512, k=FAKE, v=FAKE, slots=FAKE,
+             bt=FAKE, cl=FAKE, B=4, Hq=8, Hkv=8, D=64, bs=16, NB=64, MB=7, maxL=100, scale=0.125,
+             P=0, ws=None, wsb=0, dtype=0)
+    a.update(kw)
+    return lib.pa_store_decode(a["out"], a["q"], a["key"], a["value"], a["ks"], a["vs"], a["k"], a["v"],
+                               a["slots"], a["bt"], a["cl"], a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"],
+                               a["NB"], a["MB"], a["maxL"], a["scale"], a["P"], a["ws"], a["wsb"],
+                               a["dtype"], None)
+
+
+def test_store_decode_rejections(lib):
+    assert _store_decode(lib, B=0) == PA_OK
+    assert _store_decode(lib, key=None) == PA_ERR_INVALID_ARG
+    assert _store_decode(lib, slots=None) == PA_ERR_INVALID_ARG
+    assert _store_decode(lib, ks=500) == PA_ERR_INVALID_ARG        # below one row
+    assert _store_decode(lib, vs=514) == PA_ERR_UNSUPPORTED        # not a 16-byte multiple
+    assert _store_decode(lib, key=ctypes.c_void_p(0x100008)) == PA_ERR_UNSUPPORTED
+    assert _store_decode(lib, D=96) == PA_ERR_UNSUPPORTED          # the decode checks apply too
+    assert _store_decode(lib, P=32) == PA_ERR_WORKSPACE
+    assert "pa_store_decode" in binding.load_library().pa_last_error().decode()
+
+
 def _store(lib, **kw):
     a = dict(key=FAKE, value=FAKE, ks=512, vs=512, k=FAKE, v=FAKE, slots=FAKE, T=4, Hkv=8, D=64,
              bs=16, NB=64, dtype=0)

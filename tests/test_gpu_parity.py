@@ -266,6 +266,68 @@ def test_decode_sharing_equals_duplication(gpu):
 
 
 # ---------------------------------------------------------------------------
+# fused store + decode
+# ---------------------------------------------------------------------------
+
+STORE_DECODE_CASES = [
+    ("tiny_fp32", 1, {}, [0, 32, -1]),
+    ("mha64", 2, dict(num_seqs=8, lens=("uniform", 1, 1500), max_context=1536), [0, 256, -1]),
+    ("gqa4_bs64", 5, dict(num_seqs=16, lens=("lognormal", 300.0, 1.0, 1, 2048), max_context=2048),
+     [0, 512, -1]),
+    ("gqa2_shared", 3, dict(num_seqs=12, lens=("uniform", 300, 1800), max_context=2048,
+                            share=dict(num_sharers=6, prefix_tokens=256)), [0, 128, -1]),
+    ("bs8_len1", 2, dict(num_seqs=6, lens=("fixed", [1, 2, 8, 9, 17, 64]), block_size=8,
+                         max_context=64), [0, 16, -1]),
+]
+
+
+@pytest.mark.parametrize("name,cfg,over,parts", STORE_DECODE_CASES, ids=[c[0] for c in STORE_DECODE_CASES])
+def test_store_decode_parity(gpu, name, cfg, over, parts):
+    """The slots being written are NaN-poisoned beforehand: reading one back
+    instead of taking the new row would make the output NaN."""
+    for P in parts:
+        b = gs.snapshot_pools(wl.make_batch(wl.spec(cfg, **over), device=gpu, poison=True))
+        gs.say(f"store+decode {name} P={P} lens={b.context_lens.tolist()}")
+        _, ek, ev = gs.store_decode_parity(b, P)
+        assert wl.to_numpy(b.k_cache).tobytes() == ek.tobytes()
+        assert wl.to_numpy(b.v_cache).tobytes() == ev.tobytes()
+
+
+@pytest.mark.parametrize("P", [0, 64, -1])
+def test_store_decode_negative_slot_reads_pool(gpu, P):
+    """A sequence whose slot is negative is not stored, and attends over the
+    pool row already there; the others are fused as usual."""
+    b = wl.make_batch(wl.spec(5, num_seqs=6, lens=("uniform", 40, 300), max_context=320), device=gpu)
+    arrs = gs.device_arrays(b)
+    skip = [1, 4]
+    for i in skip:   # put the new row in the pool by hand, then drop its slot
+        s = int(b.slot_mapping[i])
+        b.k_cache.view(-1, b.num_kv_heads, b.head_dim)[s] = b.key[i]
+        b.v_cache.view(-1, b.num_kv_heads, b.head_dim)[s] = b.value[i]
+        arrs["slots"][i] = -1
+    gs.snapshot_pools(b)
+    hb, kp, vp = gs.oracle_inputs(b)
+    out = gs.gpu_store_decode(b, P, arrs)
+    torch.cuda.synchronize()
+    ref = oa.decode(hb.q, kp, vp, hb.block_tables, hb.context_lens, b.scale, b.block_size, b.dtype)
+    gs.check_close(gs.as_f64(out), ref, b.dtype, "store+decode with skipped slots")
+
+
+def test_store_decode_agrees_with_separate_calls(gpu):
+    sp = wl.spec(5, num_seqs=40, lens=("uniform", 1, 2048), max_context=2048)
+    for P in (0, 256, -1):
+        b1 = wl.make_batch(sp, device=gpu)
+        a1 = gs.device_arrays(b1)
+        gs.gpu_store(b1, a1)
+        sep = gs.as_f64(gs.gpu_decode(b1, P, a1))
+        b2 = wl.make_batch(sp, device=gpu)
+        fused = gs.as_f64(gs.gpu_store_decode(b2, P))
+        torch.cuda.synchronize()
+        assert np.abs(fused - sep).max() <= 8e-3, P
+        assert torch.equal(b1.k_cache.view(torch.int16), b2.k_cache.view(torch.int16))
+
+
+# ---------------------------------------------------------------------------
 # decode: full-size configs, sampled outputs, in the benchmark's launch form
 # ---------------------------------------------------------------------------
 
