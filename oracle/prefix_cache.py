@@ -22,7 +22,15 @@ Readings where the page is silent:
     block (the block before it in the table) also match; otherwise it is
     treated as a miss and the hash is re-pointed to the new block;
   * new blocks are taken from the front of the free list given to the
-    allocator, and reclaimed blocks go to its back.
+    allocator, and reclaimed blocks go to its back;
+  * the number of cached tokens of a new sequence (the Sequence field
+    num_cached_tokens, §3.1) is block_size times the number of leading
+    blocks that were hits;
+  * decode (the mini-vllm page's BlockAllocator serves the prefill and the
+    decode phase, architecture item 1) appends one token at a time: a new
+    block is taken when the last one is full, and a block that the append
+    fills is hashed, chained from the block before it, and its hash is
+    recorded as for a miss, so that later requests can share it.
 """
 
 from __future__ import annotations
@@ -74,10 +82,15 @@ class PrefixBlockAllocator:
 
     def allocate(self, token_ids):
         """Block table (list of physical ids) for a sequence's tokens."""
+        return self.allocate_cached(token_ids)[0]
+
+    def allocate_cached(self, token_ids):
+        """(block table, number of leading tokens whose blocks were hits)."""
         bs = self.block_size
         table = []
         h = 0
         parent = -1
+        cached = 0
         for start in range(0, len(token_ids), bs):
             chunk = [int(t) for t in token_ids[start:start + bs]]
             if len(chunk) == bs:
@@ -89,6 +102,8 @@ class PrefixBlockAllocator:
                         blk.ref_count += 1
                         table.append(blk.block_id)
                         parent = blk.block_id
+                        if cached == start:
+                            cached += bs
                         continue
                 blk = self._take_free()
                 blk.ref_count = 1
@@ -104,7 +119,28 @@ class PrefixBlockAllocator:
                 blk.parent = parent
             table.append(blk.block_id)
             parent = blk.block_id
-        return table
+        return table, cached
+
+    def append_token(self, table, num_tokens, token_id):
+        """Append token_id at position num_tokens of the sequence owning
+        table (a list, extended in place when a new block is needed); returns
+        the token's slot, block * block_size + row."""
+        bs = self.block_size
+        row = num_tokens % bs
+        if row == 0:
+            blk = self._take_free()
+            blk.ref_count = 1
+            blk.hash = NO_HASH
+            blk.token_ids = []
+            blk.parent = table[-1] if table else -1
+            table.append(blk.block_id)
+        blk = self.blocks[table[num_tokens // bs]]
+        blk.token_ids.append(int(token_id))
+        if len(blk.token_ids) == bs:
+            prev = self.blocks[blk.parent].hash if blk.parent >= 0 else 0
+            blk.hash = compute_hash(blk.token_ids, prev)
+            self.hash_to_block_id[blk.hash] = blk.block_id
+        return blk.block_id * bs + row
 
     def free_table(self, table):
         """Drop one reference from every block of a finished sequence;

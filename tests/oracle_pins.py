@@ -386,6 +386,69 @@ def pin_allocator_sharing_small():
     assert sorted(alloc.free) == list(range(10))
 
 
+def pin_cached_tokens():
+    """num_cached_tokens counts the leading blocks that were hits: all of a
+    repeated full-block prompt, none of a fresh one, and never a hit after a
+    miss."""
+    bs = 4
+    alloc = opc.PrefixBlockAllocator(list(range(12)), bs)
+    a = list(range(100, 110))                       # 2 full blocks + 2 tokens
+    assert alloc.allocate_cached(a) == ([0, 1, 2], 0)
+    assert alloc.allocate_cached(a) == ([0, 1, 3], 8)
+    assert alloc.allocate_cached(a[:8]) == ([0, 1], 8)
+    b = [1, 2, 3, 4] + a[4:8]                        # second block equal, first not
+    t, c = alloc.allocate_cached(b)
+    assert c == 0 and t[1] != 1
+    # hits are always leading blocks: a hit needs the block before it in the
+    # table to be its recorded parent, which a block just taken never is
+    rng = _rng(31)
+    alloc = opc.PrefixBlockAllocator(list(range(400)), bs)
+    base = rng.integers(0, 6, size=40).tolist()
+    for _ in range(30):
+        cut = int(rng.integers(0, 41))
+        toks = base[:cut] + rng.integers(0, 6, size=int(rng.integers(0, 12))).tolist()
+        before = alloc.ref_counts()
+        t, c = alloc.allocate_cached(toks)
+        hit = [before.get(x, 0) > 0 for x in t]
+        assert c == bs * sum(hit) and all(hit[:sum(hit)])
+
+
+def pin_append_equals_allocate():
+    """Appending a sequence token by token to an empty table builds the same
+    table, slots and block hashes as allocating it whole, on allocators with
+    the same free list."""
+    rng = _rng(23)
+    for bs, n in ((4, 1), (4, 4), (4, 13), (16, 50), (8, 64)):
+        free = rng.permutation(64).tolist()
+        toks = rng.integers(0, 50257, size=n).tolist()
+        a1 = opc.PrefixBlockAllocator(free, bs)
+        whole = a1.allocate(toks)
+        a2 = opc.PrefixBlockAllocator(free, bs)
+        table = []
+        slots = [a2.append_token(table, j, t) for j, t in enumerate(toks)]
+        assert table == whole
+        assert slots == [whole[j // bs] * bs + j % bs for j in range(n)]
+        assert a2.hash_to_block_id == a1.hash_to_block_id
+        assert a2.ref_counts() == a1.ref_counts()
+
+
+def pin_append_fills_are_shareable():
+    """Blocks that decode appends fill are hashed like prompt blocks, so a
+    later prompt with the same prefix shares them."""
+    bs = 4
+    alloc = opc.PrefixBlockAllocator(list(range(16)), bs)
+    gen = [7, 7, 8, 9, 1, 2, 3, 4, 5]
+    table = []
+    for j, t in enumerate(gen):
+        alloc.append_token(table, j, t)
+    t2, c2 = alloc.allocate_cached(gen[:8] + [99])
+    assert t2[:2] == table[:2] and c2 == 8 and t2[2] != table[2]
+    assert alloc.ref_counts()[table[0]] == 2 and alloc.ref_counts()[table[2]] == 1
+    alloc.free_table(table)
+    alloc.free_table(t2)
+    assert alloc.ref_counts() == {} and not alloc.hash_to_block_id
+
+
 def pin_allocator_matches_structure(structure, block_size, num_sharers, prefix_tokens):
     """The hash-sharing allocator, fed the drawn token ids and free list,
     reproduces the drawn block tables; reference counts add up."""
@@ -415,5 +478,6 @@ ALL_PINS = [
     pin_gqa_equals_expanded_mha, pin_partition_invariance, pin_merge_of_disjoint_states,
     pin_bf16_widening, pin_prefill_row_is_decode, pin_prefill_c0_is_causal_sdpa,
     pin_prefill_chunk_split, pin_prefill_rows_subset, pin_hash_vectors,
-    pin_hash_polynomial_and_chaining, pin_allocator_sharing_small,
+    pin_hash_polynomial_and_chaining, pin_allocator_sharing_small, pin_cached_tokens,
+    pin_append_equals_allocate, pin_append_fills_are_shareable,
 ]

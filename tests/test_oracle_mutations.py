@@ -224,6 +224,36 @@ class _AllocShareAll(opc.PrefixBlockAllocator):
         return table
 
 
+class _AppendUnchained(opc.PrefixBlockAllocator):
+    """Hashes a block that decode fills from 0, not from the block before."""
+
+    def append_token(self, table, num_tokens, token_id):
+        slot = super().append_token(table, num_tokens, token_id)
+        blk = self.blocks[table[-1]]
+        if len(blk.token_ids) == self.block_size and blk.parent >= 0:
+            del self.hash_to_block_id[blk.hash]
+            blk.hash = opc.compute_hash(blk.token_ids, 0)
+            self.hash_to_block_id[blk.hash] = blk.block_id
+        return slot
+
+
+class _AppendSlotRow(opc.PrefixBlockAllocator):
+    """Reports the slot one row too far."""
+
+    def append_token(self, table, num_tokens, token_id):
+        return super().append_token(table, num_tokens, token_id) + 1
+
+
+class _AppendNoParent(opc.PrefixBlockAllocator):
+    """Forgets the block before a new decode block."""
+
+    def append_token(self, table, num_tokens, token_id):
+        slot = super().append_token(table, num_tokens, token_id)
+        if num_tokens % self.block_size == 0:
+            self.blocks[table[-1]].parent = -1
+        return slot
+
+
 MUTANTS = {
     "attend_no_scale": (oa, "attend", _attend_no_scale),
     "attend_unnormalised": (oa, "attend", _attend_unnormalised),
@@ -247,6 +277,9 @@ MUTANTS = {
     "hash_ignores_prefix": (opc, "compute_hash", _hash_reset),
     "alloc_no_ref_increment": (opc, "PrefixBlockAllocator", _AllocNoRef),
     "alloc_shares_partial_blocks": (opc, "PrefixBlockAllocator", _AllocShareAll),
+    "append_hash_unchained": (opc, "PrefixBlockAllocator", _AppendUnchained),
+    "append_slot_off_by_one": (opc, "PrefixBlockAllocator", _AppendSlotRow),
+    "append_forgets_parent": (opc, "PrefixBlockAllocator", _AppendNoParent),
 }
 
 
