@@ -167,6 +167,47 @@ def split_name(P):
     return "balanced" if P == pa.PA_PARTITION_BALANCED else "fixed"
 
 
+def bench_block_manager():
+    """Host-side block manager: build the shared-prefix decode workload's
+    tables (256 prompts, prefix hashing and sharing), append one decode token
+    to each sequence, free everything; the same with the CPU oracle's
+    allocator."""
+    import oracle.prefix_cache as opc
+    st = wl.draw_structure(wl.spec(3))
+    bs = wl.CONFIGS[3]["block_size"]
+    free = st["free_list"].tolist()
+    ids = [np.ascontiguousarray(t, dtype=np.int32) for t in st["token_ids"]]
+    ntok = int(sum(len(t) for t in ids))
+
+    def run_ours():
+        bm = pa.BlockManager(int(st["num_blocks"]), bs, free)
+        tables = [bm.allocate(t)[0] for t in ids]
+        tables = [bm.append(t, len(ids[i]), 7)[0] for i, t in enumerate(tables)]
+        for t in tables:
+            bm.free(t)
+        bm.close()
+
+    def run_oracle():
+        al = opc.PrefixBlockAllocator(free, bs)
+        tables = [al.allocate(t.tolist()) for t in ids]
+        for i, t in enumerate(tables):
+            al.append_token(t, len(ids[i]), 7)
+        for t in tables:
+            al.free_table(t)
+    run_ours()
+    t0 = time.perf_counter()
+    reps = 5
+    for _ in range(reps):
+        run_ours()
+    ours = (time.perf_counter() - t0) / reps
+    t0 = time.perf_counter()
+    run_oracle()
+    orc = time.perf_counter() - t0
+    return dict(workload="bf16_gqa_decode_b256_shared_prefix tables: allocate + 1 append + free",
+                prompt_tokens=ntok, ms=round(ours * 1e3, 3), tokens_per_s=round(ntok / ours, 1),
+                oracle_ms=round(orc * 1e3, 1), oracle_tokens_per_s=round(ntok / orc, 1))
+
+
 def copy_probe(nbytes, device, reps=3):
     """A plain device-to-device copy of a known size, for scaling the HBM
     byte counters (FETCH_SIZE / WRITE_SIZE) of a profiling run."""
@@ -289,6 +330,8 @@ def main():
                     logical_bytes_per_launch=int(np.mean(d.kv_bytes_logical)))
                 del d
                 torch.cuda.empty_cache()
+        log("extra block manager")
+        extra["block_manager"] = bench_block_manager()
         log("extra prefill")
         extra["prefill"] = bench_prefill(20, 3, dev)
         line["extra"] = extra

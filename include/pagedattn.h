@@ -70,7 +70,8 @@ typedef enum pa_status {
   PA_ERR_INVALID_ARG = 1,  /* null pointer, negative size, inconsistent sizes */
   PA_ERR_UNSUPPORTED = 2,  /* valid but not implemented (head_dim, block_size, alignment) */
   PA_ERR_WORKSPACE = 3,    /* split decode without a large enough workspace */
-  PA_ERR_HIP = 4           /* a HIP runtime call or launch failed */
+  PA_ERR_HIP = 4,          /* a HIP runtime call or launch failed */
+  PA_ERR_OUT_OF_BLOCKS = 5 /* block manager: too few free blocks; nothing was changed */
 } pa_status;
 
 typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
@@ -203,6 +204,63 @@ pa_status pa_prefill_chunk(void* out, const void* q,
                            int32_t max_blocks_per_seq, int32_t max_query_len,
                            int32_t max_context_len, float scale,
                            pa_dtype dtype, void* stream);
+
+/*
+ * Block manager (host only; no device memory, no HIP calls).
+ *
+ * Hands out the physical blocks of a pool of num_blocks blocks of block_size
+ * tokens to sequences and shares full prompt blocks between sequences with
+ * the same prefix (the nano-vllm page: Block with reference count, hash and
+ * token ids, §3.2.1; the allocation loop, §3.2.2; the rolling hash
+ * h <- (31 h + t) mod 2^32 chained from the block before, §4.2; and the
+ * mini-vllm page's BlockAllocator, architecture item 1, which serves prefill
+ * and decode and frees a finished request's blocks). Only full blocks are
+ * hashed and shared; a hash hit counts only when the block's tokens and the
+ * block before it match. The tables and slots it produces are the
+ * block_tables rows and slot_mapping entries of the calls above.
+ *
+ * The manager owns its host memory; it is not thread-safe. Every call
+ * validates its arguments and, on failure, changes nothing.
+ */
+typedef struct pa_block_manager pa_block_manager;
+
+/* A manager over blocks 0 .. num_blocks-1. free_order (may be NULL: 0, 1,
+ * 2, ...) is a permutation of the block ids giving the free list, front
+ * first; new blocks come from its front, reclaimed blocks go to its back. */
+pa_status pa_bm_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order,
+                       pa_block_manager** out);
+void pa_bm_destroy(pa_block_manager* bm);
+
+/* Blocks for a new sequence's num_tokens prompt tokens: for each block,
+ * reuse a matching shared block (one more reference) or take a free one.
+ * Writes ceil(num_tokens/block_size) ids to table (table_capacity entries
+ * available) and their count to *num_table_blocks; *num_cached_tokens is
+ * block_size times the number of leading blocks that were reused (tokens
+ * whose K/V are already in the pool); slots (may be NULL) receives every
+ * token's slot, block * block_size + row. PA_ERR_OUT_OF_BLOCKS if the free
+ * list runs out. */
+pa_status pa_bm_allocate(pa_block_manager* bm, const int32_t* token_ids, int32_t num_tokens,
+                         int32_t* table, int32_t table_capacity, int32_t* num_table_blocks,
+                         int32_t* num_cached_tokens, int32_t* slots);
+
+/* Decode: append token_id at position num_tokens of the sequence holding
+ * table (*num_table_blocks entries). A new block is taken when the last one
+ * is full (the table grows by one entry); a block the token fills is hashed
+ * and becomes shareable. *slot receives the token's slot. */
+pa_status pa_bm_append(pa_block_manager* bm, int32_t* table, int32_t* num_table_blocks,
+                       int32_t table_capacity, int32_t num_tokens, int32_t token_id,
+                       int32_t* slot);
+
+/* A finished sequence: one reference less on each block of its table (last
+ * block first); blocks left with none return to the free list. */
+pa_status pa_bm_free(pa_block_manager* bm, const int32_t* table, int32_t num_table_blocks);
+
+/* Free blocks, and a block's reference count (-1 for an invalid id). */
+int32_t pa_bm_num_free(const pa_block_manager* bm);
+int32_t pa_bm_ref_count(const pa_block_manager* bm, int32_t block_id);
+
+/* Description of the calling thread's last failed block-manager call. */
+const char* pa_bm_last_error(void);
 
 /* Static description of a status code. */
 const char* pa_status_string(pa_status s);

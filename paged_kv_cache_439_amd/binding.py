@@ -235,3 +235,117 @@ def pa_prefill_chunk(out, q, k_cache, v_cache, block_tables, query_start_loc, co
                               block_tables.shape[1], int(max_query_len), int(max_context_len),
                               float(scale), _dtype_code(q), _stream(stream))
     _check("pa_prefill_chunk", st)
+
+
+# ---------------------------------------------------------------------------
+# block manager (host only)
+# ---------------------------------------------------------------------------
+
+_BM_SIGNATURES = {
+    "pa_bm_create": ([_i32, _i32, _c_void_p, ctypes.POINTER(_c_void_p)], ctypes.c_int),
+    "pa_bm_destroy": ([_c_void_p], None),
+    "pa_bm_allocate": ([_c_void_p, _c_void_p, _i32, _c_void_p, _i32, ctypes.POINTER(_i32),
+                        ctypes.POINTER(_i32), _c_void_p], ctypes.c_int),
+    "pa_bm_append": ([_c_void_p, _c_void_p, ctypes.POINTER(_i32), _i32, _i32, _i32,
+                      ctypes.POINTER(_i32)], ctypes.c_int),
+    "pa_bm_free": ([_c_void_p, _c_void_p, _i32], ctypes.c_int),
+    "pa_bm_num_free": ([_c_void_p], _i32),
+    "pa_bm_ref_count": ([_c_void_p, _i32], _i32),
+    "pa_bm_last_error": ([], ctypes.c_char_p),
+}
+PA_ERR_OUT_OF_BLOCKS = 5
+
+
+class OutOfBlocks(PagedAttnError):
+    pass
+
+
+def _bm_lib():
+    lib = load_library()
+    if not getattr(lib, "_bm_ready", False):
+        for name, (args, res) in _BM_SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = res
+        lib._bm_ready = True
+    return lib
+
+
+def _bm_check(func, status):
+    if status != 0:
+        msg = _bm_lib().pa_bm_last_error().decode(errors="replace")
+        cls = OutOfBlocks if status == PA_ERR_OUT_OF_BLOCKS else PagedAttnError
+        raise cls(func, status, msg)
+
+
+def _i32_array(values):
+    import numpy as np
+    return np.ascontiguousarray(np.asarray(values, dtype=np.int32))
+
+
+class BlockManager:
+    """The library's host-side block manager (pa_bm_*): block tables with
+    prefix sharing, decode appends and reference-counted frees. Tables are
+    numpy int32 arrays of the sequence's block ids."""
+
+    def __init__(self, num_blocks, block_size, free_order=None):
+        lib = _bm_lib()
+        self.block_size = int(block_size)
+        handle = _c_void_p()
+        fo = None if free_order is None else _i32_array(free_order)
+        _bm_check("pa_bm_create", lib.pa_bm_create(int(num_blocks), self.block_size,
+                                                   None if fo is None else fo.ctypes.data,
+                                                   ctypes.byref(handle)))
+        self._h = handle
+        self._lib = lib
+
+    def close(self):
+        if self._h:
+            self._lib.pa_bm_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def allocate(self, token_ids, with_slots=False):
+        """(table, num_cached_tokens[, slots]) for a new sequence's prompt."""
+        import numpy as np
+        toks = _i32_array(token_ids)
+        n = len(toks)
+        cap = max(1, -(-n // self.block_size))
+        table = np.empty(cap, dtype=np.int32)
+        slots = np.empty(max(1, n), dtype=np.int32) if with_slots else None
+        nb, cached = _i32(), _i32()
+        _bm_check("pa_bm_allocate", self._lib.pa_bm_allocate(
+            self._h, toks.ctypes.data if n else None, n, table.ctypes.data, cap, ctypes.byref(nb),
+            ctypes.byref(cached), None if slots is None else slots.ctypes.data))
+        table = table[:nb.value].copy()
+        if with_slots:
+            return table, cached.value, slots[:n].copy()
+        return table, cached.value
+
+    def append(self, table, num_tokens, token_id):
+        """Append one token at position num_tokens; returns (table, slot), the
+        table grown by one block when the last one was full."""
+        import numpy as np
+        nb = len(table)
+        buf = np.empty(nb + 1, dtype=np.int32)
+        buf[:nb] = table
+        nbv, slot = _i32(nb), _i32()
+        _bm_check("pa_bm_append", self._lib.pa_bm_append(self._h, buf.ctypes.data, ctypes.byref(nbv),
+                                                         nb + 1, int(num_tokens), int(token_id),
+                                                         ctypes.byref(slot)))
+        return buf[:nbv.value].copy(), slot.value
+
+    def free(self, table):
+        t = _i32_array(table)
+        _bm_check("pa_bm_free", self._lib.pa_bm_free(self._h, t.ctypes.data if len(t) else None, len(t)))
+
+    def num_free(self):
+        return int(self._lib.pa_bm_num_free(self._h))
+
+    def ref_count(self, block_id):
+        return int(self._lib.pa_bm_ref_count(self._h, int(block_id)))
