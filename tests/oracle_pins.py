@@ -18,6 +18,7 @@ import numpy as np
 import torch
 
 import oracle.attention as oa
+import oracle.fp8 as of8
 import oracle.prefix_cache as opc
 
 
@@ -472,6 +473,171 @@ def pin_allocator_matches_structure(structure, block_size, num_sharers, prefix_t
     assert len(rc) == logical - max(0, num_sharers - 1) * pb
 
 
+# ---------------------------------------------------------------------------
+# E4M3 KV cache
+# ---------------------------------------------------------------------------
+
+def pin_e4m3_closed_forms():
+    """Codes whose values the format's field definition fixes by hand: one,
+    two, the largest finite value, the smallest normal and subnormal, the
+    sign bit, the NaN codes."""
+    t = of8.e4m3_table()
+    want = {0x00: 0.0, 0x38: 1.0, 0x3C: 1.5, 0x40: 2.0, 0x30: 0.5, 0x7E: 448.0, 0x78: 256.0,
+            0x77: 240.0, 0x08: 2.0 ** -6, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x04: 2.0 ** -7,
+            0xB8: -1.0, 0xFE: -448.0, 0x81: -(2.0 ** -9)}
+    for code, v in want.items():
+        assert t[code] == v, (hex(code), t[code], v)
+    assert t[0x80] == 0.0 and math.copysign(1.0, t[0x80]) < 0
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF])
+    assert np.sum(np.isnan(t)) == 2
+    assert np.array_equal(t[0x80:], -t[:0x80], equal_nan=True)
+
+
+def pin_e4m3_table_vs_torch():
+    """The value table equals torch's float8_e4m3fn reading of every byte."""
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn)
+    ref = ref.to(torch.float64).numpy()
+    t = of8.e4m3_table()
+    assert np.array_equal(np.isnan(ref), np.isnan(t))
+    fin = ~np.isnan(t)
+    assert np.array_equal(ref[fin], t[fin])
+
+
+def pin_e4m3_quantize_vs_torch():
+    """Inside the finite range, quantisation with scale 1 equals torch's
+    float32 -> float8_e4m3fn conversion (nearest, ties to even), on random
+    values over every binade, on every midpoint between neighbouring codes,
+    and one float32 ulp either side of each midpoint."""
+    rng = _rng(40)
+    x = (rng.standard_normal(20000) * np.exp2(rng.uniform(-12, 9, 20000))).astype(np.float32)
+    t = of8.e4m3_table()
+    pos = t[:0x7F]
+    mid = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    up = np.nextafter(mid, np.float32(np.inf))
+    dn = np.nextafter(mid, np.float32(0))
+    x = np.concatenate([x, mid, -mid, up, dn, -up, -dn])
+    x = x[np.abs(x) <= 448]
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = of8.quantize_e4m3(x, 1.0)
+    assert np.array_equal(got, ref), np.flatnonzero(got != ref)[:5]
+
+
+def pin_e4m3_round_trip_and_ties():
+    """Every finite code survives value -> quantise; a midpoint goes to the
+    code with even mantissa; the rounding error is at most half the gap
+    between neighbouring values."""
+    t = of8.e4m3_table()
+    codes = np.array([c for c in range(256) if not np.isnan(t[c])], dtype=np.uint8)
+    assert np.array_equal(of8.quantize_e4m3(t[codes].astype(np.float32), 1.0), codes)
+    pos = t[:0x7F]
+    for c in range(0x7E):
+        m = np.float32((pos[c] + pos[c + 1]) / 2)
+        even = c if c % 2 == 0 else c + 1
+        assert of8.quantize_e4m3(m, 1.0) == even, hex(c)
+        assert of8.quantize_e4m3(-m, 1.0) == (even | 0x80)
+    x = np.linspace(-448, 448, 40001).astype(np.float32)
+    y = t[of8.quantize_e4m3(x, 1.0)]
+    gap = np.where(np.abs(x) < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -6))) - 3))
+    assert np.all(np.abs(y - x.astype(np.float64)) <= gap / 2)
+
+
+def pin_e4m3_saturation_and_specials():
+    """Magnitudes past 448, infinities included, saturate to +-448; NaN maps
+    to a NaN code; signed zeros keep their sign."""
+    q = of8.quantize_e4m3(np.array([448.0, 464.0, 480.0, 1e6, np.inf, -500.0, -np.inf],
+                                   dtype=np.float32), 1.0)
+    assert q.tolist() == [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE]
+    assert np.isnan(of8.e4m3_table()[of8.quantize_e4m3(np.float32(np.nan), 1.0)])
+    assert of8.quantize_e4m3(np.float32(0.0), 1.0) == 0x00
+    assert of8.quantize_e4m3(np.float32(-0.0), 1.0) == 0x80
+    assert of8.quantize_e4m3(np.float32(2.0 ** -11), 1.0) == 0x00   # below half the smallest subnormal
+
+
+def pin_e4m3_scale_divides():
+    """The stored code is that of x / scale (not x * scale): scaling x and
+    the scale by one power of two leaves every code unchanged."""
+    rng = _rng(41)
+    x = (rng.standard_normal(4000) * 8).astype(np.float32)
+    base = of8.quantize_e4m3(x, 1.0)
+    for k in (-3, 1, 5):
+        assert np.array_equal(of8.quantize_e4m3(x * np.float32(2.0 ** k), 2.0 ** k), base)
+    assert of8.quantize_e4m3(np.float32(3.0), 2.0) == of8.quantize_e4m3(np.float32(1.5), 1.0)
+    assert of8.quantize_e4m3(np.float32(3.0), 0.5) == 0x4C           # 6.0 = 1.5 * 2^2: e=9, m=4
+
+
+def pin_fp8_store_layout():
+    """The E4M3 store puts, at slot s, the per-head quantised row (head h with
+    its own k/v scale) and leaves every other byte alone; negative slots
+    write nothing; bf16 and f32 inputs of equal value give equal codes."""
+    rng = _rng(42)
+    NB, bs, Hkv, D = 5, 4, 3, 8
+    kp = rng.integers(0, 256, size=(NB, bs, Hkv, D), dtype=np.uint8)
+    vp = rng.integers(0, 256, size=(NB, bs, Hkv, D), dtype=np.uint8)
+    key = (rng.standard_normal((6, Hkv, D)) * 4).astype(np.float32)
+    val = (rng.standard_normal((6, Hkv, D)) * 4).astype(np.float32)
+    ks = np.array([0.5, 1.0, 0.03125])
+    vs = np.array([2.0, 0.25, 1.0])
+    slots = np.array([3, -1, 19, 0, 8, 13], dtype=np.int64)
+    k2, v2 = of8.store_kvcache_fp8(kp, vp, key, val, slots, bs, ks, vs, "f32")
+    ek = kp.reshape(NB * bs, Hkv, D).copy()
+    ev = vp.reshape(NB * bs, Hkv, D).copy()
+    t = of8.e4m3_table()
+    for i, s in enumerate(slots):
+        if s < 0:
+            continue
+        for h in range(Hkv):
+            for d in range(D):
+                ek[s, h, d] = int(np.argmin(np.abs(np.nan_to_num(t[:0x7F], nan=1e9) - abs(key[i, h, d] / ks[h])))) | (0x80 if key[i, h, d] < 0 else 0)
+                ev[s, h, d] = int(np.argmin(np.abs(np.nan_to_num(t[:0x7F], nan=1e9) - abs(val[i, h, d] / vs[h])))) | (0x80 if val[i, h, d] < 0 else 0)
+    assert k2.tobytes() == ek.reshape(kp.shape).tobytes()
+    assert v2.tobytes() == ev.reshape(vp.shape).tobytes()
+    kb = (key.view(np.uint32) >> 16).astype(np.uint16)       # bf16 truncations are exact bf16 values
+    key_b = (kb.astype(np.uint32) << 16).view(np.float32)
+    k3, _ = of8.store_kvcache_fp8(kp, vp, kb, (val.view(np.uint32) >> 16).astype(np.uint16), slots,
+                                  bs, ks, vs, "bf16")
+    k4, _ = of8.store_kvcache_fp8(kp, vp, key_b, val, slots, bs, ks, vs, "f32")
+    assert np.array_equal(k3, k4)
+
+
+def pin_fp8_decode_vs_sdpa():
+    """E4M3 decode equals torch's attention over the contiguous rows read
+    back as value(code) * scale (per KV head), the pool laid out block by
+    block; scaling k_scale by c equals scaling the softmax scale by c, and
+    scaling v_scale by c scales the output by c."""
+    rng = _rng(43)
+    lens, Hq, Hkv, D, bs = (1, 6, 13, 20), 6, 2, 16, 4
+    kcodes = [rng.integers(0, 0x7F, size=(L, Hkv, D)).astype(np.uint8) | rng.choice(np.array([0, 0x80], dtype=np.uint8), size=(L, Hkv, D)) for L in lens]
+    vcodes = [rng.integers(0, 0x7F, size=(L, Hkv, D)).astype(np.uint8) | rng.choice(np.array([0, 0x80], dtype=np.uint8), size=(L, Hkv, D)) for L in lens]
+    kcodes = [np.where((c & 0x7F) > 0x50, c & 0x87, c).astype(np.uint8) for c in kcodes]   # keep logits moderate
+    nb = sum(math.ceil(L / bs) for L in lens) + 2
+    kp, tables = _paged_from_contiguous(kcodes, bs, nb, _rng(44), fill=0x7F)
+    vp, tables_v = _paged_from_contiguous(vcodes, bs, nb, _rng(44), fill=0x7F)
+    assert np.array_equal(tables, tables_v)
+    q = rng.standard_normal((len(lens), Hq, D)).astype(np.float32)
+    ks, vs = np.array([0.5, 0.125]), np.array([2.0, 0.75])
+    scale = 1.0 / math.sqrt(D)
+    out = of8.decode_fp8(q, kp, vp, ks, vs, tables, np.array(lens), scale, bs, "f32")
+    # values by hand from the format's fields
+    def val(c):
+        c = c.astype(np.int64)
+        e, m = (c >> 3) & 15, c & 7
+        mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1 + m / 8.0) * np.exp2(e - 7.0))
+        return np.where(c & 0x80, -mag, mag)
+    G = Hq // Hkv
+    for i, L in enumerate(lens):
+        k = np.repeat(val(kcodes[i]) * ks[None, :, None], G, axis=1).transpose(1, 0, 2)
+        v = np.repeat(val(vcodes[i]) * vs[None, :, None], G, axis=1).transpose(1, 0, 2)
+        ref = _sdpa(q[i].astype(np.float64)[:, None, :], np.ascontiguousarray(k),
+                    np.ascontiguousarray(v), scale)[:, 0, :]
+        assert np.max(np.abs(out[i] - ref)) < 1e-12
+    out_k = of8.decode_fp8(q, kp, vp, ks * 3, vs, tables, np.array(lens), scale, bs, "f32")
+    out_s = of8.decode_fp8(q, kp, vp, ks, vs, tables, np.array(lens), scale * 3, bs, "f32")
+    assert np.max(np.abs(out_k - out_s)) < 1e-12
+    out_v = of8.decode_fp8(q, kp, vp, ks, vs * np.array([3.0, 1.0]), tables, np.array(lens), scale, bs, "f32")
+    assert np.max(np.abs(out_v[:, :G] - 3 * out[:, :G])) < 1e-12
+    assert np.max(np.abs(out_v[:, G:] - out[:, G:])) < 1e-12
+
+
 ALL_PINS = [
     pin_store_bytes, pin_gather_inverts_layout, pin_decode_vs_sdpa, pin_decode_closed_forms,
     pin_decode_block_permutation, pin_decode_sharing_equals_duplication,
@@ -480,4 +646,7 @@ ALL_PINS = [
     pin_prefill_chunk_split, pin_prefill_rows_subset, pin_hash_vectors,
     pin_hash_polynomial_and_chaining, pin_allocator_sharing_small, pin_cached_tokens,
     pin_append_equals_allocate, pin_append_fills_are_shareable,
+    pin_e4m3_closed_forms, pin_e4m3_table_vs_torch, pin_e4m3_quantize_vs_torch,
+    pin_e4m3_round_trip_and_ties, pin_e4m3_saturation_and_specials, pin_e4m3_scale_divides,
+    pin_fp8_store_layout, pin_fp8_decode_vs_sdpa,
 ]

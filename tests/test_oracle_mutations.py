@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 
 import oracle.attention as oa
+import oracle.fp8 as of8
 import oracle.prefix_cache as opc
 from tests import oracle_pins as pins
 
@@ -254,6 +255,68 @@ class _AppendNoParent(opc.PrefixBlockAllocator):
         return slot
 
 
+def _e4m3_bias_8():
+    out = []
+    for c in range(256):
+        sign = -1.0 if c & 0x80 else 1.0
+        e, m = (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            out.append(np.nan)
+        elif e == 0:
+            out.append(sign * m / 8.0 * 2.0 ** -7)
+        else:
+            out.append(sign * (1 + m / 8.0) * 2.0 ** (e - 8))
+    return np.array(out)
+
+
+def _make_quantize(rounding="even", multiply=False, saturate=True):
+    def quantize(x, scale):
+        pos = of8.e4m3_table()[:0x7F]
+        xf = np.asarray(x, dtype=np.float32)
+        y = (xf * np.float32(scale) if multiply else xf / np.float32(scale)).astype(np.float32)
+        a = np.abs(y.astype(np.float64))
+        nan = np.isnan(a)
+        if not saturate:
+            nan = nan | (a > 448)
+        a = np.where(nan, 0.0, np.minimum(a, 448.0))
+        hi = np.minimum(np.searchsorted(pos, a, side="left"), len(pos) - 1)
+        lo = np.maximum(hi - 1, 0)
+        dlo, dhi = a - pos[lo], pos[hi] - a
+        if rounding == "even":
+            take_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+        elif rounding == "away":
+            take_hi = dhi <= dlo
+        else:                                   # toward zero
+            take_hi = dhi == 0
+        code = np.where(take_hi, hi, lo).astype(np.uint8)
+        code = np.where(nan, np.uint8(0x7F), code)
+        return (code | np.where(np.signbit(y), np.uint8(0x80), np.uint8(0))).astype(np.uint8)
+    return quantize
+
+
+def _dequantize_heads_reversed(codes, scales):
+    vals = of8.e4m3_table()[np.asarray(codes, dtype=np.uint8)]
+    return vals * np.asarray(scales, dtype=np.float64)[::-1][:, None]
+
+
+def _make_store_fp8_k_scale_for_v():
+    orig = of8.store_kvcache_fp8
+
+    def store(k_codes, v_codes, key, value, slot_mapping, block_size, k_scale, v_scale, dtype):
+        return orig(k_codes, v_codes, key, value, slot_mapping, block_size, k_scale, k_scale, dtype)
+    return store
+
+
+def _make_decode_fp8_scales_swapped():
+    orig = of8.decode_fp8
+
+    def decode(q, k_codes, v_codes, k_scale, v_scale, block_tables, context_lens, scale,
+               block_size, q_dtype):
+        return orig(q, k_codes, v_codes, v_scale, k_scale, block_tables, context_lens, scale,
+                    block_size, q_dtype)
+    return decode
+
+
 MUTANTS = {
     "attend_no_scale": (oa, "attend", _attend_no_scale),
     "attend_unnormalised": (oa, "attend", _attend_unnormalised),
@@ -280,6 +343,14 @@ MUTANTS = {
     "append_hash_unchained": (opc, "PrefixBlockAllocator", _AppendUnchained),
     "append_slot_off_by_one": (opc, "PrefixBlockAllocator", _AppendSlotRow),
     "append_forgets_parent": (opc, "PrefixBlockAllocator", _AppendNoParent),
+    "e4m3_bias_8": (of8, "e4m3_table", _e4m3_bias_8),
+    "e4m3_ties_away": (of8, "quantize_e4m3", _make_quantize(rounding="away")),
+    "e4m3_truncates": (of8, "quantize_e4m3", _make_quantize(rounding="zero")),
+    "e4m3_multiplies_scale": (of8, "quantize_e4m3", _make_quantize(multiply=True)),
+    "e4m3_overflow_to_nan": (of8, "quantize_e4m3", _make_quantize(saturate=False)),
+    "fp8_heads_reversed": (of8, "dequantize_rows", _dequantize_heads_reversed),
+    "fp8_store_k_scale_for_v": (of8, "store_kvcache_fp8", None),
+    "fp8_decode_scales_swapped": (of8, "decode_fp8", None),
 }
 
 
@@ -302,6 +373,10 @@ def test_mutant_is_caught(name, monkeypatch):
         repl, _ = _make_decode_gqa_mod()
     elif name == "decode_context_minus_one":
         repl, _ = _make_decode_short_context()
+    elif name == "fp8_store_k_scale_for_v":
+        repl = _make_store_fp8_k_scale_for_v()
+    elif name == "fp8_decode_scales_swapped":
+        repl = _make_decode_fp8_scales_swapped()
     monkeypatch.setattr(module, attr, repl)
     caught = []
     for pin in pins.ALL_PINS + _extra_pins():
