@@ -206,6 +206,56 @@ pa_status pa_prefill_chunk(void* out, const void* q,
                            pa_dtype dtype, void* stream);
 
 /*
+ * 8-bit float (E4M3) pools.
+ *
+ * Quantisation of the cache is among the extensions both the nano-vllm page
+ * (§5.3, extension suggestions) and the Nano-vLLM tutorial page (its closing
+ * list of directions) leave for later; the pages fix no format. These calls
+ * store each K/V element as one byte in the OCP E4M3 format (1 sign, 4
+ * exponent bits with bias 7, 3 mantissa bits; no infinity; 0x7F/0xFF are
+ * NaN; largest finite value 448), with one fp32 scale per KV head for K and
+ * one for V:
+ *   stored value of element x of KV head h = value(code) * scale[h],
+ *   code = the E4M3 code nearest to fp32(x / scale[h]) (ties to the even
+ *          code), |x / scale[h]| saturated at 448; NaN -> 0x7F with x's sign.
+ * The pools are uint8 [num_blocks][block_size][num_kv_heads][head_dim],
+ * half the bytes of bf16. k_scale and v_scale are device fp32 arrays of
+ * num_kv_heads entries (4-byte aligned) owned by the caller; choosing them
+ * (e.g. max |x| / 448 per head) is the caller's business.
+ *
+ * pa_store_kvcache_fp8 -- pa_store_kvcache with quantisation: key/value are
+ * dtype (PA_BF16 or PA_F32) rows with token strides in elements (multiples
+ * of 16 bytes); head_dim a multiple of 16. The codes are bit-exact.
+ */
+pa_status pa_store_kvcache_fp8(const void* key, const void* value,
+                               int64_t key_tok_stride, int64_t value_tok_stride,
+                               void* k_cache, void* v_cache,
+                               const int32_t* slot_mapping,
+                               const float* k_scale, const float* v_scale,
+                               int32_t num_tokens, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, pa_dtype dtype, void* stream);
+
+/*
+ * pa_decode_fp8 -- pa_decode over E4M3 pools: the same operation with
+ * K[g] = value(codes) * k_scale[g] and V[g] = value(codes) * v_scale[g].
+ * q and out are dtype (PA_BF16: q . K by bf16 dot products of q with the
+ * exactly widened codes; PA_F32: fp32), accumulation fp32. Splits,
+ * workspace (pa_decode_workspace_size with the same arguments), shapes and
+ * errors as for pa_decode; there is no fused-store variant.
+ */
+pa_status pa_decode_fp8(void* out, const void* q,
+                        const void* k_cache, const void* v_cache,
+                        const float* k_scale, const float* v_scale,
+                        const int32_t* block_tables, const int32_t* context_lens,
+                        int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                        int32_t max_blocks_per_seq, int32_t max_context_len,
+                        float scale, int32_t partition_size,
+                        void* workspace, size_t workspace_bytes,
+                        pa_dtype dtype, void* stream);
+
+/*
  * Block manager (host only; no device memory, no HIP calls).
  *
  * Hands out the physical blocks of a pool of num_blocks blocks of block_size

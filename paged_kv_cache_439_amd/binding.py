@@ -51,6 +51,12 @@ _SIGNATURES = {
     "pa_prefill_chunk": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                           _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                           _f32, ctypes.c_int, _c_void_p], ctypes.c_int),
+    "pa_store_kvcache_fp8": ([_c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
+                              _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, ctypes.c_int,
+                              _c_void_p], ctypes.c_int),
+    "pa_decode_fp8": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                       _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                       _c_void_p, _size, ctypes.c_int, _c_void_p], ctypes.c_int),
     "pa_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "pa_last_error": ([], ctypes.c_char_p),
 }
@@ -210,6 +216,67 @@ def pa_store_decode(out, q, key, value, k_cache, v_cache, slot_mapping, block_ta
                              int(max_context_len), float(scale), int(partition_size), ws_ptr, ws_bytes,
                              _dtype_code(q), _stream(stream))
     _check("pa_store_decode", st)
+
+
+def _e4m3_pools(k_cache, v_cache):
+    _need(k_cache.dim() == 4 and k_cache.shape == v_cache.shape, "pools must be [NB][bs][Hkv][D]")
+    _need(k_cache.is_contiguous() and v_cache.is_contiguous(), "pools must be contiguous")
+    for t in (k_cache, v_cache):
+        _need(t.dtype in (torch.uint8, torch.float8_e4m3fn), "E4M3 pools must be uint8 or float8_e4m3fn")
+
+
+def _scales(k_scale, v_scale, num_kv_heads, device):
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        _need(t.dtype == torch.float32 and t.device == device and t.is_contiguous(),
+              f"{name} must be a contiguous float32 tensor on {device}")
+        _need(t.numel() == num_kv_heads, f"{name} must have num_kv_heads entries")
+
+
+def pa_store_kvcache_fp8(key, value, k_cache, v_cache, slot_mapping, k_scale, v_scale, stream=None):
+    """Quantise key/value rows [T][Hkv][D] (bf16 or fp32) to E4M3 codes with
+    per-KV-head scales and scatter them into the uint8 pools by slot_mapping."""
+    lib = load_library()
+    T, Hkv, D = key.shape
+    _need(value.shape == key.shape and value.dtype == key.dtype, "key and value differ")
+    _e4m3_pools(k_cache, v_cache)
+    NB, bs, Hkv2, D2 = k_cache.shape
+    _need((Hkv2, D2) == (Hkv, D), "pool head shape does not match key")
+    for t in (key, value):
+        _need(t.stride(2) == 1 and t.stride(1) == D, "key/value rows must be dense [Hkv][D]")
+    _int32_device(slot_mapping, "slot_mapping", k_cache.device)
+    _need(slot_mapping.numel() == T, "slot_mapping length differs from key")
+    _scales(k_scale, v_scale, Hkv, k_cache.device)
+    st = lib.pa_store_kvcache_fp8(_ptr(key), _ptr(value), key.stride(0), value.stride(0),
+                                  _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), _ptr(k_scale),
+                                  _ptr(v_scale), T, Hkv, D, bs, NB, _dtype_code(key), _stream(stream))
+    _check("pa_store_kvcache_fp8", st)
+
+
+def pa_decode_fp8(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                  max_context_len, scale, partition_size=0, workspace=None, stream=None):
+    """Single-token decode over E4M3 pools; out and q are [B][Hq][D] (bf16 or
+    fp32), the workspace as for pa_decode."""
+    lib = load_library()
+    B, Hq, D = q.shape
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    _need(q.is_contiguous() and out.is_contiguous(), "q and out must be contiguous")
+    _e4m3_pools(k_cache, v_cache)
+    NB, bs, Hkv, D2 = k_cache.shape
+    _need(D2 == D, "head_dim of pools and q differ")
+    _scales(k_scale, v_scale, Hkv, q.device)
+    _int32_device(block_tables, "block_tables", q.device)
+    _int32_device(context_lens, "context_lens", q.device)
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == B, "block_tables must be [B][max_blocks]")
+    _need(context_lens.numel() == B, "context_lens must have B entries")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _need(workspace.device == q.device and workspace.is_contiguous(), "bad workspace")
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    st = lib.pa_decode_fp8(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                           _ptr(v_scale), _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv, D, bs,
+                           NB, block_tables.shape[1], int(max_context_len), float(scale),
+                           int(partition_size), ws_ptr, ws_bytes, _dtype_code(q), _stream(stream))
+    _check("pa_decode_fp8", st)
 
 
 def pa_prefill_chunk(out, q, k_cache, v_cache, block_tables, query_start_loc, context_lens,

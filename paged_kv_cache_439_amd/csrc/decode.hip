@@ -40,6 +40,10 @@
 #ifndef DECODE_U
 #define DECODE_U 8
 #endif
+// Loads in flight per lane for E4M3 pools (16 elements per load).
+#ifndef DECODE_U_E4M3
+#define DECODE_U_E4M3 4
+#endif
 // Resident waves per SIMD the balanced split plans for.
 #ifndef DECODE_BAL_WAVES_PER_SIMD
 #define DECODE_BAL_WAVES_PER_SIMD 2
@@ -73,6 +77,9 @@ struct DecodeParams {
   int64_t new_k_stride, new_v_stride;  // bytes
   const int32_t* slot_mapping;
   int64_t num_slots;  // num_blocks * block_size
+  // E4M3 pools: per-KV-head scales (element = value(code) * scale[head]), else null.
+  const float* k_scale;
+  const float* v_scale;
 };
 
 // Fused store: does this call write sequence seq's newest row into the pool
@@ -120,6 +127,22 @@ template <>
 struct ElemTraits<uint16_t> {  // bf16 storage
   static constexpr int E = 2;
 };
+template <>
+struct ElemTraits<uint8_t> {  // E4M3 storage (KV pools only)
+  static constexpr int E = 1;
+};
+
+// E4M3 -> two bf16 (exact: every E4M3 value is a bf16 value) from byte
+// pair HI (0: bytes 0-1, 1: bytes 2-3) of w.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+// E4M3 -> two fp32 from byte pair HI of w.
+template <bool HI>
+__device__ __forceinline__ f32x2 e4m3x2_to_f32x2(uint32_t w) {
+  return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+}
 
 // Partial dot product of this lane's 16-byte slice of q (pre-loaded) and k.
 template <typename T>
@@ -142,7 +165,15 @@ __device__ __forceinline__ float slice_dot<float>(const uint4& qv, const uint4& 
 // Widen a 16-byte slice to EPL floats.
 template <typename T, int EPL>
 __device__ __forceinline__ void widen_slice(const uint4& v, float (&f)[EPL]) {
-  if constexpr (sizeof(T) == 2) {
+  if constexpr (sizeof(T) == 1) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f32x2 a = e4m3x2_to_f32x2<false>(w[i]);
+      const f32x2 b = e4m3x2_to_f32x2<true>(w[i]);
+      f[4 * i] = a.x; f[4 * i + 1] = a.y; f[4 * i + 2] = b.x; f[4 * i + 3] = b.y;
+    }
+  } else if constexpr (sizeof(T) == 2) {
     f[0] = bf16lo(v.x); f[1] = bf16hi(v.x);
     f[2] = bf16lo(v.y); f[3] = bf16hi(v.y);
     f[4] = bf16lo(v.z); f[5] = bf16hi(v.z);
@@ -153,18 +184,25 @@ __device__ __forceinline__ void widen_slice(const uint4& v, float (&f)[EPL]) {
   }
 }
 
-// Store EPL floats as one 16-byte slice of the output type.
+// Store EPL floats as EPL consecutive elements of the output type T, in
+// 16-byte pieces.
 template <typename T, int EPL>
 __device__ __forceinline__ void store_slice(void* dst, const float (&f)[EPL]) {
-  uint4 w;
-  if constexpr (sizeof(T) == 2) {
-    w.x = pack_bf16x2(f[0], f[1]); w.y = pack_bf16x2(f[2], f[3]);
-    w.z = pack_bf16x2(f[4], f[5]); w.w = pack_bf16x2(f[6], f[7]);
-  } else {
-    w.x = __builtin_bit_cast(uint32_t, f[0]); w.y = __builtin_bit_cast(uint32_t, f[1]);
-    w.z = __builtin_bit_cast(uint32_t, f[2]); w.w = __builtin_bit_cast(uint32_t, f[3]);
+  constexpr int PER = 16 / (int)sizeof(T);  // elements per 16-byte piece
+  static_assert(EPL % PER == 0, "slice must be whole 16-byte pieces");
+#pragma unroll
+  for (int c = 0; c < EPL / PER; ++c) {
+    const float* g = f + c * PER;
+    uint4 w;
+    if constexpr (sizeof(T) == 2) {
+      w.x = pack_bf16x2(g[0], g[1]); w.y = pack_bf16x2(g[2], g[3]);
+      w.z = pack_bf16x2(g[4], g[5]); w.w = pack_bf16x2(g[6], g[7]);
+    } else {
+      w.x = __builtin_bit_cast(uint32_t, g[0]); w.y = __builtin_bit_cast(uint32_t, g[1]);
+      w.z = __builtin_bit_cast(uint32_t, g[2]); w.w = __builtin_bit_cast(uint32_t, g[3]);
+    }
+    reinterpret_cast<uint4*>(dst)[c] = w;
   }
-  *reinterpret_cast<uint4*>(dst) = w;
 }
 
 // Merge the online states of the token-row groups that share a d-slice
@@ -206,31 +244,107 @@ struct WaveState {
   }
 };
 
-// Load this lane's 16-byte q slices of heads h0 .. h0+GT-1 of sequence seq.
-template <typename T, int D, int GT>
-__device__ __forceinline__ void load_q(const DecodeParams& p, int seq, int h0, int dc, uint4 (&qv)[GT]) {
+// This lane's slice of one query head, in the form that its partial dot
+// product with a 16-byte K slice of storage type KT needs.
+template <typename T, typename KT>
+struct QSlice {  // K in the query's own type: the raw 16 bytes
+  static_assert(sizeof(T) == sizeof(KT), "K must be stored in the query type or as E4M3");
+  uint4 v;
+  __device__ __forceinline__ void load(const char* src) { v = *reinterpret_cast<const uint4*>(src); }
+  __device__ __forceinline__ float dot(const uint4& k) const { return slice_dot<T>(v, k); }
+};
+template <>
+struct QSlice<uint16_t, uint8_t> {  // bf16 query, E4M3 keys: 16 elements, bf16 dot2
+  uint4 v[2];
+  __device__ __forceinline__ void load(const char* src) {
+    v[0] = reinterpret_cast<const uint4*>(src)[0];
+    v[1] = reinterpret_cast<const uint4*>(src)[1];
+  }
+  __device__ __forceinline__ float dot(const uint4& k) const {
+    float s = dot2_bf16(v[0].x, e4m3x2_to_bf16x2<false>(k.x), 0.0f);
+    s = dot2_bf16(v[0].y, e4m3x2_to_bf16x2<true>(k.x), s);
+    s = dot2_bf16(v[0].z, e4m3x2_to_bf16x2<false>(k.y), s);
+    s = dot2_bf16(v[0].w, e4m3x2_to_bf16x2<true>(k.y), s);
+    s = dot2_bf16(v[1].x, e4m3x2_to_bf16x2<false>(k.z), s);
+    s = dot2_bf16(v[1].y, e4m3x2_to_bf16x2<true>(k.z), s);
+    s = dot2_bf16(v[1].z, e4m3x2_to_bf16x2<false>(k.w), s);
+    return dot2_bf16(v[1].w, e4m3x2_to_bf16x2<true>(k.w), s);
+  }
+};
+template <>
+struct QSlice<float, uint8_t> {  // fp32 query, E4M3 keys: 16 elements, fp32 FMA
+  float f[16];
+  __device__ __forceinline__ void load(const char* src) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float4 x = reinterpret_cast<const float4*>(src)[c];
+      f[4 * c] = x.x; f[4 * c + 1] = x.y; f[4 * c + 2] = x.z; f[4 * c + 3] = x.w;
+    }
+  }
+  __device__ __forceinline__ float dot(const uint4& k) const {
+    float kf[16];
+    widen_slice<uint8_t, 16>(k, kf);
+    float s = f[0] * kf[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) s = fmaf(f[e], kf[e], s);
+    return s;
+  }
+};
+
+// Load this lane's q slices (EPL elements from element dc*EPL) of heads
+// h0 .. h0+GT-1 of sequence seq.
+template <typename T, typename KT, int D, int GT>
+__device__ __forceinline__ void load_q(const DecodeParams& p, int seq, int h0, int dc,
+                                       QSlice<T, KT> (&qv)[GT]) {
   constexpr int E = ElemTraits<T>::E;
+  constexpr int EPL = 16 / ElemTraits<KT>::E;
   const char* qb = static_cast<const char*>(p.q);
 #pragma unroll
   for (int h = 0; h < GT; ++h)
-    qv[h] = *reinterpret_cast<const uint4*>(qb + (((int64_t)seq * p.num_heads + h0 + h) * D) * E + dc * 16);
+    qv[h].load(qb + (((int64_t)seq * p.num_heads + h0 + h) * D + dc * EPL) * E);
+}
+
+// Logit multiplier of a KV head, log2 units: scale * log2(e), times the
+// head's K scale for an E4M3 pool.
+template <typename KT>
+__device__ __forceinline__ float logit_scale(const DecodeParams& p, int kvh) {
+  if constexpr (sizeof(KT) == 1) return p.scale_log2 * p.k_scale[kvh];
+  return p.scale_log2;
+}
+
+// E4M3 pool: the weighted sums were taken over V codes' values; multiply by
+// the head's V scale (every token of a KV head shares it).
+template <typename KT, int GT, int EPL>
+__device__ __forceinline__ void apply_v_scale(const DecodeParams& p, int kvh, float (&acc)[GT][EPL]) {
+  if constexpr (sizeof(KT) == 1) {
+    const float vs = p.v_scale[kvh];
+#pragma unroll
+    for (int h = 0; h < GT; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[h][e] *= vs;
+  }
 }
 
 // Stream tokens [tok_begin, tok_end) of sequence seq (KV head kvh) through
 // the online softmax of st. UNIFORM_BLOCK: every chunk lies inside one block
 // (block_size >= CT and tok_begin a multiple of CT), so one table lookup per
 // chunk serves all lanes; otherwise each lane looks up its own token's block.
-template <typename T, int D, int GT, int U, bool UNIFORM_BLOCK>
+// KT is the pools' storage type: T itself, or uint8_t for E4M3 codes, whose
+// logits are multiplied by sm (the logit scale times the head's K scale)
+// and whose weighted value sums still lack the head's V scale.
+template <typename T, typename KT, int D, int GT, int U, bool UNIFORM_BLOCK>
 __device__ __forceinline__ void attend_range(const DecodeParams& p, int seq, int kvh, int lane,
-                                             int tok_begin, int tok_end, const uint4 (&qv)[GT],
-                                             WaveState<GT, 16 / ElemTraits<T>::E>& st) {
+                                             int tok_begin, int tok_end,
+                                             const QSlice<T, KT> (&qv)[GT], float sm,
+                                             WaveState<GT, 16 / ElemTraits<KT>::E>& st) {
   // With a fused store, the newest token (position L-1, L = the context
   // length) comes from the new row itself, not from the pool slot this same
   // launch is writing.
-  const bool new_row = tok_end > tok_begin && stores_new_row(p, seq) &&
+  constexpr bool FUSABLE = sizeof(KT) == sizeof(T);
+  const bool new_row = FUSABLE && tok_end > tok_begin && stores_new_row(p, seq) &&
                        tok_end == min(p.context_lens[seq], p.max_context_len);
   if (new_row) --tok_end;
-  constexpr int E = ElemTraits<T>::E;
+  constexpr int E = ElemTraits<KT>::E;
   constexpr int EPL = 16 / E;     // elements per 16-byte lane slice
   constexpr int LPT = D / EPL;    // lanes per token row of one head
   constexpr int TPW = 64 / LPT;   // token rows per wave-wide load
@@ -294,14 +408,14 @@ __device__ __forceinline__ void attend_range(const DecodeParams& p, int seq, int
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int h = 0; h < GT; ++h) s[u][h] = group_sum<LPT>(slice_dot<T>(qv[h], kr[u]));
+      for (int h = 0; h < GT; ++h) s[u][h] = group_sum<LPT>(qv[h].dot(kr[u]));
 
 #pragma unroll
     for (int h = 0; h < GT; ++h) {
       float cm = NEG_BIG;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        s[u][h] = valid[u] ? s[u][h] * p.scale_log2 : -INFINITY;
+        s[u][h] = valid[u] ? s[u][h] * sm : -INFINITY;
         cm = fmaxf(cm, s[u][h]);
       }
       const float mn = fmaxf(st.m[h], cm);
@@ -320,7 +434,7 @@ __device__ __forceinline__ void attend_range(const DecodeParams& p, int seq, int
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float vf[EPL];
-      widen_slice<T, EPL>(vr[u], vf);
+      widen_slice<KT, EPL>(vr[u], vf);
 #pragma unroll
       for (int h = 0; h < GT; ++h)
 #pragma unroll
@@ -328,17 +442,18 @@ __device__ __forceinline__ void attend_range(const DecodeParams& p, int seq, int
     }
   }
 
-  if (new_row) {
+  if constexpr (FUSABLE) {
+    if (new_row) {
     // one more token, held by token-row group 0 (every lane loads the same
     // row so that the butterfly over the row's lanes stays uniform)
     const int64_t off = (int64_t)kvh * D * E + dc * 16;
     const uint4 kr = *reinterpret_cast<const uint4*>(p.new_k + seq * p.new_k_stride + off);
     const uint4 vr = *reinterpret_cast<const uint4*>(p.new_v + seq * p.new_v_stride + off);
     float vf[EPL];
-    widen_slice<T, EPL>(vr, vf);
+    widen_slice<KT, EPL>(vr, vf);
 #pragma unroll
     for (int h = 0; h < GT; ++h) {
-      float sc = group_sum<LPT>(slice_dot<T>(qv[h], kr)) * p.scale_log2;
+      float sc = group_sum<LPT>(qv[h].dot(kr)) * sm;
       sc = (tr == 0) ? sc : -INFINITY;
       const float mn = fmaxf(st.m[h], sc);
       const float alpha = fast_exp2(st.m[h] - mn);
@@ -348,10 +463,12 @@ __device__ __forceinline__ void attend_range(const DecodeParams& p, int seq, int
 #pragma unroll
       for (int e = 0; e < EPL; ++e) st.acc[h][e] = fmaf(pr, vf[e], st.acc[h][e] * alpha);
     }
+    }
   }
 }
 
-// Write the (merged) state of heads h0.. of sequence seq as the final output.
+// Write the (merged) state of heads h0.. of sequence seq as the final
+// output: this lane's EPL elements from element dc*EPL.
 template <typename T, int D, int GT, int EPL>
 __device__ __forceinline__ void store_output(const DecodeParams& p, int seq, int h0, int dc,
                                              const WaveState<GT, EPL>& st) {
@@ -367,11 +484,11 @@ __device__ __forceinline__ void store_output(const DecodeParams& p, int seq, int
   }
 }
 
-// Zeros for heads h0.. of sequence seq (the defined output of an empty context).
-template <typename T, int D, int GT>
+// Zeros for heads h0.. of sequence seq (the defined output of an empty
+// context): this lane's EPL elements from element dc*EPL.
+template <typename T, int D, int GT, int EPL>
 __device__ __forceinline__ void store_zeros(const DecodeParams& p, int seq, int h0, int dc) {
   constexpr int E = ElemTraits<T>::E;
-  constexpr int EPL = 16 / E;
   char* const out_base = static_cast<char*>(p.out);
   float z[EPL];
 #pragma unroll
@@ -382,25 +499,27 @@ __device__ __forceinline__ void store_zeros(const DecodeParams& p, int seq, int 
 }
 
 // Workgroups per CU the decode kernels are compiled for: 3 (12 waves) keeps
-// enough loads in flight; eight heads per wave need the registers of 2.
-template <int GT>
-constexpr int decode_min_wgs() { return GT >= 8 ? 2 : 3; }
+// enough loads in flight; four heads of fp32 queries over E4M3 keys (16
+// query elements per lane and head) need the registers of 2.
+template <typename T, typename KT, int GT>
+constexpr int decode_min_wgs() { return (GT >= 4 && sizeof(T) == 4 && sizeof(KT) == 1) ? 2 : 3; }
 
 // One wave = (sequence, KV head, group of GT query heads, partition).
-template <typename T, int D, int GT, int U, bool UNIFORM_BLOCK>
-__global__ __launch_bounds__(256, decode_min_wgs<GT>()) void paged_decode_kernel(DecodeParams p) {
-  constexpr int E = ElemTraits<T>::E;
-  constexpr int EPL = 16 / E;     // elements per 16-byte lane slice
-  constexpr int LPT = D / EPL;    // lanes per token row of one head
+template <typename T, typename KT, int D, int GT, int U, bool UNIFORM_BLOCK>
+__global__ __launch_bounds__(256, (decode_min_wgs<T, KT, GT>())) void paged_decode_kernel(DecodeParams p) {
+  constexpr int EPL = 16 / ElemTraits<KT>::E;  // elements per 16-byte lane slice
+  constexpr int LPT = D / EPL;                 // lanes per token row of one head
   static_assert(LPT >= 1 && LPT <= 32 && (64 % LPT) == 0, "unsupported head_dim");
 
   const int lane = threadIdx.x & 63;
   const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int seq = blockIdx.z;
   const int part = blockIdx.y;
-  if (p.new_k != nullptr && blockIdx.x == 0 && part == 0) {  // fused store of seq's row
-    const int64_t cpr = p.row_bytes / 16;
-    store_new_rows(p, (int64_t)seq * cpr + threadIdx.x, 256, (int64_t)(seq + 1) * cpr);
+  if constexpr (sizeof(KT) == sizeof(T)) {
+    if (p.new_k != nullptr && blockIdx.x == 0 && part == 0) {  // fused store of seq's row
+      const int64_t cpr = p.row_bytes / 16;
+      store_new_rows(p, (int64_t)seq * cpr + threadIdx.x, 256, (int64_t)(seq + 1) * cpr);
+    }
   }
   if (unit >= p.units) return;
   const int L = min(p.context_lens[seq], p.max_context_len);
@@ -413,18 +532,20 @@ __global__ __launch_bounds__(256, decode_min_wgs<GT>()) void paged_decode_kernel
   const int tr = lane / LPT;
 
   if (nparts == 0) {  // empty context: defined output of zeros
-    if (part == 0 && tr == 0) store_zeros<T, D, GT>(p, seq, h0, dc);
+    if (part == 0 && tr == 0) store_zeros<T, D, GT, EPL>(p, seq, h0, dc);
     return;
   }
   if (part >= nparts) return;
 
   const int tok_begin = part * P;
   const int tok_end = min(L, tok_begin + P);
-  uint4 qv[GT];
-  load_q<T, D, GT>(p, seq, h0, dc, qv);
+  QSlice<T, KT> qv[GT];
+  load_q<T, KT, D, GT>(p, seq, h0, dc, qv);
   WaveState<GT, EPL> st;
   st.reset();
-  attend_range<T, D, GT, U, UNIFORM_BLOCK>(p, seq, kvh, lane, tok_begin, tok_end, qv, st);
+  attend_range<T, KT, D, GT, U, UNIFORM_BLOCK>(p, seq, kvh, lane, tok_begin, tok_end, qv,
+                                               logit_scale<KT>(p, kvh), st);
+  apply_v_scale<KT, GT, EPL>(p, kvh, st.acc);
   merge_row_groups<LPT, GT, EPL>(st.m, st.l, st.acc);
 
   if (nparts == 1) {
@@ -570,16 +691,17 @@ __device__ __forceinline__ void chunk_prefix(const DecodeParams& p, int32_t* pfx
   __syncthreads();
 }
 
-template <typename T, int D, int GT, int U, bool UNIFORM_BLOCK>
+template <typename T, typename KT, int D, int GT, int U, bool UNIFORM_BLOCK>
 __global__ __launch_bounds__(256, 2) void paged_decode_balanced_kernel(DecodeParams p) {
-  constexpr int E = ElemTraits<T>::E;
-  constexpr int EPL = 16 / E;
+  constexpr int EPL = 16 / ElemTraits<KT>::E;
   constexpr int LPT = D / EPL;
   constexpr int TPW = 64 / LPT;
   constexpr int CT = U * TPW;
   __shared__ int32_t pfx[BAL_MAX_SEQS + 1];
-  if (p.new_k != nullptr)  // fused store: every thread of the grid copies a share of the rows
-    store_new_rows(p, (int64_t)blockIdx.x * 256 + threadIdx.x, (int64_t)gridDim.x * 256, INT64_MAX);
+  if constexpr (sizeof(KT) == sizeof(T)) {
+    if (p.new_k != nullptr)  // fused store: every thread of the grid copies a share of the rows
+      store_new_rows(p, (int64_t)blockIdx.x * 256 + threadIdx.x, (int64_t)gridDim.x * 256, INT64_MAX);
+  }
   chunk_prefix<CT>(p, pfx);
   const int B = p.num_seqs;
   if (blockIdx.x == 0)
@@ -598,6 +720,7 @@ __global__ __launch_bounds__(256, 2) void paged_decode_balanced_kernel(DecodePar
   const int h0 = kvh * p.group + (unit - kvh * p.n_sub) * GT;
   const int dc = lane % LPT;
   const int tr = lane / LPT;
+  const float sm = logit_scale<KT>(p, kvh);
 
   // Pieces are taken from the end of the range backwards. The last piece
   // begins at a context's first token (unless the range lies inside one
@@ -616,11 +739,13 @@ __global__ __launch_bounds__(256, 2) void paged_decode_balanced_kernel(DecodePar
     const int cb = pfx[i], ce = pfx[i + 1];
     const int ps = max(c0, cb), pe = min(c1, ce);
     const int L = min(p.context_lens[i], p.max_context_len);
-    uint4 qv[GT];
-    load_q<T, D, GT>(p, i, h0, dc, qv);
+    QSlice<T, KT> qv[GT];
+    load_q<T, KT, D, GT>(p, i, h0, dc, qv);
     WaveState<GT, EPL> st;
     st.reset();
-    attend_range<T, D, GT, U, UNIFORM_BLOCK>(p, i, kvh, lane, (ps - cb) * CT, min((pe - cb) * CT, L), qv, st);
+    attend_range<T, KT, D, GT, U, UNIFORM_BLOCK>(p, i, kvh, lane, (ps - cb) * CT,
+                                                 min((pe - cb) * CT, L), qv, sm, st);
+    apply_v_scale<KT, GT, EPL>(p, kvh, st.acc);
     merge_row_groups<LPT, GT, EPL>(st.m, st.l, st.acc);
     if (tr == 0) {
       if (ps == cb && pe == ce) {
@@ -666,7 +791,7 @@ __global__ __launch_bounds__(256) void paged_decode_balanced_merge_kernel(Decode
   const int tr = lane / LPT;
   const int L = min(p.context_lens[seq], p.max_context_len);
   if (L <= 0) {
-    if (tr == 0) store_zeros<T, D, GT>(p, seq, h0, dc);
+    if (tr == 0) store_zeros<T, D, GT, EPL>(p, seq, h0, dc);
     return;
   }
   const int cb = p.ws_pfx[seq], ce = p.ws_pfx[seq + 1], C = p.ws_pfx[p.num_seqs];
@@ -763,39 +888,49 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
   return pl;
 }
 
-template <typename T, int D, int GT, int U>
+template <typename T, typename KT, int D, int GT, int U>
 static void launch_u(const DecodeParams& prm, const DecodePlan& pl, dim3 grid, hipStream_t stream) {
-  constexpr int TPW = 64 / (D * (int)sizeof(T) / 16);
+  constexpr int TPW = 64 / (D * (int)sizeof(KT) / 16);
   constexpr int CT = U * TPW;
   const bool big_blocks = (1 << prm.bs_log2) >= CT;
   if (pl.balanced) {
     const int64_t waves = (int64_t)pl.workers * pl.units;
     const dim3 bgrid((unsigned)((waves + 3) / 4));
     if (big_blocks)
-      hipLaunchKernelGGL((paged_decode_balanced_kernel<T, D, GT, U, true>), bgrid, dim3(256), 0, stream, prm);
+      hipLaunchKernelGGL((paged_decode_balanced_kernel<T, KT, D, GT, U, true>), bgrid, dim3(256), 0,
+                         stream, prm);
     else
-      hipLaunchKernelGGL((paged_decode_balanced_kernel<T, D, GT, U, false>), bgrid, dim3(256), 0, stream, prm);
+      hipLaunchKernelGGL((paged_decode_balanced_kernel<T, KT, D, GT, U, false>), bgrid, dim3(256), 0,
+                         stream, prm);
     hipLaunchKernelGGL((paged_decode_balanced_merge_kernel<T, D, GT>), dim3(grid.z, grid.x), dim3(256), 0,
                        stream, prm);
     return;
   }
   const bool uniform = big_blocks && (prm.max_parts == 1 || prm.partition % CT == 0);
   if (uniform)
-    hipLaunchKernelGGL((paged_decode_kernel<T, D, GT, U, true>), grid, dim3(256), 0, stream, prm);
+    hipLaunchKernelGGL((paged_decode_kernel<T, KT, D, GT, U, true>), grid, dim3(256), 0, stream, prm);
   else
-    hipLaunchKernelGGL((paged_decode_kernel<T, D, GT, U, false>), grid, dim3(256), 0, stream, prm);
+    hipLaunchKernelGGL((paged_decode_kernel<T, KT, D, GT, U, false>), grid, dim3(256), 0, stream, prm);
   if (pl.max_parts > 1)
     hipLaunchKernelGGL((paged_decode_merge_kernel<T, D, GT>), dim3(grid.z, grid.x), dim3(256), 0,
                        stream, prm);
 }
 
-template <typename T, int D>
+template <typename T, typename KT, int D>
 static void launch_gt(const DecodeParams& prm, const DecodePlan& pl, dim3 grid, hipStream_t stream) {
+  constexpr int U = sizeof(KT) == 1 ? DECODE_U_E4M3 : DECODE_U;
   switch (pl.heads_per_unit) {
-    case 1: launch_u<T, D, 1, DECODE_U>(prm, pl, grid, stream); break;
-    case 2: launch_u<T, D, 2, DECODE_U>(prm, pl, grid, stream); break;
-    default: launch_u<T, D, 4, DECODE_U>(prm, pl, grid, stream); break;
+    case 1: launch_u<T, KT, D, 1, U>(prm, pl, grid, stream); break;
+    case 2: launch_u<T, KT, D, 2, U>(prm, pl, grid, stream); break;
+    default: launch_u<T, KT, D, 4, U>(prm, pl, grid, stream); break;
   }
+}
+
+template <typename T, typename KT>
+static void launch_d(const DecodeParams& prm, const DecodePlan& pl, int head_dim, dim3 grid,
+                     hipStream_t stream) {
+  if (head_dim == 64) launch_gt<T, KT, 64>(prm, pl, grid, stream);
+  else launch_gt<T, KT, 128>(prm, pl, grid, stream);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t stream) {
@@ -831,7 +966,9 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   prm.partition = pl.partition;
   prm.max_parts = pl.max_parts;
   prm.scale_log2 = a.scale * 1.4426950408889634f;
-  prm.row_bytes = a.num_kv_heads * a.head_dim * (a.bf16 ? 2 : 4);
+  prm.row_bytes = a.num_kv_heads * a.head_dim * (a.kv_e4m3 ? 1 : a.bf16 ? 2 : 4);
+  prm.k_scale = a.k_scale;
+  prm.v_scale = a.v_scale;
   prm.block_bytes = (int64_t)a.block_size * prm.row_bytes;
   if (a.key != nullptr) {
     prm.new_k = static_cast<const char*>(a.key);
@@ -844,12 +981,12 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
   // x: head group (fastest, so one token's rows of all heads are read by
   // neighbouring workgroups), y: partition, z: sequence.
   const dim3 grid((unsigned)((pl.units + 3) / 4), (unsigned)pl.max_parts, (unsigned)a.num_seqs);
-  if (a.bf16) {
-    if (a.head_dim == 64) launch_gt<uint16_t, 64>(prm, pl, grid, stream);
-    else launch_gt<uint16_t, 128>(prm, pl, grid, stream);
+  if (a.kv_e4m3) {
+    if (a.bf16) launch_d<uint16_t, uint8_t>(prm, pl, a.head_dim, grid, stream);
+    else launch_d<float, uint8_t>(prm, pl, a.head_dim, grid, stream);
   } else {
-    if (a.head_dim == 64) launch_gt<float, 64>(prm, pl, grid, stream);
-    else launch_gt<float, 128>(prm, pl, grid, stream);
+    if (a.bf16) launch_d<uint16_t, uint16_t>(prm, pl, a.head_dim, grid, stream);
+    else launch_d<float, float>(prm, pl, a.head_dim, grid, stream);
   }
   return hipGetLastError();
 }

@@ -154,12 +154,19 @@ struct Fusion {
   const int32_t* slot_mapping;
 };
 
+// E4M3 pools (pa_decode_fp8): per-KV-head scales.
+struct E4M3Scales {
+  const float* k_scale;
+  const float* v_scale;
+};
+
 pa_status decode_impl(const char* fn, void* out, const void* q, const void* k_cache,
                       const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
                       int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                       int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                       int32_t max_context_len, float scale, int32_t partition_size, void* workspace,
-                      size_t workspace_bytes, pa_dtype dtype, void* stream, const Fusion* fused) {
+                      size_t workspace_bytes, pa_dtype dtype, void* stream, const Fusion* fused,
+                      const E4M3Scales* e4m3) {
   if (pa_status st = check_dtype(dtype)) return st;
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_seqs=%d is negative", fn, num_seqs);
   if (num_seqs == 0) return ok();
@@ -197,6 +204,13 @@ pa_status decode_impl(const char* fn, void* out, const void* q, const void* k_ca
       return fail(PA_ERR_INVALID_ARG, "%s: num_blocks*block_size=%lld exceeds int32 slots", fn,
                   (long long)num_blocks * block_size);
   }
+  if (e4m3) {
+    if (fused) return fail(PA_ERR_UNSUPPORTED, "%s: no fused store for E4M3 pools", fn);
+    if (!e4m3->k_scale || !e4m3->v_scale)
+      return fail(PA_ERR_INVALID_ARG, "%s: null k_scale or v_scale", fn);
+    if (!aligned(e4m3->k_scale, 4) || !aligned(e4m3->v_scale, 4))
+      return fail(PA_ERR_UNSUPPORTED, "%s: k_scale/v_scale must be 4-byte aligned", fn);
+  }
   const pa::DecodePlan plan = pa::plan_decode(num_seqs, num_heads, num_kv_heads, head_dim,
                                               max_context_len, partition_size);
   if ((plan.units + 3) / 4 > 65535) return fail(PA_ERR_UNSUPPORTED, "%s: too many heads", fn);
@@ -213,7 +227,8 @@ pa_status decode_impl(const char* fn, void* out, const void* q, const void* k_ca
   pa::DecodeArgs a{out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
                    num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                    max_context_len, scale, partition_size, workspace, dtype == PA_BF16,
-                   nullptr, nullptr, 0, 0, nullptr};
+                   nullptr, nullptr, 0, 0, nullptr, e4m3 != nullptr,
+                   e4m3 ? e4m3->k_scale : nullptr, e4m3 ? e4m3->v_scale : nullptr};
   if (fused) {
     a.key = fused->key;
     a.value = fused->value;
@@ -240,7 +255,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
     return decode_impl("pa_decode", out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
                        num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                        max_context_len, scale, partition_size, workspace, workspace_bytes, dtype,
-                       stream, nullptr);
+                       stream, nullptr, nullptr);
   } catch (...) {
     return fail(PA_ERR_HIP, "unexpected C++ exception");
   }
@@ -259,7 +274,71 @@ pa_status pa_store_decode(void* out, const void* q, const void* key, const void*
     return decode_impl("pa_store_decode", out, q, k_cache, v_cache, block_tables, context_lens,
                        num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                        max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
-                       workspace_bytes, dtype, stream, &f);
+                       workspace_bytes, dtype, stream, &f, nullptr);
+  } catch (...) {
+    return fail(PA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+pa_status pa_decode_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                        const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                        const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                        int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                        float scale, int32_t partition_size, void* workspace,
+                        size_t workspace_bytes, pa_dtype dtype, void* stream) {
+  try {
+    const E4M3Scales sc{k_scale, v_scale};
+    return decode_impl("pa_decode_fp8", out, q, k_cache, v_cache, block_tables, context_lens,
+                       num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                       max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
+                       workspace_bytes, dtype, stream, nullptr, &sc);
+  } catch (...) {
+    return fail(PA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+pa_status pa_store_kvcache_fp8(const void* key, const void* value, int64_t key_tok_stride,
+                               int64_t value_tok_stride, void* k_cache, void* v_cache,
+                               const int32_t* slot_mapping, const float* k_scale,
+                               const float* v_scale, int32_t num_tokens, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                               pa_dtype dtype, void* stream) {
+  try {
+    if (pa_status st = check_dtype(dtype)) return st;
+    if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens=%d is negative", num_tokens);
+    if (num_tokens == 0) return ok();
+    if (!key || !value || !k_cache || !v_cache || !slot_mapping || !k_scale || !v_scale)
+      return fail(PA_ERR_INVALID_ARG, "null pointer argument");
+    if (num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+      return fail(PA_ERR_INVALID_ARG, "num_kv_heads, head_dim, block_size, num_blocks must be positive");
+    if (head_dim % 16 != 0)
+      return fail(PA_ERR_UNSUPPORTED, "head_dim=%d must be a multiple of 16", head_dim);
+    const int e = elem_size(dtype);
+    const int64_t row_elems = (int64_t)num_kv_heads * head_dim;
+    if (row_elems > (1 << 20))
+      return fail(PA_ERR_UNSUPPORTED, "row of %lld elements (at most 1 Mi)", (long long)row_elems);
+    if (key_tok_stride < row_elems || value_tok_stride < row_elems)
+      return fail(PA_ERR_INVALID_ARG, "token strides (%lld, %lld) below a row of %lld elements",
+                  (long long)key_tok_stride, (long long)value_tok_stride, (long long)row_elems);
+    if ((key_tok_stride * e) % 16 || (value_tok_stride * e) % 16)
+      return fail(PA_ERR_UNSUPPORTED, "token strides must be multiples of 16 bytes");
+    if (!aligned(key, 16) || !aligned(value, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(slot_mapping, 4) || !aligned(k_scale, 4) || !aligned(v_scale, 4))
+      return fail(PA_ERR_UNSUPPORTED,
+                  "pointers must be 16-byte aligned (slot_mapping and scales 4-byte)");
+    const int64_t num_slots = (int64_t)num_blocks * block_size;
+    if (num_slots > INT32_MAX)
+      return fail(PA_ERR_INVALID_ARG, "num_blocks*block_size=%lld exceeds int32 slots",
+                  (long long)num_slots);
+    if ((int64_t)num_tokens * (row_elems / 16) > (int64_t)INT32_MAX)
+      return fail(PA_ERR_UNSUPPORTED, "too many tokens in one call");
+    pa::StoreE4M3Args a{key, value, key_tok_stride * e, value_tok_stride * e, k_cache, v_cache,
+                        slot_mapping, k_scale, v_scale, num_tokens, num_kv_heads, head_dim,
+                        num_slots, dtype == PA_BF16};
+    const hipError_t err = pa::launch_store_e4m3(a, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(PA_ERR_HIP, "store launch: %s", hipGetErrorString(err));
+    return ok();
   } catch (...) {
     return fail(PA_ERR_HIP, "unexpected C++ exception");
   }

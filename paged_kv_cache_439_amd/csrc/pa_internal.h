@@ -21,6 +21,21 @@ struct StoreArgs {
   int64_t num_slots;       // num_blocks * block_size
 };
 
+struct StoreE4M3Args {
+  const void* key;
+  const void* value;
+  int64_t key_stride_bytes;
+  int64_t value_stride_bytes;
+  void* k_cache;
+  void* v_cache;
+  const int32_t* slot_mapping;
+  const float* k_scale;
+  const float* v_scale;
+  int32_t num_tokens, num_kv_heads, head_dim;
+  int64_t num_slots;       // num_blocks * block_size
+  bool bf16;               // input type: bf16 (else fp32)
+};
+
 struct DecodeArgs {
   void* out;
   const void* q;
@@ -39,6 +54,10 @@ struct DecodeArgs {
   const void* value;
   int64_t key_stride_bytes, value_stride_bytes;
   const int32_t* slot_mapping;
+  // E4M3 pools (pa_decode_fp8): per-KV-head scales; kv_e4m3 false otherwise
+  bool kv_e4m3;
+  const float* k_scale;
+  const float* v_scale;
 };
 
 struct PrefillArgs {
@@ -73,6 +92,7 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
                        int32_t head_dim, int32_t max_context_len, int32_t partition_size);
 
 hipError_t launch_store(const StoreArgs& a, hipStream_t stream);
+hipError_t launch_store_e4m3(const StoreE4M3Args& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 

@@ -34,6 +34,111 @@ __global__ __launch_bounds__(256) void store_kvcache_kernel(
   *reinterpret_cast<uint4*>(v_cache + (int64_t)s * row_bytes + (int64_t)c * 16) = vv;
 }
 
+// ---------------------------------------------------------------------------
+// E4M3 store: quantise on the way into the pool
+// ---------------------------------------------------------------------------
+//
+// Element x of KV head h is stored as the E4M3 code nearest to x / scale[h]
+// (one IEEE fp32 division, ties to the even code), magnitudes saturated at
+// 448, the largest finite E4M3 value; NaN becomes the NaN code 0x7F with the
+// input's sign. One thread converts 16 consecutive elements of one head into
+// one 16-byte piece of the pool row.
+//
+// Bound: HBM bytes (read 2 rows of the input type, write 2 rows of codes).
+
+// Four fp32 values -> four E4M3 codes (byte i from y[i]).
+__device__ __forceinline__ uint32_t to_e4m3x4(const float (&x)[4], float scale) {
+  float y[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    y[i] = x[i] / scale;
+    // saturate (comparisons with NaN are false, so NaN passes through)
+    if (__builtin_fabsf(y[i]) > 448.0f) y[i] = __builtin_copysignf(448.0f, y[i]);
+  }
+  uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+  w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], (int)w, true);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (__builtin_isnan(y[i])) {
+      const uint32_t code = 0x7Fu | (__builtin_signbit(y[i]) ? 0x80u : 0u);
+      w = (w & ~(0xFFu << (8 * i))) | (code << (8 * i));
+    }
+  }
+  return w;
+}
+
+// 16 elements of T at src -> 16 codes.
+template <typename T>
+__device__ __forceinline__ uint4 quantize16(const char* src, float scale) {
+  float f[16];
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const uint4 v = reinterpret_cast<const uint4*>(src)[c];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[8 * c + 2 * i] = bf16lo(w[i]);
+        f[8 * c + 2 * i + 1] = bf16hi(w[i]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float4 v = reinterpret_cast<const float4*>(src)[c];
+      f[4 * c] = v.x; f[4 * c + 1] = v.y; f[4 * c + 2] = v.z; f[4 * c + 3] = v.w;
+    }
+  }
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float x[4] = {f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]};
+    w[i] = to_e4m3x4(x, scale);
+  }
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void store_kvcache_e4m3_kernel(
+    const char* __restrict__ key, const char* __restrict__ value, int64_t key_stride,
+    int64_t value_stride, char* __restrict__ k_cache, char* __restrict__ v_cache,
+    const int32_t* __restrict__ slot_mapping, const float* __restrict__ k_scale,
+    const float* __restrict__ v_scale, int64_t total_pieces, int32_t pieces_per_row,
+    int32_t pieces_per_head, int64_t num_slots) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= total_pieces) return;
+  const int64_t t = idx / pieces_per_row;
+  const int32_t c = (int32_t)(idx - t * pieces_per_row);
+  const int32_t s = slot_mapping[t];
+  if (s < 0 || (int64_t)s >= num_slots) return;  // padding, or outside the pool
+  const int32_t h = c / pieces_per_head;
+  const int64_t src = (int64_t)c * 16 * (int64_t)sizeof(T);
+  const uint4 kq = quantize16<T>(key + t * key_stride + src, k_scale[h]);
+  const uint4 vq = quantize16<T>(value + t * value_stride + src, v_scale[h]);
+  const int64_t dst = (int64_t)s * pieces_per_row * 16 + (int64_t)c * 16;
+  *reinterpret_cast<uint4*>(k_cache + dst) = kq;
+  *reinterpret_cast<uint4*>(v_cache + dst) = vq;
+}
+
+hipError_t launch_store_e4m3(const StoreE4M3Args& a, hipStream_t stream) {
+  const int32_t ppr = a.num_kv_heads * a.head_dim / 16;
+  const int64_t total = (int64_t)a.num_tokens * ppr;
+  const int64_t blocks = (total + 255) / 256;
+  const char* key = static_cast<const char*>(a.key);
+  const char* value = static_cast<const char*>(a.value);
+  char* kc = static_cast<char*>(a.k_cache);
+  char* vc = static_cast<char*>(a.v_cache);
+  if (a.bf16)
+    hipLaunchKernelGGL(store_kvcache_e4m3_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       key, value, a.key_stride_bytes, a.value_stride_bytes, kc, vc, a.slot_mapping,
+                       a.k_scale, a.v_scale, total, ppr, a.head_dim / 16, a.num_slots);
+  else
+    hipLaunchKernelGGL(store_kvcache_e4m3_kernel<float>, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       key, value, a.key_stride_bytes, a.value_stride_bytes, kc, vc, a.slot_mapping,
+                       a.k_scale, a.v_scale, total, ppr, a.head_dim / 16, a.num_slots);
+  return hipGetLastError();
+}
+
 hipError_t launch_store(const StoreArgs& a, hipStream_t stream) {
   const int32_t cpr = a.row_bytes / 16;
   const int64_t total = (int64_t)a.num_tokens * cpr;

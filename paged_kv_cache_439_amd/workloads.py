@@ -96,6 +96,12 @@ class Batch:
     value: torch.Tensor | None = None
     q: torch.Tensor | None = None         # [T_q][Hq][D]
     device: str = "cpu"
+    k_scale: torch.Tensor | None = None   # E4M3 pools: float32 [Hkv] per-head scales
+    v_scale: torch.Tensor | None = None
+
+    @property
+    def kv_e4m3(self) -> bool:
+        return self.k_scale is not None
 
     @property
     def max_blocks_per_seq(self) -> int:
@@ -127,7 +133,7 @@ class Batch:
         (physical block, row) that some context covers when unique (a block
         shared by several sequences counts once), else one per
         (sequence, token)."""
-        row = self.num_kv_heads * self.head_dim * elem_bytes(self.dtype) * 2
+        row = self.num_kv_heads * self.head_dim * (1 if self.kv_e4m3 else elem_bytes(self.dtype)) * 2
         if not unique:
             return int(self.context_lens.astype(np.int64).sum()) * row
         return int(covered_rows(self).sum()) * row
@@ -258,6 +264,38 @@ def _randn(shape, dtype, device, seed, chunk_rows=None):
     return out
 
 
+# E4M3 pools (spec["kv"] == "e4m3"): pool entries are drawn as values
+# N(0, 1) * E4M3_AMP, clamped to the format's +-448 and converted by torch's
+# own float8_e4m3fn cast; they are read with per-KV-head scales
+# E4M3_SCALE_BASE * u, u ~ U[0.75, 1.25) (seeded), so that the dequantised
+# pools follow about the same N(0, 1) as the bf16 workloads.
+E4M3_AMP = 112.0
+E4M3_SCALE_BASE = 1.0 / 112.0
+
+
+def _randn_e4m3(shape, device, seed, chunk_rows=None):
+    """uint8 E4M3 codes of seeded N(0, 1) * E4M3_AMP values."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    out = torch.empty(shape, dtype=torch.uint8, device=device)
+    rows = shape[0]
+    step = chunk_rows or rows or 1
+    for r0 in range(0, rows, step):
+        r1 = min(rows, r0 + step)
+        x = torch.randn((r1 - r0,) + tuple(shape[1:]), generator=g, device=device,
+                        dtype=torch.float32) * E4M3_AMP
+        out[r0:r1] = x.clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    return out
+
+
+def e4m3_scales(num_kv_heads, seed, device):
+    """Seeded per-KV-head (k_scale, v_scale) float32 tensors."""
+    rng = np.random.Generator(np.random.PCG64(int(seed)))
+    k = (E4M3_SCALE_BASE * rng.uniform(0.75, 1.25, num_kv_heads)).astype(np.float32)
+    v = (E4M3_SCALE_BASE * rng.uniform(0.75, 1.25, num_kv_heads)).astype(np.float32)
+    return torch.from_numpy(k).to(device), torch.from_numpy(v).to(device)
+
+
 def make_batch(spec, device="cpu", seed=None, poison=False):
     """Draw a full batch for ``spec`` (an entry of CONFIGS or a variant).
 
@@ -289,8 +327,15 @@ def make_batch(spec, device="cpu", seed=None, poison=False):
     base = int(seed) * 16
     row_elems = bs * Hkv * D
     chunk_rows = max(1, (1 << 26) // row_elems)    # ~64M elements per draw
-    k_cache = _randn((num_blocks, bs, Hkv, D), dtype, device, base + 1, chunk_rows)
-    v_cache = _randn((num_blocks, bs, Hkv, D), dtype, device, base + 2, chunk_rows)
+    e4m3 = spec.get("kv") == "e4m3"
+    if e4m3:
+        k_cache = _randn_e4m3((num_blocks, bs, Hkv, D), device, base + 1, chunk_rows)
+        v_cache = _randn_e4m3((num_blocks, bs, Hkv, D), device, base + 2, chunk_rows)
+        k_scale, v_scale = e4m3_scales(Hkv, base + 6, device)
+    else:
+        k_cache = _randn((num_blocks, bs, Hkv, D), dtype, device, base + 1, chunk_rows)
+        v_cache = _randn((num_blocks, bs, Hkv, D), dtype, device, base + 2, chunk_rows)
+        k_scale = v_scale = None
     key = _randn((n_new, Hkv, D), dtype, device, base + 3)
     value = _randn((n_new, Hkv, D), dtype, device, base + 4)
     q = _randn((n_q, Hq, D), dtype, device, base + 5)
@@ -299,7 +344,7 @@ def make_batch(spec, device="cpu", seed=None, poison=False):
                   scale=float(spec.get("scale", 1.0 / math.sqrt(D))), context_lens=lens, block_tables=tables,
                   slot_mapping=slots, token_ids=token_ids, query_start_loc=qsl,
                   shared_blocks=shared, k_cache=k_cache, v_cache=v_cache, key=key,
-                  value=value, q=q, device=str(device))
+                  value=value, q=q, device=str(device), k_scale=k_scale, v_scale=v_scale)
     if poison:
         poison_unused_rows(batch)
     return batch
@@ -322,8 +367,9 @@ def poison_unused_rows(batch):
         if s >= 0:
             mask[s // bs, s % bs] = False
     dead = torch.from_numpy(~mask).to(batch.k_cache.device)
-    batch.k_cache[dead] = float("nan")
-    batch.v_cache[dead] = float("nan")
+    fill = 0x7F if batch.kv_e4m3 else float("nan")   # 0x7F: the E4M3 NaN code
+    batch.k_cache[dead] = fill
+    batch.v_cache[dead] = fill
 
 
 # ---------------------------------------------------------------------------

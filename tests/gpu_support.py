@@ -182,3 +182,50 @@ def full_config_parts(cfg, split="balanced"):
     split, or the fixed one measured beside it."""
     key = "partition_size" if split == "balanced" else "fixed_partition_size"
     return wl.CONFIGS[cfg].get(key, 0)
+
+
+# ---------------------------------------------------------------------------
+# E4M3 pools
+# ---------------------------------------------------------------------------
+
+def gpu_store_fp8(batch, arrs=None):
+    arrs = arrs or device_arrays(batch)
+    pa.pa_store_kvcache_fp8(batch.key, batch.value, batch.k_cache, batch.v_cache, arrs["slots"],
+                            batch.k_scale, batch.v_scale)
+
+
+def gpu_decode_fp8(batch, partition_size, arrs=None, workspace=None):
+    arrs = arrs or device_arrays(batch)
+    dev = batch.q.device
+    if workspace is None:
+        workspace = pa.decode_workspace(batch.num_seqs, batch.num_heads, batch.num_kv_heads,
+                                        batch.head_dim, batch.max_context_len, partition_size, dev)
+    out = torch.full_like(batch.q, float("nan"))
+    pa.pa_decode_fp8(out, batch.q, batch.k_cache, batch.v_cache, batch.k_scale, batch.v_scale,
+                     arrs["tables"], arrs["lens"], batch.max_context_len, batch.scale, partition_size,
+                     workspace)
+    return out
+
+
+def scales_np(batch):
+    return batch.k_scale.cpu().numpy().astype(np.float64), batch.v_scale.cpu().numpy().astype(np.float64)
+
+
+def decode_fp8_parity(batch, partition_size, seqs=None):
+    """E4M3 store + decode on the GPU; the oracle's E4M3 store and decode on
+    host copies of the same inputs (all sequences, or the given subset)."""
+    import oracle.fp8 as of8
+    hb = wl.host_subset(batch, seqs)
+    ks, vs = scales_np(batch)
+    kp, vp = of8.store_kvcache_fp8(hb.k_cache, hb.v_cache, hb.key, hb.value, hb.slot_mapping,
+                                   batch.block_size, ks, vs, batch.dtype)
+    arrs = device_arrays(batch)
+    gpu_store_fp8(batch, arrs)
+    out = gpu_decode_fp8(batch, partition_size, arrs)
+    torch.cuda.synchronize()
+    got = as_f64(out)
+    ref = of8.decode_fp8(hb.q, kp, vp, ks, vs, hb.block_tables, hb.context_lens, batch.scale,
+                         batch.block_size, batch.dtype)
+    if seqs is not None:
+        got = got[np.asarray(seqs)]
+    return check_close(got, ref, batch.dtype, "decode e4m3")

@@ -181,3 +181,43 @@ def test_prefill_rejections(lib):
     assert _prefill(lib, mq=5000) == PA_ERR_INVALID_ARG
     assert _prefill(lib, qsl=None) == PA_ERR_INVALID_ARG
     assert _prefill(lib, D=256) == PA_ERR_UNSUPPORTED
+
+
+def _decode_fp8(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, kscale=FAKE, vscale=FAKE, bt=FAKE, cl=FAKE, B=4, Hq=8,
+             Hkv=8, D=64, bs=16, NB=64, MB=7, maxL=100, scale=0.125, P=0, ws=None, wsb=0, dtype=1)
+    a.update(kw)
+    return lib.pa_decode_fp8(a["out"], a["q"], a["k"], a["v"], a["kscale"], a["vscale"], a["bt"],
+                             a["cl"], a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"], a["MB"],
+                             a["maxL"], a["scale"], a["P"], a["ws"], a["wsb"], a["dtype"], None)
+
+
+def test_decode_fp8_rejections(lib):
+    assert _decode_fp8(lib, B=0) == PA_OK
+    assert _decode_fp8(lib, kscale=None) == PA_ERR_INVALID_ARG
+    assert _decode_fp8(lib, vscale=None) == PA_ERR_INVALID_ARG
+    assert _decode_fp8(lib, vscale=ctypes.c_void_p(0x100002)) == PA_ERR_UNSUPPORTED
+    assert _decode_fp8(lib, D=96) == PA_ERR_UNSUPPORTED            # the decode checks apply
+    assert _decode_fp8(lib, dtype=5) == PA_ERR_INVALID_ARG
+    assert _decode_fp8(lib, P=32) == PA_ERR_WORKSPACE
+    assert "pa_decode_fp8" in binding.load_library().pa_last_error().decode()
+
+
+def _store_fp8(lib, **kw):
+    a = dict(key=FAKE, value=FAKE, ks=512, vs=512, k=FAKE, v=FAKE, slots=FAKE, kscale=FAKE,
+             vscale=FAKE, T=4, Hkv=8, D=64, bs=16, NB=64, dtype=1)
+    a.update(kw)
+    return lib.pa_store_kvcache_fp8(a["key"], a["value"], a["ks"], a["vs"], a["k"], a["v"], a["slots"],
+                                    a["kscale"], a["vscale"], a["T"], a["Hkv"], a["D"], a["bs"],
+                                    a["NB"], a["dtype"], None)
+
+
+def test_store_fp8_rejections(lib):
+    assert _store_fp8(lib, T=0) == PA_OK
+    assert _store_fp8(lib, T=-1) == PA_ERR_INVALID_ARG
+    assert _store_fp8(lib, kscale=None) == PA_ERR_INVALID_ARG
+    assert _store_fp8(lib, D=40) == PA_ERR_UNSUPPORTED             # head_dim not a multiple of 16
+    assert _store_fp8(lib, ks=500) == PA_ERR_INVALID_ARG           # below one row
+    assert _store_fp8(lib, ks=516) == PA_ERR_UNSUPPORTED           # bf16 stride not 16-byte multiple
+    assert _store_fp8(lib, k=ctypes.c_void_p(0x100008)) == PA_ERR_UNSUPPORTED
+    assert _store_fp8(lib, NB=1 << 28, bs=16) == PA_ERR_INVALID_ARG
