@@ -19,8 +19,10 @@ algorithmic K+V bytes per launch over its average duration, from HIP events
 recorded on the launch stream around each timed launch. `cpu_baseline` is the
 CPU oracle on a bounded sample of the same workload, single-threaded. `extra`
 reports the other workloads (GQA decode with shared prefix, GQA decode at 512
-sequences, each with the balanced split and with its fixed-slice split, and
-chunked prefill) measured the same way.
+sequences, each with the balanced split and with its fixed-slice split, the
+three decode workloads over 8-bit E4M3 pools, chunked prefill, and a
+continuous batch of decode tokens and prefill chunks in one pa_mixed_batch
+call beside the same work as two calls) measured the same way.
 """
 
 from __future__ import annotations
@@ -55,9 +57,10 @@ def log(msg):
 class DecodeSet:
     """R resident batches of one decode workload, with device-side arrays."""
 
-    def __init__(self, cfg, rotations, device, partition=None, fused=True):
-        self.spec = wl.spec(cfg)
-        self.fused = fused
+    def __init__(self, cfg, rotations, device, partition=None, fused=True, kv=None):
+        self.spec = wl.spec(cfg) if kv is None else wl.spec(cfg, kv=kv)
+        self.e4m3 = kv == "e4m3"
+        self.fused = fused and not self.e4m3   # E4M3 pools: separate quantising store
         self.P = self.spec.get("partition_size", 0) if partition is None else partition
         self.batches = []
         for r in range(rotations):
@@ -80,11 +83,17 @@ class DecodeSet:
         kernel writes the rows while it attends), or, with fused=False, the
         two calls pa_store_kvcache and pa_decode."""
         b, a = self.batches[i % len(self.batches)]
-        if not self.fused:
+        if self.e4m3:
+            pa.pa_store_kvcache_fp8(b.key, b.value, b.k_cache, b.v_cache, a["slots"], b.k_scale,
+                                    b.v_scale)
+        elif not self.fused:
             pa.pa_store_kvcache(b.key, b.value, b.k_cache, b.v_cache, a["slots"])
         if ev is not None:
             ev[0].record()
-        if self.fused:
+        if self.e4m3:
+            pa.pa_decode_fp8(a["out"], b.q, b.k_cache, b.v_cache, b.k_scale, b.v_scale, a["tables"],
+                             a["lens"], b.max_context_len, b.scale, self.P, self.ws)
+        elif self.fused:
             pa.pa_store_decode(a["out"], b.q, b.key, b.value, b.k_cache, b.v_cache, a["slots"],
                                a["tables"], a["lens"], b.max_context_len, b.scale, self.P, self.ws)
         else:
@@ -145,6 +154,71 @@ def bench_prefill(steps, warmup, device):
     return dict(workload=sp["name"], kernel_ms=round(ms, 4), gflop=round(flops / 1e9, 2),
                 tflops=round(tflops, 1), frac_of_bf16_mfma_peak=round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
                 tokens_per_s=round(int(b.query_start_loc[-1]) / (ms * 1e-3), 1))
+
+
+def bench_mixed(steps, warmup, device):
+    """The continuous batch (decode tokens + prefill chunks): pa_mixed_batch
+    against the same work as two calls (pa_decode on the decode tokens, then
+    pa_prefill_chunk on the chunks) and against each call alone."""
+    sp = wl.spec(6)
+    b = wl.make_batch(sp, device=device)
+    Bd = b.num_decode
+    a = dict(slots=torch.from_numpy(b.slot_mapping).to(device),
+             tables=torch.from_numpy(b.block_tables).to(device),
+             qsl=torch.from_numpy(b.query_start_loc).to(device),
+             lens=torch.from_numpy(b.context_lens).to(device))
+    pa.pa_store_kvcache(b.key, b.value, b.k_cache, b.v_cache, a["slots"])
+    out = torch.empty_like(b.q)
+    ws = pa.mixed_workspace(Bd, b.num_heads, b.num_kv_heads, b.head_dim, b.max_context_len, device)
+    tab_d, len_d = a["tables"][:Bd].contiguous(), a["lens"][:Bd].contiguous()
+    tab_p, qsl_p, len_p = (a["tables"][Bd:].contiguous(), a["qsl"][Bd:].contiguous(),
+                           a["lens"][Bd:].contiguous())
+    q_d, out_d = b.q[:Bd], out[:Bd]
+
+    def mixed():
+        pa.pa_mixed_batch(out, b.q, b.k_cache, b.v_cache, a["tables"], a["qsl"], a["lens"], Bd,
+                          b.max_query_len, b.max_context_len, b.scale, ws)
+
+    def decode_only():
+        pa.pa_decode(out_d, q_d, b.k_cache, b.v_cache, tab_d, len_d, b.max_context_len, b.scale,
+                     pa.PA_PARTITION_BALANCED, ws)
+
+    def prefill_only():
+        pa.pa_prefill_chunk(out, b.q, b.k_cache, b.v_cache, tab_p, qsl_p, len_p, b.max_query_len,
+                            b.max_context_len, b.scale)
+
+    def separate():
+        decode_only()
+        prefill_only()
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for st, en in evs:
+            st.record()
+            fn()
+            en.record()
+        torch.cuda.synchronize()
+        return float(np.mean([st.elapsed_time(en) for st, en in evs]))
+
+    ms = {name: timed(fn) for name, fn in (("mixed", mixed), ("separate", separate),
+                                           ("decode_only", decode_only), ("prefill_only", prefill_only))}
+    rows = int(b.query_start_loc[-1])
+    kv_dec = int(sum(int(L) for L in b.context_lens[:Bd])) * b.num_kv_heads * b.head_dim * 2 * 2
+    flops = 0
+    for i in range(Bd, b.num_seqs):
+        n = int(b.query_start_loc[i + 1] - b.query_start_loc[i])
+        c = int(b.context_lens[i]) - n
+        flops += 4 * b.head_dim * b.num_heads * (n * c + n * (n + 1) // 2)
+    return dict(workload=sp["name"], decode_tokens=Bd, prefill_rows=rows - Bd,
+                mixed_ms=round(ms["mixed"], 4), separate_ms=round(ms["separate"], 4),
+                decode_only_ms=round(ms["decode_only"], 4), prefill_only_ms=round(ms["prefill_only"], 4),
+                speedup_vs_separate=round(ms["separate"] / ms["mixed"], 3),
+                rows_per_s=round(rows / (ms["mixed"] * 1e-3), 1),
+                decode_kv_gb=round(kv_dec / 1e9, 3), prefill_gflop=round(flops / 1e9, 2))
 
 
 def measured_traffic(workload_name, split):
@@ -330,10 +404,27 @@ def main():
                     logical_bytes_per_launch=int(np.mean(d.kv_bytes_logical)))
                 del d
                 torch.cuda.empty_cache()
+        for cfg in (2, 3, 5):
+            P = wl.CONFIGS[cfg]["partition_size"]
+            log(f"extra workload {cfg} e4m3 partition_size={P}")
+            d = DecodeSet(cfg, 2, dev, partition=P, kv="e4m3")
+            s, ms, nb, _ = time_decode(d, 30, 5)
+            bb = d.batches[0][0]
+            extra[d.spec["name"] + "_e4m3"] = dict(
+                tokens_per_s=round(bb.num_seqs * 30 / s, 1), kernel_ms=round(ms, 4),
+                kv_gbs=round(nb / (ms * 1e-3) / 1e9, 1),
+                frac_of_hbm_peak=round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                bytes_per_launch=int(nb), split=split_name(P), partition_size=P, kv_cache="e4m3",
+                step="pa_store_kvcache_fp8 + pa_decode_fp8 (kernel_ms: pa_decode_fp8)",
+                logical_bytes_per_launch=int(np.mean(d.kv_bytes_logical)))
+            del d
+            torch.cuda.empty_cache()
         log("extra block manager")
         extra["block_manager"] = bench_block_manager()
         log("extra prefill")
         extra["prefill"] = bench_prefill(20, 3, dev)
+        log("extra mixed batch")
+        extra["mixed_batch"] = bench_mixed(20, 3, dev)
         line["extra"] = extra
     if args.copy_probe:
         log(f"copy probe {args.copy_probe} bytes")

@@ -206,6 +206,40 @@ pa_status pa_prefill_chunk(void* out, const void* q,
                            pa_dtype dtype, void* stream);
 
 /*
+ * pa_mixed_batch -- one call for a continuous batch holding decode tokens
+ * and prefill chunks together (the nano-vllm page's scheduler, §3.3, forms
+ * such batches step after step).
+ *
+ * The result is pa_prefill_chunk's over the whole batch: sequence i has
+ * n_i = query_start_loc[i+1] - query_start_loc[i] query rows, row t seeing
+ * keys 0 .. context_lens[i] - n_i + t. The batch is ordered: its first
+ * num_decode_seqs sequences are decode tokens, one row each
+ * (query_start_loc[i] = i for i <= num_decode_seqs), and the prefill chunks
+ * follow (n_i >= 1). Decode rows are computed as pa_decode computes them
+ * (balanced split), prefill chunks on bf16 MFMA as pa_prefill_chunk does;
+ * the two run in one kernel launch, side by side on the CUs, plus the small
+ * merge kernel of the decode split.
+ *
+ * max_query_len: the largest n_i. workspace: at least
+ * pa_decode_workspace_size(num_decode_seqs, num_heads, num_kv_heads,
+ * head_dim, max_context_len, PA_PARTITION_BALANCED) bytes, 256-byte aligned
+ * (may be NULL when num_decode_seqs is 0). At most 2048 decode sequences.
+ * PA_BF16 only. Other arguments, shapes and errors as for pa_prefill_chunk.
+ */
+pa_status pa_mixed_batch(void* out, const void* q,
+                         const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables,
+                         const int32_t* query_start_loc,
+                         const int32_t* context_lens,
+                         int32_t num_seqs, int32_t num_decode_seqs,
+                         int32_t num_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size,
+                         int32_t num_blocks, int32_t max_blocks_per_seq,
+                         int32_t max_query_len, int32_t max_context_len,
+                         float scale, void* workspace, size_t workspace_bytes,
+                         pa_dtype dtype, void* stream);
+
+/*
  * 8-bit float (E4M3) pools.
  *
  * Quantisation of the cache is among the extensions both the nano-vllm page

@@ -57,6 +57,9 @@ _SIGNATURES = {
     "pa_decode_fp8": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                        _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                        _c_void_p, _size, ctypes.c_int, _c_void_p], ctypes.c_int),
+    "pa_mixed_batch": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                        _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                        _c_void_p, _size, ctypes.c_int, _c_void_p], ctypes.c_int),
     "pa_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "pa_last_error": ([], ctypes.c_char_p),
 }
@@ -416,3 +419,44 @@ class BlockManager:
 
     def ref_count(self, block_id):
         return int(self._lib.pa_bm_ref_count(self._h, int(block_id)))
+
+
+def mixed_workspace(num_decode_seqs, num_heads, num_kv_heads, head_dim, max_context_len, device):
+    """The workspace pa_mixed_batch needs (None when there is no decode row)."""
+    if num_decode_seqs == 0:
+        return None
+    return decode_workspace(num_decode_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
+                            PA_PARTITION_BALANCED, device)
+
+
+def pa_mixed_batch(out, q, k_cache, v_cache, block_tables, query_start_loc, context_lens,
+                   num_decode_seqs, max_query_len, max_context_len, scale, workspace=None,
+                   stream=None):
+    """A continuous batch in one call: the first num_decode_seqs sequences are
+    decode tokens (one row each), the rest prefill chunks; out and q are
+    [T][Hq][D] bf16."""
+    lib = load_library()
+    T, Hq, D = q.shape
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    _need(q.is_contiguous() and out.is_contiguous(), "q and out must be contiguous")
+    _need(k_cache.dim() == 4 and k_cache.shape == v_cache.shape, "pools must be [NB][bs][Hkv][D]")
+    _need(k_cache.is_contiguous() and v_cache.is_contiguous(), "pools must be contiguous")
+    NB, bs, Hkv, D2 = k_cache.shape
+    _need(D2 == D, "head_dim of pools and q differ")
+    _need(q.dtype == k_cache.dtype == v_cache.dtype, "dtypes differ")
+    for name, t in (("block_tables", block_tables), ("query_start_loc", query_start_loc),
+                    ("context_lens", context_lens)):
+        _int32_device(t, name, q.device)
+    B = context_lens.numel()
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == B, "block_tables must be [B][max_blocks]")
+    _need(query_start_loc.numel() == B + 1, "query_start_loc must have B+1 entries")
+    _need(0 <= num_decode_seqs <= B and num_decode_seqs <= T, "num_decode_seqs out of range")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _need(workspace.device == q.device and workspace.is_contiguous(), "bad workspace")
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    st = lib.pa_mixed_batch(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                            _ptr(query_start_loc), _ptr(context_lens), B, int(num_decode_seqs), Hq, Hkv,
+                            D, bs, NB, block_tables.shape[1], int(max_query_len), int(max_context_len),
+                            float(scale), ws_ptr, ws_bytes, _dtype_code(q), _stream(stream))
+    _check("pa_mixed_batch", st)

@@ -1,835 +1,11 @@
-// paged_decode: one query token per sequence, attending over the sequence's
-// context through its block table, with an optional split of the context
-// into partitions whose softmax states are merged in the same launch.
-//
-// What is computed (the plain reading of the nano-vllm page's §1 and §3.1 and
-// the mini-vllm page's "KVCache" item and its cached-decode benchmark):
-//   out[i][h] = softmax(scale * K_i[g] q[i][h]) V_i[g],  g = h / (Hq/Hkv),
-// over the context_lens[i] rows of sequence i; logical row j is row
-// j % block_size of physical block block_tables[i][j / block_size].
-//
-// Work decomposition (one wave64 = one unit of work):
-//   unit = (sequence, KV head, group of GT query heads, partition of P tokens)
-//   grid = (max partitions, sequences, ceil(units per (seq, partition) / 4)),
-//   256 threads = 4 independent waves, no LDS and no barriers.
-// Lane mapping: a K or V row of one head is D*e bytes = LPT lanes x 16 bytes,
-// so a wave-wide 16-byte load covers TPW = 64/LPT token rows; U loads per lane
-// give a chunk of CT = U*TPW tokens whose K and V loads are all issued before
-// any of them is used.
-//   QK:  lane (dc, tr) forms partial dot products over its 16-byte slice
-//        (v_dot2_f32_bf16 for bf16), then a DPP butterfly over the LPT lanes
-//        of the row completes them.
-//   softmax: each token-row group tr keeps its own online state (running max
-//        m, sum l, weighted value sum acc) per head, in log2 units, so the
-//        main loop needs no cross-row communication; the TPW states are
-//        merged once at the end with the exact max-rescaling merge.
-//   PV:  acc[h][slice] += p * V-slice, all in registers.
-// Split: each partition writes (m, l, acc) in fp32 to the workspace and a
-//   second, small kernel (paged_decode_merge_kernel) combines them with the
-//   exact max-rescaling merge. The kernel boundary makes the states visible
-//   across the chip's separate L2 caches once, instead of a cache writeback
-//   per wave.
-//
-// Bound: HBM. Algorithmic bytes = context rows x 2 (K and V) x Hkv x D x e.
+// Decode planning and launch (pa_decode, pa_store_decode, pa_decode_fp8);
+// the kernels are in decode_device.h.
 
-#include "pa_device.h"
-#include "pa_internal.h"
+#include "decode_device.h"
 
 #include <algorithm>
 
-#ifndef DECODE_U
-#define DECODE_U 8
-#endif
-// Loads in flight per lane for E4M3 pools (16 elements per load).
-#ifndef DECODE_U_E4M3
-#define DECODE_U_E4M3 4
-#endif
-// Resident waves per SIMD the balanced split plans for.
-#ifndef DECODE_BAL_WAVES_PER_SIMD
-#define DECODE_BAL_WAVES_PER_SIMD 2
-#endif
-
 namespace pa {
-
-struct DecodeParams {
-  void* out;
-  const void* q;
-  const char* k_cache;
-  const char* v_cache;
-  const int32_t* block_tables;
-  const int32_t* context_lens;
-  float* ws_acc;     // fixed split: [B][Hq][max_parts][D]
-  float* ws_ml;      // fixed split: [B][Hq][max_parts][2]
-  float* part_acc;   // balanced split: [workers][2 slots][Hq][D]
-  float* part_ml;    // balanced split: [workers][2 slots][Hq][2]
-  int32_t* ws_pfx;   // balanced split: chunk prefix sums [B + 1]
-  int32_t num_seqs, workers;  // balanced split: workers per unit
-  int32_t num_heads, num_kv_heads, group, n_sub, units;
-  int32_t bs_log2, num_blocks, max_blocks_per_seq, max_context_len;
-  int32_t partition, max_parts;
-  int32_t row_bytes;    // Hkv * D * e: bytes between consecutive tokens of a block
-  int64_t block_bytes;  // block_size * row_bytes
-  float scale_log2;     // scale * log2(e): logits are kept in log2 units
-  // Fused store (pa_store_decode), else null: sequence i's newest K/V row
-  // [Hkv][D] at new_k + i*new_k_stride, to be written at slot_mapping[i].
-  const char* new_k;
-  const char* new_v;
-  int64_t new_k_stride, new_v_stride;  // bytes
-  const int32_t* slot_mapping;
-  int64_t num_slots;  // num_blocks * block_size
-  // E4M3 pools: per-KV-head scales (element = value(code) * scale[head]), else null.
-  const float* k_scale;
-  const float* v_scale;
-};
-
-// Fused store: does this call write sequence seq's newest row into the pool
-// (the same test pa_store_kvcache applies to a slot)?
-__device__ __forceinline__ bool stores_new_row(const DecodeParams& p, int seq) {
-  if (p.new_k == nullptr) return false;
-  const int32_t s = p.slot_mapping[seq];
-  return s >= 0 && (int64_t)s < p.num_slots;
-}
-
-// Fused store: copy the newest rows of sequences into the pools, 16 bytes
-// per thread: (sequence, granule) pairs first, first + stride, ... below end
-// (pairs numbered sequence-major, row_bytes / 16 granules per sequence).
-__device__ __forceinline__ void store_new_rows(const DecodeParams& p, int64_t first, int64_t stride,
-                                               int64_t end) {
-  const int32_t cpr = p.row_bytes / 16;
-  end = min(end, (int64_t)p.num_seqs * cpr);
-  for (int64_t idx = first; idx < end; idx += stride) {
-    const int64_t t = idx / cpr;
-    const int32_t c = (int32_t)(idx - t * cpr);
-    if (!stores_new_row(p, (int)t)) continue;
-    const int64_t dst = (int64_t)p.slot_mapping[t] * p.row_bytes + (int64_t)c * 16;
-    const uint4 kv = *reinterpret_cast<const uint4*>(p.new_k + t * p.new_k_stride + (int64_t)c * 16);
-    const uint4 vv = *reinterpret_cast<const uint4*>(p.new_v + t * p.new_v_stride + (int64_t)c * 16);
-    *reinterpret_cast<uint4*>(const_cast<char*>(p.k_cache) + dst) = kv;
-    *reinterpret_cast<uint4*>(const_cast<char*>(p.v_cache) + dst) = vv;
-  }
-}
-
-// 16-byte streaming load of pool data: every K/V byte is read once per call,
-// so the loads carry the nontemporal hint and do not displace reusable lines.
-__device__ __forceinline__ uint4 stream_load(const char* ptr) {
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-template <typename T>
-struct ElemTraits;
-template <>
-struct ElemTraits<float> {
-  static constexpr int E = 4;
-};
-template <>
-struct ElemTraits<uint16_t> {  // bf16 storage
-  static constexpr int E = 2;
-};
-template <>
-struct ElemTraits<uint8_t> {  // E4M3 storage (KV pools only)
-  static constexpr int E = 1;
-};
-
-// E4M3 -> two bf16 (exact: every E4M3 value is a bf16 value) from byte
-// pair HI (0: bytes 0-1, 1: bytes 2-3) of w.
-template <bool HI>
-__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
-}
-// E4M3 -> two fp32 from byte pair HI of w.
-template <bool HI>
-__device__ __forceinline__ f32x2 e4m3x2_to_f32x2(uint32_t w) {
-  return __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
-}
-
-// Partial dot product of this lane's 16-byte slice of q (pre-loaded) and k.
-template <typename T>
-__device__ __forceinline__ float slice_dot(const uint4& qv, const uint4& kv);
-template <>
-__device__ __forceinline__ float slice_dot<uint16_t>(const uint4& qv, const uint4& kv) {
-  float s = dot2_bf16(qv.x, kv.x, 0.0f);
-  s = dot2_bf16(qv.y, kv.y, s);
-  s = dot2_bf16(qv.z, kv.z, s);
-  return dot2_bf16(qv.w, kv.w, s);
-}
-template <>
-__device__ __forceinline__ float slice_dot<float>(const uint4& qv, const uint4& kv) {
-  float s = __builtin_bit_cast(float, qv.x) * __builtin_bit_cast(float, kv.x);
-  s = fmaf(__builtin_bit_cast(float, qv.y), __builtin_bit_cast(float, kv.y), s);
-  s = fmaf(__builtin_bit_cast(float, qv.z), __builtin_bit_cast(float, kv.z), s);
-  return fmaf(__builtin_bit_cast(float, qv.w), __builtin_bit_cast(float, kv.w), s);
-}
-
-// Widen a 16-byte slice to EPL floats.
-template <typename T, int EPL>
-__device__ __forceinline__ void widen_slice(const uint4& v, float (&f)[EPL]) {
-  if constexpr (sizeof(T) == 1) {
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const f32x2 a = e4m3x2_to_f32x2<false>(w[i]);
-      const f32x2 b = e4m3x2_to_f32x2<true>(w[i]);
-      f[4 * i] = a.x; f[4 * i + 1] = a.y; f[4 * i + 2] = b.x; f[4 * i + 3] = b.y;
-    }
-  } else if constexpr (sizeof(T) == 2) {
-    f[0] = bf16lo(v.x); f[1] = bf16hi(v.x);
-    f[2] = bf16lo(v.y); f[3] = bf16hi(v.y);
-    f[4] = bf16lo(v.z); f[5] = bf16hi(v.z);
-    f[6] = bf16lo(v.w); f[7] = bf16hi(v.w);
-  } else {
-    f[0] = __builtin_bit_cast(float, v.x); f[1] = __builtin_bit_cast(float, v.y);
-    f[2] = __builtin_bit_cast(float, v.z); f[3] = __builtin_bit_cast(float, v.w);
-  }
-}
-
-// Store EPL floats as EPL consecutive elements of the output type T, in
-// 16-byte pieces.
-template <typename T, int EPL>
-__device__ __forceinline__ void store_slice(void* dst, const float (&f)[EPL]) {
-  constexpr int PER = 16 / (int)sizeof(T);  // elements per 16-byte piece
-  static_assert(EPL % PER == 0, "slice must be whole 16-byte pieces");
-#pragma unroll
-  for (int c = 0; c < EPL / PER; ++c) {
-    const float* g = f + c * PER;
-    uint4 w;
-    if constexpr (sizeof(T) == 2) {
-      w.x = pack_bf16x2(g[0], g[1]); w.y = pack_bf16x2(g[2], g[3]);
-      w.z = pack_bf16x2(g[4], g[5]); w.w = pack_bf16x2(g[6], g[7]);
-    } else {
-      w.x = __builtin_bit_cast(uint32_t, g[0]); w.y = __builtin_bit_cast(uint32_t, g[1]);
-      w.z = __builtin_bit_cast(uint32_t, g[2]); w.w = __builtin_bit_cast(uint32_t, g[3]);
-    }
-    reinterpret_cast<uint4*>(dst)[c] = w;
-  }
-}
-
-// Merge the online states of the token-row groups that share a d-slice
-// (lanes that differ only in the bits at and above log2(LPT)).
-template <int LPT, int GT, int EPL>
-__device__ __forceinline__ void merge_row_groups(float (&m)[GT], float (&l)[GT],
-                                                 float (&acc)[GT][EPL]) {
-#pragma unroll
-  for (int mask = LPT; mask < 64; mask <<= 1) {
-#pragma unroll
-    for (int h = 0; h < GT; ++h) {
-      const float mo = __shfl_xor(m[h], mask);
-      const float lo = __shfl_xor(l[h], mask);
-      const float mn = fmaxf(m[h], mo);
-      const float a = fast_exp2(m[h] - mn);
-      const float b = fast_exp2(mo - mn);
-      l[h] = l[h] * a + lo * b;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] = acc[h][e] * a + __shfl_xor(acc[h][e], mask) * b;
-      m[h] = mn;
-    }
-  }
-}
-
-// The online-softmax state of one wave: per head of its group, the running
-// maximum m (log2 units), the running sum l and the weighted value sum acc
-// over this lane's d-slice, kept separately per token-row group tr.
-template <int GT, int EPL>
-struct WaveState {
-  float m[GT], l[GT], acc[GT][EPL];
-  __device__ __forceinline__ void reset() {
-#pragma unroll
-    for (int h = 0; h < GT; ++h) {
-      m[h] = NEG_BIG;
-      l[h] = 0.0f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] = 0.0f;
-    }
-  }
-};
-
-// This lane's slice of one query head, in the form that its partial dot
-// product with a 16-byte K slice of storage type KT needs.
-template <typename T, typename KT>
-struct QSlice {  // K in the query's own type: the raw 16 bytes
-  static_assert(sizeof(T) == sizeof(KT), "K must be stored in the query type or as E4M3");
-  uint4 v;
-  __device__ __forceinline__ void load(const char* src) { v = *reinterpret_cast<const uint4*>(src); }
-  __device__ __forceinline__ float dot(const uint4& k) const { return slice_dot<T>(v, k); }
-};
-template <>
-struct QSlice<uint16_t, uint8_t> {  // bf16 query, E4M3 keys: 16 elements, bf16 dot2
-  uint4 v[2];
-  __device__ __forceinline__ void load(const char* src) {
-    v[0] = reinterpret_cast<const uint4*>(src)[0];
-    v[1] = reinterpret_cast<const uint4*>(src)[1];
-  }
-  __device__ __forceinline__ float dot(const uint4& k) const {
-    float s = dot2_bf16(v[0].x, e4m3x2_to_bf16x2<false>(k.x), 0.0f);
-    s = dot2_bf16(v[0].y, e4m3x2_to_bf16x2<true>(k.x), s);
-    s = dot2_bf16(v[0].z, e4m3x2_to_bf16x2<false>(k.y), s);
-    s = dot2_bf16(v[0].w, e4m3x2_to_bf16x2<true>(k.y), s);
-    s = dot2_bf16(v[1].x, e4m3x2_to_bf16x2<false>(k.z), s);
-    s = dot2_bf16(v[1].y, e4m3x2_to_bf16x2<true>(k.z), s);
-    s = dot2_bf16(v[1].z, e4m3x2_to_bf16x2<false>(k.w), s);
-    return dot2_bf16(v[1].w, e4m3x2_to_bf16x2<true>(k.w), s);
-  }
-};
-template <>
-struct QSlice<float, uint8_t> {  // fp32 query, E4M3 keys: 16 elements, fp32 FMA
-  float f[16];
-  __device__ __forceinline__ void load(const char* src) {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float4 x = reinterpret_cast<const float4*>(src)[c];
-      f[4 * c] = x.x; f[4 * c + 1] = x.y; f[4 * c + 2] = x.z; f[4 * c + 3] = x.w;
-    }
-  }
-  __device__ __forceinline__ float dot(const uint4& k) const {
-    float kf[16];
-    widen_slice<uint8_t, 16>(k, kf);
-    float s = f[0] * kf[0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) s = fmaf(f[e], kf[e], s);
-    return s;
-  }
-};
-
-// Load this lane's q slices (EPL elements from element dc*EPL) of heads
-// h0 .. h0+GT-1 of sequence seq.
-template <typename T, typename KT, int D, int GT>
-__device__ __forceinline__ void load_q(const DecodeParams& p, int seq, int h0, int dc,
-                                       QSlice<T, KT> (&qv)[GT]) {
-  constexpr int E = ElemTraits<T>::E;
-  constexpr int EPL = 16 / ElemTraits<KT>::E;
-  const char* qb = static_cast<const char*>(p.q);
-#pragma unroll
-  for (int h = 0; h < GT; ++h)
-    qv[h].load(qb + (((int64_t)seq * p.num_heads + h0 + h) * D + dc * EPL) * E);
-}
-
-// Logit multiplier of a KV head, log2 units: scale * log2(e), times the
-// head's K scale for an E4M3 pool.
-template <typename KT>
-__device__ __forceinline__ float logit_scale(const DecodeParams& p, int kvh) {
-  if constexpr (sizeof(KT) == 1) return p.scale_log2 * p.k_scale[kvh];
-  return p.scale_log2;
-}
-
-// E4M3 pool: the weighted sums were taken over V codes' values; multiply by
-// the head's V scale (every token of a KV head shares it).
-template <typename KT, int GT, int EPL>
-__device__ __forceinline__ void apply_v_scale(const DecodeParams& p, int kvh, float (&acc)[GT][EPL]) {
-  if constexpr (sizeof(KT) == 1) {
-    const float vs = p.v_scale[kvh];
-#pragma unroll
-    for (int h = 0; h < GT; ++h)
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[h][e] *= vs;
-  }
-}
-
-// Stream tokens [tok_begin, tok_end) of sequence seq (KV head kvh) through
-// the online softmax of st. UNIFORM_BLOCK: every chunk lies inside one block
-// (block_size >= CT and tok_begin a multiple of CT), so one table lookup per
-// chunk serves all lanes; otherwise each lane looks up its own token's block.
-// KT is the pools' storage type: T itself, or uint8_t for E4M3 codes, whose
-// logits are multiplied by sm (the logit scale times the head's K scale)
-// and whose weighted value sums still lack the head's V scale.
-template <typename T, typename KT, int D, int GT, int U, bool UNIFORM_BLOCK>
-__device__ __forceinline__ void attend_range(const DecodeParams& p, int seq, int kvh, int lane,
-                                             int tok_begin, int tok_end,
-                                             const QSlice<T, KT> (&qv)[GT], float sm,
-                                             WaveState<GT, 16 / ElemTraits<KT>::E>& st) {
-  // With a fused store, the newest token (position L-1, L = the context
-  // length) comes from the new row itself, not from the pool slot this same
-  // launch is writing.
-  constexpr bool FUSABLE = sizeof(KT) == sizeof(T);
-  const bool new_row = FUSABLE && tok_end > tok_begin && stores_new_row(p, seq) &&
-                       tok_end == min(p.context_lens[seq], p.max_context_len);
-  if (new_row) --tok_end;
-  constexpr int E = ElemTraits<KT>::E;
-  constexpr int EPL = 16 / E;     // elements per 16-byte lane slice
-  constexpr int LPT = D / EPL;    // lanes per token row of one head
-  constexpr int TPW = 64 / LPT;   // token rows per wave-wide load
-  constexpr int CT = U * TPW;     // tokens per chunk
-  const int dc = lane % LPT;
-  const int tr = lane / LPT;
-  const int bs_log2 = p.bs_log2;
-  const int bs_mask = (1 << bs_log2) - 1;
-  const int row_bytes = p.row_bytes;
-  const int lane_off = kvh * D * E + dc * 16;
-  const int32_t* bt = p.block_tables + (int64_t)seq * p.max_blocks_per_seq;
-
-  // Block-table window: lane i holds the physical id of block wbase + i.
-  const int last_blk = (tok_end - 1) >> bs_log2;
-  int wbase = tok_begin >> bs_log2;
-  int tbl = (wbase + lane <= last_blk) ? clamp_block(bt[wbase + lane], p.num_blocks) : 0;
-
-  for (int j0 = tok_begin; j0 < tok_end; j0 += CT) {
-    const int chunk_last = (min(j0 + CT, tok_end) - 1) >> bs_log2;
-    if (chunk_last >= wbase + 64) {  // uniform: slide the table window
-      wbase = j0 >> bs_log2;
-      tbl = (wbase + lane <= last_blk) ? clamp_block(bt[wbase + lane], p.num_blocks) : 0;
-    }
-    // Addresses first, then every K and V load of the chunk, then compute:
-    // the whole chunk's bytes are in flight before any of them is waited on.
-    bool valid[U];
-    int64_t off[U];
-    if constexpr (UNIFORM_BLOCK) {
-      const int phys = __builtin_amdgcn_readlane(tbl, (j0 >> bs_log2) - wbase);
-      const int64_t base = (int64_t)phys * p.block_bytes;
-      const int row0 = (j0 & bs_mask) + tr;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = j0 + u * TPW + tr;
-        valid[u] = j < tok_end;
-        const int row = valid[u] ? row0 + u * TPW : (j0 & bs_mask);
-        off[u] = base + (row * row_bytes + lane_off);
-      }
-    } else {
-      int phys[U], row[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = j0 + u * TPW + tr;
-        valid[u] = j < tok_end;
-        const int jj = valid[u] ? j : j0;  // in-bounds stand-in for tail lanes
-        phys[u] = __shfl(tbl, (jj >> bs_log2) - wbase);
-        row[u] = jj & bs_mask;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < U; ++u) off[u] = (int64_t)phys[u] * p.block_bytes + (row[u] * row_bytes + lane_off);
-    }
-    uint4 kr[U], vr[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) kr[u] = stream_load(p.k_cache + off[u]);
-#pragma unroll
-    for (int u = 0; u < U; ++u) vr[u] = stream_load(p.v_cache + off[u]);
-    __builtin_amdgcn_sched_barrier(0);
-
-    float s[U][GT];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int h = 0; h < GT; ++h) s[u][h] = group_sum<LPT>(qv[h].dot(kr[u]));
-
-#pragma unroll
-    for (int h = 0; h < GT; ++h) {
-      float cm = NEG_BIG;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        s[u][h] = valid[u] ? s[u][h] * sm : -INFINITY;
-        cm = fmaxf(cm, s[u][h]);
-      }
-      const float mn = fmaxf(st.m[h], cm);
-      const float alpha = fast_exp2(st.m[h] - mn);
-      st.m[h] = mn;
-      st.l[h] *= alpha;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) st.acc[h][e] *= alpha;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        s[u][h] = fast_exp2(s[u][h] - mn);
-        st.l[h] += s[u][h];
-      }
-    }
-
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float vf[EPL];
-      widen_slice<KT, EPL>(vr[u], vf);
-#pragma unroll
-      for (int h = 0; h < GT; ++h)
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) st.acc[h][e] = fmaf(s[u][h], vf[e], st.acc[h][e]);
-    }
-  }
-
-  if constexpr (FUSABLE) {
-    if (new_row) {
-    // one more token, held by token-row group 0 (every lane loads the same
-    // row so that the butterfly over the row's lanes stays uniform)
-    const int64_t off = (int64_t)kvh * D * E + dc * 16;
-    const uint4 kr = *reinterpret_cast<const uint4*>(p.new_k + seq * p.new_k_stride + off);
-    const uint4 vr = *reinterpret_cast<const uint4*>(p.new_v + seq * p.new_v_stride + off);
-    float vf[EPL];
-    widen_slice<KT, EPL>(vr, vf);
-#pragma unroll
-    for (int h = 0; h < GT; ++h) {
-      float sc = group_sum<LPT>(qv[h].dot(kr)) * sm;
-      sc = (tr == 0) ? sc : -INFINITY;
-      const float mn = fmaxf(st.m[h], sc);
-      const float alpha = fast_exp2(st.m[h] - mn);
-      const float pr = fast_exp2(sc - mn);
-      st.m[h] = mn;
-      st.l[h] = st.l[h] * alpha + pr;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) st.acc[h][e] = fmaf(pr, vf[e], st.acc[h][e] * alpha);
-    }
-    }
-  }
-}
-
-// Write the (merged) state of heads h0.. of sequence seq as the final
-// output: this lane's EPL elements from element dc*EPL.
-template <typename T, int D, int GT, int EPL>
-__device__ __forceinline__ void store_output(const DecodeParams& p, int seq, int h0, int dc,
-                                             const WaveState<GT, EPL>& st) {
-  constexpr int E = ElemTraits<T>::E;
-  char* const out_base = static_cast<char*>(p.out);
-#pragma unroll
-  for (int h = 0; h < GT; ++h) {
-    float o[EPL];
-    const float inv = 1.0f / st.l[h];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) o[e] = st.acc[h][e] * inv;
-    store_slice<T, EPL>(out_base + (((int64_t)seq * p.num_heads + h0 + h) * D + dc * EPL) * E, o);
-  }
-}
-
-// Zeros for heads h0.. of sequence seq (the defined output of an empty
-// context): this lane's EPL elements from element dc*EPL.
-template <typename T, int D, int GT, int EPL>
-__device__ __forceinline__ void store_zeros(const DecodeParams& p, int seq, int h0, int dc) {
-  constexpr int E = ElemTraits<T>::E;
-  char* const out_base = static_cast<char*>(p.out);
-  float z[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) z[e] = 0.0f;
-#pragma unroll
-  for (int h = 0; h < GT; ++h)
-    store_slice<T, EPL>(out_base + (((int64_t)seq * p.num_heads + h0 + h) * D + dc * EPL) * E, z);
-}
-
-// Workgroups per CU the decode kernels are compiled for: 3 (12 waves) keeps
-// enough loads in flight; four heads of fp32 queries over E4M3 keys (16
-// query elements per lane and head) need the registers of 2.
-template <typename T, typename KT, int GT>
-constexpr int decode_min_wgs() { return (GT >= 4 && sizeof(T) == 4 && sizeof(KT) == 1) ? 2 : 3; }
-
-// One wave = (sequence, KV head, group of GT query heads, partition).
-template <typename T, typename KT, int D, int GT, int U, bool UNIFORM_BLOCK>
-__global__ __launch_bounds__(256, (decode_min_wgs<T, KT, GT>())) void paged_decode_kernel(DecodeParams p) {
-  constexpr int EPL = 16 / ElemTraits<KT>::E;  // elements per 16-byte lane slice
-  constexpr int LPT = D / EPL;                 // lanes per token row of one head
-  static_assert(LPT >= 1 && LPT <= 32 && (64 % LPT) == 0, "unsupported head_dim");
-
-  const int lane = threadIdx.x & 63;
-  const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int seq = blockIdx.z;
-  const int part = blockIdx.y;
-  if constexpr (sizeof(KT) == sizeof(T)) {
-    if (p.new_k != nullptr && blockIdx.x == 0 && part == 0) {  // fused store of seq's row
-      const int64_t cpr = p.row_bytes / 16;
-      store_new_rows(p, (int64_t)seq * cpr + threadIdx.x, 256, (int64_t)(seq + 1) * cpr);
-    }
-  }
-  if (unit >= p.units) return;
-  const int L = min(p.context_lens[seq], p.max_context_len);
-  const int P = p.partition;
-  const int nparts = L > 0 ? (L + P - 1) / P : 0;
-
-  const int kvh = unit / p.n_sub;
-  const int h0 = kvh * p.group + (unit - kvh * p.n_sub) * GT;
-  const int dc = lane % LPT;
-  const int tr = lane / LPT;
-
-  if (nparts == 0) {  // empty context: defined output of zeros
-    if (part == 0 && tr == 0) store_zeros<T, D, GT, EPL>(p, seq, h0, dc);
-    return;
-  }
-  if (part >= nparts) return;
-
-  const int tok_begin = part * P;
-  const int tok_end = min(L, tok_begin + P);
-  QSlice<T, KT> qv[GT];
-  load_q<T, KT, D, GT>(p, seq, h0, dc, qv);
-  WaveState<GT, EPL> st;
-  st.reset();
-  attend_range<T, KT, D, GT, U, UNIFORM_BLOCK>(p, seq, kvh, lane, tok_begin, tok_end, qv,
-                                               logit_scale<KT>(p, kvh), st);
-  apply_v_scale<KT, GT, EPL>(p, kvh, st.acc);
-  merge_row_groups<LPT, GT, EPL>(st.m, st.l, st.acc);
-
-  if (nparts == 1) {
-    if (tr == 0) store_output<T, D, GT, EPL>(p, seq, h0, dc, st);
-    return;
-  }
-
-  // ---- split: publish this partition's state for the merge kernel ----
-  if (tr == 0) {
-    const int64_t mp = p.max_parts;
-#pragma unroll
-    for (int h = 0; h < GT; ++h) {
-      const int64_t sh = (int64_t)seq * p.num_heads + h0 + h;
-      float* dst = p.ws_acc + (sh * mp + part) * D + dc * EPL;
-#pragma unroll
-      for (int e = 0; e < EPL; e += 4)
-        *reinterpret_cast<float4*>(dst + e) =
-            make_float4(st.acc[h][e], st.acc[h][e + 1], st.acc[h][e + 2], st.acc[h][e + 3]);
-      if (dc == 0) *reinterpret_cast<float2*>(p.ws_ml + (sh * mp + part) * 2) = make_float2(st.m[h], st.l[h]);
-    }
-  }
-}
-
-// Merge the partition states of every (sequence, unit) whose context was
-// split: with M the largest partition maximum and w_p = 2^(m_p - M),
-//   out = sum_p w_p acc_p / sum_p w_p l_p.
-// One wave per unit; token-row group tr takes partitions tr, tr+TPW, ...,
-// then the groups merge as in the main kernel. Contexts that fit one
-// partition were written by the main kernel and are skipped here.
-template <typename T, int D, int GT>
-__global__ __launch_bounds__(256) void paged_decode_merge_kernel(DecodeParams p) {
-  constexpr int E = ElemTraits<T>::E;
-  constexpr int EPL = 16 / E;
-  constexpr int LPT = D / EPL;
-  constexpr int TPW = 64 / LPT;
-  const int lane = threadIdx.x & 63;
-  const int unit = blockIdx.y * 4 + (threadIdx.x >> 6);
-  if (unit >= p.units) return;
-  const int seq = blockIdx.x;
-  const int L = min(p.context_lens[seq], p.max_context_len);
-  const int nparts = L > 0 ? (L + p.partition - 1) / p.partition : 0;
-  if (nparts <= 1) return;
-  const int kvh = unit / p.n_sub;
-  const int h0 = kvh * p.group + (unit - kvh * p.n_sub) * GT;
-  const int dc = lane % LPT;
-  const int tr = lane / LPT;
-  const int64_t mp = p.max_parts;
-
-  float m[GT], l[GT], acc[GT][EPL];
-#pragma unroll
-  for (int h = 0; h < GT; ++h) {
-    m[h] = NEG_BIG;
-    l[h] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.0f;
-  }
-  for (int pp = tr; pp < nparts; pp += TPW) {
-#pragma unroll
-    for (int h = 0; h < GT; ++h) {
-      const int64_t sh = (int64_t)seq * p.num_heads + h0 + h;
-      const float2 ml = *reinterpret_cast<const float2*>(p.ws_ml + (sh * mp + pp) * 2);
-      const float* src = p.ws_acc + (sh * mp + pp) * D + dc * EPL;
-      const float mn = fmaxf(m[h], ml.x);
-      const float a = fast_exp2(m[h] - mn);
-      const float b = fast_exp2(ml.x - mn);
-      l[h] = l[h] * a + ml.y * b;
-#pragma unroll
-      for (int e = 0; e < EPL; e += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(src + e);
-        acc[h][e] = acc[h][e] * a + v.x * b;
-        acc[h][e + 1] = acc[h][e + 1] * a + v.y * b;
-        acc[h][e + 2] = acc[h][e + 2] * a + v.z * b;
-        acc[h][e + 3] = acc[h][e + 3] * a + v.w * b;
-      }
-      m[h] = mn;
-    }
-  }
-  merge_row_groups<LPT, GT, EPL>(m, l, acc);
-  if (tr == 0) {
-    char* const out_base = static_cast<char*>(p.out);
-#pragma unroll
-    for (int h = 0; h < GT; ++h) {
-      float o[EPL];
-      const float inv = 1.0f / l[h];
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) o[e] = acc[h][e] * inv;
-      store_slice<T, EPL>(out_base + (((int64_t)seq * p.num_heads + h0 + h) * D + dc * EPL) * E, o);
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
-// balanced split
-// ---------------------------------------------------------------------------
-//
-// The contexts of all sequences, cut into chunks of CT tokens, are laid end
-// to end; the W workers of each unit (one wave each, all resident at once)
-// take equal contiguous ranges of that chunk sequence. A worker streams its
-// range without a break, crossing from one sequence into another: a
-// sequence wholly inside one range is written out directly, and a sequence
-// cut by a range boundary leaves a partial (m, l, acc) state in one of the
-// worker's two slots (slot 0: the piece the range starts in, slot 1: the
-// piece it ends in), which paged_decode_balanced_merge_kernel combines.
-// Every worker does the same amount of work whatever the length mix, and
-// each wave pays its start-up (prefix sums, q, table window) once.
-
-// Sequences the balanced split supports (their chunk prefix sums live in LDS).
-constexpr int BAL_MAX_SEQS = 4096;
-
-// pfx[0] = 0, pfx[k+1] = pfx[k] + ceil(L_k / CT): chunk prefix sums of the
-// clamped context lengths, computed by the whole workgroup.
-template <int CT>
-__device__ __forceinline__ void chunk_prefix(const DecodeParams& p, int32_t* pfx) {
-  __shared__ int32_t wave_total[4];
-  const int B = p.num_seqs;
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wv = tid >> 6;
-  const int per = (B + 255) / 256;
-  const int k0 = min(B, tid * per);
-  const int k1 = min(B, k0 + per);
-  auto chunks = [&](int k) {
-    const int L = min(p.context_lens[k], p.max_context_len);
-    return L > 0 ? (L + CT - 1) / CT : 0;
-  };
-  int local = 0;
-  for (int k = k0; k < k1; ++k) local += chunks(k);
-  int x = local;  // inclusive scan over the wave
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
-  if (lane == 63) wave_total[wv] = x;
-  __syncthreads();
-  int run = x - local;
-  for (int w = 0; w < wv; ++w) run += wave_total[w];
-  if (tid == 0) pfx[0] = 0;
-  for (int k = k0; k < k1; ++k) {
-    run += chunks(k);
-    pfx[k + 1] = run;
-  }
-  __syncthreads();
-}
-
-template <typename T, typename KT, int D, int GT, int U, bool UNIFORM_BLOCK>
-__global__ __launch_bounds__(256, 2) void paged_decode_balanced_kernel(DecodeParams p) {
-  constexpr int EPL = 16 / ElemTraits<KT>::E;
-  constexpr int LPT = D / EPL;
-  constexpr int TPW = 64 / LPT;
-  constexpr int CT = U * TPW;
-  __shared__ int32_t pfx[BAL_MAX_SEQS + 1];
-  if constexpr (sizeof(KT) == sizeof(T)) {
-    if (p.new_k != nullptr)  // fused store: every thread of the grid copies a share of the rows
-      store_new_rows(p, (int64_t)blockIdx.x * 256 + threadIdx.x, (int64_t)gridDim.x * 256, INT64_MAX);
-  }
-  chunk_prefix<CT>(p, pfx);
-  const int B = p.num_seqs;
-  if (blockIdx.x == 0)
-    for (int k = threadIdx.x; k <= B; k += 256) p.ws_pfx[k] = pfx[k];
-  const int C = pfx[B];
-
-  const int lane = threadIdx.x & 63;
-  const int g = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int unit = g % p.units;  // the waves of a workgroup share a range
-  const int w = g / p.units;
-  if (w >= p.workers) return;
-  const int c0 = (int)((int64_t)w * C / p.workers);
-  const int c1 = (int)((int64_t)(w + 1) * C / p.workers);
-  if (c0 >= c1) return;
-  const int kvh = unit / p.n_sub;
-  const int h0 = kvh * p.group + (unit - kvh * p.n_sub) * GT;
-  const int dc = lane % LPT;
-  const int tr = lane / LPT;
-  const float sm = logit_scale<KT>(p, kvh);
-
-  // Pieces are taken from the end of the range backwards. The last piece
-  // begins at a context's first token (unless the range lies inside one
-  // context), so the first blocks of contexts, which prefix sharing makes
-  // common to many sequences, are read by all workers near the start of the
-  // kernel, while the shared lines are still cached.
-  // The sequence holding chunk c1 - 1: the last i with pfx[i] <= c1 - 1.
-  int lo = 0, hi = B - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (pfx[mid] <= c1 - 1) lo = mid;
-    else hi = mid - 1;
-  }
-  int i = lo;
-  for (;;) {
-    const int cb = pfx[i], ce = pfx[i + 1];
-    const int ps = max(c0, cb), pe = min(c1, ce);
-    const int L = min(p.context_lens[i], p.max_context_len);
-    QSlice<T, KT> qv[GT];
-    load_q<T, KT, D, GT>(p, i, h0, dc, qv);
-    WaveState<GT, EPL> st;
-    st.reset();
-    attend_range<T, KT, D, GT, U, UNIFORM_BLOCK>(p, i, kvh, lane, (ps - cb) * CT,
-                                                 min((pe - cb) * CT, L), qv, sm, st);
-    apply_v_scale<KT, GT, EPL>(p, kvh, st.acc);
-    merge_row_groups<LPT, GT, EPL>(st.m, st.l, st.acc);
-    if (tr == 0) {
-      if (ps == cb && pe == ce) {
-        store_output<T, D, GT, EPL>(p, i, h0, dc, st);
-      } else {
-        // slot 0: the piece holding c0; slot 1: the piece holding c1 - 1
-        const int64_t slot = (int64_t)w * 2 + (ps == c0 ? 0 : 1);
-#pragma unroll
-        for (int h = 0; h < GT; ++h) {
-          const int64_t sh = slot * p.num_heads + h0 + h;
-          float* dst = p.part_acc + sh * D + dc * EPL;
-#pragma unroll
-          for (int e = 0; e < EPL; e += 4)
-            *reinterpret_cast<float4*>(dst + e) =
-                make_float4(st.acc[h][e], st.acc[h][e + 1], st.acc[h][e + 2], st.acc[h][e + 3]);
-          if (dc == 0) *reinterpret_cast<float2*>(p.part_ml + sh * 2) = make_float2(st.m[h], st.l[h]);
-        }
-      }
-    }
-    if (ps <= c0) break;
-    do {
-      --i;
-    } while (pfx[i] == pfx[i + 1]);  // skip empty contexts
-  }
-}
-
-// One wave per (sequence, unit): combine the partial states the workers
-// left for a sequence their ranges cut, and write zeros for an empty
-// context. Sequences inside one range were written by the main kernel.
-template <typename T, int D, int GT>
-__global__ __launch_bounds__(256) void paged_decode_balanced_merge_kernel(DecodeParams p) {
-  constexpr int E = ElemTraits<T>::E;
-  constexpr int EPL = 16 / E;
-  constexpr int LPT = D / EPL;
-  constexpr int TPW = 64 / LPT;
-  const int lane = threadIdx.x & 63;
-  const int unit = blockIdx.y * 4 + (threadIdx.x >> 6);
-  if (unit >= p.units) return;
-  const int seq = blockIdx.x;
-  const int kvh = unit / p.n_sub;
-  const int h0 = kvh * p.group + (unit - kvh * p.n_sub) * GT;
-  const int dc = lane % LPT;
-  const int tr = lane / LPT;
-  const int L = min(p.context_lens[seq], p.max_context_len);
-  if (L <= 0) {
-    if (tr == 0) store_zeros<T, D, GT, EPL>(p, seq, h0, dc);
-    return;
-  }
-  const int cb = p.ws_pfx[seq], ce = p.ws_pfx[seq + 1], C = p.ws_pfx[p.num_seqs];
-  const int W = p.workers;
-  auto worker_of = [&](int ch) { return (int)((((int64_t)ch + 1) * W - 1) / C); };
-  auto start_of = [&](int wk) { return (int)((int64_t)wk * C / W); };
-  const int wf = worker_of(cb), wl = worker_of(ce - 1);
-  if (wf == wl) return;
-
-  WaveState<GT, EPL> st;
-  st.reset();
-  for (int wk = wf + tr; wk <= wl; wk += TPW) {
-    const int s0 = start_of(wk);
-    if (s0 == start_of(wk + 1)) continue;  // an empty range left nothing
-    const int64_t slot = (int64_t)wk * 2 + ((wk == wf && s0 != cb) ? 1 : 0);
-#pragma unroll
-    for (int h = 0; h < GT; ++h) {
-      const int64_t sh = slot * p.num_heads + h0 + h;
-      const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + sh * 2);
-      const float* src = p.part_acc + sh * D + dc * EPL;
-      const float mn = fmaxf(st.m[h], ml.x);
-      const float a = fast_exp2(st.m[h] - mn);
-      const float b = fast_exp2(ml.x - mn);
-      st.l[h] = st.l[h] * a + ml.y * b;
-#pragma unroll
-      for (int e = 0; e < EPL; e += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(src + e);
-        st.acc[h][e] = st.acc[h][e] * a + v.x * b;
-        st.acc[h][e + 1] = st.acc[h][e + 1] * a + v.y * b;
-        st.acc[h][e + 2] = st.acc[h][e + 2] * a + v.z * b;
-        st.acc[h][e + 3] = st.acc[h][e + 3] * a + v.w * b;
-      }
-      st.m[h] = mn;
-    }
-  }
-  merge_row_groups<LPT, GT, EPL>(st.m, st.l, st.acc);
-  if (tr == 0) store_output<T, D, GT, EPL>(p, seq, h0, dc, st);
-}
 
 // ---------------------------------------------------------------------------
 // planning and launch
@@ -889,23 +65,27 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
 }
 
 template <typename T, typename KT, int D, int GT, int U>
-static void launch_u(const DecodeParams& prm, const DecodePlan& pl, dim3 grid, hipStream_t stream) {
+static void launch_balanced(const DecodeParams& prm, const DecodePlan& pl, dim3 grid, hipStream_t stream) {
   constexpr int TPW = 64 / (D * (int)sizeof(KT) / 16);
   constexpr int CT = U * TPW;
   const bool big_blocks = (1 << prm.bs_log2) >= CT;
-  if (pl.balanced) {
-    const int64_t waves = (int64_t)pl.workers * pl.units;
-    const dim3 bgrid((unsigned)((waves + 3) / 4));
-    if (big_blocks)
-      hipLaunchKernelGGL((paged_decode_balanced_kernel<T, KT, D, GT, U, true>), bgrid, dim3(256), 0,
-                         stream, prm);
-    else
-      hipLaunchKernelGGL((paged_decode_balanced_kernel<T, KT, D, GT, U, false>), bgrid, dim3(256), 0,
-                         stream, prm);
-    hipLaunchKernelGGL((paged_decode_balanced_merge_kernel<T, D, GT>), dim3(grid.z, grid.x), dim3(256), 0,
+  const int64_t waves = (int64_t)pl.workers * pl.units;
+  const dim3 bgrid((unsigned)((waves + 3) / 4));
+  if (big_blocks)
+    hipLaunchKernelGGL((paged_decode_balanced_kernel<T, KT, D, GT, U, true>), bgrid, dim3(256), 0,
                        stream, prm);
-    return;
-  }
+  else
+    hipLaunchKernelGGL((paged_decode_balanced_kernel<T, KT, D, GT, U, false>), bgrid, dim3(256), 0,
+                       stream, prm);
+  hipLaunchKernelGGL((paged_decode_balanced_merge_kernel<T, D, GT>), dim3(grid.z, grid.x), dim3(256), 0,
+                     stream, prm);
+}
+
+template <typename T, typename KT, int D, int GT, int U>
+static void launch_fixed(const DecodeParams& prm, const DecodePlan& pl, dim3 grid, hipStream_t stream) {
+  constexpr int TPW = 64 / (D * (int)sizeof(KT) / 16);
+  constexpr int CT = U * TPW;
+  const bool big_blocks = (1 << prm.bs_log2) >= CT;
   const bool uniform = big_blocks && (prm.max_parts == 1 || prm.partition % CT == 0);
   if (uniform)
     hipLaunchKernelGGL((paged_decode_kernel<T, KT, D, GT, U, true>), grid, dim3(256), 0, stream, prm);
@@ -916,13 +96,24 @@ static void launch_u(const DecodeParams& prm, const DecodePlan& pl, dim3 grid, h
                        stream, prm);
 }
 
+// Loads in flight per lane (U): DECODE_U for pools in the query type; for
+// E4M3 pools DECODE_U_E4M3 in the balanced split and half of it in the fixed
+// split, whose four-heads-per-wave kernel would otherwise spill registers.
+template <typename T, typename KT, int D, int GT>
+static void launch_split(const DecodeParams& prm, const DecodePlan& pl, dim3 grid, hipStream_t stream) {
+  constexpr bool E8 = sizeof(KT) == 1;
+  constexpr int UB = E8 ? DECODE_U_E4M3 : DECODE_U;
+  constexpr int UF = E8 ? (DECODE_U_E4M3 > 2 ? DECODE_U_E4M3 / 2 : DECODE_U_E4M3) : DECODE_U;
+  if (pl.balanced) launch_balanced<T, KT, D, GT, UB>(prm, pl, grid, stream);
+  else launch_fixed<T, KT, D, GT, UF>(prm, pl, grid, stream);
+}
+
 template <typename T, typename KT, int D>
 static void launch_gt(const DecodeParams& prm, const DecodePlan& pl, dim3 grid, hipStream_t stream) {
-  constexpr int U = sizeof(KT) == 1 ? DECODE_U_E4M3 : DECODE_U;
   switch (pl.heads_per_unit) {
-    case 1: launch_u<T, KT, D, 1, U>(prm, pl, grid, stream); break;
-    case 2: launch_u<T, KT, D, 2, U>(prm, pl, grid, stream); break;
-    default: launch_u<T, KT, D, 4, U>(prm, pl, grid, stream); break;
+    case 1: launch_split<T, KT, D, 1>(prm, pl, grid, stream); break;
+    case 2: launch_split<T, KT, D, 2>(prm, pl, grid, stream); break;
+    default: launch_split<T, KT, D, 4>(prm, pl, grid, stream); break;
   }
 }
 
@@ -933,7 +124,7 @@ static void launch_d(const DecodeParams& prm, const DecodePlan& pl, int head_dim
   else launch_gt<T, KT, 128>(prm, pl, grid, stream);
 }
 
-hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t stream) {
+DecodeParams make_decode_params(const DecodeArgs& a, const DecodePlan& pl) {
   DecodeParams prm{};
   prm.out = a.out;
   prm.q = a.q;
@@ -978,6 +169,11 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t 
     prm.slot_mapping = a.slot_mapping;
     prm.num_slots = (int64_t)a.num_blocks * a.block_size;
   }
+  return prm;
+}
+
+hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t stream) {
+  const DecodeParams prm = make_decode_params(a, pl);
   // x: head group (fastest, so one token's rows of all heads are read by
   // neighbouring workgroups), y: partition, z: sequence.
   const dim3 grid((unsigned)((pl.units + 3) / 4), (unsigned)pl.max_parts, (unsigned)a.num_seqs);

@@ -344,6 +344,36 @@ pa_status pa_store_kvcache_fp8(const void* key, const void* value, int64_t key_t
   }
 }
 
+namespace {
+
+// Validation shared by pa_prefill_chunk and pa_mixed_batch.
+pa_status check_varlen(const char* fn, void* out, const void* q, const void* k_cache,
+                       const void* v_cache, const int32_t* block_tables,
+                       const int32_t* query_start_loc, const int32_t* context_lens,
+                       int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                       int32_t max_query_len, int32_t max_context_len, float scale, pa_dtype dtype) {
+  if (pa_status st = check_dtype(dtype)) return st;
+  if (dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "%s: implemented for bf16 only", fn);
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start_loc || !context_lens)
+    return fail(PA_ERR_INVALID_ARG, "%s: null pointer argument", fn);
+  if (pa_status st = check_attention_shapes(num_heads, num_kv_heads, head_dim, block_size,
+                                            num_blocks, max_blocks_per_seq, max_context_len))
+    return st;
+  if (max_query_len <= 0 || max_query_len > max_context_len)
+    return fail(PA_ERR_INVALID_ARG, "%s: max_query_len=%d must be in [1, max_context_len=%d]", fn,
+                max_query_len, max_context_len);
+  if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "%s: num_seqs=%d above 65535", fn, num_seqs);
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "%s: scale is not finite", fn);
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(block_tables, 4) || !aligned(query_start_loc, 4) || !aligned(context_lens, 4))
+    return fail(PA_ERR_UNSUPPORTED, "%s: pointers must be 16-byte aligned (int arrays 4-byte)", fn);
+  if ((int64_t)num_heads > 65535) return fail(PA_ERR_UNSUPPORTED, "%s: too many heads", fn);
+  return PA_OK;
+}
+
+}  // namespace
+
 pa_status pa_prefill_chunk(void* out, const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* block_tables, const int32_t* query_start_loc,
                            const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
@@ -354,26 +384,62 @@ pa_status pa_prefill_chunk(void* out, const void* q, const void* k_cache, const 
     if (pa_status st = check_dtype(dtype)) return st;
     if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs=%d is negative", num_seqs);
     if (num_seqs == 0) return ok();
-    if (dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "prefill is implemented for bf16 only");
-    if (!out || !q || !k_cache || !v_cache || !block_tables || !query_start_loc || !context_lens)
-      return fail(PA_ERR_INVALID_ARG, "null pointer argument");
-    if (pa_status st = check_attention_shapes(num_heads, num_kv_heads, head_dim, block_size,
-                                              num_blocks, max_blocks_per_seq, max_context_len))
+    if (pa_status st = check_varlen("pa_prefill_chunk", out, q, k_cache, v_cache, block_tables,
+                                    query_start_loc, context_lens, num_seqs, num_heads,
+                                    num_kv_heads, head_dim, block_size, num_blocks,
+                                    max_blocks_per_seq, max_query_len, max_context_len, scale, dtype))
       return st;
-    if (max_query_len <= 0 || max_query_len > max_context_len)
-      return fail(PA_ERR_INVALID_ARG, "max_query_len=%d must be in [1, max_context_len=%d]",
-                  max_query_len, max_context_len);
-    if (num_seqs > 65535) return fail(PA_ERR_UNSUPPORTED, "num_seqs=%d above 65535", num_seqs);
-    if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
-    if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
-        !aligned(block_tables, 4) || !aligned(query_start_loc, 4) || !aligned(context_lens, 4))
-      return fail(PA_ERR_UNSUPPORTED, "pointers must be 16-byte aligned (int arrays 4-byte)");
-    if ((int64_t)num_heads > 65535) return fail(PA_ERR_UNSUPPORTED, "too many heads");
     pa::PrefillArgs a{out, q, k_cache, v_cache, block_tables, query_start_loc, context_lens,
                       num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                       max_blocks_per_seq, max_query_len, max_context_len, scale};
     const hipError_t err = pa::launch_prefill(a, static_cast<hipStream_t>(stream));
     if (err != hipSuccess) return fail(PA_ERR_HIP, "prefill launch: %s", hipGetErrorString(err));
+    return ok();
+  } catch (...) {
+    return fail(PA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+pa_status pa_mixed_batch(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* query_start_loc,
+                         const int32_t* context_lens, int32_t num_seqs, int32_t num_decode_seqs,
+                         int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                         int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
+                         int32_t max_query_len, int32_t max_context_len, float scale,
+                         void* workspace, size_t workspace_bytes, pa_dtype dtype, void* stream) {
+  try {
+    if (pa_status st = check_dtype(dtype)) return st;
+    if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "pa_mixed_batch: num_seqs=%d is negative", num_seqs);
+    if (num_seqs == 0) return ok();
+    if (num_decode_seqs < 0 || num_decode_seqs > num_seqs)
+      return fail(PA_ERR_INVALID_ARG, "pa_mixed_batch: num_decode_seqs=%d not in [0, num_seqs=%d]",
+                  num_decode_seqs, num_seqs);
+    if (num_decode_seqs > 2048)
+      return fail(PA_ERR_UNSUPPORTED, "pa_mixed_batch: at most 2048 decode sequences (got %d)",
+                  num_decode_seqs);
+    if (pa_status st = check_varlen("pa_mixed_batch", out, q, k_cache, v_cache, block_tables,
+                                    query_start_loc, context_lens, num_seqs, num_heads,
+                                    num_kv_heads, head_dim, block_size, num_blocks,
+                                    max_blocks_per_seq, max_query_len, max_context_len, scale, dtype))
+      return st;
+    if (num_decode_seqs > 0) {
+      const size_t need = pa::plan_decode(num_decode_seqs, num_heads, num_kv_heads, head_dim,
+                                          max_context_len, PA_PARTITION_BALANCED)
+                              .total_bytes;
+      if (!workspace)
+        return fail(PA_ERR_WORKSPACE, "pa_mixed_batch: a workspace of %zu bytes is needed", need);
+      if (workspace_bytes < need)
+        return fail(PA_ERR_WORKSPACE, "pa_mixed_batch: workspace of %zu bytes, %zu needed",
+                    workspace_bytes, need);
+      if (!aligned(workspace, 256))
+        return fail(PA_ERR_WORKSPACE, "pa_mixed_batch: workspace must be 256-byte aligned");
+    }
+    pa::PrefillArgs a{out, q, k_cache, v_cache, block_tables, query_start_loc, context_lens,
+                      num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                      max_blocks_per_seq, max_query_len, max_context_len, scale};
+    const hipError_t err = pa::launch_mixed(a, num_decode_seqs, workspace,
+                                            static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(PA_ERR_HIP, "pa_mixed_batch launch: %s", hipGetErrorString(err));
     return ok();
   } catch (...) {
     return fail(PA_ERR_HIP, "unexpected C++ exception");

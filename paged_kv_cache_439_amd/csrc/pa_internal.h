@@ -95,5 +95,9 @@ hipError_t launch_store(const StoreArgs& a, hipStream_t stream);
 hipError_t launch_store_e4m3(const StoreE4M3Args& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+// a describes the whole batch; its first num_decode sequences are decode
+// tokens (workspace: the balanced decode workspace for num_decode sequences).
+hipError_t launch_mixed(const PrefillArgs& a, int32_t num_decode, void* workspace,
+                        hipStream_t stream);
 
 }  // namespace pa

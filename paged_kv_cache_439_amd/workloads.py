@@ -60,6 +60,14 @@ CONFIGS = {
             num_seqs=512, num_heads=32, num_kv_heads=8, head_dim=128, block_size=64,
             lens=("lognormal", 1500.0, 1.0, 64, 4096), pool=("factor", 1.25),
             max_context=4096, partition_size=-1, fixed_partition_size=512),
+    # A continuous batch (pa_mixed_batch): 256 decode tokens (contexts uniform
+    # in [512, 4096]) followed by 4 prefill chunks of 512 new tokens over
+    # cached contexts uniform in [0, 3584], on the GQA 32/8 model of the
+    # prefill workload.
+    6: dict(name="bf16_gqa_mixed_decode256_prefill4x512", kind="mixed", dtype="bf16", num_seqs=260,
+            num_decode=256, num_heads=32, num_kv_heads=8, head_dim=128, block_size=256,
+            decode_lens=("uniform", 512, 4096), cached=("uniform", 0, 3584), chunk=512,
+            pool=("factor", 1.25), max_context=4096),
 }
 
 
@@ -75,7 +83,7 @@ def elem_bytes(dtype: str) -> int:
 class Batch:
     """One batch of paged-attention inputs."""
     spec: dict
-    kind: str                      # "decode" | "prefill"
+    kind: str                      # "decode" | "prefill" | "mixed" (decode rows, then chunks)
     dtype: str                     # "f32" | "bf16"
     num_seqs: int
     num_heads: int
@@ -102,6 +110,11 @@ class Batch:
     @property
     def kv_e4m3(self) -> bool:
         return self.k_scale is not None
+
+    @property
+    def num_decode(self) -> int:
+        """Leading sequences that are decode tokens, one row each (mixed batches)."""
+        return int(self.spec.get("num_decode", 0)) if self.kind == "mixed" else 0
 
     @property
     def max_blocks_per_seq(self) -> int:
@@ -222,6 +235,16 @@ def _structure(spec, seed):
                 lens[redo] = _draw_lengths(rng, spec["lens"], int(redo.sum()), lo_override=lo)
                 redo = sharers & (lens < lo)
         chunks = None
+    elif spec["kind"] == "mixed":
+        # decode tokens first (one new row each), then the prefill chunks
+        Bd = spec["num_decode"]
+        lens_d = _draw_lengths(rng, spec["decode_lens"], Bd)
+        cached = _draw_lengths(rng, spec["cached"], B - Bd)
+        chunk = spec["chunk"]
+        tail = (np.full(B - Bd, chunk, dtype=np.int64) if np.isscalar(chunk)
+                else np.asarray(chunk, np.int64))
+        chunks = np.concatenate([np.ones(Bd, dtype=np.int64), tail])
+        lens = np.concatenate([lens_d, cached + tail])
     else:
         cached = _draw_lengths(rng, spec["cached"], B)
         chunk = spec["chunk"]

@@ -142,11 +142,26 @@ def snapshot_pools(batch):
     return batch
 
 
-def prefill_parity(batch, sample_rows=None, seed=0):
+def gpu_mixed(batch, arrs=None, workspace=None):
+    """pa_mixed_batch over the batch (its first num_decode sequences decode)."""
+    arrs = arrs or device_arrays(batch)
+    if workspace is None:
+        workspace = pa.mixed_workspace(batch.num_decode, batch.num_heads, batch.num_kv_heads,
+                                       batch.head_dim, batch.max_context_len, batch.q.device)
+    out = torch.full_like(batch.q, float("nan"))
+    pa.pa_mixed_batch(out, batch.q, batch.k_cache, batch.v_cache, arrs["tables"], arrs["qsl"],
+                      arrs["lens"], batch.num_decode, batch.max_query_len, batch.max_context_len,
+                      batch.scale, workspace)
+    return out
+
+
+def prefill_parity(batch, sample_rows=None, seed=0, runner=None):
+    """Store + varlen attention on the GPU (pa_prefill_chunk, or runner)
+    against the oracle's store and prefill."""
     hb, kp, vp = oracle_inputs(batch)
     arrs = device_arrays(batch)
     gpu_store(batch, arrs)
-    out = gpu_prefill(batch, arrs)
+    out = (runner or gpu_prefill)(batch, arrs)
     torch.cuda.synchronize()
     got = as_f64(out)
     if sample_rows is None:

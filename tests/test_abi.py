@@ -221,3 +221,26 @@ def test_store_fp8_rejections(lib):
     assert _store_fp8(lib, ks=516) == PA_ERR_UNSUPPORTED           # bf16 stride not 16-byte multiple
     assert _store_fp8(lib, k=ctypes.c_void_p(0x100008)) == PA_ERR_UNSUPPORTED
     assert _store_fp8(lib, NB=1 << 28, bs=16) == PA_ERR_INVALID_ARG
+
+
+def _mixed(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, qsl=FAKE, cl=FAKE, B=260, Bd=256, Hq=32, Hkv=8,
+             D=128, bs=256, NB=4000, MB=16, mq=512, maxL=4096, scale=0.088, ws=FAKE, wsb=1 << 30, dtype=1)
+    a.update(kw)
+    return lib.pa_mixed_batch(a["out"], a["q"], a["k"], a["v"], a["bt"], a["qsl"], a["cl"], a["B"], a["Bd"],
+                              a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"], a["MB"], a["mq"], a["maxL"],
+                              a["scale"], a["ws"], a["wsb"], a["dtype"], None)
+
+
+def test_mixed_rejections(lib):
+    assert _mixed(lib, B=0) == PA_OK
+    assert _mixed(lib, Bd=-1) == PA_ERR_INVALID_ARG
+    assert _mixed(lib, Bd=261) == PA_ERR_INVALID_ARG            # more decode rows than sequences
+    assert _mixed(lib, B=3000, Bd=2049) == PA_ERR_UNSUPPORTED  # decode prefix sums live in LDS
+    assert _mixed(lib, dtype=0) == PA_ERR_UNSUPPORTED
+    assert _mixed(lib, qsl=None) == PA_ERR_INVALID_ARG
+    assert _mixed(lib, mq=0) == PA_ERR_INVALID_ARG
+    assert _mixed(lib, ws=None) == PA_ERR_WORKSPACE
+    assert _mixed(lib, wsb=16) == PA_ERR_WORKSPACE
+    assert _mixed(lib, ws=ctypes.c_void_p(0x100010)) == PA_ERR_WORKSPACE   # not 256-byte aligned
+    assert "pa_mixed_batch" in binding.load_library().pa_last_error().decode()
