@@ -695,6 +695,53 @@ __device__ __forceinline__ void chunk_prefix(const DecodeParams& p, int32_t* pfx
   __syncthreads();
 }
 
+// The worker whose range holds chunk ch, and the first chunk of worker wk's
+// range, when C chunks are cut into W equal ranges.
+__device__ __forceinline__ int bal_worker_of(int ch, int C, int W) {
+  return (int)((((int64_t)ch + 1) * W - 1) / C);
+}
+__device__ __forceinline__ int bal_start_of(int wk, int C, int W) { return (int)((int64_t)wk * C / W); }
+
+// Combine the partial states the workers left for a sequence whose chunks
+// cb .. ce-1 their ranges cut, and write heads h0.. of its output. Lane
+// mapping (dc, tr) as in the caller: token-row group tr takes the pieces of
+// workers wf+tr, wf+tr+TPW, ...; the groups merge at the end.
+template <typename T, int D, int GT, int EPL, int LPT>
+__device__ __forceinline__ void merge_pieces(const DecodeParams& p, int seq, int h0, int dc, int tr,
+                                             int cb, int ce, int C) {
+  constexpr int TPW = 64 / LPT;
+  const int W = p.workers;
+  const int wf = bal_worker_of(cb, C, W), wl = bal_worker_of(ce - 1, C, W);
+  WaveState<GT, EPL> st;
+  st.reset();
+  for (int wk = wf + tr; wk <= wl; wk += TPW) {
+    const int s0 = bal_start_of(wk, C, W);
+    if (s0 == bal_start_of(wk + 1, C, W)) continue;  // an empty range left nothing
+    const int64_t slot = (int64_t)wk * 2 + ((wk == wf && s0 != cb) ? 1 : 0);
+#pragma unroll
+    for (int h = 0; h < GT; ++h) {
+      const int64_t sh = slot * p.num_heads + h0 + h;
+      const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + sh * 2);
+      const float* src = p.part_acc + sh * D + dc * EPL;
+      const float mn = fmaxf(st.m[h], ml.x);
+      const float a = fast_exp2(st.m[h] - mn);
+      const float b = fast_exp2(ml.x - mn);
+      st.l[h] = st.l[h] * a + ml.y * b;
+#pragma unroll
+      for (int e = 0; e < EPL; e += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(src + e);
+        st.acc[h][e] = st.acc[h][e] * a + v.x * b;
+        st.acc[h][e + 1] = st.acc[h][e + 1] * a + v.y * b;
+        st.acc[h][e + 2] = st.acc[h][e + 2] * a + v.z * b;
+        st.acc[h][e + 3] = st.acc[h][e + 3] * a + v.w * b;
+      }
+      st.m[h] = mn;
+    }
+  }
+  merge_row_groups<LPT, GT, EPL>(st.m, st.l, st.acc);
+  if (tr == 0) store_output<T, D, GT, EPL>(p, seq, h0, dc, st);
+}
+
 // The balanced split's workers, as workgroup wg of num_wgs (each workgroup
 // holds 4 waves, i.e. 4 (unit, worker) pairs). MAXS bounds num_seqs (the
 // chunk prefix sums live in LDS).
@@ -792,7 +839,6 @@ __global__ __launch_bounds__(256) void paged_decode_balanced_merge_kernel(Decode
   constexpr int E = ElemTraits<T>::E;
   constexpr int EPL = 16 / E;
   constexpr int LPT = D / EPL;
-  constexpr int TPW = 64 / LPT;
   const int lane = threadIdx.x & 63;
   const int unit = blockIdx.y * 4 + (threadIdx.x >> 6);
   if (unit >= p.units) return;
@@ -808,39 +854,8 @@ __global__ __launch_bounds__(256) void paged_decode_balanced_merge_kernel(Decode
   }
   const int cb = p.ws_pfx[seq], ce = p.ws_pfx[seq + 1], C = p.ws_pfx[p.num_seqs];
   const int W = p.workers;
-  auto worker_of = [&](int ch) { return (int)((((int64_t)ch + 1) * W - 1) / C); };
-  auto start_of = [&](int wk) { return (int)((int64_t)wk * C / W); };
-  const int wf = worker_of(cb), wl = worker_of(ce - 1);
-  if (wf == wl) return;
-
-  WaveState<GT, EPL> st;
-  st.reset();
-  for (int wk = wf + tr; wk <= wl; wk += TPW) {
-    const int s0 = start_of(wk);
-    if (s0 == start_of(wk + 1)) continue;  // an empty range left nothing
-    const int64_t slot = (int64_t)wk * 2 + ((wk == wf && s0 != cb) ? 1 : 0);
-#pragma unroll
-    for (int h = 0; h < GT; ++h) {
-      const int64_t sh = slot * p.num_heads + h0 + h;
-      const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + sh * 2);
-      const float* src = p.part_acc + sh * D + dc * EPL;
-      const float mn = fmaxf(st.m[h], ml.x);
-      const float a = fast_exp2(st.m[h] - mn);
-      const float b = fast_exp2(ml.x - mn);
-      st.l[h] = st.l[h] * a + ml.y * b;
-#pragma unroll
-      for (int e = 0; e < EPL; e += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(src + e);
-        st.acc[h][e] = st.acc[h][e] * a + v.x * b;
-        st.acc[h][e + 1] = st.acc[h][e + 1] * a + v.y * b;
-        st.acc[h][e + 2] = st.acc[h][e + 2] * a + v.z * b;
-        st.acc[h][e + 3] = st.acc[h][e + 3] * a + v.w * b;
-      }
-      st.m[h] = mn;
-    }
-  }
-  merge_row_groups<LPT, GT, EPL>(st.m, st.l, st.acc);
-  if (tr == 0) store_output<T, D, GT, EPL>(p, seq, h0, dc, st);
+  if (bal_worker_of(cb, C, W) == bal_worker_of(ce - 1, C, W)) return;  // written by one worker
+  merge_pieces<T, D, GT, EPL, LPT>(p, seq, h0, dc, tr, cb, ce, C);
 }
 
 // DecodeParams of a validated call and its plan (decode.hip).
