@@ -25,8 +25,14 @@
 //   softmax: each token-row group tr keeps its own online state (running max
 //        m, sum l, weighted value sum acc) per head, in log2 units, so the
 //        main loop needs no cross-row communication; the TPW states are
-//        merged once at the end with the exact max-rescaling merge.
-//   PV:  acc[h][slice] += p * V-slice, all in registers.
+//        merged once at the end with the exact max-rescaling merge. With
+//        GT >= 2 heads per wave the softmax is spread over lanes (lane dc
+//        owns head dc % GT: one exp per token and lane instead of GT; the
+//        probabilities reach the other lanes of the quad by DPP) and the
+//        running maximum is raised lazily (only past a 2^16 margin).
+//   PV:  acc[h][slice] += p * V-slice, all in registers; with GT >= 2 and
+//        bf16 outputs, two tokens at a time on v_dot2_f32_bf16 (the
+//        probabilities rounded to bf16, the values widened exactly).
 // Split: each partition writes (m, l, acc) in fp32 to the workspace and a
 //   second, small kernel (paged_decode_merge_kernel) combines them with the
 //   exact max-rescaling merge. The kernel boundary makes the states visible
@@ -36,6 +42,8 @@
 // Bound: HBM. Algorithmic bytes = context rows x 2 (K and V) x Hkv x D x e.
 
 #pragma once
+
+#include <type_traits>
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -113,11 +121,19 @@ __device__ __forceinline__ void store_new_rows(const DecodeParams& p, int64_t fi
   }
 }
 
-// 16-byte streaming load of pool data: every K/V byte is read once per call,
-// so the loads carry the nontemporal hint and do not displace reusable lines.
+// 16-byte load of pool data. Every K/V byte is read once per call, so the
+// loads carry the nontemporal hint and do not displace reusable lines --
+// except when a head's row is shorter than a 128-byte line (E4M3, head_dim
+// 64): the other half of each line belongs to the neighbouring KV head,
+// which a sibling wave of the same workgroup reads moments later, and a
+// plain load keeps it in L2 for that read (measured: 7% faster there, 1-8%
+// slower everywhere else).
+template <bool NT>
 __device__ __forceinline__ uint4 stream_load(const char* ptr) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
+  u32x4 v;
+  if constexpr (NT) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
+  else v = *reinterpret_cast<const u32x4*>(ptr);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -329,6 +345,89 @@ __device__ __forceinline__ void apply_v_scale(const DecodeParams& p, int kvh, fl
   }
 }
 
+// Waves serving GT >= 2 query heads spread the softmax over lanes: lane
+// (dc, tr) owns head dc % GT of its token rows, so each logit's exp is taken
+// once per GT lanes instead of in every lane, and the probabilities reach
+// the other lanes of the quad by DPP.
+//
+// The value v of the lane owning head H, among the GT consecutive lanes
+// that share this lane's rows (quad_perm broadcast within each quad).
+template <int GT, int H>
+__device__ __forceinline__ uint32_t from_head_owner(uint32_t v) {
+  static_assert(GT == 2 || GT == 4, "heads per wave");
+  constexpr int CTRL = GT == 4 ? H * 0x55 : (H | (H << 2) | ((2 + H) << 4) | ((2 + H) << 6));
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int GT, int H>
+__device__ __forceinline__ float from_head_owner(float v) {
+  return __builtin_bit_cast(float, from_head_owner<GT, H>(__builtin_bit_cast(uint32_t, v)));
+}
+// This lane's own entry of t[GT] (head myh = dc % GT), chosen with bitwise
+// selects on lane masks: written as a conditional, the choice becomes a
+// dynamically indexed private array, whose scratch reads wait on every
+// outstanding global load.
+__device__ __forceinline__ float bit_select(uint32_t mask, float if_set, float if_clear) {
+  const uint32_t a = __builtin_bit_cast(uint32_t, if_set), b = __builtin_bit_cast(uint32_t, if_clear);
+  return __builtin_bit_cast(float, (a & mask) | (b & ~mask));
+}
+template <int GT>
+__device__ __forceinline__ float own_head(const float (&t)[GT], int myh) {
+  const uint32_t m0 = 0u - (uint32_t)(myh & 1);
+  if constexpr (GT == 2) {
+    return bit_select(m0, t[1], t[0]);
+  } else {
+    const uint32_t m1 = 0u - (uint32_t)((myh >> 1) & 1);
+    return bit_select(m1, bit_select(m0, t[3], t[2]), bit_select(m0, t[1], t[0]));
+  }
+}
+template <int GT, typename F>
+__device__ __forceinline__ void for_heads(F&& f) {
+  f(std::integral_constant<int, 0>{});
+  f(std::integral_constant<int, 1>{});
+  if constexpr (GT == 4) {
+    f(std::integral_constant<int, 2>{});
+    f(std::integral_constant<int, 3>{});
+  }
+}
+
+// Lazy rescale of the spread softmax (log2 units): the running maximum is
+// raised, and the accumulators rescaled, only when a logit exceeds it by
+// more than this, so probabilities stay below 2^16 (exact range for bf16 and
+// fp32, and a row sum of up to 2^16 per key cannot overflow fp32).
+constexpr float DECODE_RESCALE_SLACK = 16.0f;
+
+// acc[h][*] += p_u[h] v_u + p_u1[h] v_u1 for the EPL elements of two tokens'
+// 16-byte V slices, with the probabilities of both tokens packed as bf16
+// pairs (pp[h]: low half token u) and the values widened exactly to bf16,
+// paired across the two tokens by v_perm, one v_dot2_f32_bf16 per element.
+template <typename KT, int GT, int EPL>
+__device__ __forceinline__ void pv_token_pair(const uint4& vu, const uint4& vu1, const uint32_t (&pp)[GT],
+                                              float (&acc)[GT][EPL]) {
+  const uint32_t a[4] = {vu.x, vu.y, vu.z, vu.w};
+  const uint32_t b[4] = {vu1.x, vu1.y, vu1.z, vu1.w};
+  constexpr uint32_t LO = 0x05040100u, HI = 0x07060302u;  // (a.lo16, b.lo16), (a.hi16, b.hi16)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (sizeof(KT) == 1) {  // 4 E4M3 codes per dword
+      const uint32_t a01 = e4m3x2_to_bf16x2<false>(a[i]), a23 = e4m3x2_to_bf16x2<true>(a[i]);
+      const uint32_t b01 = e4m3x2_to_bf16x2<false>(b[i]), b23 = e4m3x2_to_bf16x2<true>(b[i]);
+      const uint32_t e[4] = {__builtin_amdgcn_perm(b01, a01, LO), __builtin_amdgcn_perm(b01, a01, HI),
+                             __builtin_amdgcn_perm(b23, a23, LO), __builtin_amdgcn_perm(b23, a23, HI)};
+#pragma unroll
+      for (int h = 0; h < GT; ++h)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[h][4 * i + k] = dot2_bf16(pp[h], e[k], acc[h][4 * i + k]);
+    } else {  // 2 bf16 per dword
+      const uint32_t lo = __builtin_amdgcn_perm(b[i], a[i], LO), hi = __builtin_amdgcn_perm(b[i], a[i], HI);
+#pragma unroll
+      for (int h = 0; h < GT; ++h) {
+        acc[h][2 * i] = dot2_bf16(pp[h], lo, acc[h][2 * i]);
+        acc[h][2 * i + 1] = dot2_bf16(pp[h], hi, acc[h][2 * i + 1]);
+      }
+    }
+  }
+}
+
 // Stream tokens [tok_begin, tok_end) of sequence seq (KV head kvh) through
 // the online softmax of st. UNIFORM_BLOCK: every chunk lies inside one block
 // (block_size >= CT and tok_begin a multiple of CT), so one table lookup per
@@ -353,6 +452,7 @@ __device__ __forceinline__ void attend_range(const DecodeParams& p, int seq, int
   constexpr int LPT = D / EPL;    // lanes per token row of one head
   constexpr int TPW = 64 / LPT;   // token rows per wave-wide load
   constexpr int CT = U * TPW;     // tokens per chunk
+  constexpr bool NT = D * E >= 128;  // whole lines per head row: streaming hint
   const int dc = lane % LPT;
   const int tr = lane / LPT;
   const int bs_log2 = p.bs_log2;
@@ -360,6 +460,19 @@ __device__ __forceinline__ void attend_range(const DecodeParams& p, int seq, int
   const int row_bytes = p.row_bytes;
   const int lane_off = kvh * D * E + dc * 16;
   const int32_t* bt = p.block_tables + (int64_t)seq * p.max_blocks_per_seq;
+
+  // Spread softmax (GT >= 2): this lane's head, its running maximum and sum.
+  // bf16 outputs take the V product on v_dot2 with the probabilities rounded
+  // to bf16 (the row sum adds the same rounded values); fp32 outputs keep
+  // fp32 probabilities and FMAs.
+  constexpr bool SPREAD = GT >= 2;
+  constexpr bool PV_BF16 = SPREAD && sizeof(T) == 2;
+  const int myh = dc % GT;
+  float mm = 0.0f, ll = 0.0f;
+  if constexpr (SPREAD) {
+    mm = own_head<GT>(st.m, myh);
+    ll = own_head<GT>(st.l, myh);
+  }
 
   // Block-table window: lane i holds the physical id of block wbase + i.
   const int last_blk = (tok_end - 1) >> bs_log2;
@@ -403,47 +516,104 @@ __device__ __forceinline__ void attend_range(const DecodeParams& p, int seq, int
     }
     uint4 kr[U], vr[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) kr[u] = stream_load(p.k_cache + off[u]);
+    for (int u = 0; u < U; ++u) kr[u] = stream_load<NT>(p.k_cache + off[u]);
 #pragma unroll
-    for (int u = 0; u < U; ++u) vr[u] = stream_load(p.v_cache + off[u]);
+    for (int u = 0; u < U; ++u) vr[u] = stream_load<NT>(p.v_cache + off[u]);
     __builtin_amdgcn_sched_barrier(0);
 
-    float s[U][GT];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int h = 0; h < GT; ++h) s[u][h] = group_sum<LPT>(qv[h].dot(kr[u]));
-
-#pragma unroll
-    for (int h = 0; h < GT; ++h) {
-      float cm = NEG_BIG;
+    if constexpr (SPREAD) {
+      float sc[U];
+      float cm = -INFINITY;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        s[u][h] = valid[u] ? s[u][h] * sm : -INFINITY;
-        cm = fmaxf(cm, s[u][h]);
-      }
-      const float mn = fmaxf(st.m[h], cm);
-      const float alpha = fast_exp2(st.m[h] - mn);
-      st.m[h] = mn;
-      st.l[h] *= alpha;
+        float t[GT];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) st.acc[h][e] *= alpha;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        s[u][h] = fast_exp2(s[u][h] - mn);
-        st.l[h] += s[u][h];
+        for (int h = 0; h < GT; ++h) t[h] = group_sum<LPT>(qv[h].dot(kr[u]));
+        // branch-free (a conditional here becomes a branch per token)
+        sc[u] = bit_select(0u - (uint32_t)valid[u], own_head<GT>(t, myh) * sm, -INFINITY);
+        cm = fmaxf(cm, sc[u]);
       }
-    }
+      if (__any(cm > mm + DECODE_RESCALE_SLACK)) {  // raise the maximum (wave-uniform)
+        const float mn = fmaxf(mm, cm);
+        const float alpha = fast_exp2(mm - mn);
+        mm = mn;
+        ll *= alpha;
+        for_heads<GT>([&](auto H) {
+          const float a = from_head_owner<GT, H.value>(alpha);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) st.acc[H.value][e] *= a;
+        });
+      }
+      if constexpr (PV_BF16) {
+        static_assert(U % 2 == 0, "token pairs");
+#pragma unroll
+        for (int u = 0; u < U; u += 2) {
+          const uint32_t mine = pack2_bf16(fast_exp2(sc[u] - mm), fast_exp2(sc[u + 1] - mm));
+          ll = dot2_bf16(mine, 0x3F803F80u, ll);  // + both rounded probabilities
+          uint32_t pp[GT];
+          for_heads<GT>([&](auto H) { pp[H.value] = from_head_owner<GT, H.value>(mine); });
+          pv_token_pair<KT, GT, EPL>(vr[u], vr[u + 1], pp, st.acc);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const float pu = fast_exp2(sc[u] - mm);
+          ll += pu;
+          float ph[GT];
+          for_heads<GT>([&](auto H) { ph[H.value] = from_head_owner<GT, H.value>(pu); });
+          float vf[EPL];
+          widen_slice<KT, EPL>(vr[u], vf);
+#pragma unroll
+          for (int h = 0; h < GT; ++h)
+#pragma unroll
+            for (int e = 0; e < EPL; ++e) st.acc[h][e] = fmaf(ph[h], vf[e], st.acc[h][e]);
+        }
+      }
+    } else {
+      float s[U][GT];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int h = 0; h < GT; ++h) s[u][h] = group_sum<LPT>(qv[h].dot(kr[u]));
 
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float vf[EPL];
-      widen_slice<KT, EPL>(vr[u], vf);
+      for (int h = 0; h < GT; ++h) {
+        float cm = NEG_BIG;
 #pragma unroll
-      for (int h = 0; h < GT; ++h)
+        for (int u = 0; u < U; ++u) {
+          s[u][h] = valid[u] ? s[u][h] * sm : -INFINITY;
+          cm = fmaxf(cm, s[u][h]);
+        }
+        const float mn = fmaxf(st.m[h], cm);
+        const float alpha = fast_exp2(st.m[h] - mn);
+        st.m[h] = mn;
+        st.l[h] *= alpha;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) st.acc[h][e] = fmaf(s[u][h], vf[e], st.acc[h][e]);
+        for (int e = 0; e < EPL; ++e) st.acc[h][e] *= alpha;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          s[u][h] = fast_exp2(s[u][h] - mn);
+          st.l[h] += s[u][h];
+        }
+      }
+
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        float vf[EPL];
+        widen_slice<KT, EPL>(vr[u], vf);
+#pragma unroll
+        for (int h = 0; h < GT; ++h)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) st.acc[h][e] = fmaf(s[u][h], vf[e], st.acc[h][e]);
+      }
     }
+  }
+
+  if constexpr (SPREAD) {  // every lane gets every head's (m, l) back
+    for_heads<GT>([&](auto H) {
+      st.m[H.value] = from_head_owner<GT, H.value>(mm);
+      st.l[H.value] = from_head_owner<GT, H.value>(ll);
+    });
   }
 
   if constexpr (FUSABLE) {
@@ -827,7 +997,7 @@ __device__ __forceinline__ void balanced_body(const DecodeParams& p, int wg, int
 }
 
 template <typename T, typename KT, int D, int GT, int U, bool UNIFORM_BLOCK>
-__global__ __launch_bounds__(256, 2) void paged_decode_balanced_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256, DECODE_BAL_WAVES_PER_SIMD) void paged_decode_balanced_kernel(DecodeParams p) {
   balanced_body<T, KT, D, GT, U, UNIFORM_BLOCK, BAL_MAX_SEQS>(p, blockIdx.x, gridDim.x);
 }
 

@@ -5,8 +5,8 @@ pa_prefill_chunk calls it combines.
 
 Bars: bf16 attention max-abs 2e-2, mean-abs 2e-3 against the fp64 oracle;
 bit-identical to pa_prefill_chunk on the chunk rows (same code, same work
-items), and to pa_decode's decode rows up to fp32 rounding (the mixed launch
-splits the decode contexts over fewer workers). Pools are NaN-poisoned
+items), and within a few bf16 ulps of pa_decode's decode rows (the mixed
+launch splits the decode contexts over fewer workers). Pools are NaN-poisoned
 outside every context.
 """
 
@@ -60,9 +60,11 @@ def test_mixed_variants(gpu, name):
 
 def test_mixed_equals_separate_calls(gpu):
     """The mixed launch gives pa_prefill_chunk's chunk rows bit for bit, and
-    pa_decode's (balanced split) decode rows up to the fp32 rounding of a
-    different worker split (at most a couple of bf16 units in the last
-    place)."""
+    pa_decode's (balanced split) decode rows up to the rounding of a
+    different worker split: the probabilities are rounded to bf16 relative
+    to a running maximum that depends on where a worker's range starts, so
+    the two agree to a few bf16 units in the last place (both are checked
+    against the oracle by the other tests)."""
     b = wl.make_batch(wl.spec(6, num_seqs=40, num_decode=36, decode_lens=("uniform", 1, 3000),
                               chunk=[512, 200, 37, 1]), device=gpu, poison=True)
     arrs = gs.device_arrays(b)
@@ -81,7 +83,7 @@ def test_mixed_equals_separate_calls(gpu):
     torch.cuda.synchronize()
     assert torch.equal(mixed[Bd:], pre[Bd:])
     diff = (mixed[:Bd].float() - dec.float()).abs()
-    bound = 2.0 ** -7 * dec.float().abs().clamp(min=2.0 ** -6)   # two bf16 half-ulps of relative size
+    bound = 2.0 ** -9 + 2.0 ** -6 * dec.float().abs()   # about 4 bf16 ulps
     assert bool(torch.isfinite(mixed[:Bd]).all()) and bool((diff <= bound).all()), float(diff.max())
 
 
