@@ -331,6 +331,10 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="also run a device copy of this many bytes (counter calibration)")
+    ap.add_argument("--only", choices=["decode", "prefill", "mixed"], default=None,
+                    help="profiling runs: one section (decode: the headline and the decode extras; "
+                         "prefill / mixed: that extra alone), so that kernels shared by sections "
+                         "are not pooled in a profile")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
@@ -341,6 +345,14 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     pa.load_library()
+    if args.only in ("prefill", "mixed"):
+        fn = bench_prefill if args.only == "prefill" else bench_mixed
+        log(f"{args.only} only")
+        r = fn(max(args.steps, 3), args.warmup, dev)
+        if args.copy_probe:
+            copy_probe(args.copy_probe, dev)
+        print(json.dumps({"section": args.only, **r}), flush=True)
+        return
 
     log(f"building workload {args.workload} x{args.rotations}")
     ds = DecodeSet(args.workload, args.rotations, dev)
@@ -419,12 +431,13 @@ def main():
                 logical_bytes_per_launch=int(np.mean(d.kv_bytes_logical)))
             del d
             torch.cuda.empty_cache()
-        log("extra block manager")
-        extra["block_manager"] = bench_block_manager()
-        log("extra prefill")
-        extra["prefill"] = bench_prefill(20, 3, dev)
-        log("extra mixed batch")
-        extra["mixed_batch"] = bench_mixed(20, 3, dev)
+        if args.only is None:
+            log("extra block manager")
+            extra["block_manager"] = bench_block_manager()
+            log("extra prefill")
+            extra["prefill"] = bench_prefill(20, 3, dev)
+            log("extra mixed batch")
+            extra["mixed_batch"] = bench_mixed(20, 3, dev)
         line["extra"] = extra
     if args.copy_probe:
         log(f"copy probe {args.copy_probe} bytes")

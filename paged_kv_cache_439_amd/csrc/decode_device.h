@@ -1017,12 +1017,12 @@ __global__ __launch_bounds__(256) void paged_decode_balanced_merge_kernel(Decode
   const int h0 = kvh * p.group + (unit - kvh * p.n_sub) * GT;
   const int dc = lane % LPT;
   const int tr = lane / LPT;
-  const int L = min(p.context_lens[seq], p.max_context_len);
-  if (L <= 0) {
+  // one round of loads: the chunk prefix sums (an empty context has none)
+  const int cb = p.ws_pfx[seq], ce = p.ws_pfx[seq + 1], C = p.ws_pfx[p.num_seqs];
+  if (cb == ce) {
     if (tr == 0) store_zeros<T, D, GT, EPL>(p, seq, h0, dc);
     return;
   }
-  const int cb = p.ws_pfx[seq], ce = p.ws_pfx[seq + 1], C = p.ws_pfx[p.num_seqs];
   const int W = p.workers;
   if (bal_worker_of(cb, C, W) == bal_worker_of(ce - 1, C, W)) return;  // written by one worker
   merge_pieces<T, D, GT, EPL, LPT>(p, seq, h0, dc, tr, cb, ce, C);

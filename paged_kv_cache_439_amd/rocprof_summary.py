@@ -25,7 +25,7 @@ import re
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 DECODE_SOURCES = [os.path.join(ROOT, "paged_kv_cache_439_amd", "csrc", f)
-                  for f in ("decode.hip", "pa_device.h")]
+                  for f in ("decode_device.h", "decode.hip", "pa_device.h")]
 
 
 def decode_source_hash():
@@ -92,7 +92,9 @@ def traffic(fetch_csv, write_csv, out_json, out_md, copy_bytes, cmd_fetch, cmd_w
     # fixed-slice split's main and merge kernels
     workloads = {}
     for k, v in kernels.items():
-        m = re.search(r"paged_decode(_balanced)?(_merge)?_kernel<unsigned short, (\d+), (\d+)", k)
+        # bf16 pools only (main kernels name the query and pool types, merge
+        # kernels the output type)
+        m = re.search(r"paged_decode(_balanced)?(_merge)?_kernel<unsigned short, (?:unsigned short, )?(\d+), (\d+)", k)
         if not m:
             continue
         wname = KERNEL_WORKLOAD.get((m.group(3), m.group(4)))
