@@ -153,6 +153,21 @@ def test_decode_fp8_variants(gpu, name):
         gs.decode_fp8_parity(b, P)
 
 
+@pytest.mark.parametrize("cfg,over", [
+    (5, dict(num_seqs=8, lens=("uniform", 1, 1500), max_context=1536)),
+    (3, dict(num_seqs=6, lens=("uniform", 1, 1200), max_context=1280, share=None)),
+    (2, dict(num_seqs=5, lens=("uniform", 1, 1500), max_context=1536)),
+])
+def test_decode_fp8_peaked_logits(gpu, cfg, over):
+    """Scale 1.0 and K scales 4x larger: log2-logits span about +-60, so the
+    lazily raised maximum moves many times along each context."""
+    for P in (0, -1):
+        b = wl.make_batch(wl.spec(cfg, kv="e4m3", scale=1.0, **over), device=gpu, poison=True)
+        b.k_scale *= 4.0
+        gs.say(f"decode e4m3 peaked cfg{cfg} P={P}")
+        gs.decode_fp8_parity(b, P)
+
+
 def test_decode_fp8_edge_lengths(gpu):
     """Lengths 1, one block, one partition, partition+1, a full table."""
     lens = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128]

@@ -120,6 +120,58 @@ def test_decode_variants(gpu, name):
         gs.decode_parity(b, P)
 
 
+def _grow_keys(b, factor=3.0):
+    """Scale every K row of each context by 1 + factor * j / L (j the position,
+    L the length), and the new row by 1 + factor, so that logits grow in
+    magnitude along the context and the running maximum keeps moving."""
+    bs = b.block_size
+    blocks, rows, scales = [], [], []
+    for i, L in enumerate(b.context_lens.tolist()):
+        for j in range(L - 1):
+            blocks.append(int(b.block_tables[i, j // bs]))
+            rows.append(j % bs)
+            scales.append(1.0 + factor * j / L)
+    dev = b.k_cache.device
+    bi = torch.tensor(blocks, device=dev)
+    ri = torch.tensor(rows, device=dev)
+    sc = torch.tensor(scales, device=dev, dtype=torch.float32)[:, None, None]
+    b.k_cache[bi, ri] = (b.k_cache[bi, ri].float() * sc).to(b.k_cache.dtype)
+    b.key = (b.key.float() * (1.0 + factor)).to(b.key.dtype)
+    return b
+
+
+PEAKED_DECODE = {
+    # scale 1.0 with D=128: log2-logits span about +-40, far past the 2^16
+    # margin of the lazily raised maximum, and keys grow along the context
+    "gqa4_scale1": (5, dict(num_seqs=10, lens=("uniform", 1, 1500), max_context=1536, scale=1.0)),
+    "gqa2_scale1": (3, dict(num_seqs=8, lens=("uniform", 1, 1200), max_context=1280, share=None,
+                            scale=1.0)),
+    "mha_scale1": (2, dict(num_seqs=6, lens=("uniform", 1, 1500), max_context=1536, scale=1.0)),
+    "gqa4_negative": (5, dict(num_seqs=6, lens=("uniform", 1, 900), max_context=1024, scale=-0.3)),
+    "f32_gqa4_scale1": (5, dict(dtype="f32", num_seqs=4, lens=("uniform", 1, 700), max_context=768,
+                                block_size=32, scale=1.0)),
+}
+
+
+# fp32 at scale 1.0: logits reach about 45 (natural units), where rounding a
+# 128-term fp32 dot product is already ~1e-5 of a logit, i.e. a relative
+# error of ~1e-5 in the probabilities; the kernels before and after the lazy
+# rescale give the same 1.4e-5. The fp32 bar of the workloads (1e-5 at scale
+# 1/sqrt(head_dim)) is therefore widened to 4e-5 for this stress case only.
+F32_PEAKED_MAX_ABS = 4e-5
+
+
+@pytest.mark.parametrize("name", sorted(PEAKED_DECODE))
+def test_decode_peaked_growing_logits(gpu, name, monkeypatch):
+    cfg, over = PEAKED_DECODE[name]
+    if over.get("dtype") == "f32":
+        monkeypatch.setattr(gs, "F32_MAX_ABS", F32_PEAKED_MAX_ABS)
+    for P in (0, 64, -1):
+        b = _grow_keys(wl.make_batch(wl.spec(cfg, **over), device=gpu, poison=True))
+        gs.say(f"decode peaked {name} P={P}")
+        gs.decode_parity(b, P)
+
+
 def test_decode_edge_lengths(gpu):
     """Lengths 1, one block, one partition, partition+1, full table."""
     bs, P = 16, 32
