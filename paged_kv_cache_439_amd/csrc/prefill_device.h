@@ -77,6 +77,19 @@ struct PrefillParams {
 // order (row blocks from the end of the chunk first).
 constexpr int RANK_MAX_ITEMS = 512;
 
+// Maximum over lanes l, l^16, l^32, l^48 (the four lanes that hold one row
+// of an MFMA C tile): the cross-half and cross-row swaps of gfx950, with
+// copies of x in both operands, leave x of lane l and of its partner lane
+// in the two results.
+__device__ __forceinline__ float max_over_row_groups(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  x = __builtin_elementwise_maximum(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t v = __float_as_uint(x);
+  const auto b = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return __builtin_elementwise_maximum(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Lazy-rescale threshold in log2 units: probabilities stay below 2^32. bf16
 // and fp32 keep their relative precision at that size, and a row sum of at
 // most 2^32 per key cannot overflow fp32, so after the first tile a rescale
@@ -299,6 +312,16 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int bx, int
           s[c2][hf][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[ks], qreg[1][ks], s[c2][hf][1], 0, 0, 0);
         }
       }
+    // Schedule: the K operands of two (c2, hf) groups, then each group's
+    // MFMAs followed by the next group's operand reads, so that the reads
+    // run one group ahead and at most two groups' operands are live.
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * KS, 0);  // LDS reads
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * KS, 0);  // MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, KS, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * KS, 0);
 
     // ---- online softmax per query row (lane row lrow of tile rt) ----
     // Logits are s * sl2 with sl2 >= 0 (a negative scale was moved into the
@@ -326,19 +349,21 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int bx, int
               }
               mx = __builtin_elementwise_maximum(mx, v);
             }
-        mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 16));
-        mx = __builtin_elementwise_maximum(mx, __shfl_xor(mx, 32));
+        mx = max_over_row_groups(mx);
         mt[rt] = (MASKED && mx == -INFINITY) ? -INFINITY : mx * sl2;
       }
       // Raise a row's running maximum only when the tile's maximum exceeds it
-      // by more than the slack. The four lanes that hold a row agree on the
-      // decision; the branch is skipped when no lane needs it.
+      // by more than the slack. The wave takes the branch when any of its
+      // rows needs it; rows that keep their maximum scale by exp2(0) = 1
+      // exactly.
+      const bool raise0 = mt[0] > m[0] + RESCALE_SLACK;
+      const bool raise1 = mt[1] > m[1] + RESCALE_SLACK;
+      if (__builtin_amdgcn_ballot_w64(raise0 || raise1) != 0) {
 #pragma unroll
-      for (int rt = 0; rt < 2; ++rt) {
-        if (mt[rt] > m[rt] + RESCALE_SLACK) {
-          asm volatile("" ::: "memory");  // keep it a branch, not selects
-          const float alpha = fast_exp2(m[rt] - mt[rt]);
-          m[rt] = mt[rt];
+        for (int rt = 0; rt < 2; ++rt) {
+          const float nm = (rt == 0 ? raise0 : raise1) ? mt[rt] : m[rt];
+          const float alpha = fast_exp2(m[rt] - nm);
+          m[rt] = nm;
           lsum[rt] *= alpha;
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) o[dt][rt] *= alpha;
@@ -397,6 +422,15 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int bx, int
         o[dt][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[c2], pb[1][c2], o[dt][1], 0, 0, 0);
       }
     }
+    // Schedule: the V^T operands of two d tiles, then each d tile's MFMAs
+    // followed by the reads of the d tile two ahead.
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int g = 0; g < DT - 2; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
   };
 
   for (int kt0 = 0; kt0 < kv_end; kt0 += 2 * KT) {
