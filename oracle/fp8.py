@@ -1,5 +1,5 @@
-"""8-bit float (E4M3) KV cache: quantise on store, dequantise in decode (CPU
-oracle).
+"""8-bit float (E4M3) KV cache: quantise on store, dequantise in decode and
+chunked prefill (CPU oracle).
 
 TEST INFRASTRUCTURE ONLY -- imported by tests, the smoke check and the
 benchmark's CPU-baseline leg; never by the library.
@@ -22,7 +22,8 @@ Readings where the pages are silent:
     division is one IEEE float32 division and |x / scale_h| is first
     saturated at 448; the per-head scales are caller inputs;
   * decode reads element x back as value(code) * scale_h and attends in the
-    usual way (oracle.attention.attend) over those values.
+    usual way (oracle.attention.attend) over those values; chunked prefill
+    does the same for each row of a chunk over its causal prefix.
 """
 
 from __future__ import annotations
@@ -121,3 +122,50 @@ def decode_fp8(q, k_codes, v_codes, k_scale, v_scale, block_tables, context_lens
             g = h // group
             out[i, h] = oa.attend(qf[i, h], kc[:, g, :], vc[:, g, :], scale)
     return out
+
+
+def prefill_fp8(q, k_codes, v_codes, k_scale, v_scale, block_tables, query_start_loc,
+                context_lens, scale, block_size, q_dtype, rows=None):
+    """Chunked causal prefill over an E4M3 cache: the chunked-prefill
+    definition (sequence i owns query rows query_start_loc[i] ..
+    query_start_loc[i+1]-1; row t of its chunk sits at position c_i + t with
+    c_i = context_lens[i] - n_i and attends to keys 0 .. c_i + t) over the
+    context read back as value(code) * scale_h for K and V.
+
+    q is [sum n_i][Hq][D] of q_dtype. Without rows: fp64 [sum n_i][Hq][D].
+    With rows, a list of (query row, head) pairs: fp64 [len(rows)][D] for
+    just those (sampled checks at sizes the full chunk is too slow for)."""
+    T, Hq, D = q.shape
+    Hkv = k_codes.shape[2]
+    group = Hq // Hkv
+    qsl = np.asarray(query_start_loc, dtype=np.int64)
+    qf = oa.widen(q, q_dtype)
+    wanted = {}
+    if rows is None:
+        for r in range(T):
+            for h in range(Hq):
+                wanted.setdefault(r, []).append(h)
+    else:
+        for r, h in rows:
+            wanted.setdefault(int(r), []).append(int(h))
+    result = {}
+    for i in range(len(context_lens)):
+        start, stop = int(qsl[i]), int(qsl[i + 1])
+        mine = [r for r in wanted if start <= r < stop]
+        if not mine:
+            continue
+        L = int(context_lens[i])
+        c = L - (stop - start)
+        kc = dequantize_rows(oa.gather_context(k_codes, block_tables[i], L, block_size), k_scale)
+        vc = dequantize_rows(oa.gather_context(v_codes, block_tables[i], L, block_size), v_scale)
+        for r in mine:
+            visible = c + (r - start) + 1
+            for h in wanted[r]:
+                g = h // group
+                result[(r, h)] = oa.attend(qf[r, h], kc[:visible, g, :], vc[:visible, g, :], scale)
+    if rows is None:
+        out = np.zeros((T, Hq, D), dtype=np.float64)
+        for (r, h), v in result.items():
+            out[r, h] = v
+        return out
+    return np.stack([result[(int(r), int(h))] for r, h in rows]) if rows else np.zeros((0, D))

@@ -599,6 +599,22 @@ def pin_fp8_store_layout():
     assert np.array_equal(k3, k4)
 
 
+def _e4m3_by_fields(c):
+    """E4M3 code values by hand from the format's fields (no NaN codes)."""
+    c = c.astype(np.int64)
+    e, m = (c >> 3) & 15, c & 7
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1 + m / 8.0) * np.exp2(e - 7.0))
+    return np.where(c & 0x80, -mag, mag)
+
+
+def _fp8_codes(rng, shape, moderate=False):
+    c = rng.integers(0, 0x7F, size=shape).astype(np.uint8) | rng.choice(
+        np.array([0, 0x80], dtype=np.uint8), size=shape)
+    if moderate:  # keep logits moderate
+        c = np.where((c & 0x7F) > 0x50, c & 0x87, c).astype(np.uint8)
+    return c
+
+
 def pin_fp8_decode_vs_sdpa():
     """E4M3 decode equals torch's attention over the contiguous rows read
     back as value(code) * scale (per KV head), the pool laid out block by
@@ -617,12 +633,7 @@ def pin_fp8_decode_vs_sdpa():
     ks, vs = np.array([0.5, 0.125]), np.array([2.0, 0.75])
     scale = 1.0 / math.sqrt(D)
     out = of8.decode_fp8(q, kp, vp, ks, vs, tables, np.array(lens), scale, bs, "f32")
-    # values by hand from the format's fields
-    def val(c):
-        c = c.astype(np.int64)
-        e, m = (c >> 3) & 15, c & 7
-        mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1 + m / 8.0) * np.exp2(e - 7.0))
-        return np.where(c & 0x80, -mag, mag)
+    val = _e4m3_by_fields
     G = Hq // Hkv
     for i, L in enumerate(lens):
         k = np.repeat(val(kcodes[i]) * ks[None, :, None], G, axis=1).transpose(1, 0, 2)
@@ -638,6 +649,80 @@ def pin_fp8_decode_vs_sdpa():
     assert np.max(np.abs(out_v[:, G:] - out[:, G:])) < 1e-12
 
 
+def _fp8_prefill_case(seed, cached, chunk, Hq=6, Hkv=2, D=16, bs=4):
+    rng = _rng(seed)
+    lens = [c + n for c, n in zip(cached, chunk)]
+    kcodes = [_fp8_codes(rng, (L, Hkv, D), moderate=True) for L in lens]
+    vcodes = [_fp8_codes(rng, (L, Hkv, D)) for L in lens]
+    nb = sum(math.ceil(L / bs) for L in lens) + 2
+    kp, tables = _paged_from_contiguous(kcodes, bs, nb, _rng(seed + 1), fill=0x7F)
+    vp, tables_v = _paged_from_contiguous(vcodes, bs, nb, _rng(seed + 1), fill=0x7F)
+    assert np.array_equal(tables, tables_v)
+    qsl = np.concatenate([[0], np.cumsum(chunk)]).astype(np.int64)
+    q = rng.standard_normal((int(qsl[-1]), Hq, D)).astype(np.float32)
+    ks, vs = rng.uniform(0.1, 2.0, Hkv), rng.uniform(0.1, 2.0, Hkv)
+    return dict(q=q, kp=kp, vp=vp, tables=tables, lens=np.array(lens), qsl=qsl, kcodes=kcodes,
+                vcodes=vcodes, ks=ks, vs=vs, bs=bs, scale=1.0 / math.sqrt(D), Hq=Hq, Hkv=Hkv,
+                cached=cached, chunk=chunk)
+
+
+def _prefill_fp8_of(c, **kw):
+    return of8.prefill_fp8(c["q"], c["kp"], c["vp"], c["ks"], c["vs"], c["tables"], c["qsl"],
+                           c["lens"], c["scale"], c["bs"], "f32", **kw)
+
+
+def pin_fp8_prefill_vs_sdpa():
+    """E4M3 chunked prefill equals torch's attention over the contiguous
+    rows read back (by hand, from the format's fields) as value(code) *
+    scale, with the causal mask aligned to the end of the context (row t
+    sees keys 0 .. c + t); with nothing cached it is torch's ordinary causal
+    attention."""
+    c = _fp8_prefill_case(45, cached=[0, 7, 10], chunk=[9, 5, 1])
+    out = _prefill_fp8_of(c)
+    G = c["Hq"] // c["Hkv"]
+    for i in range(3):
+        rows = slice(int(c["qsl"][i]), int(c["qsl"][i + 1]))
+        n, L = c["chunk"][i], int(c["lens"][i])
+        k = np.repeat(_e4m3_by_fields(c["kcodes"][i]) * c["ks"][None, :, None], G, axis=1)
+        v = np.repeat(_e4m3_by_fields(c["vcodes"][i]) * c["vs"][None, :, None], G, axis=1)
+        q = c["q"][rows].astype(np.float64).transpose(1, 0, 2)
+        mask = np.arange(L)[None, :] <= (L - n + np.arange(n))[:, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(np.ascontiguousarray(q))[None],
+            torch.from_numpy(np.ascontiguousarray(k.transpose(1, 0, 2)))[None],
+            torch.from_numpy(np.ascontiguousarray(v.transpose(1, 0, 2)))[None],
+            attn_mask=torch.from_numpy(mask), scale=c["scale"])[0].numpy().transpose(1, 0, 2)
+        assert np.max(np.abs(out[rows] - ref)) < 1e-12
+        if c["cached"][i] == 0:
+            causal = _sdpa(np.ascontiguousarray(q), np.ascontiguousarray(k.transpose(1, 0, 2)),
+                           np.ascontiguousarray(v.transpose(1, 0, 2)), c["scale"], causal=True)
+            assert np.max(np.abs(out[rows] - causal.transpose(1, 0, 2))) < 1e-12
+
+
+def pin_fp8_prefill_row_is_decode():
+    """E4M3 prefill row t of a sequence equals E4M3 decode of that row's
+    query over the first c + t + 1 tokens, bit for bit."""
+    c = _fp8_prefill_case(46, cached=[0, 6, 3], chunk=[4, 3, 7])
+    out = _prefill_fp8_of(c)
+    for i in range(3):
+        for t in range(c["chunk"][i]):
+            r = int(c["qsl"][i]) + t
+            one = of8.decode_fp8(c["q"][r:r + 1], c["kp"], c["vp"], c["ks"], c["vs"],
+                                 c["tables"][i:i + 1], np.array([c["cached"][i] + t + 1]),
+                                 c["scale"], c["bs"], "f32")
+            assert out[r].tobytes() == one[0].tobytes()
+
+
+def pin_fp8_prefill_rows_subset():
+    """The sampled-row form of E4M3 prefill returns the full form's values."""
+    c = _fp8_prefill_case(47, cached=[5, 2], chunk=[3, 6])
+    full = _prefill_fp8_of(c)
+    rng = _rng(48)
+    picks = [(int(r), int(h)) for r, h in zip(rng.integers(0, 9, 12), rng.integers(0, c["Hq"], 12))]
+    sub = _prefill_fp8_of(c, rows=picks)
+    assert np.stack([full[r, h] for r, h in picks]).tobytes() == sub.tobytes()
+
+
 ALL_PINS = [
     pin_store_bytes, pin_gather_inverts_layout, pin_decode_vs_sdpa, pin_decode_closed_forms,
     pin_decode_block_permutation, pin_decode_sharing_equals_duplication,
@@ -648,5 +733,6 @@ ALL_PINS = [
     pin_append_equals_allocate, pin_append_fills_are_shareable,
     pin_e4m3_closed_forms, pin_e4m3_table_vs_torch, pin_e4m3_quantize_vs_torch,
     pin_e4m3_round_trip_and_ties, pin_e4m3_saturation_and_specials, pin_e4m3_scale_divides,
-    pin_fp8_store_layout, pin_fp8_decode_vs_sdpa,
+    pin_fp8_store_layout, pin_fp8_decode_vs_sdpa, pin_fp8_prefill_vs_sdpa,
+    pin_fp8_prefill_row_is_decode, pin_fp8_prefill_rows_subset,
 ]

@@ -317,6 +317,26 @@ def _make_decode_fp8_scales_swapped():
     return decode
 
 
+def _make_prefill_fp8_scales_swapped():
+    orig = of8.prefill_fp8
+
+    def prefill(q, k_codes, v_codes, k_scale, v_scale, *rest, **kw):
+        return orig(q, k_codes, v_codes, v_scale, k_scale, *rest, **kw)
+    return prefill
+
+
+def _make_prefill_fp8_one_key_ahead():
+    """Causal alignment off by one: each row also sees the key after its own
+    position (the context counted one token longer than the chunk ends)."""
+    orig = of8.prefill_fp8
+
+    def prefill(q, k_codes, v_codes, k_scale, v_scale, block_tables, query_start_loc,
+                context_lens, *rest, **kw):
+        return orig(q, k_codes, v_codes, k_scale, v_scale, block_tables, query_start_loc,
+                    np.asarray(context_lens) + 1, *rest, **kw)
+    return prefill
+
+
 MUTANTS = {
     "attend_no_scale": (oa, "attend", _attend_no_scale),
     "attend_unnormalised": (oa, "attend", _attend_unnormalised),
@@ -351,6 +371,8 @@ MUTANTS = {
     "fp8_heads_reversed": (of8, "dequantize_rows", _dequantize_heads_reversed),
     "fp8_store_k_scale_for_v": (of8, "store_kvcache_fp8", None),
     "fp8_decode_scales_swapped": (of8, "decode_fp8", None),
+    "fp8_prefill_scales_swapped": (of8, "prefill_fp8", None),
+    "fp8_prefill_one_key_ahead": (of8, "prefill_fp8", None),
 }
 
 
@@ -377,6 +399,10 @@ def test_mutant_is_caught(name, monkeypatch):
         repl = _make_store_fp8_k_scale_for_v()
     elif name == "fp8_decode_scales_swapped":
         repl = _make_decode_fp8_scales_swapped()
+    elif name == "fp8_prefill_scales_swapped":
+        repl = _make_prefill_fp8_scales_swapped()
+    elif name == "fp8_prefill_one_key_ahead":
+        repl = _make_prefill_fp8_one_key_ahead()
     monkeypatch.setattr(module, attr, repl)
     caught = []
     for pin in pins.ALL_PINS + _extra_pins():
