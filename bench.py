@@ -20,7 +20,8 @@ recorded on the launch stream around each timed launch. `cpu_baseline` is the
 CPU oracle on a bounded sample of the same workload, single-threaded. `extra`
 reports the other workloads (GQA decode with shared prefix, GQA decode at 512
 sequences, each with the balanced split and with its fixed-slice split, the
-three decode workloads over 8-bit E4M3 pools, chunked prefill, and a
+three decode workloads over 8-bit E4M3 pools, chunked prefill over bf16 and
+over E4M3 pools, and a
 continuous batch of decode tokens and prefill chunks in one pa_mixed_batch
 call beside the same work as two calls) measured the same way.
 """
@@ -121,8 +122,10 @@ def time_decode(ds, steps, warmup):
     return secs, float(np.mean(kms)), float(np.mean(nbytes)), kms
 
 
-def bench_prefill(steps, warmup, device):
-    sp = wl.spec(4)
+def bench_prefill(steps, warmup, device, kv=None):
+    """The chunked-prefill workload: pa_prefill_chunk on bf16 pools, or
+    (kv="e4m3") pa_prefill_chunk_fp8 on E4M3 pools with per-head scales."""
+    sp = wl.spec(4, kv="e4m3") if kv == "e4m3" else wl.spec(4)
     b = wl.make_batch(sp, device=device)
     slots = torch.from_numpy(b.slot_mapping).to(device)
     tables = torch.from_numpy(b.block_tables).to(device)
@@ -134,11 +137,18 @@ def bench_prefill(steps, warmup, device):
         n = int(b.query_start_loc[i + 1] - b.query_start_loc[i])
         c = int(b.context_lens[i]) - n
         flops += 4 * b.head_dim * b.num_heads * (n * c + n * (n + 1) // 2)
-    pa.pa_store_kvcache(b.key, b.value, b.k_cache, b.v_cache, slots)
+    if kv == "e4m3":
+        pa.pa_store_kvcache_fp8(b.key, b.value, b.k_cache, b.v_cache, slots, b.k_scale, b.v_scale)
 
-    def run():
-        pa.pa_prefill_chunk(out, b.q, b.k_cache, b.v_cache, tables, qsl, lens, b.max_query_len,
-                            b.max_context_len, b.scale)
+        def run():
+            pa.pa_prefill_chunk_fp8(out, b.q, b.k_cache, b.v_cache, b.k_scale, b.v_scale, tables, qsl,
+                                    lens, b.max_query_len, b.max_context_len, b.scale)
+    else:
+        pa.pa_store_kvcache(b.key, b.value, b.k_cache, b.v_cache, slots)
+
+        def run():
+            pa.pa_prefill_chunk(out, b.q, b.k_cache, b.v_cache, tables, qsl, lens, b.max_query_len,
+                                b.max_context_len, b.scale)
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
@@ -153,7 +163,8 @@ def bench_prefill(steps, warmup, device):
     tflops = flops / (ms * 1e-3) / 1e12
     return dict(workload=sp["name"], kernel_ms=round(ms, 4), gflop=round(flops / 1e9, 2),
                 tflops=round(tflops, 1), frac_of_bf16_mfma_peak=round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-                tokens_per_s=round(int(b.query_start_loc[-1]) / (ms * 1e-3), 1))
+                tokens_per_s=round(int(b.query_start_loc[-1]) / (ms * 1e-3), 1),
+                kv_cache=kv or "bf16")
 
 
 def bench_mixed(steps, warmup, device):
@@ -349,6 +360,8 @@ def main():
         fn = bench_prefill if args.only == "prefill" else bench_mixed
         log(f"{args.only} only")
         r = fn(max(args.steps, 3), args.warmup, dev)
+        if args.only == "prefill":
+            r["e4m3"] = bench_prefill(max(args.steps, 3), args.warmup, dev, kv="e4m3")
         if args.copy_probe:
             copy_probe(args.copy_probe, dev)
         print(json.dumps({"section": args.only, **r}), flush=True)
@@ -436,6 +449,8 @@ def main():
             extra["block_manager"] = bench_block_manager()
             log("extra prefill")
             extra["prefill"] = bench_prefill(20, 3, dev)
+            log("extra prefill e4m3")
+            extra["prefill_e4m3"] = bench_prefill(20, 3, dev, kv="e4m3")
             log("extra mixed batch")
             extra["mixed_batch"] = bench_mixed(20, 3, dev)
         line["extra"] = extra

@@ -290,6 +290,30 @@ pa_status pa_decode_fp8(void* out, const void* q,
                         pa_dtype dtype, void* stream);
 
 /*
+ * pa_prefill_chunk_fp8 -- pa_prefill_chunk over E4M3 pools: the same
+ * chunked causal attention with K[g] = value(codes) * k_scale[g] and
+ * V[g] = value(codes) * v_scale[g]. The codes are widened exactly to bf16
+ * and the products run on bf16 MFMA with fp32 accumulation; the K scale
+ * multiplies the logit scale, the V scale the output. q and out are
+ * PA_BF16 [sum n_i][num_heads][head_dim]; scales as for pa_decode_fp8.
+ * Shapes, preconditions and errors as for pa_prefill_chunk, plus
+ * PA_ERR_INVALID_ARG for a null scale array and PA_ERR_UNSUPPORTED for one
+ * not 4-byte aligned.
+ */
+pa_status pa_prefill_chunk_fp8(void* out, const void* q,
+                               const void* k_cache, const void* v_cache,
+                               const float* k_scale, const float* v_scale,
+                               const int32_t* block_tables,
+                               const int32_t* query_start_loc,
+                               const int32_t* context_lens,
+                               int32_t num_seqs, int32_t num_heads,
+                               int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int32_t num_blocks,
+                               int32_t max_blocks_per_seq, int32_t max_query_len,
+                               int32_t max_context_len, float scale,
+                               pa_dtype dtype, void* stream);
+
+/*
  * Block manager (host only; no device memory, no HIP calls).
  *
  * Hands out the physical blocks of a pool of num_blocks blocks of block_size

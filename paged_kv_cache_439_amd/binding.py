@@ -57,6 +57,9 @@ _SIGNATURES = {
     "pa_decode_fp8": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                        _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                        _c_void_p, _size, ctypes.c_int, _c_void_p], ctypes.c_int),
+    "pa_prefill_chunk_fp8": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                              _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32,
+                              _i32, _i32, _i32, _f32, ctypes.c_int, _c_void_p], ctypes.c_int),
     "pa_mixed_batch": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                         _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                         _c_void_p, _size, ctypes.c_int, _c_void_p], ctypes.c_int),
@@ -305,6 +308,32 @@ def pa_prefill_chunk(out, q, k_cache, v_cache, block_tables, query_start_loc, co
                               block_tables.shape[1], int(max_query_len), int(max_context_len),
                               float(scale), _dtype_code(q), _stream(stream))
     _check("pa_prefill_chunk", st)
+
+
+def pa_prefill_chunk_fp8(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, query_start_loc,
+                         context_lens, max_query_len, max_context_len, scale, stream=None):
+    """Chunked causal prefill over E4M3 pools; out and q are bf16
+    [sum n_i][Hq][D], the pools uint8 codes, the scales fp32 [Hkv]."""
+    lib = load_library()
+    T, Hq, D = q.shape
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    _need(q.is_contiguous() and out.is_contiguous(), "q and out must be contiguous")
+    _e4m3_pools(k_cache, v_cache)
+    NB, bs, Hkv, D2 = k_cache.shape
+    _need(D2 == D, "head_dim of pools and q differ")
+    _scales(k_scale, v_scale, Hkv, q.device)
+    for name, t in (("block_tables", block_tables), ("query_start_loc", query_start_loc),
+                    ("context_lens", context_lens)):
+        _int32_device(t, name, q.device)
+    B = context_lens.numel()
+    _need(query_start_loc.numel() == B + 1, "query_start_loc must have B+1 entries")
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == B, "block_tables must be [B][max_blocks]")
+    st = lib.pa_prefill_chunk_fp8(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                  _ptr(v_scale), _ptr(block_tables), _ptr(query_start_loc),
+                                  _ptr(context_lens), B, Hq, Hkv, D, bs, NB, block_tables.shape[1],
+                                  int(max_query_len), int(max_context_len), float(scale),
+                                  _dtype_code(q), _stream(stream))
+    _check("pa_prefill_chunk_fp8", st)
 
 
 # ---------------------------------------------------------------------------

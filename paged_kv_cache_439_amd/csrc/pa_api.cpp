@@ -400,6 +400,41 @@ pa_status pa_prefill_chunk(void* out, const void* q, const void* k_cache, const 
   }
 }
 
+pa_status pa_prefill_chunk_fp8(void* out, const void* q, const void* k_cache,
+                               const void* v_cache, const float* k_scale, const float* v_scale,
+                               const int32_t* block_tables, const int32_t* query_start_loc,
+                               const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t num_blocks, int32_t max_blocks_per_seq,
+                               int32_t max_query_len, int32_t max_context_len, float scale,
+                               pa_dtype dtype, void* stream) {
+  try {
+    if (pa_status st = check_dtype(dtype)) return st;
+    if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "num_seqs=%d is negative", num_seqs);
+    if (num_seqs == 0) return ok();
+    if (pa_status st = check_varlen("pa_prefill_chunk_fp8", out, q, k_cache, v_cache, block_tables,
+                                    query_start_loc, context_lens, num_seqs, num_heads,
+                                    num_kv_heads, head_dim, block_size, num_blocks,
+                                    max_blocks_per_seq, max_query_len, max_context_len, scale, dtype))
+      return st;
+    if (!k_scale || !v_scale)
+      return fail(PA_ERR_INVALID_ARG, "pa_prefill_chunk_fp8: null k_scale or v_scale");
+    if (!aligned(k_scale, 4) || !aligned(v_scale, 4))
+      return fail(PA_ERR_UNSUPPORTED, "pa_prefill_chunk_fp8: k_scale/v_scale must be 4-byte aligned");
+    pa::PrefillArgs a{out, q, k_cache, v_cache, block_tables, query_start_loc, context_lens,
+                      num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                      max_blocks_per_seq, max_query_len, max_context_len, scale};
+    a.kv_e4m3 = true;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    const hipError_t err = pa::launch_prefill(a, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(PA_ERR_HIP, "prefill launch: %s", hipGetErrorString(err));
+    return ok();
+  } catch (...) {
+    return fail(PA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
 pa_status pa_mixed_batch(void* out, const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* block_tables, const int32_t* query_start_loc,
                          const int32_t* context_lens, int32_t num_seqs, int32_t num_decode_seqs,

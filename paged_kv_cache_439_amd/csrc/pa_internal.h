@@ -71,6 +71,9 @@ struct PrefillArgs {
   int32_t num_seqs, num_heads, num_kv_heads, head_dim;
   int32_t block_size, num_blocks, max_blocks_per_seq, max_query_len, max_context_len;
   float scale;
+  bool kv_e4m3 = false;             // pools hold E4M3 codes (pa_prefill_chunk_fp8)
+  const float* k_scale = nullptr;   // E4M3: per-KV-head scales
+  const float* v_scale = nullptr;
 };
 
 // partition_size value that selects the balanced split (pagedattn.h).

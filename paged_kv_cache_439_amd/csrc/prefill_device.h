@@ -70,6 +70,8 @@ struct PrefillParams {
   int32_t num_seqs;
   int32_t row_blocks;  // gridDim.z: ceil(max_query_len / ROWS)
   float scale_log2;
+  const float* k_scale;  // E4M3 pools: per-KV-head scales (else null)
+  const float* v_scale;
 };
 
 // Work items (sequence, row block) are ranked by their number of key tiles
@@ -106,6 +108,13 @@ __device__ __forceinline__ void load_lds16(const void* gptr, void* lds_base) {
                                    (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
 
+// Two E4M3 codes (byte pair HI of w: 0 = bytes 0-1, 1 = bytes 2-3) as two
+// bf16 (exact: every E4M3 value is a bf16 value).
+template <bool HI>
+__device__ __forceinline__ uint32_t widen_e4m3x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
 // Transposing LDS read of 4 bf16. Within each group of 16 lanes, lane i
 // receives element i % 4 of the 8 bytes addressed by lanes 4j + i/4,
 // j = 0..3: when lane s of the group points at row r0 + s/4, columns
@@ -118,9 +127,11 @@ __device__ __forceinline__ uint2 lds_read_tr4(const uint16_t* ptr) {
 
 // One workgroup's work: head group bx, sequence by, row block bz of the
 // grid (head groups x sequences x row blocks) that prefill_chunk_kernel
-// launches.
-template <int D, int HW>
+// launches. CT is the pools' element type: uint16_t (bf16) or uint8_t (E4M3
+// codes, read back as value(code) * scale of the KV head).
+template <int D, int HW, typename CT = uint16_t>
 __device__ __forceinline__ void prefill_body(const PrefillParams& p, int bx, int by, int bz) {
+  constexpr bool E4 = sizeof(CT) == 1;
   constexpr int RG = 4 / HW;      // row groups of 32 rows
   constexpr int ROWS = 32 * RG;   // query positions per workgroup
   constexpr int KT = 64;          // keys per tile
@@ -133,11 +144,15 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int bx, int
   constexpr int TBL = 512;        // block-table window (entries)
   static_assert(NIW >= 1, "tile shape");
 
-  // Two stages, each [0 = K, 1 = V][key][granule] with granules XOR-swizzled
-  // per key. Separate arrays, so the compiler can tell that a load into one
-  // stage does not feed the reads of the other.
+  // bf16 pools: two stages, each [0 = K, 1 = V][key][granule] with granules
+  // XOR-swizzled per key. Separate arrays, so the compiler can tell that a
+  // load into one stage does not feed the reads of the other.
+  // E4M3 pools: the codes of two tiles, f8[stage][K/V][key][D bytes] in pool
+  // order, and one bf16 stage (kv0) in the layout above that the workgroup
+  // widens each tile's codes into.
   __shared__ __attribute__((aligned(16))) uint16_t kv0[2][TE];
-  __shared__ __attribute__((aligned(16))) uint16_t kv1[2][TE];
+  __shared__ __attribute__((aligned(16))) uint16_t kv1[2][E4 ? 8 : TE];
+  __shared__ __attribute__((aligned(16))) uint8_t f8[E4 ? 2 : 1][2][E4 ? TE : 16];
   __shared__ int32_t tbl[TBL];
 
   const int tid = threadIdx.x;
@@ -199,8 +214,8 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int bx, int
   const int wave_last_key = c + wrow0 + 31;          // last key any row of this wave sees
   const int bs_log2 = p.bs_log2;
   const int bs_mask = (1 << bs_log2) - 1;
-  const int64_t row_bytes = (int64_t)p.num_kv_heads * D * 2;
-  const int64_t head_off = (int64_t)kvh * D * 2;
+  const int64_t row_bytes = (int64_t)p.num_kv_heads * D * (int)sizeof(CT);
+  const int64_t head_off = (int64_t)kvh * D * (int)sizeof(CT);
   const int32_t* bt = p.block_tables + (int64_t)seq * p.max_blocks_per_seq;
   const int nblk = (kv_end + bs_mask) >> bs_log2;
 
@@ -240,11 +255,61 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int bx, int
     }
   };
 
+  // E4M3: issue the global->LDS loads of tile kt0's codes into code stage
+  // st (a wave-wide 16-byte load covers KPL keys of D codes), clamped to the
+  // last needed key like the bf16 loads.
+  constexpr int CPR = D / 16;   // 16-byte code chunks per row of one head
+  constexpr int KPL = 64 / CPR;  // keys one wave-wide load covers
+  auto issue_codes = [&](int kt0, int st) {
+    constexpr int NIW8 = KT / KPL / 4;
+    const bool one_block = KT <= (1 << bs_log2);
+    const int phys0 = __builtin_amdgcn_readfirstlane(tbl[(kt0 >> bs_log2) - wb]);
+#pragma unroll
+    for (int i = 0; i < NIW8; ++i) {
+      const int ins = wave * NIW8 + i;
+      const int key = ins * KPL + lane / CPR;
+      const int j = min(kt0 + key, kv_end - 1);
+      const int phys = one_block ? phys0 : tbl[(j >> bs_log2) - wb];
+      const int64_t row =
+          (((int64_t)phys << bs_log2) + (j & bs_mask)) * row_bytes + head_off + (lane % CPR) * 16;
+      load_lds16(p.k_cache + row, &f8[st][0][ins * KPL * D]);
+      load_lds16(p.v_cache + row, &f8[st][1][ins * KPL * D]);
+    }
+  };
+  // E4M3: widen code stage st into the bf16 stage kv0; each thread takes
+  // 16 codes (two bf16 granules) of a key row per tensor and chunk.
+  auto widen_codes = [&](int st) {
+    constexpr int PER = KT * CPR / 256;
+#pragma unroll
+    for (int x = 0; x < PER; ++x) {
+      const int ci = tid + 256 * x;
+      const int key = ci / CPR, part = ci % CPR;
+#pragma unroll
+      for (int tsr = 0; tsr < 2; ++tsr) {
+        const uint4 w = *reinterpret_cast<const uint4*>(&f8[st][tsr][ci * 16]);
+        const uint4 lo = make_uint4(widen_e4m3x2<false>(w.x), widen_e4m3x2<true>(w.x),
+                                    widen_e4m3x2<false>(w.y), widen_e4m3x2<true>(w.y));
+        const uint4 hi = make_uint4(widen_e4m3x2<false>(w.z), widen_e4m3x2<true>(w.z),
+                                    widen_e4m3x2<false>(w.w), widen_e4m3x2<true>(w.w));
+        const int sw = tsr == 0 ? swz_k(key) : swz_v(key);
+        *reinterpret_cast<uint4*>(&kv0[tsr][key * D + (((2 * part) ^ sw) * 8)]) = lo;
+        *reinterpret_cast<uint4*>(&kv0[tsr][key * D + (((2 * part + 1) ^ sw) * 8)]) = hi;
+      }
+    }
+  };
+
   // Q^T B operands: lane holds Q[row lrow][32*ks + 8*qgrp .. +8] per tile.
   // A negative scale is applied as an (exact) sign flip of Q, so that the
-  // logit scale sl2 below is never negative.
-  const uint32_t qsign = p.scale_log2 < 0.0f ? 0x80008000u : 0u;
-  const float sl2 = fabsf(p.scale_log2);
+  // logit scale sl2 below is never negative. E4M3: the KV head's K scale
+  // multiplies the logit scale, its V scale the output.
+  float eff_scale = p.scale_log2;
+  float out_scale = 1.0f;
+  if constexpr (E4) {
+    eff_scale *= p.k_scale[kvh];
+    out_scale = p.v_scale[kvh];
+  }
+  const uint32_t qsign = eff_scale < 0.0f ? 0x80008000u : 0u;
+  const float sl2 = fabsf(eff_scale);
   bf16x8 qreg[2][KS];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
@@ -271,11 +336,16 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int bx, int
   }
 
   __syncthreads();  // table window visible
-  issue(0, kv0);
+  if constexpr (E4) issue_codes(0, 0);
+  else issue(0, kv0);
 
   // One 64-key tile: wait for its loads, start the next tile's loads into
   // the other stage, then compute from this stage.
-  auto step = [&](int kt0, uint16_t (&cur)[2][TE], uint16_t (&nxt_stage)[2][TE]) {
+  // One 64-key tile: wait for its loads, start the next tile's loads into
+  // the other stage, then compute from this stage. E4M3 pools: the loads are
+  // the codes (code stage st, the next tile's into st ^ 1), widened into kv0
+  // (cur) before the products.
+  auto step = [&](int kt0, uint16_t (&cur)[2][TE], uint16_t (&nxt_stage)[2][TE], int st) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of tile kt0 landed
     __syncthreads();  // the whole tile is in LDS; every wave is done with the other stage
     const int nxt = kt0 + KT;
@@ -286,7 +356,12 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int bx, int
         load_window(wb);
         __syncthreads();
       }
-      issue(nxt, nxt_stage);  // in flight while this tile is computed
+      if constexpr (E4) issue_codes(nxt, st ^ 1);
+      else issue(nxt, nxt_stage);  // in flight while this tile is computed
+    }
+    if constexpr (E4) {
+      widen_codes(st);
+      __syncthreads();  // kv0 holds tile kt0 as bf16
     }
     if (kt0 > wave_last_key) return;  // every key of this tile is masked for this wave
     const uint16_t* Kt = cur[0];
@@ -434,8 +509,13 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int bx, int
   };
 
   for (int kt0 = 0; kt0 < kv_end; kt0 += 2 * KT) {
-    step(kt0, kv0, kv1);
-    if (kt0 + KT < kv_end) step(kt0 + KT, kv1, kv0);
+    if constexpr (E4) {
+      step(kt0, kv0, kv0, 0);
+      if (kt0 + KT < kv_end) step(kt0 + KT, kv0, kv0, 1);
+    } else {
+      step(kt0, kv0, kv1, 0);
+      if (kt0 + KT < kv_end) step(kt0 + KT, kv1, kv0, 1);
+    }
   }
 
   // ---- normalise and write: lane holds O[row][16*dt + 4*qgrp + 0..3] ----
@@ -444,7 +524,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int bx, int
     float lt = lsum[rt];
     lt += __shfl_xor(lt, 16);
     lt += __shfl_xor(lt, 32);
-    const float inv = 1.0f / lt;
+    const float inv = out_scale / lt;
     const int t = wrow0 + rt * 16 + lrow;
     if (t < n) {
       uint16_t* dst = p.out + ((int64_t)(qs + t) * p.num_heads + head) * D + 4 * qgrp;
@@ -459,9 +539,9 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int bx, int
   }
 }
 
-template <int D, int HW>
+template <int D, int HW, typename CT>
 __global__ __launch_bounds__(256, 2) void prefill_chunk_kernel(PrefillParams p) {
-  prefill_body<D, HW>(p, blockIdx.x, blockIdx.y, blockIdx.z);
+  prefill_body<D, HW, CT>(p, blockIdx.x, blockIdx.y, blockIdx.z);
 }
 
 // Query heads one prefill workgroup serves (4 waves: HW heads x 4/HW row

@@ -244,3 +244,45 @@ def decode_fp8_parity(batch, partition_size, seqs=None):
     if seqs is not None:
         got = got[np.asarray(seqs)]
     return check_close(got, ref, batch.dtype, "decode e4m3")
+
+
+def gpu_prefill_fp8(batch, arrs=None):
+    arrs = arrs or device_arrays(batch)
+    out = torch.full_like(batch.q, float("nan"))
+    pa.pa_prefill_chunk_fp8(out, batch.q, batch.k_cache, batch.v_cache, batch.k_scale, batch.v_scale,
+                            arrs["tables"], arrs["qsl"], arrs["lens"], batch.max_query_len,
+                            batch.max_context_len, batch.scale)
+    return out
+
+
+def sample_prefill_rows(batch, total_rows, sample_rows, seed):
+    """sample_rows random (row, head) pairs plus every sequence's first and
+    last row (each with a random head)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    toks = rng.choice(total_rows, size=sample_rows, replace=False)
+    qsl = batch.query_start_loc
+    edge = [int(qsl[i]) for i in range(batch.num_seqs)] + [int(qsl[i + 1]) - 1 for i in range(batch.num_seqs)]
+    toks = sorted(set(toks.tolist()) | set(edge))
+    heads = rng.integers(0, batch.num_heads, size=len(toks))
+    return list(zip(toks, heads.tolist()))
+
+
+def prefill_fp8_parity(batch, sample_rows=None, seed=0):
+    """E4M3 store + chunked prefill on the GPU against the oracle's E4M3 store
+    and prefill on host copies of the same inputs (every row, or a sample)."""
+    import oracle.fp8 as of8
+    hb = wl.host_subset(batch)
+    ks, vs = scales_np(batch)
+    kp, vp = of8.store_kvcache_fp8(hb.k_cache, hb.v_cache, hb.key, hb.value, hb.slot_mapping,
+                                   batch.block_size, ks, vs, batch.dtype)
+    arrs = device_arrays(batch)
+    gpu_store_fp8(batch, arrs)
+    out = gpu_prefill_fp8(batch, arrs)
+    torch.cuda.synchronize()
+    got = as_f64(out)
+    rows = None if sample_rows is None else sample_prefill_rows(batch, got.shape[0], sample_rows, seed)
+    ref = of8.prefill_fp8(hb.q, kp, vp, ks, vs, hb.block_tables, hb.query_start_loc, hb.context_lens,
+                          batch.scale, batch.block_size, batch.dtype, rows=rows)
+    if rows is not None:
+        got = np.stack([got[t, h] for t, h in rows])
+    return check_close(got, ref, batch.dtype, "prefill e4m3" + ("" if rows is None else " (sampled)"))

@@ -183,6 +183,28 @@ def test_prefill_rejections(lib):
     assert _prefill(lib, D=256) == PA_ERR_UNSUPPORTED
 
 
+def _prefill_fp8(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, kscale=FAKE, vscale=FAKE, bt=FAKE, qsl=FAKE, cl=FAKE,
+             B=8, Hq=32, Hkv=8, D=128, bs=256, NB=200, MB=16, mq=512, maxL=4096, scale=0.088, dtype=1)
+    a.update(kw)
+    return lib.pa_prefill_chunk_fp8(a["out"], a["q"], a["k"], a["v"], a["kscale"], a["vscale"],
+                                    a["bt"], a["qsl"], a["cl"], a["B"], a["Hq"], a["Hkv"], a["D"],
+                                    a["bs"], a["NB"], a["MB"], a["mq"], a["maxL"], a["scale"],
+                                    a["dtype"], None)
+
+
+def test_prefill_fp8_rejections(lib):
+    assert _prefill_fp8(lib, B=0) == PA_OK
+    assert _prefill_fp8(lib, B=-1) == PA_ERR_INVALID_ARG
+    assert _prefill_fp8(lib, kscale=None) == PA_ERR_INVALID_ARG
+    assert "pa_prefill_chunk_fp8" in binding.load_library().pa_last_error().decode()
+    assert _prefill_fp8(lib, vscale=None) == PA_ERR_INVALID_ARG
+    assert _prefill_fp8(lib, kscale=ctypes.c_void_p(0x100002)) == PA_ERR_UNSUPPORTED
+    assert _prefill_fp8(lib, dtype=0) == PA_ERR_UNSUPPORTED            # bf16 q/out only
+    assert _prefill_fp8(lib, mq=5000) == PA_ERR_INVALID_ARG            # the prefill checks apply
+    assert _prefill_fp8(lib, D=96) == PA_ERR_UNSUPPORTED
+
+
 def _decode_fp8(lib, **kw):
     a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, kscale=FAKE, vscale=FAKE, bt=FAKE, cl=FAKE, B=4, Hq=8,
              Hkv=8, D=64, bs=16, NB=64, MB=7, maxL=100, scale=0.125, P=0, ws=None, wsb=0, dtype=1)

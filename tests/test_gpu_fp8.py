@@ -1,10 +1,10 @@
 """GPU parity of the E4M3 (8-bit float) KV cache: the HIP library through its
-C ABI against the CPU oracle's E4M3 store and decode.
+C ABI against the CPU oracle's E4M3 store, decode and chunked prefill.
 
 Bars: the quantising store is bit-exact over the whole pool (the codes are
 integers decided in fp32 on both sides: one IEEE division, nearest code,
-ties to even); decode over the codes meets the attention tolerances of the
-unquantised path (bf16 q/out: max-abs 2e-2, mean-abs 2e-3; fp32: 1e-5),
+ties to even); decode and prefill over the codes meet the attention
+tolerances of the unquantised path (bf16 q/out: max-abs 2e-2, mean-abs 2e-3; fp32: 1e-5),
 since the oracle attends over exactly the values the codes stand for. Pool
 rows outside every context hold the NaN code 0x7F.
 """
@@ -235,3 +235,62 @@ def test_decode_fp8_full_config_sampled(gpu, cfg, nseq):
     P = gs.full_config_parts(cfg, "balanced")
     gs.say(f"decode e4m3 full cfg{cfg} seqs={seqs} P={P}")
     gs.decode_fp8_parity(b, P, seqs=seqs)
+
+
+# ---------------------------------------------------------------------------
+# chunked prefill over E4M3 pools (pa_prefill_chunk_fp8), against the
+# oracle's E4M3 prefill after both sides' quantising stores
+
+FP8_PREFILL_VARIANTS = {
+    "gqa4_small": dict(num_seqs=3, cached=("uniform", 0, 700), chunk=[100, 257, 31], max_context=1024),
+    "cached_zero": dict(num_seqs=2, cached=("fixed", [0, 0]), chunk=[130, 64], max_context=256),
+    "mha_d64_bs16": dict(num_seqs=2, num_heads=8, num_kv_heads=8, head_dim=64, block_size=16,
+                         cached=("uniform", 0, 300), chunk=[77, 140], max_context=512),
+    "gqa2_bs64": dict(num_seqs=3, num_heads=16, num_kv_heads=8, block_size=64,
+                      cached=("uniform", 1, 400), chunk=[1, 65, 200], max_context=640),
+    "group3_d64": dict(num_seqs=2, num_heads=12, num_kv_heads=4, head_dim=64, block_size=128,
+                       cached=("uniform", 0, 500), chunk=[50, 129], max_context=768),
+    # 568 blocks of 8 tokens: more than the kernel's block-table window holds at once
+    "bs8_long_context": dict(num_seqs=2, num_heads=8, num_kv_heads=2, block_size=8,
+                             cached=("fixed", [4500, 70]), chunk=[40, 90], max_context=4608),
+    # scale 1: logits with std ~11, so the running maximum moves by large steps
+    "peaked_scores": dict(num_seqs=2, cached=("uniform", 0, 700), chunk=[100, 31], max_context=1024,
+                          scale=1.0),
+    # negative scale: the softmax favours the smallest dot products
+    "negative_scale": dict(num_seqs=2, num_heads=8, num_kv_heads=8, head_dim=64, block_size=32,
+                           cached=("uniform", 0, 300), chunk=[45, 70], max_context=512, scale=-0.125),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FP8_PREFILL_VARIANTS))
+def test_prefill_fp8_variants(gpu, name):
+    b = wl.make_batch(wl.spec(4, kv="e4m3", **FP8_PREFILL_VARIANTS[name]), device=gpu, poison=True)
+    gs.say(f"prefill e4m3 {name} lens={b.context_lens.tolist()} qsl={b.query_start_loc.tolist()}")
+    gs.prefill_fp8_parity(b)
+
+
+def test_prefill_fp8_full_config_sampled(gpu):
+    """The chunked-prefill workload (8 chunks of 512 over cached contexts of
+    up to 3584 tokens) on E4M3 pools, in the benchmark's launch form; 96
+    sampled rows plus each chunk's first and last."""
+    b = wl.make_batch(wl.spec(4, kv="e4m3"), device=gpu, poison=True)
+    gs.say(f"prefill e4m3 full lens={b.context_lens.tolist()}")
+    gs.prefill_fp8_parity(b, sample_rows=96, seed=4)
+
+
+def test_prefill_fp8_last_row_matches_decode_fp8(gpu):
+    """The last row of each chunk attends to the whole context, as E4M3
+    decode of that query does (both within the bf16 bar of each other)."""
+    b = wl.make_batch(wl.spec(4, kv="e4m3", num_seqs=4, cached=("uniform", 0, 900), chunk=64,
+                              max_context=1024), device=gpu)
+    arrs = gs.device_arrays(b)
+    gs.gpu_store_fp8(b, arrs)
+    pre = gs.gpu_prefill_fp8(b, arrs)
+    last = torch.from_numpy(b.query_start_loc[1:] - 1).long().to(gpu)
+    q_last = b.q.index_select(0, last).contiguous()
+    dec = torch.empty_like(q_last)
+    pa.pa_decode_fp8(dec, q_last, b.k_cache, b.v_cache, b.k_scale, b.v_scale, arrs["tables"],
+                     arrs["lens"], b.max_context_len, b.scale, 0, None)
+    torch.cuda.synchronize()
+    diff = (pre.index_select(0, last).float() - dec.float()).abs().max().item()
+    assert diff <= 2e-2
