@@ -20,10 +20,10 @@ recorded on the launch stream around each timed launch. `cpu_baseline` is the
 CPU oracle on a bounded sample of the same workload, single-threaded. `extra`
 reports the other workloads (GQA decode with shared prefix, GQA decode at 512
 sequences, each with the balanced split and with its fixed-slice split, the
-three decode workloads over 8-bit E4M3 pools, chunked prefill over bf16 and
-over E4M3 pools, and a
+three decode workloads over 8-bit E4M3 pools, chunked prefill, and a
 continuous batch of decode tokens and prefill chunks in one pa_mixed_batch
-call beside the same work as two calls) measured the same way.
+call beside the same work as two calls, the last two also over E4M3 pools)
+measured the same way.
 """
 
 from __future__ import annotations
@@ -167,18 +167,24 @@ def bench_prefill(steps, warmup, device, kv=None):
                 kv_cache=kv or "bf16")
 
 
-def bench_mixed(steps, warmup, device):
+def bench_mixed(steps, warmup, device, kv=None):
     """The continuous batch (decode tokens + prefill chunks): pa_mixed_batch
     against the same work as two calls (pa_decode on the decode tokens, then
-    pa_prefill_chunk on the chunks) and against each call alone."""
-    sp = wl.spec(6)
+    pa_prefill_chunk on the chunks) and against each call alone; with
+    kv="e4m3" the same over E4M3 pools (pa_mixed_batch_fp8, pa_decode_fp8,
+    pa_prefill_chunk_fp8)."""
+    e4 = kv == "e4m3"
+    sp = wl.spec(6, kv="e4m3") if e4 else wl.spec(6)
     b = wl.make_batch(sp, device=device)
     Bd = b.num_decode
     a = dict(slots=torch.from_numpy(b.slot_mapping).to(device),
              tables=torch.from_numpy(b.block_tables).to(device),
              qsl=torch.from_numpy(b.query_start_loc).to(device),
              lens=torch.from_numpy(b.context_lens).to(device))
-    pa.pa_store_kvcache(b.key, b.value, b.k_cache, b.v_cache, a["slots"])
+    if e4:
+        pa.pa_store_kvcache_fp8(b.key, b.value, b.k_cache, b.v_cache, a["slots"], b.k_scale, b.v_scale)
+    else:
+        pa.pa_store_kvcache(b.key, b.value, b.k_cache, b.v_cache, a["slots"])
     out = torch.empty_like(b.q)
     ws = pa.mixed_workspace(Bd, b.num_heads, b.num_kv_heads, b.head_dim, b.max_context_len, device)
     tab_d, len_d = a["tables"][:Bd].contiguous(), a["lens"][:Bd].contiguous()
@@ -187,16 +193,29 @@ def bench_mixed(steps, warmup, device):
     q_d, out_d = b.q[:Bd], out[:Bd]
 
     def mixed():
-        pa.pa_mixed_batch(out, b.q, b.k_cache, b.v_cache, a["tables"], a["qsl"], a["lens"], Bd,
-                          b.max_query_len, b.max_context_len, b.scale, ws)
+        if e4:
+            pa.pa_mixed_batch_fp8(out, b.q, b.k_cache, b.v_cache, b.k_scale, b.v_scale, a["tables"],
+                                  a["qsl"], a["lens"], Bd, b.max_query_len, b.max_context_len, b.scale,
+                                  ws)
+        else:
+            pa.pa_mixed_batch(out, b.q, b.k_cache, b.v_cache, a["tables"], a["qsl"], a["lens"], Bd,
+                              b.max_query_len, b.max_context_len, b.scale, ws)
 
     def decode_only():
-        pa.pa_decode(out_d, q_d, b.k_cache, b.v_cache, tab_d, len_d, b.max_context_len, b.scale,
-                     pa.PA_PARTITION_BALANCED, ws)
+        if e4:
+            pa.pa_decode_fp8(out_d, q_d, b.k_cache, b.v_cache, b.k_scale, b.v_scale, tab_d, len_d,
+                             b.max_context_len, b.scale, pa.PA_PARTITION_BALANCED, ws)
+        else:
+            pa.pa_decode(out_d, q_d, b.k_cache, b.v_cache, tab_d, len_d, b.max_context_len, b.scale,
+                         pa.PA_PARTITION_BALANCED, ws)
 
     def prefill_only():
-        pa.pa_prefill_chunk(out, b.q, b.k_cache, b.v_cache, tab_p, qsl_p, len_p, b.max_query_len,
-                            b.max_context_len, b.scale)
+        if e4:
+            pa.pa_prefill_chunk_fp8(out, b.q, b.k_cache, b.v_cache, b.k_scale, b.v_scale, tab_p, qsl_p,
+                                    len_p, b.max_query_len, b.max_context_len, b.scale)
+        else:
+            pa.pa_prefill_chunk(out, b.q, b.k_cache, b.v_cache, tab_p, qsl_p, len_p, b.max_query_len,
+                                b.max_context_len, b.scale)
 
     def separate():
         decode_only()
@@ -218,7 +237,7 @@ def bench_mixed(steps, warmup, device):
     ms = {name: timed(fn) for name, fn in (("mixed", mixed), ("separate", separate),
                                            ("decode_only", decode_only), ("prefill_only", prefill_only))}
     rows = int(b.query_start_loc[-1])
-    kv_dec = int(sum(int(L) for L in b.context_lens[:Bd])) * b.num_kv_heads * b.head_dim * 2 * 2
+    kv_dec = int(sum(int(L) for L in b.context_lens[:Bd])) * b.num_kv_heads * b.head_dim * 2 * (1 if e4 else 2)
     flops = 0
     for i in range(Bd, b.num_seqs):
         n = int(b.query_start_loc[i + 1] - b.query_start_loc[i])
@@ -229,7 +248,8 @@ def bench_mixed(steps, warmup, device):
                 decode_only_ms=round(ms["decode_only"], 4), prefill_only_ms=round(ms["prefill_only"], 4),
                 speedup_vs_separate=round(ms["separate"] / ms["mixed"], 3),
                 rows_per_s=round(rows / (ms["mixed"] * 1e-3), 1),
-                decode_kv_gb=round(kv_dec / 1e9, 3), prefill_gflop=round(flops / 1e9, 2))
+                decode_kv_gb=round(kv_dec / 1e9, 3), prefill_gflop=round(flops / 1e9, 2),
+                kv_cache=kv or "bf16")
 
 
 def measured_traffic(workload_name, split):
@@ -360,8 +380,7 @@ def main():
         fn = bench_prefill if args.only == "prefill" else bench_mixed
         log(f"{args.only} only")
         r = fn(max(args.steps, 3), args.warmup, dev)
-        if args.only == "prefill":
-            r["e4m3"] = bench_prefill(max(args.steps, 3), args.warmup, dev, kv="e4m3")
+        r["e4m3"] = fn(max(args.steps, 3), args.warmup, dev, kv="e4m3")
         if args.copy_probe:
             copy_probe(args.copy_probe, dev)
         print(json.dumps({"section": args.only, **r}), flush=True)
@@ -453,6 +472,8 @@ def main():
             extra["prefill_e4m3"] = bench_prefill(20, 3, dev, kv="e4m3")
             log("extra mixed batch")
             extra["mixed_batch"] = bench_mixed(20, 3, dev)
+            log("extra mixed batch e4m3")
+            extra["mixed_batch_e4m3"] = bench_mixed(20, 3, dev, kv="e4m3")
         line["extra"] = extra
     if args.copy_probe:
         log(f"copy probe {args.copy_probe} bytes")

@@ -314,6 +314,28 @@ pa_status pa_prefill_chunk_fp8(void* out, const void* q,
                                pa_dtype dtype, void* stream);
 
 /*
+ * pa_mixed_batch_fp8 -- pa_mixed_batch over E4M3 pools: the same batch
+ * layout and launch, its decode rows computed as pa_decode_fp8 computes them
+ * (balanced split) and its prefill chunks as pa_prefill_chunk_fp8 does.
+ * Scales as for pa_decode_fp8; workspace, shapes and errors as for
+ * pa_mixed_batch, plus PA_ERR_INVALID_ARG for a null scale array and
+ * PA_ERR_UNSUPPORTED for one not 4-byte aligned. PA_BF16 q/out only.
+ */
+pa_status pa_mixed_batch_fp8(void* out, const void* q,
+                             const void* k_cache, const void* v_cache,
+                             const float* k_scale, const float* v_scale,
+                             const int32_t* block_tables,
+                             const int32_t* query_start_loc,
+                             const int32_t* context_lens,
+                             int32_t num_seqs, int32_t num_decode_seqs,
+                             int32_t num_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size,
+                             int32_t num_blocks, int32_t max_blocks_per_seq,
+                             int32_t max_query_len, int32_t max_context_len,
+                             float scale, void* workspace, size_t workspace_bytes,
+                             pa_dtype dtype, void* stream);
+
+/*
  * Block manager (host only; no device memory, no HIP calls).
  *
  * Hands out the physical blocks of a pool of num_blocks blocks of block_size

@@ -63,6 +63,10 @@ _SIGNATURES = {
     "pa_mixed_batch": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                         _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                         _c_void_p, _size, ctypes.c_int, _c_void_p], ctypes.c_int),
+    "pa_mixed_batch_fp8": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                            _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32,
+                            _i32, _i32, _i32, _i32, _f32, _c_void_p, _size, ctypes.c_int,
+                            _c_void_p], ctypes.c_int),
     "pa_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "pa_last_error": ([], ctypes.c_char_p),
 }
@@ -489,3 +493,35 @@ def pa_mixed_batch(out, q, k_cache, v_cache, block_tables, query_start_loc, cont
                             D, bs, NB, block_tables.shape[1], int(max_query_len), int(max_context_len),
                             float(scale), ws_ptr, ws_bytes, _dtype_code(q), _stream(stream))
     _check("pa_mixed_batch", st)
+
+
+def pa_mixed_batch_fp8(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, query_start_loc,
+                       context_lens, num_decode_seqs, max_query_len, max_context_len, scale,
+                       workspace=None, stream=None):
+    """pa_mixed_batch over E4M3 pools (uint8 codes, fp32 per-head scales);
+    out and q are [T][Hq][D] bf16, the workspace as for pa_mixed_batch."""
+    lib = load_library()
+    T, Hq, D = q.shape
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    _need(q.is_contiguous() and out.is_contiguous(), "q and out must be contiguous")
+    _e4m3_pools(k_cache, v_cache)
+    NB, bs, Hkv, D2 = k_cache.shape
+    _need(D2 == D, "head_dim of pools and q differ")
+    _scales(k_scale, v_scale, Hkv, q.device)
+    for name, t in (("block_tables", block_tables), ("query_start_loc", query_start_loc),
+                    ("context_lens", context_lens)):
+        _int32_device(t, name, q.device)
+    B = context_lens.numel()
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == B, "block_tables must be [B][max_blocks]")
+    _need(query_start_loc.numel() == B + 1, "query_start_loc must have B+1 entries")
+    _need(0 <= num_decode_seqs <= B and num_decode_seqs <= T, "num_decode_seqs out of range")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _need(workspace.device == q.device and workspace.is_contiguous(), "bad workspace")
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    st = lib.pa_mixed_batch_fp8(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                _ptr(v_scale), _ptr(block_tables), _ptr(query_start_loc),
+                                _ptr(context_lens), B, int(num_decode_seqs), Hq, Hkv, D, bs, NB,
+                                block_tables.shape[1], int(max_query_len), int(max_context_len),
+                                float(scale), ws_ptr, ws_bytes, _dtype_code(q), _stream(stream))
+    _check("pa_mixed_batch_fp8", st)

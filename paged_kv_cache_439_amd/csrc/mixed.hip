@@ -56,8 +56,16 @@ struct MixedParams {
   int32_t fx, fy;   // prefill grid extents: head groups, sequences
 };
 
-// Workgroup k of the grid, in the order MIXED_ORDER selects.
-template <int D, int G, bool UNIFORM_BLOCK>
+// Loads in flight per lane of the decode workers for pools of element type
+// KT (bf16, or E4M3 codes).
+template <typename KT>
+constexpr int mixed_decode_u() {
+  return sizeof(KT) == 1 ? DECODE_U_BALANCED_E4M3 : DECODE_U_BALANCED;
+}
+
+// Workgroup k of the grid, in the order MIXED_ORDER selects. KT: the pools'
+// element type (uint16_t bf16, uint8_t E4M3 codes).
+template <int D, int G, bool UNIFORM_BLOCK, typename KT>
 __global__ __launch_bounds__(256, 2) void mixed_batch_kernel(MixedParams p) {
   const int k = blockIdx.x;
   bool prefill;
@@ -80,25 +88,39 @@ __global__ __launch_bounds__(256, 2) void mixed_batch_kernel(MixedParams p) {
   }
   if (prefill) {
     const int r = idx / p.fx;
-    prefill_body<D, G>(p.f, idx - r * p.fx, r % p.fy, r / p.fy);
+    prefill_body<D, G, KT>(p.f, idx - r * p.fx, r % p.fy, r / p.fy);
   } else {
-    balanced_body<uint16_t, uint16_t, D, G, DECODE_U_BALANCED, UNIFORM_BLOCK, MIXED_MAX_DECODE_SEQS>(
+    balanced_body<uint16_t, KT, D, G, mixed_decode_u<KT>(), UNIFORM_BLOCK, MIXED_MAX_DECODE_SEQS>(
         p.d, idx, p.nd);
   }
 }
 
-template <int D, int G>
+template <int D, int G, typename KT>
 static void launch_mixed_t(const MixedParams& prm, int32_t bs, hipStream_t stream) {
-  constexpr int TPW = 64 / (D * 2 / 16);
-  constexpr int CT = DECODE_U_BALANCED * TPW;
+  constexpr int TPW = 64 / (D * (int)sizeof(KT) / 16);
+  constexpr int CT = mixed_decode_u<KT>() * TPW;
   const dim3 grid((unsigned)(prm.np + prm.nd));
   if (bs >= CT)
-    hipLaunchKernelGGL((mixed_batch_kernel<D, G, true>), grid, dim3(256), 0, stream, prm);
+    hipLaunchKernelGGL((mixed_batch_kernel<D, G, true, KT>), grid, dim3(256), 0, stream, prm);
   else
-    hipLaunchKernelGGL((mixed_batch_kernel<D, G, false>), grid, dim3(256), 0, stream, prm);
+    hipLaunchKernelGGL((mixed_batch_kernel<D, G, false, KT>), grid, dim3(256), 0, stream, prm);
   hipLaunchKernelGGL((paged_decode_balanced_merge_kernel<uint16_t, D, G>),
                      dim3((unsigned)prm.d.num_seqs, (unsigned)((prm.d.units + 3) / 4)), dim3(256), 0,
                      stream, prm.d);
+}
+
+template <typename KT>
+static void launch_mixed_kt(const MixedParams& prm, const PrefillArgs& a, int32_t G,
+                            hipStream_t stream) {
+  if (a.head_dim == 64) {
+    if (G == 4) launch_mixed_t<64, 4, KT>(prm, a.block_size, stream);
+    else if (G == 2) launch_mixed_t<64, 2, KT>(prm, a.block_size, stream);
+    else launch_mixed_t<64, 1, KT>(prm, a.block_size, stream);
+  } else {
+    if (G == 4) launch_mixed_t<128, 4, KT>(prm, a.block_size, stream);
+    else if (G == 2) launch_mixed_t<128, 2, KT>(prm, a.block_size, stream);
+    else launch_mixed_t<128, 1, KT>(prm, a.block_size, stream);
+  }
 }
 
 hipError_t launch_mixed(const PrefillArgs& a, int32_t num_decode, void* workspace,
@@ -124,6 +146,9 @@ hipError_t launch_mixed(const PrefillArgs& a, int32_t num_decode, void* workspac
   da.partition_size = PA_PARTITION_BALANCED_VALUE;
   da.workspace = workspace;
   da.bf16 = true;
+  da.kv_e4m3 = a.kv_e4m3;
+  da.k_scale = a.k_scale;
+  da.v_scale = a.v_scale;
   DecodePlan plan = plan_decode(Bd, a.num_heads, a.num_kv_heads, a.head_dim, a.max_context_len,
                                 PA_PARTITION_BALANCED_VALUE);
   if (Bp == 0) return launch_decode(da, plan, stream);
@@ -149,15 +174,8 @@ hipError_t launch_mixed(const PrefillArgs& a, int32_t num_decode, void* workspac
   prm.fy = Bp;
   prm.np = prm.fx * Bp * prm.f.row_blocks;
   prm.nd = (int32_t)(((int64_t)plan.workers * plan.units + 3) / 4);
-  if (a.head_dim == 64) {
-    if (G == 4) launch_mixed_t<64, 4>(prm, a.block_size, stream);
-    else if (G == 2) launch_mixed_t<64, 2>(prm, a.block_size, stream);
-    else launch_mixed_t<64, 1>(prm, a.block_size, stream);
-  } else {
-    if (G == 4) launch_mixed_t<128, 4>(prm, a.block_size, stream);
-    else if (G == 2) launch_mixed_t<128, 2>(prm, a.block_size, stream);
-    else launch_mixed_t<128, 1>(prm, a.block_size, stream);
-  }
+  if (a.kv_e4m3) launch_mixed_kt<uint8_t>(prm, a, G, stream);
+  else launch_mixed_kt<uint16_t>(prm, a, G, stream);
   return hipGetLastError();
 }
 

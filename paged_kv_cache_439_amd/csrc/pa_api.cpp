@@ -435,6 +435,63 @@ pa_status pa_prefill_chunk_fp8(void* out, const void* q, const void* k_cache,
   }
 }
 
+namespace {
+
+pa_status mixed_impl(const char* fn, void* out, const void* q, const void* k_cache,
+                     const void* v_cache, const int32_t* block_tables,
+                     const int32_t* query_start_loc, const int32_t* context_lens, int32_t num_seqs,
+                     int32_t num_decode_seqs, int32_t num_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                     int32_t max_blocks_per_seq, int32_t max_query_len, int32_t max_context_len,
+                     float scale, void* workspace, size_t workspace_bytes, pa_dtype dtype,
+                     void* stream, const E4M3Scales* e4m3) {
+  if (pa_status st = check_dtype(dtype)) return st;
+  if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_seqs=%d is negative", fn, num_seqs);
+  if (num_seqs == 0) return ok();
+  if (num_decode_seqs < 0 || num_decode_seqs > num_seqs)
+    return fail(PA_ERR_INVALID_ARG, "%s: num_decode_seqs=%d not in [0, num_seqs=%d]", fn,
+                num_decode_seqs, num_seqs);
+  if (num_decode_seqs > 2048)
+    return fail(PA_ERR_UNSUPPORTED, "%s: at most 2048 decode sequences (got %d)", fn,
+                num_decode_seqs);
+  if (pa_status st = check_varlen(fn, out, q, k_cache, v_cache, block_tables, query_start_loc,
+                                  context_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                                  block_size, num_blocks, max_blocks_per_seq, max_query_len,
+                                  max_context_len, scale, dtype))
+    return st;
+  if (e4m3) {
+    if (!e4m3->k_scale || !e4m3->v_scale)
+      return fail(PA_ERR_INVALID_ARG, "%s: null k_scale or v_scale", fn);
+    if (!aligned(e4m3->k_scale, 4) || !aligned(e4m3->v_scale, 4))
+      return fail(PA_ERR_UNSUPPORTED, "%s: k_scale/v_scale must be 4-byte aligned", fn);
+  }
+  if (num_decode_seqs > 0) {
+    const size_t need = pa::plan_decode(num_decode_seqs, num_heads, num_kv_heads, head_dim,
+                                        max_context_len, PA_PARTITION_BALANCED)
+                            .total_bytes;
+    if (!workspace) return fail(PA_ERR_WORKSPACE, "%s: a workspace of %zu bytes is needed", fn, need);
+    if (workspace_bytes < need)
+      return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes,
+                  need);
+    if (!aligned(workspace, 256))
+      return fail(PA_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
+  }
+  pa::PrefillArgs a{out, q, k_cache, v_cache, block_tables, query_start_loc, context_lens,
+                    num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                    max_blocks_per_seq, max_query_len, max_context_len, scale};
+  if (e4m3) {
+    a.kv_e4m3 = true;
+    a.k_scale = e4m3->k_scale;
+    a.v_scale = e4m3->v_scale;
+  }
+  const hipError_t err = pa::launch_mixed(a, num_decode_seqs, workspace,
+                                          static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(PA_ERR_HIP, "%s launch: %s", fn, hipGetErrorString(err));
+  return ok();
+}
+
+}  // namespace
+
 pa_status pa_mixed_batch(void* out, const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* block_tables, const int32_t* query_start_loc,
                          const int32_t* context_lens, int32_t num_seqs, int32_t num_decode_seqs,
@@ -443,39 +500,31 @@ pa_status pa_mixed_batch(void* out, const void* q, const void* k_cache, const vo
                          int32_t max_query_len, int32_t max_context_len, float scale,
                          void* workspace, size_t workspace_bytes, pa_dtype dtype, void* stream) {
   try {
-    if (pa_status st = check_dtype(dtype)) return st;
-    if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "pa_mixed_batch: num_seqs=%d is negative", num_seqs);
-    if (num_seqs == 0) return ok();
-    if (num_decode_seqs < 0 || num_decode_seqs > num_seqs)
-      return fail(PA_ERR_INVALID_ARG, "pa_mixed_batch: num_decode_seqs=%d not in [0, num_seqs=%d]",
-                  num_decode_seqs, num_seqs);
-    if (num_decode_seqs > 2048)
-      return fail(PA_ERR_UNSUPPORTED, "pa_mixed_batch: at most 2048 decode sequences (got %d)",
-                  num_decode_seqs);
-    if (pa_status st = check_varlen("pa_mixed_batch", out, q, k_cache, v_cache, block_tables,
-                                    query_start_loc, context_lens, num_seqs, num_heads,
-                                    num_kv_heads, head_dim, block_size, num_blocks,
-                                    max_blocks_per_seq, max_query_len, max_context_len, scale, dtype))
-      return st;
-    if (num_decode_seqs > 0) {
-      const size_t need = pa::plan_decode(num_decode_seqs, num_heads, num_kv_heads, head_dim,
-                                          max_context_len, PA_PARTITION_BALANCED)
-                              .total_bytes;
-      if (!workspace)
-        return fail(PA_ERR_WORKSPACE, "pa_mixed_batch: a workspace of %zu bytes is needed", need);
-      if (workspace_bytes < need)
-        return fail(PA_ERR_WORKSPACE, "pa_mixed_batch: workspace of %zu bytes, %zu needed",
-                    workspace_bytes, need);
-      if (!aligned(workspace, 256))
-        return fail(PA_ERR_WORKSPACE, "pa_mixed_batch: workspace must be 256-byte aligned");
-    }
-    pa::PrefillArgs a{out, q, k_cache, v_cache, block_tables, query_start_loc, context_lens,
-                      num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                      max_blocks_per_seq, max_query_len, max_context_len, scale};
-    const hipError_t err = pa::launch_mixed(a, num_decode_seqs, workspace,
-                                            static_cast<hipStream_t>(stream));
-    if (err != hipSuccess) return fail(PA_ERR_HIP, "pa_mixed_batch launch: %s", hipGetErrorString(err));
-    return ok();
+    return mixed_impl("pa_mixed_batch", out, q, k_cache, v_cache, block_tables, query_start_loc,
+                      context_lens, num_seqs, num_decode_seqs, num_heads, num_kv_heads, head_dim,
+                      block_size, num_blocks, max_blocks_per_seq, max_query_len, max_context_len,
+                      scale, workspace, workspace_bytes, dtype, stream, nullptr);
+  } catch (...) {
+    return fail(PA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+pa_status pa_mixed_batch_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
+                             const float* k_scale, const float* v_scale,
+                             const int32_t* block_tables, const int32_t* query_start_loc,
+                             const int32_t* context_lens, int32_t num_seqs,
+                             int32_t num_decode_seqs, int32_t num_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                             int32_t max_blocks_per_seq, int32_t max_query_len,
+                             int32_t max_context_len, float scale, void* workspace,
+                             size_t workspace_bytes, pa_dtype dtype, void* stream) {
+  try {
+    const E4M3Scales sc{k_scale, v_scale};
+    return mixed_impl("pa_mixed_batch_fp8", out, q, k_cache, v_cache, block_tables,
+                      query_start_loc, context_lens, num_seqs, num_decode_seqs, num_heads,
+                      num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                      max_query_len, max_context_len, scale, workspace, workspace_bytes, dtype,
+                      stream, &sc);
   } catch (...) {
     return fail(PA_ERR_HIP, "unexpected C++ exception");
   }

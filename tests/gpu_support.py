@@ -267,9 +267,23 @@ def sample_prefill_rows(batch, total_rows, sample_rows, seed):
     return list(zip(toks, heads.tolist()))
 
 
-def prefill_fp8_parity(batch, sample_rows=None, seed=0):
-    """E4M3 store + chunked prefill on the GPU against the oracle's E4M3 store
-    and prefill on host copies of the same inputs (every row, or a sample)."""
+def gpu_mixed_fp8(batch, arrs=None, workspace=None):
+    """pa_mixed_batch_fp8 over the batch (its first num_decode sequences decode)."""
+    arrs = arrs or device_arrays(batch)
+    if workspace is None:
+        workspace = pa.mixed_workspace(batch.num_decode, batch.num_heads, batch.num_kv_heads,
+                                       batch.head_dim, batch.max_context_len, batch.q.device)
+    out = torch.full_like(batch.q, float("nan"))
+    pa.pa_mixed_batch_fp8(out, batch.q, batch.k_cache, batch.v_cache, batch.k_scale, batch.v_scale,
+                          arrs["tables"], arrs["qsl"], arrs["lens"], batch.num_decode,
+                          batch.max_query_len, batch.max_context_len, batch.scale, workspace)
+    return out
+
+
+def prefill_fp8_parity(batch, sample_rows=None, seed=0, runner=None):
+    """E4M3 store + chunked prefill (pa_prefill_chunk_fp8, or runner) on the
+    GPU against the oracle's E4M3 store and prefill on host copies of the
+    same inputs (every row, or a sample)."""
     import oracle.fp8 as of8
     hb = wl.host_subset(batch)
     ks, vs = scales_np(batch)
@@ -277,7 +291,7 @@ def prefill_fp8_parity(batch, sample_rows=None, seed=0):
                                    batch.block_size, ks, vs, batch.dtype)
     arrs = device_arrays(batch)
     gpu_store_fp8(batch, arrs)
-    out = gpu_prefill_fp8(batch, arrs)
+    out = (runner or gpu_prefill_fp8)(batch, arrs)
     torch.cuda.synchronize()
     got = as_f64(out)
     rows = None if sample_rows is None else sample_prefill_rows(batch, got.shape[0], sample_rows, seed)

@@ -1,7 +1,7 @@
-"""GPU parity of pa_mixed_batch: a continuous batch of decode tokens and
-prefill chunks in one call, against the oracle's varlen prefill (a decode
-token is a chunk of one row) and against the separate pa_decode and
-pa_prefill_chunk calls it combines.
+"""GPU parity of pa_mixed_batch (and pa_mixed_batch_fp8 over E4M3 pools): a
+continuous batch of decode tokens and prefill chunks in one call, against the
+oracle's varlen prefill (a decode token is a chunk of one row) and against
+the separate decode and prefill calls it combines.
 
 Bars: bf16 attention max-abs 2e-2, mean-abs 2e-3 against the fp64 oracle;
 bit-identical to pa_prefill_chunk on the chunk rows (same code, same work
@@ -123,3 +123,52 @@ def test_mixed_full_config_sampled(gpu):
                           b.block_size, b.dtype, rows)
     sel = np.stack([got[t, h] for t, h in full_rows])
     gs.check_close(sel, ref, b.dtype, "mixed (sampled)")
+
+
+# ---------------------------------------------------------------------------
+# the same calls over E4M3 pools (pa_mixed_batch_fp8) against the oracle's
+# E4M3 prefill, whose decode tokens are chunks of one row
+
+FP8_MIXED_VARIANTS = ["gqa4_bs16", "mha_d64", "edges", "all_decode", "all_prefill"]
+
+
+@pytest.mark.parametrize("name", FP8_MIXED_VARIANTS)
+def test_mixed_fp8_variants(gpu, name):
+    b = wl.make_batch(wl.spec(6, kv="e4m3", **MIXED_VARIANTS[name]), device=gpu, poison=True)
+    gs.say(f"mixed e4m3 {name} decode={b.num_decode} lens={b.context_lens.tolist()} "
+           f"qsl={b.query_start_loc.tolist()}")
+    gs.prefill_fp8_parity(b, runner=gs.gpu_mixed_fp8)
+
+
+def test_mixed_fp8_equals_separate_calls(gpu):
+    """Over E4M3 pools the mixed launch gives pa_prefill_chunk_fp8's chunk rows
+    bit for bit and pa_decode_fp8's (balanced split) decode rows up to the
+    rounding of a different worker split, as over bf16 pools."""
+    b = wl.make_batch(wl.spec(6, kv="e4m3", num_seqs=40, num_decode=36, decode_lens=("uniform", 1, 3000),
+                              chunk=[512, 200, 37, 1]), device=gpu, poison=True)
+    arrs = gs.device_arrays(b)
+    gs.gpu_store_fp8(b, arrs)
+    mixed = gs.gpu_mixed_fp8(b, arrs)
+    Bd = b.num_decode
+    dec = torch.full_like(b.q[:Bd], float("nan"))
+    ws = pa.decode_workspace(Bd, b.num_heads, b.num_kv_heads, b.head_dim, b.max_context_len,
+                             pa.PA_PARTITION_BALANCED, gpu)
+    pa.pa_decode_fp8(dec, b.q[:Bd].contiguous(), b.k_cache, b.v_cache, b.k_scale, b.v_scale,
+                     arrs["tables"][:Bd].contiguous(), arrs["lens"][:Bd].contiguous(), b.max_context_len,
+                     b.scale, pa.PA_PARTITION_BALANCED, ws)
+    pre = torch.full_like(b.q, float("nan"))
+    pa.pa_prefill_chunk_fp8(pre, b.q, b.k_cache, b.v_cache, b.k_scale, b.v_scale,
+                            arrs["tables"][Bd:].contiguous(), arrs["qsl"][Bd:].contiguous(),
+                            arrs["lens"][Bd:].contiguous(), b.max_query_len, b.max_context_len, b.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(mixed[Bd:], pre[Bd:])
+    diff = (mixed[:Bd].float() - dec.float()).abs()
+    bound = 2.0 ** -9 + 2.0 ** -6 * dec.float().abs()   # about 4 bf16 ulps
+    assert bool(torch.isfinite(mixed[:Bd]).all()) and bool((diff <= bound).all()), float(diff.max())
+
+
+def test_mixed_fp8_full_config_sampled(gpu):
+    """The full continuous batch (256 decode tokens, 4 chunks of 512) over
+    E4M3 pools; 96 sampled rows plus every chunk's first and last."""
+    b = wl.make_batch(wl.spec(6, kv="e4m3"), device=gpu, poison=True)
+    gs.prefill_fp8_parity(b, sample_rows=96, seed=6, runner=gs.gpu_mixed_fp8)
