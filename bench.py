@@ -15,8 +15,10 @@ the steps cycle through them, so consecutive steps never find their K/V in the
 
 Prints ONE JSON line. `value` is decode tokens/s (sequences x steps / timed
 seconds). `roofline` covers the decode call (its main and merge kernels):
-algorithmic K+V bytes per launch over its average duration, from HIP events
-recorded on the launch stream around each timed launch. `cpu_baseline` is the
+algorithmic K+V bytes per launch over its average duration: one pair of HIP
+events on the launch stream around the timed run of launches, divided by the
+number of launches (an event pair around every launch would add GPU time to
+each step). `cpu_baseline` is the
 CPU oracle on a bounded sample of the same workload, single-threaded. `extra`
 reports the other workloads (GQA decode with shared prefix, GQA decode at 512
 sequences, each with the balanced split and with its fixed-slice split, the
@@ -79,18 +81,25 @@ class DecodeSet:
         self.kv_bytes = [b.kv_bytes(unique=True) for b, _ in self.batches]
         self.kv_bytes_logical = [b.kv_bytes(unique=False) for b, _ in self.batches]
 
-    def step(self, i, ev=None):
+    @property
+    def separate_store(self):
+        return self.e4m3 or not self.fused
+
+    def step(self, i):
         """Store the new rows and decode: one pa_store_decode call (its main
-        kernel writes the rows while it attends), or, with fused=False, the
-        two calls pa_store_kvcache and pa_decode."""
+        kernel writes the rows while it attends), or, with a separate store,
+        the store call then the decode call."""
         b, a = self.batches[i % len(self.batches)]
         if self.e4m3:
             pa.pa_store_kvcache_fp8(b.key, b.value, b.k_cache, b.v_cache, a["slots"], b.k_scale,
                                     b.v_scale)
         elif not self.fused:
             pa.pa_store_kvcache(b.key, b.value, b.k_cache, b.v_cache, a["slots"])
-        if ev is not None:
-            ev[0].record()
+        self.decode(i)
+
+    def decode(self, i):
+        """The decode call of step i (with a fused store, the whole step)."""
+        b, a = self.batches[i % len(self.batches)]
         if self.e4m3:
             pa.pa_decode_fp8(a["out"], b.q, b.k_cache, b.v_cache, b.k_scale, b.v_scale, a["tables"],
                              a["lens"], b.max_context_len, b.scale, self.P, self.ws)
@@ -100,26 +109,52 @@ class DecodeSet:
         else:
             pa.pa_decode(a["out"], b.q, b.k_cache, b.v_cache, a["tables"], a["lens"],
                          b.max_context_len, b.scale, self.P, self.ws)
-        if ev is not None:
-            ev[1].record()
 
 
 def time_decode(ds, steps, warmup):
-    """Returns (seconds for `steps` steps, mean decode-kernel ms, bytes/launch)."""
+    """Returns (seconds for `steps` steps by the host clock, ms per decode
+    call, mean bytes per launch).
+
+    The ms per call come from one pair of HIP events on the launch stream
+    around the timed run of calls, divided by the number of calls: with a
+    fused store the run is the timed steps themselves; with a separate store,
+    a second run of the decode calls alone. An event pair around every call
+    would add GPU time to every step (about 6 us per step on MI355X at b64)."""
     for i in range(warmup):
         ds.step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    e0.record()
     for i in range(steps):
-        ds.step(i, evs[i])
+        ds.step(i)
+    e1.record()
     torch.cuda.synchronize()
     secs = time.perf_counter() - t0
-    kms = [s.elapsed_time(e) for s, e in evs]
+    if ds.separate_store:
+        e0.record()
+        for i in range(steps):
+            ds.decode(i)
+        e1.record()
+        torch.cuda.synchronize()
+    kms = e0.elapsed_time(e1) / steps
     nbytes = [ds.kv_bytes[i % len(ds.batches)] for i in range(steps)]
-    return secs, float(np.mean(kms)), float(np.mean(nbytes)), kms
+    return secs, kms, float(np.mean(nbytes))
+
+
+def time_run(fn, steps, warmup):
+    """ms per call of fn: one pair of HIP events on the launch stream around
+    `steps` calls, after `warmup` untimed ones."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
 
 
 def bench_prefill(steps, warmup, device, kv=None):
@@ -149,17 +184,7 @@ def bench_prefill(steps, warmup, device, kv=None):
         def run():
             pa.pa_prefill_chunk(out, b.q, b.k_cache, b.v_cache, tables, qsl, lens, b.max_query_len,
                                 b.max_context_len, b.scale)
-    for _ in range(warmup):
-        run()
-    torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    for s, e in evs:
-        s.record()
-        run()
-        e.record()
-    torch.cuda.synchronize()
-    ms = float(np.mean([s.elapsed_time(e) for s, e in evs]))
+    ms = time_run(run, steps, warmup)
     tflops = flops / (ms * 1e-3) / 1e12
     return dict(workload=sp["name"], kernel_ms=round(ms, 4), gflop=round(flops / 1e9, 2),
                 tflops=round(tflops, 1), frac_of_bf16_mfma_peak=round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
@@ -221,20 +246,7 @@ def bench_mixed(steps, warmup, device, kv=None):
         decode_only()
         prefill_only()
 
-    def timed(fn):
-        for _ in range(warmup):
-            fn()
-        torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(steps)]
-        for st, en in evs:
-            st.record()
-            fn()
-            en.record()
-        torch.cuda.synchronize()
-        return float(np.mean([st.elapsed_time(en) for st, en in evs]))
-
-    ms = {name: timed(fn) for name, fn in (("mixed", mixed), ("separate", separate),
+    ms = {name: time_run(fn, steps, warmup) for name, fn in (("mixed", mixed), ("separate", separate),
                                            ("decode_only", decode_only), ("prefill_only", prefill_only))}
     rows = int(b.query_start_loc[-1])
     kv_dec = int(sum(int(L) for L in b.context_lens[:Bd])) * b.num_kv_heads * b.head_dim * 2 * (1 if e4 else 2)
@@ -390,7 +402,7 @@ def main():
     ds = DecodeSet(args.workload, args.rotations, dev)
     b0 = ds.batches[0][0]
     log("timing")
-    secs, kms, kbytes, _ = time_decode(ds, args.steps, args.warmup)
+    secs, kms, kbytes = time_decode(ds, args.steps, args.warmup)
     tokens = b0.num_seqs * args.steps
     achieved = kbytes / (kms * 1e-3) / 1e9
     line = {
@@ -435,7 +447,7 @@ def main():
                     continue
                 log(f"extra workload {cfg} partition_size={P} fused={fused}")
                 d = DecodeSet(cfg, 2, dev, partition=P, fused=fused)
-                s, ms, nb, _ = time_decode(d, 30, 5)
+                s, ms, nb = time_decode(d, 30, 5)
                 bb = d.batches[0][0]
                 key = d.spec["name"] + ("" if P == pa.PA_PARTITION_BALANCED else f"_fixed_p{P}")
                 key += "" if fused else "_separate_store"
@@ -452,7 +464,7 @@ def main():
             P = wl.CONFIGS[cfg]["partition_size"]
             log(f"extra workload {cfg} e4m3 partition_size={P}")
             d = DecodeSet(cfg, 2, dev, partition=P, kv="e4m3")
-            s, ms, nb, _ = time_decode(d, 30, 5)
+            s, ms, nb = time_decode(d, 30, 5)
             bb = d.batches[0][0]
             extra[d.spec["name"] + "_e4m3"] = dict(
                 tokens_per_s=round(bb.num_seqs * 30 / s, 1), kernel_ms=round(ms, 4),
