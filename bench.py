@@ -63,7 +63,7 @@ class DecodeSet:
     def __init__(self, cfg, rotations, device, partition=None, fused=True, kv=None):
         self.spec = wl.spec(cfg) if kv is None else wl.spec(cfg, kv=kv)
         self.e4m3 = kv == "e4m3"
-        self.fused = fused and not self.e4m3   # E4M3 pools: separate quantising store
+        self.fused = fused
         self.P = self.spec.get("partition_size", 0) if partition is None else partition
         self.batches = []
         for r in range(rotations):
@@ -83,24 +83,30 @@ class DecodeSet:
 
     @property
     def separate_store(self):
-        return self.e4m3 or not self.fused
+        return not self.fused
 
     def step(self, i):
         """Store the new rows and decode: one pa_store_decode call (its main
-        kernel writes the rows while it attends), or, with a separate store,
-        the store call then the decode call."""
+        kernel writes the rows while it attends; pa_store_decode_fp8 over
+        E4M3 pools), or, with a separate store, the store call then the
+        decode call."""
         b, a = self.batches[i % len(self.batches)]
-        if self.e4m3:
-            pa.pa_store_kvcache_fp8(b.key, b.value, b.k_cache, b.v_cache, a["slots"], b.k_scale,
-                                    b.v_scale)
-        elif not self.fused:
-            pa.pa_store_kvcache(b.key, b.value, b.k_cache, b.v_cache, a["slots"])
+        if not self.fused:
+            if self.e4m3:
+                pa.pa_store_kvcache_fp8(b.key, b.value, b.k_cache, b.v_cache, a["slots"], b.k_scale,
+                                        b.v_scale)
+            else:
+                pa.pa_store_kvcache(b.key, b.value, b.k_cache, b.v_cache, a["slots"])
         self.decode(i)
 
     def decode(self, i):
         """The decode call of step i (with a fused store, the whole step)."""
         b, a = self.batches[i % len(self.batches)]
-        if self.e4m3:
+        if self.e4m3 and self.fused:
+            pa.pa_store_decode_fp8(a["out"], b.q, b.key, b.value, b.k_cache, b.v_cache, b.k_scale,
+                                   b.v_scale, a["slots"], a["tables"], a["lens"], b.max_context_len,
+                                   b.scale, self.P, self.ws)
+        elif self.e4m3:
             pa.pa_decode_fp8(a["out"], b.q, b.k_cache, b.v_cache, b.k_scale, b.v_scale, a["tables"],
                              a["lens"], b.max_context_len, b.scale, self.P, self.ws)
         elif self.fused:
@@ -109,6 +115,13 @@ class DecodeSet:
         else:
             pa.pa_decode(a["out"], b.q, b.k_cache, b.v_cache, a["tables"], a["lens"],
                          b.max_context_len, b.scale, self.P, self.ws)
+
+
+# Untimed calls before each extra decode measurement. The first few dozen
+# calls over freshly built large batches run slower than later ones (an E4M3
+# batch of 512 sequences: about 420 us per call over the first 30, 364 us
+# after), so each leg warms up over this many calls first.
+LEG_WARMUP = 40
 
 
 def time_decode(ds, steps, warmup):
@@ -367,7 +380,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 5])
     ap.add_argument("--rotations", type=int, default=4)
     ap.add_argument("--no-extra", action="store_true")
@@ -447,7 +460,7 @@ def main():
                     continue
                 log(f"extra workload {cfg} partition_size={P} fused={fused}")
                 d = DecodeSet(cfg, 2, dev, partition=P, fused=fused)
-                s, ms, nb = time_decode(d, 30, 5)
+                s, ms, nb = time_decode(d, 30, LEG_WARMUP)
                 bb = d.batches[0][0]
                 key = d.spec["name"] + ("" if P == pa.PA_PARTITION_BALANCED else f"_fixed_p{P}")
                 key += "" if fused else "_separate_store"
@@ -463,8 +476,10 @@ def main():
         for cfg in (2, 3, 5):
             P = wl.CONFIGS[cfg]["partition_size"]
             log(f"extra workload {cfg} e4m3 partition_size={P}")
-            d = DecodeSet(cfg, 2, dev, partition=P, kv="e4m3")
-            s, ms, nb = time_decode(d, 30, 5)
+            d = DecodeSet(cfg, 2, dev, partition=P, kv="e4m3", fused=False)
+            s, ms, nb = time_decode(d, 30, LEG_WARMUP)
+            d.fused = True
+            s_f, ms_f, _ = time_decode(d, 30, LEG_WARMUP)
             bb = d.batches[0][0]
             extra[d.spec["name"] + "_e4m3"] = dict(
                 tokens_per_s=round(bb.num_seqs * 30 / s, 1), kernel_ms=round(ms, 4),
@@ -472,6 +487,8 @@ def main():
                 frac_of_hbm_peak=round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 bytes_per_launch=int(nb), split=split_name(P), partition_size=P, kv_cache="e4m3",
                 step="pa_store_kvcache_fp8 + pa_decode_fp8 (kernel_ms: pa_decode_fp8)",
+                fused_step="pa_store_decode_fp8, one launch (+ merge)",
+                fused_tokens_per_s=round(bb.num_seqs * 30 / s_f, 1), fused_call_ms=round(ms_f, 4),
                 logical_bytes_per_launch=int(np.mean(d.kv_bytes_logical)))
             del d
             torch.cuda.empty_cache()
@@ -479,13 +496,13 @@ def main():
             log("extra block manager")
             extra["block_manager"] = bench_block_manager()
             log("extra prefill")
-            extra["prefill"] = bench_prefill(20, 3, dev)
+            extra["prefill"] = bench_prefill(20, 10, dev)
             log("extra prefill e4m3")
-            extra["prefill_e4m3"] = bench_prefill(20, 3, dev, kv="e4m3")
+            extra["prefill_e4m3"] = bench_prefill(20, 10, dev, kv="e4m3")
             log("extra mixed batch")
-            extra["mixed_batch"] = bench_mixed(20, 3, dev)
+            extra["mixed_batch"] = bench_mixed(20, 10, dev)
             log("extra mixed batch e4m3")
-            extra["mixed_batch_e4m3"] = bench_mixed(20, 3, dev, kv="e4m3")
+            extra["mixed_batch_e4m3"] = bench_mixed(20, 10, dev, kv="e4m3")
         line["extra"] = extra
     if args.copy_probe:
         log(f"copy probe {args.copy_probe} bytes")

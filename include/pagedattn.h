@@ -276,7 +276,8 @@ pa_status pa_store_kvcache_fp8(const void* key, const void* value,
  * q and out are dtype (PA_BF16: q . K by bf16 dot products of q with the
  * exactly widened codes; PA_F32: fp32), accumulation fp32. Splits,
  * workspace (pa_decode_workspace_size with the same arguments), shapes and
- * errors as for pa_decode; there is no fused-store variant.
+ * errors as for pa_decode (pa_store_decode_fp8 below is the fused-store
+ * form).
  */
 pa_status pa_decode_fp8(void* out, const void* q,
                         const void* k_cache, const void* v_cache,
@@ -288,6 +289,31 @@ pa_status pa_decode_fp8(void* out, const void* q,
                         float scale, int32_t partition_size,
                         void* workspace, size_t workspace_bytes,
                         pa_dtype dtype, void* stream);
+
+/*
+ * pa_store_decode_fp8 -- pa_store_decode over E4M3 pools: in one launch,
+ * sequence i's new K/V row (key/value rows i, dtype elements, token strides
+ * in elements as for pa_store_kvcache_fp8) is quantised into slot
+ * slot_mapping[i] exactly as pa_store_kvcache_fp8 quantises it, and the
+ * sequence attends as pa_decode_fp8 does, its newest token taken as those
+ * same codes. A negative slot stores nothing and that sequence reads its
+ * newest token from the pool. Equal to pa_store_kvcache_fp8 followed by
+ * pa_decode_fp8 up to the rounding order of the newest token; arguments,
+ * workspace and errors as for those two calls, except that only PA_BF16 is
+ * implemented here (PA_F32 returns PA_ERR_UNSUPPORTED).
+ */
+pa_status pa_store_decode_fp8(void* out, const void* q, const void* key,
+                              const void* value, int64_t key_tok_stride,
+                              int64_t value_tok_stride, void* k_cache, void* v_cache,
+                              const float* k_scale, const float* v_scale,
+                              const int32_t* slot_mapping,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                              int32_t max_blocks_per_seq, int32_t max_context_len,
+                              float scale, int32_t partition_size,
+                              void* workspace, size_t workspace_bytes,
+                              pa_dtype dtype, void* stream);
 
 /*
  * pa_prefill_chunk_fp8 -- pa_prefill_chunk over E4M3 pools: the same

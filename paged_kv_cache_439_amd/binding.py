@@ -48,6 +48,10 @@ _SIGNATURES = {
     "pa_store_decode": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p,
                          _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                          _i32, _f32, _i32, _c_void_p, _size, ctypes.c_int, _c_void_p], ctypes.c_int),
+    "pa_store_decode_fp8": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _c_void_p,
+                             _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32,
+                             _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _c_void_p, _size,
+                             ctypes.c_int, _c_void_p], ctypes.c_int),
     "pa_prefill_chunk": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                           _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                           _f32, ctypes.c_int, _c_void_p], ctypes.c_int),
@@ -226,6 +230,42 @@ def pa_store_decode(out, q, key, value, k_cache, v_cache, slot_mapping, block_ta
                              int(max_context_len), float(scale), int(partition_size), ws_ptr, ws_bytes,
                              _dtype_code(q), _stream(stream))
     _check("pa_store_decode", st)
+
+
+def pa_store_decode_fp8(out, q, key, value, k_cache, v_cache, k_scale, v_scale, slot_mapping,
+                        block_tables, context_lens, max_context_len, scale, partition_size=0,
+                        workspace=None, stream=None):
+    """pa_store_decode over E4M3 pools: quantise each sequence's newest K/V
+    row [B][Hkv][D] (the dtype of q) into its slot and decode, in one launch."""
+    lib = load_library()
+    B, Hq, D = q.shape
+    _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
+    _need(q.is_contiguous() and out.is_contiguous(), "q and out must be contiguous")
+    _e4m3_pools(k_cache, v_cache)
+    NB, bs, Hkv, D2 = k_cache.shape
+    _need(D2 == D, "head_dim of pools and q differ")
+    _scales(k_scale, v_scale, Hkv, q.device)
+    _need(key.shape == value.shape == (B, Hkv, D), "key/value must be [B][Hkv][D]")
+    for t in (key, value):
+        _need(t.stride(2) == 1 and t.stride(1) == D, "key/value rows must be dense [Hkv][D]")
+        _need(t.dtype == q.dtype, "key/value must have the dtype of q")
+    for name, t in (("slot_mapping", slot_mapping), ("block_tables", block_tables),
+                    ("context_lens", context_lens)):
+        _int32_device(t, name, q.device)
+    _need(slot_mapping.numel() == B, "slot_mapping must have B entries")
+    _need(block_tables.dim() == 2 and block_tables.shape[0] == B, "block_tables must be [B][max_blocks]")
+    _need(context_lens.numel() == B, "context_lens must have B entries")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _need(workspace.device == q.device and workspace.is_contiguous(), "bad workspace")
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    st = lib.pa_store_decode_fp8(_ptr(out), _ptr(q), _ptr(key), _ptr(value), key.stride(0),
+                                 value.stride(0), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
+                                 _ptr(v_scale), _ptr(slot_mapping), _ptr(block_tables),
+                                 _ptr(context_lens), B, Hq, Hkv, D, bs, NB, block_tables.shape[1],
+                                 int(max_context_len), float(scale), int(partition_size), ws_ptr,
+                                 ws_bytes, _dtype_code(q), _stream(stream))
+    _check("pa_store_decode_fp8", st)
 
 
 def _e4m3_pools(k_cache, v_cache):

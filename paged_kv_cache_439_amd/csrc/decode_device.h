@@ -94,6 +94,14 @@ struct DecodeParams {
   const float* v_scale;
 };
 
+// Fused store + decode is built for pools in the query type and for E4M3
+// pools with bf16 queries (with fp32 queries the four-head E4M3 kernel
+// would spill registers inside its streaming loop).
+template <typename T, typename KT>
+constexpr bool fused_store_supported() {
+  return sizeof(KT) == sizeof(T) || sizeof(T) == 2;
+}
+
 // Fused store: does this call write sequence seq's newest row into the pool
 // (the same test pa_store_kvcache applies to a slot)?
 __device__ __forceinline__ bool stores_new_row(const DecodeParams& p, int seq) {
@@ -102,9 +110,13 @@ __device__ __forceinline__ bool stores_new_row(const DecodeParams& p, int seq) {
   return s >= 0 && (int64_t)s < p.num_slots;
 }
 
-// Fused store: copy the newest rows of sequences into the pools, 16 bytes
-// per thread: (sequence, granule) pairs first, first + stride, ... below end
-// (pairs numbered sequence-major, row_bytes / 16 granules per sequence).
+// Fused store: write the newest rows of sequences into the pools, 16 pool
+// bytes per thread: (sequence, granule) pairs first, first + stride, ...
+// below end (pairs numbered sequence-major, row_bytes / 16 granules per
+// sequence). Pools in the input type T take a copy; E4M3 pools (KT =
+// uint8_t) take the codes of 16 input elements of one head, quantised as
+// pa_store_kvcache_fp8 quantises them.
+template <typename T, typename KT>
 __device__ __forceinline__ void store_new_rows(const DecodeParams& p, int64_t first, int64_t stride,
                                                int64_t end) {
   const int32_t cpr = p.row_bytes / 16;
@@ -114,8 +126,16 @@ __device__ __forceinline__ void store_new_rows(const DecodeParams& p, int64_t fi
     const int32_t c = (int32_t)(idx - t * cpr);
     if (!stores_new_row(p, (int)t)) continue;
     const int64_t dst = (int64_t)p.slot_mapping[t] * p.row_bytes + (int64_t)c * 16;
-    const uint4 kv = *reinterpret_cast<const uint4*>(p.new_k + t * p.new_k_stride + (int64_t)c * 16);
-    const uint4 vv = *reinterpret_cast<const uint4*>(p.new_v + t * p.new_v_stride + (int64_t)c * 16);
+    uint4 kv, vv;
+    if constexpr (sizeof(KT) == 1) {
+      const int32_t h = c / (cpr / p.num_kv_heads);
+      const int64_t src = (int64_t)c * 16 * (int64_t)sizeof(T);
+      kv = quantize16<T>(p.new_k + t * p.new_k_stride + src, p.k_scale[h]);
+      vv = quantize16<T>(p.new_v + t * p.new_v_stride + src, p.v_scale[h]);
+    } else {
+      kv = *reinterpret_cast<const uint4*>(p.new_k + t * p.new_k_stride + (int64_t)c * 16);
+      vv = *reinterpret_cast<const uint4*>(p.new_v + t * p.new_v_stride + (int64_t)c * 16);
+    }
     *reinterpret_cast<uint4*>(const_cast<char*>(p.k_cache) + dst) = kv;
     *reinterpret_cast<uint4*>(const_cast<char*>(p.v_cache) + dst) = vv;
   }
@@ -442,8 +462,8 @@ __device__ __forceinline__ void attend_range(const DecodeParams& p, int seq, int
                                              WaveState<GT, 16 / ElemTraits<KT>::E>& st) {
   // With a fused store, the newest token (position L-1, L = the context
   // length) comes from the new row itself, not from the pool slot this same
-  // launch is writing.
-  constexpr bool FUSABLE = sizeof(KT) == sizeof(T);
+  // launch is writing (over E4M3 pools, as the codes the store writes).
+  constexpr bool FUSABLE = fused_store_supported<T, KT>();
   const bool new_row = FUSABLE && tok_end > tok_begin && stores_new_row(p, seq) &&
                        tok_end == min(p.context_lens[seq], p.max_context_len);
   if (new_row) --tok_end;
@@ -620,9 +640,16 @@ __device__ __forceinline__ void attend_range(const DecodeParams& p, int seq, int
     if (new_row) {
     // one more token, held by token-row group 0 (every lane loads the same
     // row so that the butterfly over the row's lanes stays uniform)
-    const int64_t off = (int64_t)kvh * D * E + dc * 16;
-    const uint4 kr = *reinterpret_cast<const uint4*>(p.new_k + seq * p.new_k_stride + off);
-    const uint4 vr = *reinterpret_cast<const uint4*>(p.new_v + seq * p.new_v_stride + off);
+    uint4 kr, vr;
+    if constexpr (E == 1) {  // E4M3 pools: this lane's 16 elements, quantised
+      const int64_t src = ((int64_t)kvh * D + dc * 16) * (int64_t)sizeof(T);
+      kr = quantize16<T>(p.new_k + seq * p.new_k_stride + src, p.k_scale[kvh]);
+      vr = quantize16<T>(p.new_v + seq * p.new_v_stride + src, p.v_scale[kvh]);
+    } else {
+      const int64_t off = (int64_t)kvh * D * E + dc * 16;
+      kr = *reinterpret_cast<const uint4*>(p.new_k + seq * p.new_k_stride + off);
+      vr = *reinterpret_cast<const uint4*>(p.new_v + seq * p.new_v_stride + off);
+    }
     float vf[EPL];
     widen_slice<KT, EPL>(vr, vf);
 #pragma unroll
@@ -689,10 +716,10 @@ __global__ __launch_bounds__(256, (decode_min_wgs<T, KT, GT>())) void paged_deco
   const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int seq = blockIdx.z;
   const int part = blockIdx.y;
-  if constexpr (sizeof(KT) == sizeof(T)) {
+  if constexpr (fused_store_supported<T, KT>()) {
     if (p.new_k != nullptr && blockIdx.x == 0 && part == 0) {  // fused store of seq's row
       const int64_t cpr = p.row_bytes / 16;
-      store_new_rows(p, (int64_t)seq * cpr + threadIdx.x, 256, (int64_t)(seq + 1) * cpr);
+      store_new_rows<T, KT>(p, (int64_t)seq * cpr + threadIdx.x, 256, (int64_t)(seq + 1) * cpr);
     }
   }
   if (unit >= p.units) return;
@@ -922,9 +949,9 @@ __device__ __forceinline__ void balanced_body(const DecodeParams& p, int wg, int
   constexpr int TPW = 64 / LPT;
   constexpr int CT = U * TPW;
   __shared__ int32_t pfx[MAXS + 1];
-  if constexpr (sizeof(KT) == sizeof(T)) {
-    if (p.new_k != nullptr)  // fused store: every thread of the grid copies a share of the rows
-      store_new_rows(p, (int64_t)wg * 256 + threadIdx.x, (int64_t)num_wgs * 256, INT64_MAX);
+  if constexpr (fused_store_supported<T, KT>()) {
+    if (p.new_k != nullptr)  // fused store: every thread of the grid writes a share of the rows
+      store_new_rows<T, KT>(p, (int64_t)wg * 256 + threadIdx.x, (int64_t)num_wgs * 256, INT64_MAX);
   }
   chunk_prefix<CT>(p, pfx);
   const int B = p.num_seqs;

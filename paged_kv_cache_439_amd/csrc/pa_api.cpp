@@ -205,7 +205,8 @@ pa_status decode_impl(const char* fn, void* out, const void* q, const void* k_ca
                   (long long)num_blocks * block_size);
   }
   if (e4m3) {
-    if (fused) return fail(PA_ERR_UNSUPPORTED, "%s: no fused store for E4M3 pools", fn);
+    if (fused && dtype != PA_BF16)
+      return fail(PA_ERR_UNSUPPORTED, "%s: the fused E4M3 store takes bf16 queries only", fn);
     if (!e4m3->k_scale || !e4m3->v_scale)
       return fail(PA_ERR_INVALID_ARG, "%s: null k_scale or v_scale", fn);
     if (!aligned(e4m3->k_scale, 4) || !aligned(e4m3->v_scale, 4))
@@ -275,6 +276,28 @@ pa_status pa_store_decode(void* out, const void* q, const void* key, const void*
                        num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                        max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
                        workspace_bytes, dtype, stream, &f, nullptr);
+  } catch (...) {
+    return fail(PA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+pa_status pa_store_decode_fp8(void* out, const void* q, const void* key, const void* value,
+                              int64_t key_tok_stride, int64_t value_tok_stride, void* k_cache,
+                              void* v_cache, const float* k_scale, const float* v_scale,
+                              const int32_t* slot_mapping, const int32_t* block_tables,
+                              const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                              int32_t num_blocks, int32_t max_blocks_per_seq,
+                              int32_t max_context_len, float scale, int32_t partition_size,
+                              void* workspace, size_t workspace_bytes, pa_dtype dtype,
+                              void* stream) {
+  try {
+    const Fusion f{key, value, key_tok_stride, value_tok_stride, slot_mapping};
+    const E4M3Scales sc{k_scale, v_scale};
+    return decode_impl("pa_store_decode_fp8", out, q, k_cache, v_cache, block_tables,
+                       context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                       num_blocks, max_blocks_per_seq, max_context_len, scale, partition_size,
+                       workspace, workspace_bytes, dtype, stream, &f, &sc);
   } catch (...) {
     return fail(PA_ERR_HIP, "unexpected C++ exception");
   }

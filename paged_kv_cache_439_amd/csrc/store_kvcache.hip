@@ -46,58 +46,6 @@ __global__ __launch_bounds__(256) void store_kvcache_kernel(
 //
 // Bound: HBM bytes (read 2 rows of the input type, write 2 rows of codes).
 
-// Four fp32 values -> four E4M3 codes (byte i from y[i]).
-__device__ __forceinline__ uint32_t to_e4m3x4(const float (&x)[4], float scale) {
-  float y[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    y[i] = x[i] / scale;
-    // saturate (comparisons with NaN are false, so NaN passes through)
-    if (__builtin_fabsf(y[i]) > 448.0f) y[i] = __builtin_copysignf(448.0f, y[i]);
-  }
-  uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
-  w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], (int)w, true);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (__builtin_isnan(y[i])) {
-      const uint32_t code = 0x7Fu | (__builtin_signbit(y[i]) ? 0x80u : 0u);
-      w = (w & ~(0xFFu << (8 * i))) | (code << (8 * i));
-    }
-  }
-  return w;
-}
-
-// 16 elements of T at src -> 16 codes.
-template <typename T>
-__device__ __forceinline__ uint4 quantize16(const char* src, float scale) {
-  float f[16];
-  if constexpr (sizeof(T) == 2) {
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const uint4 v = reinterpret_cast<const uint4*>(src)[c];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f[8 * c + 2 * i] = bf16lo(w[i]);
-        f[8 * c + 2 * i + 1] = bf16hi(w[i]);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float4 v = reinterpret_cast<const float4*>(src)[c];
-      f[4 * c] = v.x; f[4 * c + 1] = v.y; f[4 * c + 2] = v.z; f[4 * c + 3] = v.w;
-    }
-  }
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float x[4] = {f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]};
-    w[i] = to_e4m3x4(x, scale);
-  }
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
 template <typename T>
 __global__ __launch_bounds__(256) void store_kvcache_e4m3_kernel(
     const char* __restrict__ key, const char* __restrict__ value, int64_t key_stride,

@@ -300,3 +300,38 @@ def prefill_fp8_parity(batch, sample_rows=None, seed=0, runner=None):
     if rows is not None:
         got = np.stack([got[t, h] for t, h in rows])
     return check_close(got, ref, batch.dtype, "prefill e4m3" + ("" if rows is None else " (sampled)"))
+
+
+def gpu_store_decode_fp8(batch, partition_size, arrs=None, workspace=None):
+    """The fused E4M3 store + decode call."""
+    arrs = arrs or device_arrays(batch)
+    dev = batch.q.device
+    if workspace is None:
+        workspace = pa.decode_workspace(batch.num_seqs, batch.num_heads, batch.num_kv_heads,
+                                        batch.head_dim, batch.max_context_len, partition_size, dev)
+    out = torch.full_like(batch.q, float("nan"))
+    pa.pa_store_decode_fp8(out, batch.q, batch.key, batch.value, batch.k_cache, batch.v_cache,
+                           batch.k_scale, batch.v_scale, arrs["slots"], arrs["tables"], arrs["lens"],
+                           batch.max_context_len, batch.scale, partition_size, workspace)
+    return out
+
+
+def store_decode_fp8_parity(batch, partition_size):
+    """Fused E4M3 store + decode on the GPU against the oracle's E4M3 store
+    followed by its E4M3 decode; returns the oracle's stored pools (whole
+    pools, from the snapshot taken before the call) for a byte comparison."""
+    import oracle.fp8 as of8
+    hb = wl.host_subset(batch)
+    ks, vs = scales_np(batch)
+    kp, vp = of8.store_kvcache_fp8(hb.k_cache, hb.v_cache, hb.key, hb.value, hb.slot_mapping,
+                                   batch.block_size, ks, vs, batch.dtype)
+    arrs = device_arrays(batch)
+    out = gpu_store_decode_fp8(batch, partition_size, arrs)
+    torch.cuda.synchronize()
+    ref = of8.decode_fp8(hb.q, kp, vp, ks, vs, hb.block_tables, hb.context_lens, batch.scale,
+                         batch.block_size, batch.dtype)
+    res = check_close(as_f64(out), ref, batch.dtype, "store+decode e4m3")
+    ek, ev = of8.store_kvcache_fp8(wl_full_pool(batch, "k"), wl_full_pool(batch, "v"),
+                                   wl.to_numpy(batch.key), wl.to_numpy(batch.value), batch.slot_mapping,
+                                   batch.block_size, ks, vs, batch.dtype)
+    return res, ek, ev

@@ -288,3 +288,24 @@ def test_mixed_fp8_rejections(lib):
     assert _mixed_fp8(lib, Bd=261) == PA_ERR_INVALID_ARG          # the mixed checks apply
     assert _mixed_fp8(lib, dtype=0) == PA_ERR_UNSUPPORTED
     assert _mixed_fp8(lib, ws=None) == PA_ERR_WORKSPACE
+
+
+def _store_decode_fp8(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, key=FAKE, value=FAKE, ks=512, vs=512, k=FAKE, v=FAKE, kscale=FAKE,
+             vscale=FAKE, slots=FAKE, bt=FAKE, cl=FAKE, B=4, Hq=8, Hkv=8, D=64, bs=16, NB=64, MB=7,
+             maxL=100, scale=0.125, P=0, ws=None, wsb=0, dtype=1)
+    a.update(kw)
+    return lib.pa_store_decode_fp8(a["out"], a["q"], a["key"], a["value"], a["ks"], a["vs"], a["k"],
+                                   a["v"], a["kscale"], a["vscale"], a["slots"], a["bt"], a["cl"], a["B"],
+                                   a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"], a["MB"], a["maxL"],
+                                   a["scale"], a["P"], a["ws"], a["wsb"], a["dtype"], None)
+
+
+def test_store_decode_fp8_rejections(lib):
+    assert _store_decode_fp8(lib, B=0) == PA_OK
+    assert _store_decode_fp8(lib, kscale=None) == PA_ERR_INVALID_ARG
+    assert "pa_store_decode_fp8" in binding.load_library().pa_last_error().decode()
+    assert _store_decode_fp8(lib, key=None) == PA_ERR_INVALID_ARG
+    assert _store_decode_fp8(lib, dtype=0) == PA_ERR_UNSUPPORTED       # bf16 queries only
+    assert _store_decode_fp8(lib, ks=500) == PA_ERR_INVALID_ARG        # stride below one row
+    assert _store_decode_fp8(lib, P=32) == PA_ERR_WORKSPACE

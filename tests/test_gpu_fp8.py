@@ -294,3 +294,74 @@ def test_prefill_fp8_last_row_matches_decode_fp8(gpu):
     torch.cuda.synchronize()
     diff = (pre.index_select(0, last).float() - dec.float()).abs().max().item()
     assert diff <= 2e-2
+
+
+# ---------------------------------------------------------------------------
+# fused E4M3 store + decode (pa_store_decode_fp8)
+
+FP8_STORE_DECODE_CASES = [
+    ("mha64", 2, dict(num_seqs=8, lens=("uniform", 1, 1500), max_context=1536), [0, 256, -1]),
+    ("gqa4_bs64", 5, dict(num_seqs=16, lens=("lognormal", 300.0, 1.0, 1, 2048), max_context=2048),
+     [0, 512, -1]),
+    ("gqa2_shared", 3, dict(num_seqs=12, lens=("uniform", 300, 1800), max_context=2048,
+                            share=dict(num_sharers=6, prefix_tokens=256)), [0, 128, -1]),
+    ("bs8_len1", 2, dict(num_seqs=6, lens=("fixed", [1, 2, 8, 9, 17, 64]), block_size=8,
+                         max_context=64), [0, 16, -1]),
+]
+
+
+@pytest.mark.parametrize("name,cfg,over,parts", FP8_STORE_DECODE_CASES,
+                         ids=[c[0] for c in FP8_STORE_DECODE_CASES])
+def test_store_decode_fp8_parity(gpu, name, cfg, over, parts):
+    """The slots being written hold the NaN code beforehand: reading one back
+    instead of taking the quantised new row would make the output NaN. The
+    pools afterwards equal the oracle's quantising store byte for byte."""
+    for P in parts:
+        b = gs.snapshot_pools(wl.make_batch(wl.spec(cfg, kv="e4m3", **over), device=gpu, poison=True))
+        gs.say(f"store+decode e4m3 {name} P={P} lens={b.context_lens.tolist()}")
+        _, ek, ev = gs.store_decode_fp8_parity(b, P)
+        assert wl.to_numpy(b.k_cache).tobytes() == ek.tobytes()
+        assert wl.to_numpy(b.v_cache).tobytes() == ev.tobytes()
+
+
+@pytest.mark.parametrize("P", [0, 64, -1])
+def test_store_decode_fp8_negative_slot_reads_pool(gpu, P):
+    """A sequence whose slot is negative is not stored, and attends over the
+    codes already in the pool; the others are fused as usual."""
+    import oracle.fp8 as of8
+    b = wl.make_batch(wl.spec(5, kv="e4m3", num_seqs=6, lens=("uniform", 40, 300), max_context=320),
+                      device=gpu)
+    arrs = gs.device_arrays(b)
+    skip = [1, 4]
+    gs.gpu_store_fp8(b, arrs)          # every new row's codes into its slot
+    for i in skip:
+        arrs["slots"][i] = -1
+    slots_np = b.slot_mapping.copy()
+    slots_np[skip] = -1
+    b.slot_mapping = slots_np
+    hb = wl.host_subset(b)             # the pools now hold the skipped rows' codes
+    ks, vs = gs.scales_np(b)
+    kp, vp = of8.store_kvcache_fp8(hb.k_cache, hb.v_cache, hb.key, hb.value, hb.slot_mapping,
+                                   b.block_size, ks, vs, b.dtype)
+    out = gs.gpu_store_decode_fp8(b, P, arrs)
+    torch.cuda.synchronize()
+    ref = of8.decode_fp8(hb.q, kp, vp, ks, vs, hb.block_tables, hb.context_lens, b.scale, b.block_size,
+                         b.dtype)
+    gs.check_close(gs.as_f64(out), ref, b.dtype, "store+decode e4m3 with skipped slots")
+
+
+def test_store_decode_fp8_agrees_with_separate_calls(gpu):
+    """The fused call writes the same codes as pa_store_kvcache_fp8 and
+    decodes as pa_decode_fp8 does after it, up to the rounding order of the
+    newest token."""
+    sp = wl.spec(5, kv="e4m3", num_seqs=40, lens=("uniform", 1, 2048), max_context=2048)
+    for P in (0, 256, -1):
+        b1 = wl.make_batch(sp, device=gpu)
+        a1 = gs.device_arrays(b1)
+        gs.gpu_store_fp8(b1, a1)
+        sep = gs.as_f64(gs.gpu_decode_fp8(b1, P, a1))
+        b2 = wl.make_batch(sp, device=gpu)
+        fused = gs.as_f64(gs.gpu_store_decode_fp8(b2, P))
+        torch.cuda.synchronize()
+        assert np.abs(fused - sep).max() <= 8e-3, P
+        assert torch.equal(b1.k_cache, b2.k_cache) and torch.equal(b1.v_cache, b2.v_cache)
