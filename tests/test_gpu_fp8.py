@@ -259,6 +259,8 @@ FP8_PREFILL_VARIANTS = {
     # negative scale: the softmax favours the smallest dot products
     "negative_scale": dict(num_seqs=2, num_heads=8, num_kv_heads=8, head_dim=64, block_size=32,
                            cached=("uniform", 0, 300), chunk=[45, 70], max_context=512, scale=-0.125),
+    "bs1024_gqa4": dict(num_seqs=2, block_size=1024, cached=("fixed", [1000, 3]), chunk=[100, 64],
+                        max_context=2048),
 }
 
 

@@ -47,6 +47,9 @@ MIXED_VARIANTS = {
     # one of each
     "one_each": dict(num_seqs=2, num_decode=1, decode_lens=("fixed", [3000]), cached=("fixed", [2000]),
                      chunk=[512], max_context=4096),
+    # blocks of 512 tokens
+    "bs512": dict(num_seqs=5, num_decode=3, block_size=512, decode_lens=("uniform", 1, 1500),
+                  cached=("uniform", 0, 800), chunk=[100, 33], max_context=2048),
 }
 
 
@@ -129,7 +132,7 @@ def test_mixed_full_config_sampled(gpu):
 # the same calls over E4M3 pools (pa_mixed_batch_fp8) against the oracle's
 # E4M3 prefill, whose decode tokens are chunks of one row
 
-FP8_MIXED_VARIANTS = ["gqa4_bs16", "mha_d64", "edges", "all_decode", "all_prefill"]
+FP8_MIXED_VARIANTS = ["gqa4_bs16", "mha_d64", "edges", "all_decode", "all_prefill", "bs512"]
 
 
 @pytest.mark.parametrize("name", FP8_MIXED_VARIANTS)

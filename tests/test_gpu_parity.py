@@ -435,6 +435,11 @@ PREFILL_VARIANTS = {
     "negative_scale": dict(num_seqs=2, num_heads=8, num_kv_heads=8, head_dim=64, block_size=32,
                            cached=("uniform", 0, 300), chunk=[45, 70], max_context=512,
                            scale=-0.125),
+    # the largest blocks the call accepts: a tile inside one block, chunks crossing block edges
+    "bs512_gqa4": dict(num_seqs=2, block_size=512, cached=("uniform", 0, 1500), chunk=[300, 129],
+                       max_context=2048),
+    "bs1024_mha_d64": dict(num_seqs=2, num_heads=8, num_kv_heads=8, head_dim=64, block_size=1024,
+                           cached=("fixed", [1000, 0]), chunk=[64, 257], max_context=2048),
 }
 
 
