@@ -1,6 +1,6 @@
 """Benchmark: paged decode on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 2] [--no-extra]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-extra]
 
 A step is one pass of the decode hot path over one batch: pa_store_decode
 writes the new token's K/V row of every sequence into the pool and attends
@@ -173,7 +173,7 @@ def time_run(fn, steps, warmup):
 def bench_prefill(steps, warmup, device, kv=None):
     """The chunked-prefill workload: pa_prefill_chunk on bf16 pools, or
     (kv="e4m3") pa_prefill_chunk_fp8 on E4M3 pools with per-head scales."""
-    sp = wl.spec(4, kv="e4m3") if kv == "e4m3" else wl.spec(4)
+    sp = wl.spec(wl.CHUNKED_PREFILL, kv="e4m3") if kv == "e4m3" else wl.spec(wl.CHUNKED_PREFILL)
     b = wl.make_batch(sp, device=device)
     slots = torch.from_numpy(b.slot_mapping).to(device)
     tables = torch.from_numpy(b.block_tables).to(device)
@@ -212,7 +212,7 @@ def bench_mixed(steps, warmup, device, kv=None):
     kv="e4m3" the same over E4M3 pools (pa_mixed_batch_fp8, pa_decode_fp8,
     pa_prefill_chunk_fp8)."""
     e4 = kv == "e4m3"
-    sp = wl.spec(6, kv="e4m3") if e4 else wl.spec(6)
+    sp = wl.spec(wl.MIXED_BATCH, kv="e4m3") if e4 else wl.spec(wl.MIXED_BATCH)
     b = wl.make_batch(sp, device=device)
     Bd = b.num_decode
     a = dict(slots=torch.from_numpy(b.slot_mapping).to(device),
@@ -303,8 +303,8 @@ def bench_block_manager():
     to each sequence, free everything; the same with the CPU oracle's
     allocator."""
     import oracle.prefix_cache as opc
-    st = wl.draw_structure(wl.spec(3))
-    bs = wl.CONFIGS[3]["block_size"]
+    st = wl.draw_structure(wl.spec(wl.B256_SHARED_PREFIX_DECODE))
+    bs = wl.WORKLOADS[wl.B256_SHARED_PREFIX_DECODE]["block_size"]
     free = st["free_list"].tolist()
     ids = [np.ascontiguousarray(t, dtype=np.int32) for t in st["token_ids"]]
     ntok = int(sum(len(t) for t in ids))
@@ -381,7 +381,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--workload", type=int, default=2, choices=[2, 3, 5])
+    by_name = {wl.WORKLOADS[w]["name"]: w for w in wl.DECODE_WORKLOADS}
+    ap.add_argument("--workload", default=wl.WORKLOADS[wl.B64_MHA_DECODE]["name"], choices=sorted(by_name))
     ap.add_argument("--rotations", type=int, default=4)
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -412,7 +413,8 @@ def main():
         return
 
     log(f"building workload {args.workload} x{args.rotations}")
-    ds = DecodeSet(args.workload, args.rotations, dev)
+    workload = by_name[args.workload]
+    ds = DecodeSet(workload, args.rotations, dev)
     b0 = ds.batches[0][0]
     log("timing")
     secs, kms, kbytes = time_decode(ds, args.steps, args.warmup)
@@ -435,7 +437,7 @@ def main():
             "workload": ds.spec["name"],
             "num_seqs": b0.num_seqs, "num_heads": b0.num_heads, "num_kv_heads": b0.num_kv_heads,
             "head_dim": b0.head_dim, "block_size": b0.block_size,
-            "context_lens": "uniform[512,4096]" if args.workload == 2 else str(ds.spec["lens"]),
+            "context_lens": "uniform[512,4096]" if workload == wl.B64_MHA_DECODE else str(ds.spec["lens"]),
             "split": split_name(ds.P), "partition_size": ds.P, "rotating_batches": args.rotations,
             "step": "pa_store_decode: store the new rows + decode, one launch (+ merge)",
         },
@@ -451,14 +453,14 @@ def main():
     }
     if not args.no_extra:
         extra = {}
-        for cfg in (2, 3, 5):
-            runs = [(wl.CONFIGS[cfg]["partition_size"], True), (wl.CONFIGS[cfg]["fixed_partition_size"], True)]
-            if cfg == args.workload:
+        for cfg in wl.DECODE_WORKLOADS:
+            runs = [(wl.WORKLOADS[cfg]["partition_size"], True), (wl.WORKLOADS[cfg]["fixed_partition_size"], True)]
+            if cfg == workload:
                 runs.append((ds.P, False))
             for P, fused in runs:
-                if cfg == args.workload and P == ds.P and fused:
+                if cfg == workload and P == ds.P and fused:
                     continue
-                log(f"extra workload {cfg} partition_size={P} fused={fused}")
+                log(f"extra workload {wl.WORKLOADS[cfg]['name']} partition_size={P} fused={fused}")
                 d = DecodeSet(cfg, 2, dev, partition=P, fused=fused)
                 s, ms, nb = time_decode(d, 30, LEG_WARMUP)
                 bb = d.batches[0][0]
@@ -473,8 +475,8 @@ def main():
                     logical_bytes_per_launch=int(np.mean(d.kv_bytes_logical)))
                 del d
                 torch.cuda.empty_cache()
-        for cfg in (2, 3, 5):
-            P = wl.CONFIGS[cfg]["partition_size"]
+        for cfg in wl.DECODE_WORKLOADS:
+            P = wl.WORKLOADS[cfg]["partition_size"]
             log(f"extra workload {cfg} e4m3 partition_size={P}")
             d = DecodeSet(cfg, 2, dev, partition=P, kv="e4m3", fused=False)
             s, ms, nb = time_decode(d, 30, LEG_WARMUP)

@@ -5,7 +5,7 @@ none of the prefix-hash arithmetic, and it serves both the library's tests and
 benchmark and the CPU oracle's checks.
 
 Structure (context lengths, token ids, block tables, slot mapping) is drawn
-with numpy's PCG64 from seed ``439000 + config id`` in this order:
+with numpy's PCG64 from seed ``439000 + workload id`` in this order:
 
   1. for prefix-sharing workloads, the subset of sequences that share;
   2. context lengths (decode) or cached lengths (prefill);
@@ -34,11 +34,21 @@ import torch
 VOCAB = 50257
 SEED_BASE = 439000
 
-# The five workloads. Lengths include the newest token. partition_size is the
-# decode split the benchmark times (-1: the library's balanced split);
-# fixed_partition_size is the fixed-slice split measured beside it (0: whole
-# contexts), the 512-token slices the b512 workload names among them.
-CONFIGS = {
+# The workloads, by name; each integer is the workload's seed id (structure is
+# drawn from PCG64(SEED_BASE + id)). Lengths include the newest token.
+# partition_size is the decode split the benchmark times (-1: the library's
+# balanced split); fixed_partition_size is the fixed-slice split measured
+# beside it (0: whole contexts), the 512-token slices the b512 workload names
+# among them.
+TINY_FP32_DECODE = 1           # 4 sequences, fp32 MHA 8 heads, D 64, block 16
+B64_MHA_DECODE = 2             # 64 sequences, bf16 MHA 12 heads, D 64, block 256, lengths U[512, 4096]
+B256_SHARED_PREFIX_DECODE = 3  # 256 sequences, bf16 GQA 16/8, D 128, block 256; 128 share a 1024-token prefix
+CHUNKED_PREFILL = 4            # 8 chunks of 512 over cached U[0, 3584], bf16 GQA 32/8, D 128, block 256
+B512_LOGNORMAL_DECODE = 5      # 512 sequences, bf16 GQA 32/8, D 128, block 64, lognormal lengths (median 1500)
+MIXED_BATCH = 6                # 256 decode tokens and 4 chunks of 512, bf16 GQA 32/8, D 128, block 256
+DECODE_WORKLOADS = (B64_MHA_DECODE, B256_SHARED_PREFIX_DECODE, B512_LOGNORMAL_DECODE)
+
+WORKLOADS = {
     1: dict(name="tiny_fp32_mha_decode", kind="decode", dtype="f32", num_seqs=4,
             num_heads=8, num_kv_heads=8, head_dim=64, block_size=16,
             lens=("fixed", [17, 33, 64, 100]), pool=("blocks", 64),
@@ -320,7 +330,7 @@ def e4m3_scales(num_kv_heads, seed, device):
 
 
 def make_batch(spec, device="cpu", seed=None, poison=False):
-    """Draw a full batch for ``spec`` (an entry of CONFIGS or a variant).
+    """Draw a full batch for ``spec`` (an entry of WORKLOADS or a variant).
 
     poison=True fills every pool row that no context covers, and the rows the
     new tokens are about to be stored into, with NaN; a kernel that reads
@@ -475,9 +485,9 @@ def host_subset(batch: Batch, seqs=None):
                      query_start_loc=qsl, new_rows=rows)
 
 
-def spec(config_id, **overrides):
-    """A copy of CONFIGS[config_id] with overrides, tagged with its id."""
-    s = dict(CONFIGS[config_id])
-    s["id"] = config_id
+def spec(workload, **overrides):
+    """A copy of WORKLOADS[workload] with overrides, tagged with its id."""
+    s = dict(WORKLOADS[workload])
+    s["id"] = workload
     s.update(overrides)
     return s

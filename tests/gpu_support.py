@@ -196,7 +196,7 @@ def full_config_parts(cfg, split="balanced"):
     """The decode split the benchmark times for a workload: its balanced
     split, or the fixed one measured beside it."""
     key = "partition_size" if split == "balanced" else "fixed_partition_size"
-    return wl.CONFIGS[cfg].get(key, 0)
+    return wl.WORKLOADS[cfg].get(key, 0)
 
 
 # ---------------------------------------------------------------------------

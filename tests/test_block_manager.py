@@ -88,8 +88,8 @@ def test_random_operations_match_oracle(seed, bs, num_blocks, vocab):
 def test_reproduces_shared_prefix_workload_tables():
     """Fed the shared-prefix decode workload's token ids and free list, the
     manager rebuilds its block tables exactly (4 blocks with 128 references)."""
-    st = wl.draw_structure(wl.spec(3))
-    bs = wl.CONFIGS[3]["block_size"]
+    st = wl.draw_structure(wl.spec(wl.B256_SHARED_PREFIX_DECODE))
+    bs = wl.WORKLOADS[wl.B256_SHARED_PREFIX_DECODE]["block_size"]
     bm = binding.BlockManager(int(st["num_blocks"]), bs, st["free_list"].tolist())
     lens = st["context_lens"]
     for i, ids in enumerate(st["token_ids"]):

@@ -41,7 +41,7 @@ def _specials_batch(gpu, dtype):
     """A store batch whose first tokens carry the special values (scaled by a
     power-of-two k/v scale, so that x / scale is exact) and whose other
     tokens are the drawn N(0, 1) rows."""
-    b = wl.make_batch(wl.spec(5, num_seqs=40, lens=("uniform", 1, 500), max_context=512,
+    b = wl.make_batch(wl.spec(wl.B512_LOGNORMAL_DECODE, num_seqs=40, lens=("uniform", 1, 500), max_context=512,
                               num_heads=8, num_kv_heads=2, kv="e4m3", dtype=dtype), device=gpu,
                       poison=True)
     sc = np.float32(2.0 ** -5)
@@ -99,8 +99,8 @@ def test_store_fp8_full_pool(gpu, cfg, over):
 
 
 def test_store_fp8_skips_negative_slots_and_strided_key(gpu):
-    b = wl.make_batch(wl.spec(3, num_seqs=6, lens=("uniform", 300, 700), max_context=768, share=None,
-                              kv="e4m3"), device=gpu)
+    b = wl.make_batch(wl.spec(wl.B256_SHARED_PREFIX_DECODE, num_seqs=6, lens=("uniform", 300, 700), max_context=768,
+                              share=None, kv="e4m3"), device=gpu)
     T, Hkv, D = b.key.shape
     fused = torch.randn(T, 3, Hkv, D, device=gpu).to(b.key.dtype)
     fused[:, 1] = b.key
@@ -171,7 +171,7 @@ def test_decode_fp8_peaked_logits(gpu, cfg, over):
 def test_decode_fp8_edge_lengths(gpu):
     """Lengths 1, one block, one partition, partition+1, a full table."""
     lens = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128]
-    sp = wl.spec(5, num_seqs=len(lens), lens=("fixed", lens), block_size=16, max_context=128,
+    sp = wl.spec(wl.B512_LOGNORMAL_DECODE, num_seqs=len(lens), lens=("fixed", lens), block_size=16, max_context=128,
                  pool=("factor", 1.5), kv="e4m3")
     for part in (0, 32, 16, 112, -1):
         b = wl.make_batch(sp, device=gpu, poison=True)
@@ -181,7 +181,7 @@ def test_decode_fp8_edge_lengths(gpu):
 
 @pytest.mark.parametrize("P", [0, 16, -1])
 def test_decode_fp8_zero_length_gives_zeros(gpu, P):
-    b = wl.make_batch(wl.spec(5, num_seqs=4, lens=("fixed", [5, 40, 9, 70]), block_size=16,
+    b = wl.make_batch(wl.spec(wl.B512_LOGNORMAL_DECODE, num_seqs=4, lens=("fixed", [5, 40, 9, 70]), block_size=16,
                               max_context=80, kv="e4m3"), device=gpu)
     lens = torch.tensor([5, 0, 9, 0], dtype=torch.int32, device=gpu)
     tables = torch.from_numpy(b.block_tables).to(gpu)
@@ -225,7 +225,8 @@ def test_decode_fp8_value_codes_read_exactly(gpu):
             assert np.array_equal(got[i, h], want), (i, h)
 
 
-@pytest.mark.parametrize("cfg,nseq", [(2, 8), (3, 6), (5, 6)])
+@pytest.mark.parametrize("cfg,nseq", [(wl.B64_MHA_DECODE, 8), (wl.B256_SHARED_PREFIX_DECODE, 6),
+                                      (wl.B512_LOGNORMAL_DECODE, 6)])
 def test_decode_fp8_full_config_sampled(gpu, cfg, nseq):
     b = wl.make_batch(wl.spec(cfg, kv="e4m3"), device=gpu, poison=True)
     seqs = gs.sample_seqs(b, nseq, seed=cfg)
@@ -266,7 +267,7 @@ FP8_PREFILL_VARIANTS = {
 
 @pytest.mark.parametrize("name", sorted(FP8_PREFILL_VARIANTS))
 def test_prefill_fp8_variants(gpu, name):
-    b = wl.make_batch(wl.spec(4, kv="e4m3", **FP8_PREFILL_VARIANTS[name]), device=gpu, poison=True)
+    b = wl.make_batch(wl.spec(wl.CHUNKED_PREFILL, kv="e4m3", **FP8_PREFILL_VARIANTS[name]), device=gpu, poison=True)
     gs.say(f"prefill e4m3 {name} lens={b.context_lens.tolist()} qsl={b.query_start_loc.tolist()}")
     gs.prefill_fp8_parity(b)
 
@@ -275,7 +276,7 @@ def test_prefill_fp8_full_config_sampled(gpu):
     """The chunked-prefill workload (8 chunks of 512 over cached contexts of
     up to 3584 tokens) on E4M3 pools, in the benchmark's launch form; 96
     sampled rows plus each chunk's first and last."""
-    b = wl.make_batch(wl.spec(4, kv="e4m3"), device=gpu, poison=True)
+    b = wl.make_batch(wl.spec(wl.CHUNKED_PREFILL, kv="e4m3"), device=gpu, poison=True)
     gs.say(f"prefill e4m3 full lens={b.context_lens.tolist()}")
     gs.prefill_fp8_parity(b, sample_rows=96, seed=4)
 
@@ -283,7 +284,7 @@ def test_prefill_fp8_full_config_sampled(gpu):
 def test_prefill_fp8_last_row_matches_decode_fp8(gpu):
     """The last row of each chunk attends to the whole context, as E4M3
     decode of that query does (both within the bf16 bar of each other)."""
-    b = wl.make_batch(wl.spec(4, kv="e4m3", num_seqs=4, cached=("uniform", 0, 900), chunk=64,
+    b = wl.make_batch(wl.spec(wl.CHUNKED_PREFILL, kv="e4m3", num_seqs=4, cached=("uniform", 0, 900), chunk=64,
                               max_context=1024), device=gpu)
     arrs = gs.device_arrays(b)
     gs.gpu_store_fp8(b, arrs)
@@ -331,8 +332,8 @@ def test_store_decode_fp8_negative_slot_reads_pool(gpu, P):
     """A sequence whose slot is negative is not stored, and attends over the
     codes already in the pool; the others are fused as usual."""
     import oracle.fp8 as of8
-    b = wl.make_batch(wl.spec(5, kv="e4m3", num_seqs=6, lens=("uniform", 40, 300), max_context=320),
-                      device=gpu)
+    b = wl.make_batch(wl.spec(wl.B512_LOGNORMAL_DECODE, kv="e4m3", num_seqs=6, lens=("uniform", 40, 300),
+                              max_context=320), device=gpu)
     arrs = gs.device_arrays(b)
     skip = [1, 4]
     gs.gpu_store_fp8(b, arrs)          # every new row's codes into its slot
@@ -356,7 +357,7 @@ def test_store_decode_fp8_agrees_with_separate_calls(gpu):
     """The fused call writes the same codes as pa_store_kvcache_fp8 and
     decodes as pa_decode_fp8 does after it, up to the rounding order of the
     newest token."""
-    sp = wl.spec(5, kv="e4m3", num_seqs=40, lens=("uniform", 1, 2048), max_context=2048)
+    sp = wl.spec(wl.B512_LOGNORMAL_DECODE, kv="e4m3", num_seqs=40, lens=("uniform", 1, 2048), max_context=2048)
     for P in (0, 256, -1):
         b1 = wl.make_batch(sp, device=gpu)
         a1 = gs.device_arrays(b1)

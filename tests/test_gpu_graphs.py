@@ -44,7 +44,7 @@ def _capture_and_replay(call, out, eager_between):
 
 def _other_decode(gpu):
     """Some unrelated eager library work to run between replays."""
-    b = wl.make_batch(wl.spec(2, num_seqs=4, lens=("uniform", 10, 300), max_context=320), device=gpu)
+    b = wl.make_batch(wl.spec(wl.B64_MHA_DECODE, num_seqs=4, lens=("uniform", 10, 300), max_context=320), device=gpu)
     arrs = gs.device_arrays(b)
 
     def run():
@@ -55,7 +55,8 @@ def _other_decode(gpu):
 
 @pytest.mark.parametrize("P", [-1, 256])
 def test_store_decode_in_graph(gpu, P):
-    b = wl.make_batch(wl.spec(2, num_seqs=16, lens=("uniform", 100, 2000), max_context=2048), device=gpu)
+    b = wl.make_batch(wl.spec(wl.B64_MHA_DECODE, num_seqs=16, lens=("uniform", 100, 2000), max_context=2048),
+                      device=gpu)
     arrs = gs.device_arrays(b)
     ws = pa.decode_workspace(b.num_seqs, b.num_heads, b.num_kv_heads, b.head_dim, b.max_context_len, P, gpu)
     out = torch.empty_like(b.q)
@@ -68,7 +69,7 @@ def test_store_decode_in_graph(gpu, P):
 
 
 def test_prefill_in_graph(gpu):
-    b = wl.make_batch(wl.spec(4, num_seqs=3, cached=("uniform", 0, 700), chunk=[100, 257, 31],
+    b = wl.make_batch(wl.spec(wl.CHUNKED_PREFILL, num_seqs=3, cached=("uniform", 0, 700), chunk=[100, 257, 31],
                               max_context=1024), device=gpu)
     arrs = gs.device_arrays(b)
     gs.gpu_store(b, arrs)
@@ -82,7 +83,7 @@ def test_prefill_in_graph(gpu):
 
 
 def test_mixed_batch_in_graph(gpu):
-    b = wl.make_batch(wl.spec(6, num_seqs=12, num_decode=8, decode_lens=("uniform", 1, 600),
+    b = wl.make_batch(wl.spec(wl.MIXED_BATCH, num_seqs=12, num_decode=8, decode_lens=("uniform", 1, 600),
                               cached=("uniform", 0, 300), chunk=[40, 1, 77, 129], block_size=16,
                               max_context=1024), device=gpu)
     arrs = gs.device_arrays(b)
@@ -98,7 +99,7 @@ def test_mixed_batch_in_graph(gpu):
 
 
 def test_store_decode_fp8_in_graph(gpu):
-    b = wl.make_batch(wl.spec(5, kv="e4m3", num_seqs=16, lens=("lognormal", 300.0, 1.0, 1, 2048),
+    b = wl.make_batch(wl.spec(wl.B512_LOGNORMAL_DECODE, kv="e4m3", num_seqs=16, lens=("lognormal", 300.0, 1.0, 1, 2048),
                               max_context=2048), device=gpu)
     arrs = gs.device_arrays(b)
     P = pa.PA_PARTITION_BALANCED

@@ -55,7 +55,7 @@ MIXED_VARIANTS = {
 
 @pytest.mark.parametrize("name", sorted(MIXED_VARIANTS))
 def test_mixed_variants(gpu, name):
-    b = wl.make_batch(wl.spec(6, **MIXED_VARIANTS[name]), device=gpu, poison=True)
+    b = wl.make_batch(wl.spec(wl.MIXED_BATCH, **MIXED_VARIANTS[name]), device=gpu, poison=True)
     gs.say(f"mixed {name} decode={b.num_decode} lens={b.context_lens.tolist()} "
            f"qsl={b.query_start_loc.tolist()}")
     gs.prefill_parity(b, runner=gs.gpu_mixed)
@@ -68,7 +68,7 @@ def test_mixed_equals_separate_calls(gpu):
     to a running maximum that depends on where a worker's range starts, so
     the two agree to a few bf16 units in the last place (both are checked
     against the oracle by the other tests)."""
-    b = wl.make_batch(wl.spec(6, num_seqs=40, num_decode=36, decode_lens=("uniform", 1, 3000),
+    b = wl.make_batch(wl.spec(wl.MIXED_BATCH, num_seqs=40, num_decode=36, decode_lens=("uniform", 1, 3000),
                               chunk=[512, 200, 37, 1]), device=gpu, poison=True)
     arrs = gs.device_arrays(b)
     gs.gpu_store(b, arrs)
@@ -94,7 +94,7 @@ def test_mixed_full_config_sampled(gpu):
     """The full continuous batch (256 decode tokens, 4 chunks of 512), in
     the benchmark's launch form; every row of 12 decode sequences (all heads)
     and 26 rows of each chunk (4 heads each) against the oracle."""
-    b = wl.make_batch(wl.spec(6), device=gpu, poison=True)
+    b = wl.make_batch(wl.spec(wl.MIXED_BATCH), device=gpu, poison=True)
     arrs = gs.device_arrays(b)
     Bd = b.num_decode
     rng = np.random.Generator(np.random.PCG64(6))
@@ -137,7 +137,7 @@ FP8_MIXED_VARIANTS = ["gqa4_bs16", "mha_d64", "edges", "all_decode", "all_prefil
 
 @pytest.mark.parametrize("name", FP8_MIXED_VARIANTS)
 def test_mixed_fp8_variants(gpu, name):
-    b = wl.make_batch(wl.spec(6, kv="e4m3", **MIXED_VARIANTS[name]), device=gpu, poison=True)
+    b = wl.make_batch(wl.spec(wl.MIXED_BATCH, kv="e4m3", **MIXED_VARIANTS[name]), device=gpu, poison=True)
     gs.say(f"mixed e4m3 {name} decode={b.num_decode} lens={b.context_lens.tolist()} "
            f"qsl={b.query_start_loc.tolist()}")
     gs.prefill_fp8_parity(b, runner=gs.gpu_mixed_fp8)
@@ -147,7 +147,7 @@ def test_mixed_fp8_equals_separate_calls(gpu):
     """Over E4M3 pools the mixed launch gives pa_prefill_chunk_fp8's chunk rows
     bit for bit and pa_decode_fp8's (balanced split) decode rows up to the
     rounding of a different worker split, as over bf16 pools."""
-    b = wl.make_batch(wl.spec(6, kv="e4m3", num_seqs=40, num_decode=36, decode_lens=("uniform", 1, 3000),
+    b = wl.make_batch(wl.spec(wl.MIXED_BATCH, kv="e4m3", num_seqs=40, num_decode=36, decode_lens=("uniform", 1, 3000),
                               chunk=[512, 200, 37, 1]), device=gpu, poison=True)
     arrs = gs.device_arrays(b)
     gs.gpu_store_fp8(b, arrs)
@@ -173,5 +173,5 @@ def test_mixed_fp8_equals_separate_calls(gpu):
 def test_mixed_fp8_full_config_sampled(gpu):
     """The full continuous batch (256 decode tokens, 4 chunks of 512) over
     E4M3 pools; 96 sampled rows plus every chunk's first and last."""
-    b = wl.make_batch(wl.spec(6, kv="e4m3"), device=gpu, poison=True)
+    b = wl.make_batch(wl.spec(wl.MIXED_BATCH, kv="e4m3"), device=gpu, poison=True)
     gs.prefill_fp8_parity(b, sample_rows=96, seed=6, runner=gs.gpu_mixed_fp8)

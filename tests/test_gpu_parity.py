@@ -42,7 +42,7 @@ def test_store_bit_exact_whole_pool(gpu, cfg, over):
 
 
 def test_store_skips_negative_and_out_of_pool_slots(gpu):
-    b = wl.make_batch(wl.spec(1), device=gpu)
+    b = wl.make_batch(wl.spec(wl.TINY_FP32_DECODE), device=gpu)
     slots = b.slot_mapping.copy()
     slots[1] = -1
     slots[2] = b.num_blocks * b.block_size + 5      # past the pool: skipped
@@ -57,7 +57,7 @@ def test_store_skips_negative_and_out_of_pool_slots(gpu):
 
 def test_store_strided_key(gpu):
     """key/value as slices of a fused [T][3][Hkv][D] tensor."""
-    b = wl.make_batch(wl.spec(4, num_seqs=2, cached=("uniform", 0, 200), chunk=40, max_context=512),
+    b = wl.make_batch(wl.spec(wl.CHUNKED_PREFILL, num_seqs=2, cached=("uniform", 0, 200), chunk=40, max_context=512),
                       device=gpu)
     T, Hkv, D = b.key.shape
     fused = torch.randn(T, 3, Hkv, D, device=gpu).to(b.key.dtype)
@@ -74,12 +74,12 @@ def test_store_strided_key(gpu):
 
 
 # ---------------------------------------------------------------------------
-# decode: small configs compared in full
+# decode: small cases compared in full
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("P", [0, 16, 32, 48, 64, -1])
 def test_decode_tiny_fp32(gpu, P):
-    b = wl.make_batch(wl.spec(1), device=gpu, poison=True)
+    b = wl.make_batch(wl.spec(wl.TINY_FP32_DECODE), device=gpu, poison=True)
     gs.say(f"decode cfg1 P={P}")
     gs.decode_parity(b, P)
 
@@ -176,7 +176,7 @@ def test_decode_edge_lengths(gpu):
     """Lengths 1, one block, one partition, partition+1, full table."""
     bs, P = 16, 32
     lens = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128]
-    sp = wl.spec(5, num_seqs=len(lens), lens=("fixed", lens), block_size=bs, max_context=128,
+    sp = wl.spec(wl.B512_LOGNORMAL_DECODE, num_seqs=len(lens), lens=("fixed", lens), block_size=bs, max_context=128,
                  pool=("factor", 1.5))
     for part in (0, P, 16, 112, -1):
         b = wl.make_batch(sp, device=gpu, poison=True)
@@ -186,7 +186,7 @@ def test_decode_edge_lengths(gpu):
 
 @pytest.mark.parametrize("P", [0, 16, -1])
 def test_decode_zero_length_gives_zeros(gpu, P):
-    b = wl.make_batch(wl.spec(1), device=gpu)
+    b = wl.make_batch(wl.spec(wl.TINY_FP32_DECODE), device=gpu)
     arrs = gs.device_arrays(b)
     arrs["lens"][2] = 0
     out = gs.gpu_decode(b, P, arrs)
@@ -199,9 +199,9 @@ def test_decode_workspace_reuse_across_shapes(gpu):
     """One workspace, filled with NaN bytes first, reused by calls of
     different shapes back to back: its prior contents never matter."""
     ws = torch.full((64 << 20,), 0xFF, dtype=torch.uint8, device=gpu)
-    specs = [wl.spec(5, num_seqs=16, lens=("uniform", 1, 2048), max_context=2048),
-             wl.spec(2, num_seqs=5, lens=("uniform", 1, 1024), max_context=1024),
-             wl.spec(5, num_seqs=9, lens=("uniform", 600, 2048), max_context=2048)]
+    specs = [wl.spec(wl.B512_LOGNORMAL_DECODE, num_seqs=16, lens=("uniform", 1, 2048), max_context=2048),
+             wl.spec(wl.B64_MHA_DECODE, num_seqs=5, lens=("uniform", 1, 1024), max_context=1024),
+             wl.spec(wl.B512_LOGNORMAL_DECODE, num_seqs=9, lens=("uniform", 600, 2048), max_context=2048)]
     for i, sp in enumerate(specs * 2):
         b = wl.make_batch(sp, device=gpu, seed=1000 + i, poison=True)
         hb, kp, vp = gs.oracle_inputs(b)
@@ -214,7 +214,7 @@ def test_decode_workspace_reuse_across_shapes(gpu):
 
 
 def test_decode_split_agrees_with_unsplit(gpu):
-    b = wl.make_batch(wl.spec(5, num_seqs=32, lens=("uniform", 1, 4096)), device=gpu)
+    b = wl.make_batch(wl.spec(wl.B512_LOGNORMAL_DECODE, num_seqs=32, lens=("uniform", 1, 4096)), device=gpu)
     arrs = gs.device_arrays(b)
     gs.gpu_store(b, arrs)
     base = gs.as_f64(gs.gpu_decode(b, 0, arrs))
@@ -228,7 +228,7 @@ def test_decode_balanced_many_short_and_empty(gpu):
     whole sequences each, and empty contexts give zeros."""
     rng = np.random.Generator(np.random.PCG64(77))
     lens = rng.integers(1, 41, size=600)
-    sp = wl.spec(5, num_seqs=600, lens=("fixed", lens.tolist()), block_size=16, max_context=48,
+    sp = wl.spec(wl.B512_LOGNORMAL_DECODE, num_seqs=600, lens=("fixed", lens.tolist()), block_size=16, max_context=48,
                  pool=("factor", 1.25))
     b = wl.make_batch(sp, device=gpu, poison=True)
     gs.say("decode balanced: 600 short contexts")
@@ -245,7 +245,7 @@ def test_decode_balanced_many_short_and_empty(gpu):
 
 def test_decode_balanced_few_long(gpu):
     """Two long contexts cut across hundreds of ranges each."""
-    sp = wl.spec(5, num_seqs=2, lens=("fixed", [4096, 3001]), max_context=4096)
+    sp = wl.spec(wl.B512_LOGNORMAL_DECODE, num_seqs=2, lens=("fixed", [4096, 3001]), max_context=4096)
     b = wl.make_batch(sp, device=gpu, poison=True)
     gs.say("decode balanced: 2 long contexts")
     gs.decode_parity(b, pa.PA_PARTITION_BALANCED)
@@ -253,7 +253,7 @@ def test_decode_balanced_few_long(gpu):
 
 def test_decode_balanced_at_sequence_limit(gpu):
     """4096 sequences, the most the balanced split takes."""
-    sp = wl.spec(2, num_seqs=4096, lens=("uniform", 1, 64), block_size=16, max_context=64)
+    sp = wl.spec(wl.B64_MHA_DECODE, num_seqs=4096, lens=("uniform", 1, 64), block_size=16, max_context=64)
     b = wl.make_batch(sp, device=gpu, poison=True)
     seqs = gs.sample_seqs(b, 24, seed=9) + [4095]
     gs.say("decode balanced: 4096 sequences")
@@ -263,7 +263,7 @@ def test_decode_balanced_at_sequence_limit(gpu):
 def test_decode_block_permutation_bit_identical(gpu):
     """Renumbering physical blocks leaves the GPU result bit-identical (its
     reduction order depends only on logical positions)."""
-    b = wl.make_batch(wl.spec(3, num_seqs=10, lens=("uniform", 100, 1500), max_context=1536,
+    b = wl.make_batch(wl.spec(wl.B256_SHARED_PREFIX_DECODE, num_seqs=10, lens=("uniform", 100, 1500), max_context=1536,
                               share=dict(num_sharers=4, prefix_tokens=256)), device=gpu)
     arrs = gs.device_arrays(b)
     gs.gpu_store(b, arrs)
@@ -287,7 +287,7 @@ def test_decode_block_permutation_bit_identical(gpu):
 def test_decode_sharing_equals_duplication(gpu):
     """Sequences reading shared prefix blocks match the same sequences reading
     private copies, bit for bit."""
-    sp = wl.spec(3, num_seqs=8, lens=("uniform", 600, 1500), max_context=1536,
+    sp = wl.spec(wl.B256_SHARED_PREFIX_DECODE, num_seqs=8, lens=("uniform", 600, 1500), max_context=1536,
                  share=dict(num_sharers=5, prefix_tokens=512))
     b = wl.make_batch(sp, device=gpu)
     arrs = gs.device_arrays(b)
@@ -349,7 +349,8 @@ def test_store_decode_parity(gpu, name, cfg, over, parts):
 def test_store_decode_negative_slot_reads_pool(gpu, P):
     """A sequence whose slot is negative is not stored, and attends over the
     pool row already there; the others are fused as usual."""
-    b = wl.make_batch(wl.spec(5, num_seqs=6, lens=("uniform", 40, 300), max_context=320), device=gpu)
+    b = wl.make_batch(wl.spec(wl.B512_LOGNORMAL_DECODE, num_seqs=6, lens=("uniform", 40, 300), max_context=320),
+                      device=gpu)
     arrs = gs.device_arrays(b)
     skip = [1, 4]
     for i in skip:   # put the new row in the pool by hand, then drop its slot
@@ -366,7 +367,7 @@ def test_store_decode_negative_slot_reads_pool(gpu, P):
 
 
 def test_store_decode_agrees_with_separate_calls(gpu):
-    sp = wl.spec(5, num_seqs=40, lens=("uniform", 1, 2048), max_context=2048)
+    sp = wl.spec(wl.B512_LOGNORMAL_DECODE, num_seqs=40, lens=("uniform", 1, 2048), max_context=2048)
     for P in (0, 256, -1):
         b1 = wl.make_batch(sp, device=gpu)
         a1 = gs.device_arrays(b1)
@@ -380,10 +381,11 @@ def test_store_decode_agrees_with_separate_calls(gpu):
 
 
 # ---------------------------------------------------------------------------
-# decode: full-size configs, sampled outputs, in the benchmark's launch form
+# decode: full-size workloads, sampled outputs, in the benchmark's launch form
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("cfg,nseq", [(2, 8), (3, 6), (5, 6)])
+@pytest.mark.parametrize("cfg,nseq", [(wl.B64_MHA_DECODE, 8), (wl.B256_SHARED_PREFIX_DECODE, 6),
+                                      (wl.B512_LOGNORMAL_DECODE, 6)])
 @pytest.mark.parametrize("split", ["fixed", "balanced"])
 def test_decode_full_config_sampled(gpu, cfg, nseq, split):
     b = wl.make_batch(wl.spec(cfg), device=gpu, poison=True)
@@ -400,7 +402,7 @@ def test_decode_full_config_properties(gpu):
     """Every output of the largest decode workload is finite and, being a
     convex combination of value rows, lies within the range of its head's
     values."""
-    b = wl.make_batch(wl.spec(5), device=gpu, poison=True)
+    b = wl.make_batch(wl.spec(wl.B512_LOGNORMAL_DECODE), device=gpu, poison=True)
     arrs = gs.device_arrays(b)
     gs.gpu_store(b, arrs)
     out = gs.gpu_decode(b, 512, arrs)
@@ -445,13 +447,13 @@ PREFILL_VARIANTS = {
 
 @pytest.mark.parametrize("name", sorted(PREFILL_VARIANTS))
 def test_prefill_variants(gpu, name):
-    b = wl.make_batch(wl.spec(4, **PREFILL_VARIANTS[name]), device=gpu, poison=True)
+    b = wl.make_batch(wl.spec(wl.CHUNKED_PREFILL, **PREFILL_VARIANTS[name]), device=gpu, poison=True)
     gs.say(f"prefill {name} lens={b.context_lens.tolist()} qsl={b.query_start_loc.tolist()}")
     gs.prefill_parity(b)
 
 
 def test_prefill_full_config_sampled(gpu):
-    b = wl.make_batch(wl.spec(4), device=gpu, poison=True)
+    b = wl.make_batch(wl.spec(wl.CHUNKED_PREFILL), device=gpu, poison=True)
     gs.say(f"prefill full cfg4 lens={b.context_lens.tolist()}")
     gs.prefill_parity(b, sample_rows=96, seed=4)
 
@@ -459,7 +461,7 @@ def test_prefill_full_config_sampled(gpu):
 def test_prefill_last_row_matches_decode(gpu):
     """The last row of each chunk attends to the whole context, as a decode
     of that query does."""
-    b = wl.make_batch(wl.spec(4, num_seqs=4, cached=("uniform", 0, 900), chunk=64, max_context=1024),
+    b = wl.make_batch(wl.spec(wl.CHUNKED_PREFILL, num_seqs=4, cached=("uniform", 0, 900), chunk=64, max_context=1024),
                       device=gpu)
     arrs = gs.device_arrays(b)
     gs.gpu_store(b, arrs)

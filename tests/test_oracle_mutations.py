@@ -380,7 +380,7 @@ def _extra_pins():
     """Full-size allocator check on the shared-prefix workload (cheap: no
     dense values)."""
     from paged_kv_cache_439_amd import workloads as wl
-    sp = wl.spec(3, num_seqs=16, share=dict(num_sharers=8, prefix_tokens=512))
+    sp = wl.spec(wl.B256_SHARED_PREFIX_DECODE, num_seqs=16, share=dict(num_sharers=8, prefix_tokens=512))
 
     def pin_alloc_cfg3_like():
         st = wl.draw_structure(sp)

@@ -11,7 +11,8 @@ def test_pin(pin):
     pin()
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 5])
+@pytest.mark.parametrize("cfg", [wl.TINY_FP32_DECODE, wl.B64_MHA_DECODE, wl.B256_SHARED_PREFIX_DECODE,
+                                 wl.B512_LOGNORMAL_DECODE])
 def test_allocator_reproduces_drawn_tables(cfg):
     """Full-size structures: the pages' hash-sharing allocation over the
     drawn token ids gives exactly the drawn tables (cfg 3 shares a 1024-token
@@ -24,6 +25,6 @@ def test_allocator_reproduces_drawn_tables(cfg):
 
 
 def test_prefill_structure_allocation():
-    sp = wl.spec(4)
+    sp = wl.spec(wl.CHUNKED_PREFILL)
     st = wl.draw_structure(sp)
     pins.pin_allocator_matches_structure(st, sp["block_size"], 0, 0)
