@@ -60,10 +60,11 @@ def log(msg):
 class DecodeSet:
     """R resident batches of one decode workload, with device-side arrays."""
 
-    def __init__(self, cfg, rotations, device, partition=None, fused=True, kv=None):
+    def __init__(self, cfg, rotations, device, partition=None, fused=True, kv=None, hint=True):
         self.spec = wl.spec(cfg) if kv is None else wl.spec(cfg, kv=kv)
         self.e4m3 = kv == "e4m3"
         self.fused = fused
+        self.hint = hint  # pass shared_lens (the shared-prefix load-policy hint)
         self.P = self.spec.get("partition_size", 0) if partition is None else partition
         self.batches = []
         for r in range(rotations):
@@ -71,6 +72,7 @@ class DecodeSet:
             arrs = dict(slots=torch.from_numpy(b.slot_mapping).to(device),
                         tables=torch.from_numpy(b.block_tables).to(device),
                         lens=torch.from_numpy(b.context_lens).to(device),
+                        shared=torch.from_numpy(b.shared_lens).to(device) if hint else None,
                         out=torch.empty_like(b.q))
             self.batches.append((b, arrs))
         b0 = self.batches[0][0]
@@ -105,16 +107,18 @@ class DecodeSet:
         if self.e4m3 and self.fused:
             pa.pa_store_decode_fp8(a["out"], b.q, b.key, b.value, b.k_cache, b.v_cache, b.k_scale,
                                    b.v_scale, a["slots"], a["tables"], a["lens"], b.max_context_len,
-                                   b.scale, self.P, self.ws)
+                                   b.scale, self.P, self.ws, shared_lens=a["shared"])
         elif self.e4m3:
             pa.pa_decode_fp8(a["out"], b.q, b.k_cache, b.v_cache, b.k_scale, b.v_scale, a["tables"],
-                             a["lens"], b.max_context_len, b.scale, self.P, self.ws)
+                             a["lens"], b.max_context_len, b.scale, self.P, self.ws,
+                             shared_lens=a["shared"])
         elif self.fused:
             pa.pa_store_decode(a["out"], b.q, b.key, b.value, b.k_cache, b.v_cache, a["slots"],
-                               a["tables"], a["lens"], b.max_context_len, b.scale, self.P, self.ws)
+                               a["tables"], a["lens"], b.max_context_len, b.scale, self.P, self.ws,
+                               shared_lens=a["shared"])
         else:
             pa.pa_decode(a["out"], b.q, b.k_cache, b.v_cache, a["tables"], a["lens"],
-                         b.max_context_len, b.scale, self.P, self.ws)
+                         b.max_context_len, b.scale, self.P, self.ws, shared_lens=a["shared"])
 
 
 # Untimed calls before each extra decode measurement. The first few dozen
@@ -454,24 +458,32 @@ def main():
     if not args.no_extra:
         extra = {}
         for cfg in wl.DECODE_WORKLOADS:
-            runs = [(wl.WORKLOADS[cfg]["partition_size"], True), (wl.WORKLOADS[cfg]["fixed_partition_size"], True)]
+            P_bal = wl.WORKLOADS[cfg]["partition_size"]
+            runs = [(P_bal, True, True), (wl.WORKLOADS[cfg]["fixed_partition_size"], True, True)]
             if cfg == workload:
-                runs.append((ds.P, False))
-            for P, fused in runs:
-                if cfg == workload and P == ds.P and fused:
+                runs.append((ds.P, False, True))
+            if cfg == wl.B256_SHARED_PREFIX_DECODE and args.only is None:
+                # every block streamed: what the hint gains (left out of the
+                # profiling runs, whose per-kernel figures would pool both)
+                runs.append((P_bal, True, False))
+            for P, fused, hint in runs:
+                if cfg == workload and P == ds.P and fused and hint:
                     continue
-                log(f"extra workload {wl.WORKLOADS[cfg]['name']} partition_size={P} fused={fused}")
-                d = DecodeSet(cfg, 2, dev, partition=P, fused=fused)
+                log(f"extra workload {wl.WORKLOADS[cfg]['name']} partition_size={P} fused={fused} "
+                    f"shared_lens={hint}")
+                d = DecodeSet(cfg, 2, dev, partition=P, fused=fused, hint=hint)
                 s, ms, nb = time_decode(d, 30, LEG_WARMUP)
                 bb = d.batches[0][0]
                 key = d.spec["name"] + ("" if P == pa.PA_PARTITION_BALANCED else f"_fixed_p{P}")
                 key += "" if fused else "_separate_store"
+                key += "" if hint else "_no_shared_lens"
                 extra[key] = dict(
                     tokens_per_s=round(bb.num_seqs * 30 / s, 1), kernel_ms=round(ms, 4),
                     kv_gbs=round(nb / (ms * 1e-3) / 1e9, 1),
                     frac_of_hbm_peak=round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                     bytes_per_launch=int(nb), split=split_name(P), partition_size=P, fused_store=fused,
-                    traffic=measured_traffic(d.spec["name"], split_name(P)),
+                    shared_lens=hint,
+                    traffic=measured_traffic(d.spec["name"], split_name(P)) if hint else None,
                     logical_bytes_per_launch=int(np.mean(d.kv_bytes_logical)))
                 del d
                 torch.cuda.empty_cache()

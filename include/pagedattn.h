@@ -138,10 +138,23 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
  * 256-byte aligned; its contents on entry do not matter and are scratch
  * afterwards. Calls sharing a workspace must not overlap in time (same
  * stream, or synchronised). May be NULL when the size is 0.
+ *
+ * shared_lens: NULL, or int32 [num_seqs] on the device (4-byte aligned):
+ * the number of leading context tokens of sequence i that lie in blocks
+ * other sequences of the batch also read. Prefix sharing (the nano-vllm
+ * page, sections 3.2 and 4.2: full blocks found by their rolling hash, with
+ * reference counts) only ever shares a sequence's leading blocks, so one
+ * count per sequence describes it; the Sequence's num_cached_tokens
+ * (pa_bm_allocate) is such a count. Those tokens are read with a
+ * cache-retaining load policy, so that the sequences sharing them find them
+ * in L2, while every other K/V byte is streamed past the caches. It is a
+ * hint only: the result is bit-identical for any values (or NULL, which
+ * streams everything).
  */
 pa_status pa_decode(void* out, const void* q,
                     const void* k_cache, const void* v_cache,
                     const int32_t* block_tables, const int32_t* context_lens,
+                    const int32_t* shared_lens,
                     int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                     int32_t head_dim, int32_t block_size, int32_t num_blocks,
                     int32_t max_blocks_per_seq, int32_t max_context_len,
@@ -172,6 +185,7 @@ pa_status pa_store_decode(void* out, const void* q,
                           void* k_cache, void* v_cache,
                           const int32_t* slot_mapping,
                           const int32_t* block_tables, const int32_t* context_lens,
+                          const int32_t* shared_lens,
                           int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                           int32_t head_dim, int32_t block_size, int32_t num_blocks,
                           int32_t max_blocks_per_seq, int32_t max_context_len,
@@ -276,13 +290,14 @@ pa_status pa_store_kvcache_fp8(const void* key, const void* value,
  * q and out are dtype (PA_BF16: q . K by bf16 dot products of q with the
  * exactly widened codes; PA_F32: fp32), accumulation fp32. Splits,
  * workspace (pa_decode_workspace_size with the same arguments), shapes and
- * errors as for pa_decode (pa_store_decode_fp8 below is the fused-store
- * form).
+ * errors as for pa_decode, and so is shared_lens (pa_store_decode_fp8 below
+ * is the fused-store form).
  */
 pa_status pa_decode_fp8(void* out, const void* q,
                         const void* k_cache, const void* v_cache,
                         const float* k_scale, const float* v_scale,
                         const int32_t* block_tables, const int32_t* context_lens,
+                        const int32_t* shared_lens,
                         int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                         int32_t head_dim, int32_t block_size, int32_t num_blocks,
                         int32_t max_blocks_per_seq, int32_t max_context_len,
@@ -308,6 +323,7 @@ pa_status pa_store_decode_fp8(void* out, const void* q, const void* key,
                               const float* k_scale, const float* v_scale,
                               const int32_t* slot_mapping,
                               const int32_t* block_tables, const int32_t* context_lens,
+                              const int32_t* shared_lens,
                               int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                               int32_t head_dim, int32_t block_size, int32_t num_blocks,
                               int32_t max_blocks_per_seq, int32_t max_context_len,

@@ -42,15 +42,15 @@ _SIGNATURES = {
     "pa_store_kvcache": ([_c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
                           _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _c_void_p], ctypes.c_int),
     "pa_decode_workspace_size": ([_i32, _i32, _i32, _i32, _i32, _i32], _size),
-    "pa_decode": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+    "pa_decode": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                    _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                    _c_void_p, _size, ctypes.c_int, _c_void_p], ctypes.c_int),
     "pa_store_decode": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p,
-                         _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                         _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                          _i32, _f32, _i32, _c_void_p, _size, ctypes.c_int, _c_void_p], ctypes.c_int),
     "pa_store_decode_fp8": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _c_void_p,
-                             _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32,
-                             _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _c_void_p, _size,
+                             _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                             _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _c_void_p, _size,
                              ctypes.c_int, _c_void_p], ctypes.c_int),
     "pa_prefill_chunk": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                           _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -59,7 +59,7 @@ _SIGNATURES = {
                               _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, ctypes.c_int,
                               _c_void_p], ctypes.c_int),
     "pa_decode_fp8": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
-                       _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                       _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                        _c_void_p, _size, ctypes.c_int, _c_void_p], ctypes.c_int),
     "pa_prefill_chunk_fp8": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                               _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -171,9 +171,20 @@ def decode_workspace(num_seqs, num_heads, num_kv_heads, head_dim, max_context_le
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+def _shared_lens(t, num_seqs, device):
+    """Pointer of the optional shared_lens hint (None stays NULL)."""
+    if t is None:
+        return None
+    _int32_device(t, "shared_lens", device)
+    _need(t.numel() == num_seqs, "shared_lens must have B entries")
+    return _ptr(t)
+
+
 def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
-              partition_size=0, workspace=None, stream=None):
-    """Single-token decode; out and q are [B][Hq][D]."""
+              partition_size=0, workspace=None, stream=None, shared_lens=None):
+    """Single-token decode; out and q are [B][Hq][D]. shared_lens (int32 [B]
+    or None): leading context tokens of each sequence in blocks other
+    sequences also read, a load-policy hint that leaves the result unchanged."""
     lib = load_library()
     B, Hq, D = q.shape
     _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
@@ -191,17 +202,20 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_
     if workspace is not None:
         _need(workspace.device == q.device and workspace.is_contiguous(), "bad workspace")
         ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    sl = _shared_lens(shared_lens, B, q.device)
     st = lib.pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-                       _ptr(context_lens), B, Hq, Hkv, D, bs, NB, block_tables.shape[1],
+                       _ptr(context_lens), sl, B, Hq, Hkv, D, bs, NB, block_tables.shape[1],
                        int(max_context_len), float(scale), int(partition_size), ws_ptr, ws_bytes,
                        _dtype_code(q), _stream(stream))
     _check("pa_decode", st)
 
 
 def pa_store_decode(out, q, key, value, k_cache, v_cache, slot_mapping, block_tables, context_lens,
-                    max_context_len, scale, partition_size=0, workspace=None, stream=None):
+                    max_context_len, scale, partition_size=0, workspace=None, stream=None,
+                    shared_lens=None):
     """Store each sequence's newest K/V row [B][Hkv][D] and decode, in one
-    launch; the same as pa_store_kvcache followed by pa_decode."""
+    launch; the same as pa_store_kvcache followed by pa_decode (shared_lens
+    as for pa_decode)."""
     lib = load_library()
     B, Hq, D = q.shape
     _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
@@ -224,9 +238,10 @@ def pa_store_decode(out, q, key, value, k_cache, v_cache, slot_mapping, block_ta
     if workspace is not None:
         _need(workspace.device == q.device and workspace.is_contiguous(), "bad workspace")
         ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    sl = _shared_lens(shared_lens, B, q.device)
     st = lib.pa_store_decode(_ptr(out), _ptr(q), _ptr(key), _ptr(value), key.stride(0), value.stride(0),
                              _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), _ptr(block_tables),
-                             _ptr(context_lens), B, Hq, Hkv, D, bs, NB, block_tables.shape[1],
+                             _ptr(context_lens), sl, B, Hq, Hkv, D, bs, NB, block_tables.shape[1],
                              int(max_context_len), float(scale), int(partition_size), ws_ptr, ws_bytes,
                              _dtype_code(q), _stream(stream))
     _check("pa_store_decode", st)
@@ -234,7 +249,7 @@ def pa_store_decode(out, q, key, value, k_cache, v_cache, slot_mapping, block_ta
 
 def pa_store_decode_fp8(out, q, key, value, k_cache, v_cache, k_scale, v_scale, slot_mapping,
                         block_tables, context_lens, max_context_len, scale, partition_size=0,
-                        workspace=None, stream=None):
+                        workspace=None, stream=None, shared_lens=None):
     """pa_store_decode over E4M3 pools: quantise each sequence's newest K/V
     row [B][Hkv][D] (the dtype of q) into its slot and decode, in one launch."""
     lib = load_library()
@@ -259,10 +274,11 @@ def pa_store_decode_fp8(out, q, key, value, k_cache, v_cache, k_scale, v_scale, 
     if workspace is not None:
         _need(workspace.device == q.device and workspace.is_contiguous(), "bad workspace")
         ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    sl = _shared_lens(shared_lens, B, q.device)
     st = lib.pa_store_decode_fp8(_ptr(out), _ptr(q), _ptr(key), _ptr(value), key.stride(0),
                                  value.stride(0), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
                                  _ptr(v_scale), _ptr(slot_mapping), _ptr(block_tables),
-                                 _ptr(context_lens), B, Hq, Hkv, D, bs, NB, block_tables.shape[1],
+                                 _ptr(context_lens), sl, B, Hq, Hkv, D, bs, NB, block_tables.shape[1],
                                  int(max_context_len), float(scale), int(partition_size), ws_ptr,
                                  ws_bytes, _dtype_code(q), _stream(stream))
     _check("pa_store_decode_fp8", st)
@@ -303,9 +319,10 @@ def pa_store_kvcache_fp8(key, value, k_cache, v_cache, slot_mapping, k_scale, v_
 
 
 def pa_decode_fp8(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
-                  max_context_len, scale, partition_size=0, workspace=None, stream=None):
+                  max_context_len, scale, partition_size=0, workspace=None, stream=None,
+                  shared_lens=None):
     """Single-token decode over E4M3 pools; out and q are [B][Hq][D] (bf16 or
-    fp32), the workspace as for pa_decode."""
+    fp32), the workspace and shared_lens as for pa_decode."""
     lib = load_library()
     B, Hq, D = q.shape
     _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
@@ -322,8 +339,9 @@ def pa_decode_fp8(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, cont
     if workspace is not None:
         _need(workspace.device == q.device and workspace.is_contiguous(), "bad workspace")
         ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    sl = _shared_lens(shared_lens, B, q.device)
     st = lib.pa_decode_fp8(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
-                           _ptr(v_scale), _ptr(block_tables), _ptr(context_lens), B, Hq, Hkv, D, bs,
+                           _ptr(v_scale), _ptr(block_tables), _ptr(context_lens), sl, B, Hq, Hkv, D, bs,
                            NB, block_tables.shape[1], int(max_context_len), float(scale),
                            int(partition_size), ws_ptr, ws_bytes, _dtype_code(q), _stream(stream))
     _check("pa_decode_fp8", st)

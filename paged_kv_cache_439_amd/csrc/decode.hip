@@ -132,6 +132,7 @@ DecodeParams make_decode_params(const DecodeArgs& a, const DecodePlan& pl) {
   prm.v_cache = static_cast<const char*>(a.v_cache);
   prm.block_tables = a.block_tables;
   prm.context_lens = a.context_lens;
+  prm.shared_lens = a.shared_lens;
   if (pl.total_bytes) {
     char* ws = static_cast<char*>(a.workspace);
     if (pl.balanced) {

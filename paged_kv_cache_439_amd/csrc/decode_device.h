@@ -70,6 +70,7 @@ struct DecodeParams {
   const char* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
+  const int32_t* shared_lens;  // [B] leading tokens in blocks other sequences read, or null
   float* ws_acc;     // fixed split: [B][Hq][max_parts][D]
   float* ws_ml;      // fixed split: [B][Hq][max_parts][2]
   float* part_acc;   // balanced split: [workers][2 slots][Hq][D]
@@ -154,6 +155,18 @@ __device__ __forceinline__ uint4 stream_load(const char* ptr) {
   u32x4 v;
   if constexpr (NT) v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ptr));
   else v = *reinterpret_cast<const u32x4*>(ptr);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// 16-byte load of pool data that other sequences also read (a shared
+// prefix block): the default policy keeps the lines in L2 for them. The
+// compiler must not take these loads for the nontemporal ones of the other
+// branch and hoist the pair out of the branches, which drops the hint from
+// both: the caller issues them in another order (V before K), and they are
+// typed with 8-byte alignment (still one global_load_dwordx4 each).
+__device__ __forceinline__ uint4 shared_load(const char* ptr) {
+  typedef unsigned int u32x4a8 __attribute__((ext_vector_type(4), aligned(8)));
+  const u32x4a8 v = *reinterpret_cast<const u32x4a8*>(ptr);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -480,6 +493,11 @@ __device__ __forceinline__ void attend_range(const DecodeParams& p, int seq, int
   const int row_bytes = p.row_bytes;
   const int lane_off = kvh * D * E + dc * 16;
   const int32_t* bt = p.block_tables + (int64_t)seq * p.max_blocks_per_seq;
+  // Tokens [0, shared_len) lie in blocks that other sequences read too
+  // (prefix sharing shares leading blocks only): they are loaded with the
+  // cache-retaining policy, so that the other readers find them in L2,
+  // while the rest of the context streams past. Only the hint differs.
+  const int shared_len = (NT && p.shared_lens != nullptr) ? p.shared_lens[seq] : 0;
 
   // Spread softmax (GT >= 2): this lane's head, its running maximum and sum.
   // bf16 outputs take the V product on v_dot2 with the probabilities rounded
@@ -535,10 +553,17 @@ __device__ __forceinline__ void attend_range(const DecodeParams& p, int seq, int
       for (int u = 0; u < U; ++u) off[u] = (int64_t)phys[u] * p.block_bytes + (row[u] * row_bytes + lane_off);
     }
     uint4 kr[U], vr[U];
+    if (j0 < shared_len) {  // V first: see shared_load
 #pragma unroll
-    for (int u = 0; u < U; ++u) kr[u] = stream_load<NT>(p.k_cache + off[u]);
+      for (int u = 0; u < U; ++u) vr[u] = shared_load(p.v_cache + off[u]);
 #pragma unroll
-    for (int u = 0; u < U; ++u) vr[u] = stream_load<NT>(p.v_cache + off[u]);
+      for (int u = 0; u < U; ++u) kr[u] = shared_load(p.k_cache + off[u]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) kr[u] = stream_load<NT>(p.k_cache + off[u]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) vr[u] = stream_load<NT>(p.v_cache + off[u]);
+    }
     __builtin_amdgcn_sched_barrier(0);
 
     if constexpr (SPREAD) {

@@ -162,7 +162,8 @@ struct E4M3Scales {
 
 pa_status decode_impl(const char* fn, void* out, const void* q, const void* k_cache,
                       const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
-                      int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                      const int32_t* shared_lens, int32_t num_seqs, int32_t num_heads,
+                      int32_t num_kv_heads, int32_t head_dim,
                       int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                       int32_t max_context_len, float scale, int32_t partition_size, void* workspace,
                       size_t workspace_bytes, pa_dtype dtype, void* stream, const Fusion* fused,
@@ -185,7 +186,7 @@ pa_status decode_impl(const char* fn, void* out, const void* q, const void* k_ca
     return fail(PA_ERR_UNSUPPORTED, "%s: the balanced split supports at most 4096 sequences (got %d)",
                 fn, num_seqs);
   if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
-      !aligned(block_tables, 4) || !aligned(context_lens, 4))
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || !aligned(shared_lens, 4))
     return fail(PA_ERR_UNSUPPORTED, "%s: pointers must be 16-byte aligned (int arrays 4-byte)", fn);
   const int e = elem_size(dtype);
   if (fused) {
@@ -225,7 +226,7 @@ pa_status decode_impl(const char* fn, void* out, const void* q, const void* k_ca
     if (!aligned(workspace, 256))
       return fail(PA_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", fn);
   }
-  pa::DecodeArgs a{out, q, k_cache, v_cache, block_tables, context_lens, num_seqs, num_heads,
+  pa::DecodeArgs a{out, q, k_cache, v_cache, block_tables, context_lens, shared_lens, num_seqs, num_heads,
                    num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                    max_context_len, scale, partition_size, workspace, dtype == PA_BF16,
                    nullptr, nullptr, 0, 0, nullptr, e4m3 != nullptr,
@@ -247,13 +248,14 @@ pa_status decode_impl(const char* fn, void* out, const void* q, const void* k_ca
 extern "C" {
 
 pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-                    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
+                    const int32_t* block_tables, const int32_t* context_lens,
+                    const int32_t* shared_lens, int32_t num_seqs,
                     int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                     int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                     float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
                     pa_dtype dtype, void* stream) {
   try {
-    return decode_impl("pa_decode", out, q, k_cache, v_cache, block_tables, context_lens, num_seqs,
+    return decode_impl("pa_decode", out, q, k_cache, v_cache, block_tables, context_lens, shared_lens, num_seqs,
                        num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                        max_context_len, scale, partition_size, workspace, workspace_bytes, dtype,
                        stream, nullptr, nullptr);
@@ -265,14 +267,15 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
 pa_status pa_store_decode(void* out, const void* q, const void* key, const void* value,
                           int64_t key_tok_stride, int64_t value_tok_stride, void* k_cache,
                           void* v_cache, const int32_t* slot_mapping, const int32_t* block_tables,
-                          const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                          const int32_t* context_lens, const int32_t* shared_lens, int32_t num_seqs,
+                          int32_t num_heads,
                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                           int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                           float scale, int32_t partition_size, void* workspace,
                           size_t workspace_bytes, pa_dtype dtype, void* stream) {
   try {
     const Fusion f{key, value, key_tok_stride, value_tok_stride, slot_mapping};
-    return decode_impl("pa_store_decode", out, q, k_cache, v_cache, block_tables, context_lens,
+    return decode_impl("pa_store_decode", out, q, k_cache, v_cache, block_tables, context_lens, shared_lens,
                        num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                        max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
                        workspace_bytes, dtype, stream, &f, nullptr);
@@ -285,7 +288,8 @@ pa_status pa_store_decode_fp8(void* out, const void* q, const void* key, const v
                               int64_t key_tok_stride, int64_t value_tok_stride, void* k_cache,
                               void* v_cache, const float* k_scale, const float* v_scale,
                               const int32_t* slot_mapping, const int32_t* block_tables,
-                              const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                              const int32_t* context_lens, const int32_t* shared_lens, int32_t num_seqs,
+                              int32_t num_heads,
                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                               int32_t num_blocks, int32_t max_blocks_per_seq,
                               int32_t max_context_len, float scale, int32_t partition_size,
@@ -295,7 +299,7 @@ pa_status pa_store_decode_fp8(void* out, const void* q, const void* key, const v
     const Fusion f{key, value, key_tok_stride, value_tok_stride, slot_mapping};
     const E4M3Scales sc{k_scale, v_scale};
     return decode_impl("pa_store_decode_fp8", out, q, k_cache, v_cache, block_tables,
-                       context_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                       context_lens, shared_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                        num_blocks, max_blocks_per_seq, max_context_len, scale, partition_size,
                        workspace, workspace_bytes, dtype, stream, &f, &sc);
   } catch (...) {
@@ -305,14 +309,15 @@ pa_status pa_store_decode_fp8(void* out, const void* q, const void* key, const v
 
 pa_status pa_decode_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
                         const float* k_scale, const float* v_scale, const int32_t* block_tables,
-                        const int32_t* context_lens, int32_t num_seqs, int32_t num_heads,
+                        const int32_t* context_lens, const int32_t* shared_lens, int32_t num_seqs,
+                        int32_t num_heads,
                         int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                         int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                         float scale, int32_t partition_size, void* workspace,
                         size_t workspace_bytes, pa_dtype dtype, void* stream) {
   try {
     const E4M3Scales sc{k_scale, v_scale};
-    return decode_impl("pa_decode_fp8", out, q, k_cache, v_cache, block_tables, context_lens,
+    return decode_impl("pa_decode_fp8", out, q, k_cache, v_cache, block_tables, context_lens, shared_lens,
                        num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
                        max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
                        workspace_bytes, dtype, stream, nullptr, &sc);

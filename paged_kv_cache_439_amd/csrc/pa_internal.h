@@ -43,6 +43,7 @@ struct DecodeArgs {
   const void* v_cache;
   const int32_t* block_tables;
   const int32_t* context_lens;
+  const int32_t* shared_lens;  // null: no sequence shares blocks (a load-policy hint)
   int32_t num_seqs, num_heads, num_kv_heads, head_dim;
   int32_t block_size, num_blocks, max_blocks_per_seq, max_context_len;
   float scale;

@@ -3,6 +3,7 @@
     python -m paged_kv_cache_439_amd.rocprof_summary trace STATS_CSV OUT_MD --cmd "..."
     python -m paged_kv_cache_439_amd.rocprof_summary traffic FETCH_CSV WRITE_CSV OUT_JSON OUT_MD \
         --copy-bytes N --cmd-fetch "..." --cmd-write "..."
+    python -m paged_kv_cache_439_amd.rocprof_summary counters COUNTER_CSV OUT_MD --cmd "..."
 
 trace:   kernel-trace statistics of this library's kernels as a table.
 traffic: HBM bytes per dispatch from the FETCH_SIZE and WRITE_SIZE counter
@@ -11,6 +12,12 @@ traffic: HBM bytes per dispatch from the FETCH_SIZE and WRITE_SIZE counter
          last three copy dispatches whose WRITE_SIZE equals that size). The
          JSON carries the sha256 of the decode sources it was measured on;
          bench.py reports the traffic only while the sources still match.
+counters: SQ/GRBM counters per dispatch of this library's kernels (median
+         over dispatches), with the MFMA and VALU busy percentages (the
+         MfmaUtil and VALUBusy expressions of rocprofiler-sdk's counter
+         definitions, over the per-XCD active cycles), the shader clock the
+         dispatch ran at and the bf16 MFMA flops the counters saw (512 per
+         SQ_INSTS_VALU_MFMA_MOPS_BF16).
 """
 
 from __future__ import annotations
@@ -127,6 +134,54 @@ def traffic(fetch_csv, write_csv, out_json, out_md, copy_bytes, cmd_fetch, cmd_w
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
+def counters(counter_csv, out_md, cmd, cus=256, simds_per_cu=4, xcds=8):
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    names, dur = {}, {}
+    for r in csv.DictReader(open(counter_csv)):
+        if not _ours(r["Kernel_Name"]):
+            continue
+        d = int(r["Dispatch_Id"])
+        names[d] = _short(r["Kernel_Name"])
+        dur[d] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+        per[d][r["Counter_Name"]] += float(r["Counter_Value"])
+    by_kernel = collections.defaultdict(list)
+    for d in sorted(per):
+        by_kernel[names[d]].append(d)
+    cols = sorted({k for c in per.values() for k in c})
+
+    def med(xs):
+        xs = sorted(xs)
+        return xs[len(xs) // 2]
+
+    lines = ["# Counters per dispatch: libpagedattn kernels", "", "Command:", "", "```", cmd, "```", "",
+             f"Each figure is the median over a kernel's dispatches. GRBM_GUI_ACTIVE is reported summed over "
+             f"the {xcds} XCDs, so the elapsed cycles of a dispatch are GRBM_GUI_ACTIVE / {xcds}; divided by "
+             f"the dispatch's duration they give the shader clock it ran at.", "",
+             f"Derived ({cus} CUs, {cus * simds_per_cu} SIMDs):", "",
+             f"- MFMA busy % = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {xcds} x SIMDs) x 100",
+             f"- VALU busy % = SQ_ACTIVE_INST_VALU / (GRBM_GUI_ACTIVE / {xcds} x CUs) x 100",
+             "- bf16 MFMA GFLOP = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / 1e9 (masked products included)", "",
+             "| kernel | dispatches | us | clock GHz | MFMA busy % | VALU busy % | bf16 MFMA GFLOP |",
+             "|---|---|---|---|---|---|---|"]
+    avg = {}
+    for k, ds in sorted(by_kernel.items()):
+        a = {c: med([per[d].get(c, 0.0) for d in ds]) for c in cols}
+        avg[k] = a
+        t = med([dur[d] for d in ds])
+        cyc = a.get("GRBM_GUI_ACTIVE", 0.0) / xcds
+        nan = float("nan")
+        mf = 100 * a["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * cus * simds_per_cu) if cyc and "SQ_VALU_MFMA_BUSY_CYCLES" in a else nan
+        va = 100 * a["SQ_ACTIVE_INST_VALU"] / (cyc * cus) if cyc and "SQ_ACTIVE_INST_VALU" in a else nan
+        fl = a.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", nan) * 512 / 1e9
+        ghz = cyc / t / 1e9 if t > 0 else nan
+        lines.append(f"| `{k}` | {len(ds)} | {t * 1e6:.1f} | {ghz:.2f} | {mf:.1f} | {va:.1f} | {fl:.2f} |")
+    lines += ["", "Raw medians per dispatch:", "", "| kernel | " + " | ".join(cols) + " |",
+              "|---|" + "---|" * len(cols)]
+    for k, a in sorted(avg.items()):
+        lines.append(f"| `{k}` | " + " | ".join(f"{a[c]:.4g}" for c in cols) + " |")
+    open(out_md, "w").write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -142,8 +197,14 @@ def main():
     f.add_argument("--copy-bytes", type=int, required=True)
     f.add_argument("--cmd-fetch", required=True)
     f.add_argument("--cmd-write", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("counter_csv")
+    c.add_argument("out_md")
+    c.add_argument("--cmd", required=True)
     a = ap.parse_args()
-    if a.mode == "trace":
+    if a.mode == "counters":
+        counters(a.counter_csv, a.out_md, a.cmd)
+    elif a.mode == "trace":
         trace(a.stats_csv, a.out_md, a.cmd)
     else:
         traffic(a.fetch_csv, a.write_csv, a.out_json, a.out_md, a.copy_bytes, a.cmd_fetch, a.cmd_write)

@@ -135,6 +135,21 @@ class Batch:
         return int(self.context_lens.max()) if len(self.context_lens) else 0
 
     @property
+    def shared_lens(self) -> np.ndarray:
+        """int32 [B]: leading context tokens of each sequence that lie in the
+        shared prefix blocks (the decode calls' load-policy hint); 0 for a
+        sequence that shares nothing."""
+        shared = set(int(b) for b in self.shared_blocks)
+        out = np.zeros(self.num_seqs, dtype=np.int32)
+        bs = self.block_size
+        for i, L in enumerate(self.context_lens.tolist()):
+            k = 0
+            while k * bs < L and int(self.block_tables[i, k]) in shared:
+                k += 1
+            out[i] = min(k * bs, L)
+        return out
+
+    @property
     def max_query_len(self) -> int:
         if self.query_start_loc is None:
             return 1

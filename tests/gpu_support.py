@@ -37,7 +37,16 @@ def gpu_store(batch, arrs=None):
     pa.pa_store_kvcache(batch.key, batch.value, batch.k_cache, batch.v_cache, arrs["slots"])
 
 
-def gpu_decode(batch, partition_size, arrs=None, workspace=None):
+def shared_lens_arg(batch, hint):
+    """The decode calls' shared_lens: None, the batch's own (hint=True), or a
+    given int32 array."""
+    if hint is None or hint is False:
+        return None
+    vals = batch.shared_lens if hint is True else np.asarray(hint, dtype=np.int32)
+    return torch.from_numpy(vals).to(batch.q.device)
+
+
+def gpu_decode(batch, partition_size, arrs=None, workspace=None, hint=None):
     arrs = arrs or device_arrays(batch)
     dev = batch.q.device
     if workspace is None:
@@ -45,11 +54,12 @@ def gpu_decode(batch, partition_size, arrs=None, workspace=None):
                                         batch.head_dim, batch.max_context_len, partition_size, dev)
     out = torch.full_like(batch.q, float("nan"))
     pa.pa_decode(out, batch.q, batch.k_cache, batch.v_cache, arrs["tables"], arrs["lens"],
-                 batch.max_context_len, batch.scale, partition_size, workspace)
+                 batch.max_context_len, batch.scale, partition_size, workspace,
+                 shared_lens=shared_lens_arg(batch, hint))
     return out
 
 
-def gpu_store_decode(batch, partition_size, arrs=None, workspace=None):
+def gpu_store_decode(batch, partition_size, arrs=None, workspace=None, hint=None):
     """The fused store + decode call."""
     arrs = arrs or device_arrays(batch)
     dev = batch.q.device
@@ -59,7 +69,7 @@ def gpu_store_decode(batch, partition_size, arrs=None, workspace=None):
     out = torch.full_like(batch.q, float("nan"))
     pa.pa_store_decode(out, batch.q, batch.key, batch.value, batch.k_cache, batch.v_cache, arrs["slots"],
                        arrs["tables"], arrs["lens"], batch.max_context_len, batch.scale, partition_size,
-                       workspace)
+                       workspace, shared_lens=shared_lens_arg(batch, hint))
     return out
 
 
@@ -95,12 +105,12 @@ def check_close(got, ref, dtype, what):
     return float(err.max()), float(err.mean())
 
 
-def decode_parity(batch, partition_size, seqs=None, heads=None):
+def decode_parity(batch, partition_size, seqs=None, heads=None, hint=None):
     """Store + decode on the GPU; oracle on the host copies taken before."""
     hb, kp, vp = oracle_inputs(batch, seqs)
     arrs = device_arrays(batch)
     gpu_store(batch, arrs)
-    out = gpu_decode(batch, partition_size, arrs)
+    out = gpu_decode(batch, partition_size, arrs, hint=hint)
     torch.cuda.synchronize()
     got = as_f64(out)
     if seqs is None:
@@ -209,7 +219,7 @@ def gpu_store_fp8(batch, arrs=None):
                             batch.k_scale, batch.v_scale)
 
 
-def gpu_decode_fp8(batch, partition_size, arrs=None, workspace=None):
+def gpu_decode_fp8(batch, partition_size, arrs=None, workspace=None, hint=None):
     arrs = arrs or device_arrays(batch)
     dev = batch.q.device
     if workspace is None:
@@ -218,7 +228,7 @@ def gpu_decode_fp8(batch, partition_size, arrs=None, workspace=None):
     out = torch.full_like(batch.q, float("nan"))
     pa.pa_decode_fp8(out, batch.q, batch.k_cache, batch.v_cache, batch.k_scale, batch.v_scale,
                      arrs["tables"], arrs["lens"], batch.max_context_len, batch.scale, partition_size,
-                     workspace)
+                     workspace, shared_lens=shared_lens_arg(batch, hint))
     return out
 
 
@@ -226,7 +236,7 @@ def scales_np(batch):
     return batch.k_scale.cpu().numpy().astype(np.float64), batch.v_scale.cpu().numpy().astype(np.float64)
 
 
-def decode_fp8_parity(batch, partition_size, seqs=None):
+def decode_fp8_parity(batch, partition_size, seqs=None, hint=None):
     """E4M3 store + decode on the GPU; the oracle's E4M3 store and decode on
     host copies of the same inputs (all sequences, or the given subset)."""
     import oracle.fp8 as of8
@@ -236,7 +246,7 @@ def decode_fp8_parity(batch, partition_size, seqs=None):
                                    batch.block_size, ks, vs, batch.dtype)
     arrs = device_arrays(batch)
     gpu_store_fp8(batch, arrs)
-    out = gpu_decode_fp8(batch, partition_size, arrs)
+    out = gpu_decode_fp8(batch, partition_size, arrs, hint=hint)
     torch.cuda.synchronize()
     got = as_f64(out)
     ref = of8.decode_fp8(hb.q, kp, vp, ks, vs, hb.block_tables, hb.context_lens, batch.scale,

@@ -51,12 +51,12 @@ FAKE = ctypes.c_void_p(0x100000)  # 16-byte aligned, never dereferenced on these
 
 
 def _decode(lib, **kw):
-    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, B=4, Hq=8, Hkv=8, D=64, bs=16,
-             NB=64, MB=7, maxL=100, scale=0.125, P=0, ws=None, wsb=0, dtype=0)
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, sl=None, B=4, Hq=8, Hkv=8, D=64,
+             bs=16, NB=64, MB=7, maxL=100, scale=0.125, P=0, ws=None, wsb=0, dtype=0)
     a.update(kw)
-    return lib.pa_decode(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["B"], a["Hq"], a["Hkv"],
-                         a["D"], a["bs"], a["NB"], a["MB"], a["maxL"], a["scale"], a["P"], a["ws"],
-                         a["wsb"], a["dtype"], None)
+    return lib.pa_decode(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["sl"], a["B"], a["Hq"],
+                         a["Hkv"], a["D"], a["bs"], a["NB"], a["MB"], a["maxL"], a["scale"], a["P"],
+                         a["ws"], a["wsb"], a["dtype"], None)
 
 
 def test_decode_rejections(lib):
@@ -68,6 +68,7 @@ def test_decode_rejections(lib):
     assert _decode(lib, bs=24) == PA_ERR_UNSUPPORTED
     assert _decode(lib, bs=4) == PA_ERR_UNSUPPORTED
     assert _decode(lib, maxL=113) == PA_ERR_INVALID_ARG   # > 7 blocks x 16
+    assert _decode(lib, sl=ctypes.c_void_p(0x100002)) == PA_ERR_UNSUPPORTED  # shared_lens misaligned
     assert _decode(lib, P=24) == PA_ERR_INVALID_ARG
     assert _decode(lib, scale=float("nan")) == PA_ERR_INVALID_ARG
     assert _decode(lib, dtype=7) == PA_ERR_INVALID_ARG
@@ -126,11 +127,11 @@ def test_balanced_rejections(lib):
 
 def _store_decode(lib, **kw):
     a = dict(out=FAKE, q=FAKE, key=FAKE, value=FAKE, ks=512, vs=512, k=FAKE, v=FAKE, slots=FAKE,
-             bt=FAKE, cl=FAKE, B=4, Hq=8, Hkv=8, D=64, bs=16, NB=64, MB=7, maxL=100, scale=0.125,
-             P=0, ws=None, wsb=0, dtype=0)
+             bt=FAKE, cl=FAKE, sl=None, B=4, Hq=8, Hkv=8, D=64, bs=16, NB=64, MB=7, maxL=100,
+             scale=0.125, P=0, ws=None, wsb=0, dtype=0)
     a.update(kw)
     return lib.pa_store_decode(a["out"], a["q"], a["key"], a["value"], a["ks"], a["vs"], a["k"], a["v"],
-                               a["slots"], a["bt"], a["cl"], a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"],
+                               a["slots"], a["bt"], a["cl"], a["sl"], a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"],
                                a["NB"], a["MB"], a["maxL"], a["scale"], a["P"], a["ws"], a["wsb"],
                                a["dtype"], None)
 
@@ -206,11 +207,12 @@ def test_prefill_fp8_rejections(lib):
 
 
 def _decode_fp8(lib, **kw):
-    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, kscale=FAKE, vscale=FAKE, bt=FAKE, cl=FAKE, B=4, Hq=8,
-             Hkv=8, D=64, bs=16, NB=64, MB=7, maxL=100, scale=0.125, P=0, ws=None, wsb=0, dtype=1)
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, kscale=FAKE, vscale=FAKE, bt=FAKE, cl=FAKE, sl=None,
+             B=4, Hq=8, Hkv=8, D=64, bs=16, NB=64, MB=7, maxL=100, scale=0.125, P=0, ws=None, wsb=0,
+             dtype=1)
     a.update(kw)
     return lib.pa_decode_fp8(a["out"], a["q"], a["k"], a["v"], a["kscale"], a["vscale"], a["bt"],
-                             a["cl"], a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"], a["MB"],
+                             a["cl"], a["sl"], a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"], a["MB"],
                              a["maxL"], a["scale"], a["P"], a["ws"], a["wsb"], a["dtype"], None)
 
 
@@ -292,11 +294,12 @@ def test_mixed_fp8_rejections(lib):
 
 def _store_decode_fp8(lib, **kw):
     a = dict(out=FAKE, q=FAKE, key=FAKE, value=FAKE, ks=512, vs=512, k=FAKE, v=FAKE, kscale=FAKE,
-             vscale=FAKE, slots=FAKE, bt=FAKE, cl=FAKE, B=4, Hq=8, Hkv=8, D=64, bs=16, NB=64, MB=7,
-             maxL=100, scale=0.125, P=0, ws=None, wsb=0, dtype=1)
+             vscale=FAKE, slots=FAKE, bt=FAKE, cl=FAKE, sl=None, B=4, Hq=8, Hkv=8, D=64, bs=16,
+             NB=64, MB=7, maxL=100, scale=0.125, P=0, ws=None, wsb=0, dtype=1)
     a.update(kw)
     return lib.pa_store_decode_fp8(a["out"], a["q"], a["key"], a["value"], a["ks"], a["vs"], a["k"],
-                                   a["v"], a["kscale"], a["vscale"], a["slots"], a["bt"], a["cl"], a["B"],
+                                   a["v"], a["kscale"], a["vscale"], a["slots"], a["bt"], a["cl"],
+                                   a["sl"], a["B"],
                                    a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"], a["MB"], a["maxL"],
                                    a["scale"], a["P"], a["ws"], a["wsb"], a["dtype"], None)
 
