@@ -156,7 +156,8 @@ def counters(counter_csv, out_md, cmd, cus=256, simds_per_cu=4, xcds=8):
     lines = ["# Counters per dispatch: libpagedattn kernels", "", "Command:", "", "```", cmd, "```", "",
              f"Each figure is the median over a kernel's dispatches. GRBM_GUI_ACTIVE is reported summed over "
              f"the {xcds} XCDs, so the elapsed cycles of a dispatch are GRBM_GUI_ACTIVE / {xcds}; divided by "
-             f"the dispatch's duration they give the shader clock it ran at.", "",
+             f"the dispatch's duration they give the shader clock it ran at (shown for dispatches of 50 us "
+             f"or more: the counters' window is a few us longer than the dispatch).", "",
              f"Derived ({cus} CUs, {cus * simds_per_cu} SIMDs):", "",
              f"- MFMA busy % = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {xcds} x SIMDs) x 100",
              f"- VALU busy % = SQ_ACTIVE_INST_VALU / (GRBM_GUI_ACTIVE / {xcds} x CUs) x 100",
@@ -173,8 +174,10 @@ def counters(counter_csv, out_md, cmd, cus=256, simds_per_cu=4, xcds=8):
         mf = 100 * a["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * cus * simds_per_cu) if cyc and "SQ_VALU_MFMA_BUSY_CYCLES" in a else nan
         va = 100 * a["SQ_ACTIVE_INST_VALU"] / (cyc * cus) if cyc and "SQ_ACTIVE_INST_VALU" in a else nan
         fl = a.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", nan) * 512 / 1e9
-        ghz = cyc / t / 1e9 if t > 0 else nan
-        lines.append(f"| `{k}` | {len(ds)} | {t * 1e6:.1f} | {ghz:.2f} | {mf:.1f} | {va:.1f} | {fl:.2f} |")
+        # the counters' window is a few us longer than the dispatch itself,
+        # so the clock is only given for dispatches long enough to hide that
+        ghz = f"{cyc / t / 1e9:.2f}" if t >= 50e-6 else "-"
+        lines.append(f"| `{k}` | {len(ds)} | {t * 1e6:.1f} | {ghz} | {mf:.1f} | {va:.1f} | {fl:.2f} |")
     lines += ["", "Raw medians per dispatch:", "", "| kernel | " + " | ".join(cols) + " |",
               "|---|" + "---|" * len(cols)]
     for k, a in sorted(avg.items()):
