@@ -78,6 +78,7 @@ struct DecodeParams {
   int32_t* ws_pfx;   // balanced split: chunk prefix sums [B + 1]
   int32_t num_seqs, workers;  // balanced split: workers per unit
   int32_t num_heads, num_kv_heads, group, n_sub, units;
+  int32_t pair;         // balanced split: 1 when a unit is a pair of KV heads (units = Hkv / 2)
   int32_t bs_log2, num_blocks, max_blocks_per_seq, max_context_len;
   int32_t partition, max_parts;
   int32_t row_bytes;    // Hkv * D * e: bytes between consecutive tokens of a block
@@ -468,7 +469,13 @@ __device__ __forceinline__ void pv_token_pair(const uint4& vu, const uint4& vu1,
 // KT is the pools' storage type: T itself, or uint8_t for E4M3 codes, whose
 // logits are multiplied by sm (the logit scale times the head's K scale)
 // and whose weighted value sums still lack the head's V scale.
-template <typename T, typename KT, int D, int GT, int U, bool UNIFORM_BLOCK>
+//
+// PAIR (E4M3 pools, head_dim 64, one query head per wave): the wave reads two
+// adjacent KV heads, so that each token row it reads is one whole 128-byte
+// line; lanes 0-3 of every 8 hold the first head's slices and lanes 4-7 the
+// second's, kvh is this lane's own head, and each head keeps its own
+// online-softmax state (the dot products reduce over 4 lanes).
+template <typename T, typename KT, int D, int GT, int U, bool UNIFORM_BLOCK, bool PAIR = false>
 __device__ __forceinline__ void attend_range(const DecodeParams& p, int seq, int kvh, int lane,
                                              int tok_begin, int tok_end,
                                              const QSlice<T, KT> (&qv)[GT], float sm,
@@ -483,11 +490,13 @@ __device__ __forceinline__ void attend_range(const DecodeParams& p, int seq, int
   constexpr int E = ElemTraits<KT>::E;
   constexpr int EPL = 16 / E;     // elements per 16-byte lane slice
   constexpr int LPT = D / EPL;    // lanes per token row of one head
-  constexpr int TPW = 64 / LPT;   // token rows per wave-wide load
+  constexpr int LPR = PAIR ? 2 * LPT : LPT;  // lanes per token row the wave reads
+  constexpr int TPW = 64 / LPR;   // token rows per wave-wide load
   constexpr int CT = U * TPW;     // tokens per chunk
-  constexpr bool NT = D * E >= 128;  // whole lines per head row: streaming hint
+  constexpr bool NT = LPR * 16 >= 128;  // whole lines per row read: streaming hint
+  static_assert(!PAIR || (GT == 1 && LPR * 16 == 128), "pairs: one head per lane group, whole lines");
   const int dc = lane % LPT;
-  const int tr = lane / LPT;
+  const int tr = lane / LPR;
   const int bs_log2 = p.bs_log2;
   const int bs_mask = (1 << bs_log2) - 1;
   const int row_bytes = p.row_bytes;
@@ -967,11 +976,13 @@ __device__ __forceinline__ void merge_pieces(const DecodeParams& p, int seq, int
 // The balanced split's workers, as workgroup wg of num_wgs (each workgroup
 // holds 4 waves, i.e. 4 (unit, worker) pairs). MAXS bounds num_seqs (the
 // chunk prefix sums live in LDS).
-template <typename T, typename KT, int D, int GT, int U, bool UNIFORM_BLOCK, int MAXS>
+template <typename T, typename KT, int D, int GT, int U, bool UNIFORM_BLOCK, int MAXS,
+          bool PAIR = false>
 __device__ __forceinline__ void balanced_body(const DecodeParams& p, int wg, int num_wgs) {
   constexpr int EPL = 16 / ElemTraits<KT>::E;
   constexpr int LPT = D / EPL;
-  constexpr int TPW = 64 / LPT;
+  constexpr int LPR = PAIR ? 2 * LPT : LPT;  // lanes per token row the wave reads
+  constexpr int TPW = 64 / LPR;
   constexpr int CT = U * TPW;
   __shared__ int32_t pfx[MAXS + 1];
   if constexpr (fused_store_supported<T, KT>()) {
@@ -992,10 +1003,11 @@ __device__ __forceinline__ void balanced_body(const DecodeParams& p, int wg, int
   const int c0 = (int)((int64_t)w * C / p.workers);
   const int c1 = (int)((int64_t)(w + 1) * C / p.workers);
   if (c0 >= c1) return;
-  const int kvh = unit / p.n_sub;
-  const int h0 = kvh * p.group + (unit - kvh * p.n_sub) * GT;
+  // this lane's KV head (a pair's first or second) and first query head
+  const int kvh = PAIR ? 2 * unit + (lane % LPR) / LPT : unit / p.n_sub;
+  const int h0 = PAIR ? kvh : kvh * p.group + (unit - kvh * p.n_sub) * GT;
   const int dc = lane % LPT;
-  const int tr = lane / LPT;
+  const int tr = lane / LPR;
   const float sm = logit_scale<KT>(p, kvh);
 
   // Pieces are taken from the end of the range backwards. The last piece
@@ -1019,10 +1031,10 @@ __device__ __forceinline__ void balanced_body(const DecodeParams& p, int wg, int
     load_q<T, KT, D, GT>(p, i, h0, dc, qv);
     WaveState<GT, EPL> st;
     st.reset();
-    attend_range<T, KT, D, GT, U, UNIFORM_BLOCK>(p, i, kvh, lane, (ps - cb) * CT,
-                                                 min((pe - cb) * CT, L), qv, sm, st);
+    attend_range<T, KT, D, GT, U, UNIFORM_BLOCK, PAIR>(p, i, kvh, lane, (ps - cb) * CT,
+                                                       min((pe - cb) * CT, L), qv, sm, st);
     apply_v_scale<KT, GT, EPL>(p, kvh, st.acc);
-    merge_row_groups<LPT, GT, EPL>(st.m, st.l, st.acc);
+    merge_row_groups<LPR, GT, EPL>(st.m, st.l, st.acc);
     if (tr == 0) {
       if (ps == cb && pe == ce) {
         store_output<T, D, GT, EPL>(p, i, h0, dc, st);
@@ -1048,9 +1060,9 @@ __device__ __forceinline__ void balanced_body(const DecodeParams& p, int wg, int
   }
 }
 
-template <typename T, typename KT, int D, int GT, int U, bool UNIFORM_BLOCK>
+template <typename T, typename KT, int D, int GT, int U, bool UNIFORM_BLOCK, bool PAIR = false>
 __global__ __launch_bounds__(256, DECODE_BAL_WAVES_PER_SIMD) void paged_decode_balanced_kernel(DecodeParams p) {
-  balanced_body<T, KT, D, GT, U, UNIFORM_BLOCK, BAL_MAX_SEQS>(p, blockIdx.x, gridDim.x);
+  balanced_body<T, KT, D, GT, U, UNIFORM_BLOCK, BAL_MAX_SEQS, PAIR>(p, blockIdx.x, gridDim.x);
 }
 
 // One wave per (sequence, unit): combine the partial states the workers
@@ -1063,7 +1075,7 @@ __global__ __launch_bounds__(256) void paged_decode_balanced_merge_kernel(Decode
   constexpr int LPT = D / EPL;
   const int lane = threadIdx.x & 63;
   const int unit = blockIdx.y * 4 + (threadIdx.x >> 6);
-  if (unit >= p.units) return;
+  if (unit >= (p.units << p.pair)) return;  // one KV head per unit (a pair's heads separately)
   const int seq = blockIdx.x;
   const int kvh = unit / p.n_sub;
   const int h0 = kvh * p.group + (unit - kvh * p.n_sub) * GT;

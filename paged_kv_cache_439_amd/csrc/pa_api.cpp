@@ -2,6 +2,7 @@
 // the kernel launchers. No exception crosses the interface; every failure is
 // a pa_status plus a per-thread message (pa_last_error).
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -136,9 +137,14 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num
       head_dim <= 0 || max_context_len <= 0 ||
       (partition_size < 0 && partition_size != PA_PARTITION_BALANCED))
     return 0;
-  return pa::plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
-                         partition_size)
-      .total_bytes;
+  // the larger of the two plans: over E4M3 pools the balanced split may pair
+  // KV heads, which doubles its workers (the same call serves pa_decode_fp8)
+  return std::max(pa::plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
+                                  partition_size, false)
+                      .total_bytes,
+                  pa::plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
+                                  partition_size, true)
+                      .total_bytes);
 }
 
 }  // extern "C"
@@ -214,7 +220,7 @@ pa_status decode_impl(const char* fn, void* out, const void* q, const void* k_ca
       return fail(PA_ERR_UNSUPPORTED, "%s: k_scale/v_scale must be 4-byte aligned", fn);
   }
   const pa::DecodePlan plan = pa::plan_decode(num_seqs, num_heads, num_kv_heads, head_dim,
-                                              max_context_len, partition_size);
+                                              max_context_len, partition_size, e4m3 != nullptr);
   if ((plan.units + 3) / 4 > 65535) return fail(PA_ERR_UNSUPPORTED, "%s: too many heads", fn);
   if (plan.total_bytes) {
     if (!workspace)

@@ -88,12 +88,15 @@ struct DecodePlan {
   int32_t partition;       // tokens per partition (> 0)
   int32_t max_parts;       // partitions of the longest context
   bool balanced;           // balanced split: equal chunk ranges per worker
+  bool pair;               // balanced split over E4M3 pools, head_dim 64, one query head per KV
+                           // head: a unit is a pair of adjacent KV heads (units = Hkv / 2)
   int32_t workers;         // balanced split: workers (waves) per unit
   size_t acc_bytes, ml_bytes, pfx_bytes, total_bytes;  // workspace regions (0 if unsplit)
 };
 
 DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                       int32_t head_dim, int32_t max_context_len, int32_t partition_size);
+                       int32_t head_dim, int32_t max_context_len, int32_t partition_size,
+                       bool kv_e4m3 = false);
 
 hipError_t launch_store(const StoreArgs& a, hipStream_t stream);
 hipError_t launch_store_e4m3(const StoreE4M3Args& a, hipStream_t stream);

@@ -102,27 +102,39 @@ def test_workspace_sizes(lib):
 def test_balanced_workspace_size(lib):
     """Balanced split: 2 waves per SIMD of a 256-CU device (assumed when no
     device is visible), each wave with two (acc[D], m, l) slots per head of
-    its unit, plus the chunk prefix sums."""
+    its unit, plus the chunk prefix sums. The size serves E4M3 pools too,
+    where head_dim 64 with one query head per KV head and an even number of
+    KV heads pairs the heads (half the units, twice the workers): the larger
+    of the two."""
     if _gpu_visible():
         pytest.skip("the size depends on the visible device")
     r = lambda x: (x + 255) // 256 * 256
-    for (B, Hq, Hkv, D) in [(4, 8, 8, 64), (512, 32, 8, 128), (7, 12, 4, 64)]:
+
+    def size(B, Hq, units, D):
+        workers = (2 * 4 * 256) // units
+        slots = workers * 2 * Hq
+        return r(slots * D * 4) + r(slots * 2 * 4) + r((B + 1) * 4)
+
+    for (B, Hq, Hkv, D) in [(4, 8, 8, 64), (512, 32, 8, 128), (7, 12, 4, 64), (64, 12, 12, 64),
+                            (5, 5, 5, 64), (3, 6, 6, 128)]:
         G = Hq // Hkv
         gt = 4 if G % 4 == 0 else 2 if G % 2 == 0 else 1
         units = Hkv * (G // gt)
-        workers = (2 * 4 * 256) // units
-        slots = workers * 2 * Hq
-        want = r(slots * D * 4) + r(slots * 2 * 4) + r((B + 1) * 4)
-        assert lib.pa_decode_workspace_size(B, Hq, Hkv, D, 4096, -1) == want
+        want = size(B, Hq, units, D)
+        if D == 64 and G == 1 and Hkv % 2 == 0:
+            want = max(want, size(B, Hq, Hkv // 2, D))
+        assert lib.pa_decode_workspace_size(B, Hq, Hkv, D, 4096, -1) == want, (B, Hq, Hkv, D)
 
 
 def test_balanced_rejections(lib):
-    need = lib.pa_decode_workspace_size(4, 8, 8, 64, 100, -1)
+    # head_dim 128: no KV-head pairing, so the size is exactly what the call
+    # checks, and one byte less is rejected before anything is launched
+    need = lib.pa_decode_workspace_size(4, 8, 8, 128, 100, -1)
     assert need > 0
-    assert _decode(lib, P=-1) == PA_ERR_WORKSPACE
-    assert _decode(lib, P=-1, ws=FAKE, wsb=need - 1) == PA_ERR_WORKSPACE
-    assert _decode(lib, P=-2, ws=FAKE, wsb=need) == PA_ERR_INVALID_ARG
-    assert _decode(lib, P=-1, B=4097, ws=FAKE, wsb=1 << 40) == PA_ERR_UNSUPPORTED
+    assert _decode(lib, D=128, P=-1) == PA_ERR_WORKSPACE
+    assert _decode(lib, D=128, P=-1, ws=FAKE, wsb=need - 1) == PA_ERR_WORKSPACE
+    assert _decode(lib, D=128, P=-2, ws=FAKE, wsb=need) == PA_ERR_INVALID_ARG
+    assert _decode(lib, D=128, P=-1, B=4097, ws=FAKE, wsb=1 << 40) == PA_ERR_UNSUPPORTED
 
 
 def _store_decode(lib, **kw):
@@ -217,6 +229,10 @@ def _decode_fp8(lib, **kw):
 
 
 def test_decode_fp8_rejections(lib):
+    # E4M3, head_dim 64, 8 KV heads: the balanced split pairs the heads and
+    # needs the whole workspace size; one byte less is rejected up front
+    need = lib.pa_decode_workspace_size(4, 8, 8, 64, 100, -1)
+    assert _decode_fp8(lib, P=-1, ws=FAKE, wsb=need - 1) == PA_ERR_WORKSPACE
     assert _decode_fp8(lib, B=0) == PA_OK
     assert _decode_fp8(lib, kscale=None) == PA_ERR_INVALID_ARG
     assert _decode_fp8(lib, vscale=None) == PA_ERR_INVALID_ARG

@@ -141,6 +141,13 @@ FP8_DECODE_VARIANTS = {
     # bf16 group 3, D=64, block 8
     "group3_d64": (2, dict(num_seqs=5, num_heads=12, num_kv_heads=4, lens=("uniform", 1, 600),
                            max_context=640, block_size=8), [0, 32, -1]),
+    # MHA D=64 with an odd number of KV heads (the balanced split cannot pair them)
+    "mha64_odd_heads": (2, dict(num_seqs=7, num_heads=5, num_kv_heads=5, lens=("uniform", 1, 900),
+                                max_context=960, block_size=32), [-1, 0]),
+    # fp32 q/out, MHA D=64 over 16-token blocks: KV head pairs whose 64-token chunks straddle blocks
+    "f32_mha64_pairs_bs16": (2, dict(dtype="f32", num_seqs=9, num_heads=6, num_kv_heads=6,
+                                     lens=("uniform", 1, 700), max_context=704, block_size=16),
+                             [-1, 64]),
 }
 
 

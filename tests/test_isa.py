@@ -43,13 +43,16 @@ def kernel_body(asm, pattern):
 
 
 # balanced and fixed-split kernels over bf16 pools, D 128, 1/2/4 heads per
-# wave, 8 loads per lane per tensor (mangled template arguments)
+# wave, 8 loads per lane per tensor, and the paired E4M3 kernel (mangled
+# template arguments)
 STREAMING = [
     "paged_decode_balanced_kernelIttLi128ELi1ELi8ELb1E",
     "paged_decode_balanced_kernelIttLi128ELi2ELi8ELb1E",
     "paged_decode_balanced_kernelIttLi128ELi4ELi8ELb1E",
     "paged_decode_balanced_kernelIttLi64ELi1ELi8ELb1E",
     "paged_decode_kernelIttLi128ELi2ELi8ELb1E",
+    # E4M3 pools, head_dim 64, one head per wave: KV head pairs (whole lines)
+    "paged_decode_balanced_kernelIthLi64ELi1ELi8ELb1ELb1E",
 ]
 
 
