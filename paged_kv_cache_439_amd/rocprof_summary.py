@@ -177,7 +177,8 @@ def counters(counter_csv, out_md, cmd, cus=256, simds_per_cu=4, xcds=8):
         # the counters' window is a few us longer than the dispatch itself,
         # so the clock is only given for dispatches long enough to hide that
         ghz = f"{cyc / t / 1e9:.2f}" if t >= 50e-6 else "-"
-        lines.append(f"| `{k}` | {len(ds)} | {t * 1e6:.1f} | {ghz} | {mf:.1f} | {va:.1f} | {fl:.2f} |")
+        fmt = lambda x, d: "-" if x != x else f"{x:.{d}f}"  # a counter the pass did not take
+        lines.append(f"| `{k}` | {len(ds)} | {t * 1e6:.1f} | {ghz} | {fmt(mf, 1)} | {fmt(va, 1)} | {fmt(fl, 2)} |")
     lines += ["", "Raw medians per dispatch:", "", "| kernel | " + " | ".join(cols) + " |",
               "|---|" + "---|" * len(cols)]
     for k, a in sorted(avg.items()):
