@@ -19,7 +19,9 @@ algorithmic K+V bytes per launch over its average duration: one pair of HIP
 events on the launch stream around the timed run of launches, divided by the
 number of launches (an event pair around every launch would add GPU time to
 each step). `cpu_baseline` is the
-CPU oracle on a bounded sample of the same workload, single-threaded. `extra`
+CPU oracle on a bounded sample of the same workload, single-threaded, and
+under `parallel` the same oracle's decode parallel over sequences in a
+fork-based pool of up to 16 processes (forked before any GPU call). `extra`
 reports the other workloads (GQA decode with shared prefix, GQA decode at 512
 sequences, each with the balanced split and with its fixed-slice split, the
 three decode workloads over 8-bit E4M3 pools, chunked prefill, and a
@@ -380,6 +382,77 @@ def cpu_baseline(ds, budget_s=12.0):
                        f"{secs:.1f} s on 1 thread")
 
 
+_PAR = None  # the host batch the parallel oracle's forked workers inherit
+
+
+def _par_worker(task):
+    """One forked worker: decode sequences w, w+n, ... of the inherited batch
+    (wrapping around) until budget_s has passed; returns (sequences, tokens)."""
+    import oracle.attention as oa
+    from threadpoolctl import threadpool_limits
+    w, n, budget_s = task
+    hb, kp, vp, scale, bs, dtype = _PAR
+    B = len(hb.context_lens)
+    done = toks = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        i = w % B
+        while time.perf_counter() - t0 < budget_s:
+            oa.decode(hb.q[i:i + 1], kp, vp, hb.block_tables[i:i + 1], hb.context_lens[i:i + 1],
+                      scale, bs, dtype)
+            done += 1
+            toks += int(hb.context_lens[i])
+            i = (i + n) % B
+    return done, toks
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline_parallel(cfg, budget_s=10.0, max_workers=16):
+    """The CPU oracle's decode of whole sequences, parallel over sequences in
+    a fork-based process pool (at most max_workers, the host share of one
+    GPU), on a copy of the workload's first batch built on the host. It runs
+    before anything initialises the GPU, so the workers are forks of a
+    process that holds no device state. The oracle's store runs once per
+    batch, untimed (it copies whole pools)."""
+    global _PAR
+    import multiprocessing as mp
+    import oracle.attention as oa
+    b = wl.make_batch(wl.spec(cfg), device="cpu", seed=wl.SEED_BASE + cfg)
+    hb = wl.host_subset(b)
+    kp, vp = oa.store_kvcache(hb.k_cache, hb.v_cache, hb.key, hb.value, hb.slot_mapping, b.block_size)
+    _PAR = (hb, kp, vp, b.scale, b.block_size, b.dtype)
+    n = max(1, min(max_workers, os.cpu_count() or 1))
+    pool = mp.get_context("fork").Pool(n)
+    try:
+        t0 = time.perf_counter()
+        res = pool.map_async(_par_worker, [(w, n, budget_s) for w in range(n)])
+        out = res.get(timeout=budget_s + 120)
+        secs = time.perf_counter() - t0
+    except mp.TimeoutError:
+        pool.terminate()
+        return None
+    finally:
+        pool.close()
+        pool.join()
+        _PAR = None
+    done = sum(d for d, _ in out)
+    return dict(value=round(done / secs, 2), unit="tokens/s", cores=n, cpu_model=cpu_model(),
+                kind="oracle",
+                sample=f"{done} whole-sequence decodes of the first batch (mean context "
+                       f"{float(b.context_lens.mean()):.0f} tokens) in fp64, {secs:.1f} s on {n} "
+                       f"forked processes, one thread each; the store once per batch, untimed")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -401,6 +474,11 @@ def main():
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    # the parallel CPU oracle forks worker processes: before any GPU call
+    par = None
+    if not args.no_cpu and args.only is None:
+        log("cpu baseline, parallel")
+        par = cpu_baseline_parallel(by_name[args.workload])
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
@@ -524,6 +602,9 @@ def main():
     if not args.no_cpu:
         log("cpu baseline")
         line["cpu_baseline"] = cpu_baseline(ds)
+        line["cpu_baseline"]["cpu_model"] = cpu_model()
+        if par is not None:
+            line["cpu_baseline"]["parallel"] = par
     print(json.dumps(line), flush=True)
 
 
