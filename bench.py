@@ -18,7 +18,9 @@ seconds). `roofline` covers the decode call (its main and merge kernels):
 algorithmic K+V bytes per launch over its average duration: one pair of HIP
 events on the launch stream around the timed run of launches, divided by the
 number of launches (an event pair around every launch would add GPU time to
-each step). `cpu_baseline` is the
+each step). The roofline also gives the device's streaming-read rate measured in the
+same run (pa_stream_read, a measurement aid of the library) and the decode
+rate as a fraction of it. `cpu_baseline` is the
 CPU oracle on a bounded sample of the same workload, single-threaded, and
 under `parallel` the same oracle's decode parallel over sequences in a
 fork-based pool of up to 16 processes (forked before any GPU call). `extra`
@@ -299,6 +301,26 @@ def measured_traffic(workload_name, split):
     return int(w["hbm_bytes_per_launch"])
 
 
+def stream_read_probe(dev, nbytes=4 << 30, iters=10):
+    """The device's sustained streaming-read rate (GB/s): pa_stream_read over
+    a buffer of nbytes, one pair of HIP events on the launch stream around
+    iters reads."""
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    out = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        pa.pa_stream_read(buf, out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        n = pa.pa_stream_read(buf, out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    del buf
+    torch.cuda.empty_cache()
+    return n / (ms * 1e-3) / 1e9
+
+
 def split_name(P):
     return "balanced" if P == pa.PA_PARTITION_BALANCED else "fixed"
 
@@ -502,6 +524,8 @@ def main():
     secs, kms, kbytes = time_decode(ds, args.steps, args.warmup)
     tokens = b0.num_seqs * args.steps
     achieved = kbytes / (kms * 1e-3) / 1e9
+    log("stream read probe")
+    stream_gbs = stream_read_probe(dev)
     line = {
         "metric": "paged-decode tokens/s + achieved KV GB/s as % of MI355X HBM peak",
         "value": round(tokens / secs, 1),
@@ -531,6 +555,9 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(ds.spec["name"], split_name(ds.P)),
             "kernel_ms": round(kms, 4), "bytes_per_launch": int(kbytes),
+            # the device's sustained streaming-read rate measured in this run
+            # (pa_stream_read), and the decode rate as a fraction of it
+            "stream_read_gbs": round(stream_gbs, 1), "frac_of_stream": round(achieved / stream_gbs, 4),
         },
     }
     if not args.no_extra:
@@ -559,6 +586,7 @@ def main():
                     tokens_per_s=round(bb.num_seqs * 30 / s, 1), kernel_ms=round(ms, 4),
                     kv_gbs=round(nb / (ms * 1e-3) / 1e9, 1),
                     frac_of_hbm_peak=round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    frac_of_stream=round(nb / (ms * 1e-3) / 1e9 / stream_gbs, 4),
                     bytes_per_launch=int(nb), split=split_name(P), partition_size=P, fused_store=fused,
                     shared_lens=hint,
                     traffic=measured_traffic(d.spec["name"], split_name(P)) if hint else None,
@@ -577,6 +605,7 @@ def main():
                 tokens_per_s=round(bb.num_seqs * 30 / s, 1), kernel_ms=round(ms, 4),
                 kv_gbs=round(nb / (ms * 1e-3) / 1e9, 1),
                 frac_of_hbm_peak=round(nb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                frac_of_stream=round(nb / (ms * 1e-3) / 1e9 / stream_gbs, 4),
                 bytes_per_launch=int(nb), split=split_name(P), partition_size=P, kv_cache="e4m3",
                 step="pa_store_kvcache_fp8 + pa_decode_fp8 (kernel_ms: pa_decode_fp8)",
                 fused_step="pa_store_decode_fp8, one launch (+ merge)",

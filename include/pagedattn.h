@@ -434,6 +434,23 @@ int32_t pa_bm_ref_count(const pa_block_manager* bm, int32_t block_id);
 /* Description of the calling thread's last failed block-manager call. */
 const char* pa_bm_last_error(void);
 
+/*
+ * pa_stream_read -- a measurement aid, not an operation of the pages: the
+ * rate at which this device sustains plain streaming reads, the reference
+ * the decode calls' K/V read rate is compared with. Reads the first
+ * *bytes_read bytes of buf (a whole number of equal per-wave slices, at most
+ * bytes) once, each wave one contiguous slice with 16-byte nontemporal
+ * loads at two waves per SIMD, and combines them into a value that decides
+ * whether *out (device, 4-byte aligned) is written; in practice it is not.
+ * buf: device memory, 16-byte aligned, at least 16 KB per resident wave
+ * (16 MB on a 256-CU device), contents irrelevant. *bytes_read (host) is
+ * set before the launch, which is asynchronous on stream. Errors:
+ * PA_ERR_INVALID_ARG for null pointers or a buffer below the minimum,
+ * PA_ERR_UNSUPPORTED for misaligned pointers, PA_ERR_HIP for a failed launch.
+ */
+pa_status pa_stream_read(const void* buf, size_t bytes, uint32_t* out, size_t* bytes_read,
+                         void* stream);
+
 /* Static description of a status code. */
 const char* pa_status_string(pa_status s);
 

@@ -71,6 +71,7 @@ _SIGNATURES = {
                             _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32,
                             _i32, _i32, _i32, _i32, _f32, _c_void_p, _size, ctypes.c_int,
                             _c_void_p], ctypes.c_int),
+    "pa_stream_read": ([_c_void_p, _size, _c_void_p, ctypes.POINTER(_size), _c_void_p], ctypes.c_int),
     "pa_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "pa_last_error": ([], ctypes.c_char_p),
 }
@@ -583,3 +584,19 @@ def pa_mixed_batch_fp8(out, q, k_cache, v_cache, k_scale, v_scale, block_tables,
                                 block_tables.shape[1], int(max_query_len), int(max_context_len),
                                 float(scale), ws_ptr, ws_bytes, _dtype_code(q), _stream(stream))
     _check("pa_mixed_batch_fp8", st)
+
+
+def pa_stream_read(buf, out, stream=None):
+    """One streaming read of the device tensor buf (a measurement aid: the
+    device's sustained read rate); out is a one-element int32 tensor on the
+    same device. Returns the bytes the launch reads."""
+    lib = load_library()
+    _need(buf.is_cuda and buf.is_contiguous(), "buf must be a contiguous device tensor")
+    _need(out.device == buf.device and out.dtype == torch.int32 and out.numel() >= 1,
+          "out must be an int32 tensor on the device of buf")
+    n = _size(0)
+    st = lib.pa_stream_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out), ctypes.byref(n),
+                            _stream(stream))
+    _check("pa_stream_read", st)
+    return int(n.value)
+

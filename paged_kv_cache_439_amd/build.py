@@ -23,7 +23,7 @@ OUT = os.path.join(HERE, "libpagedattn.so")
 ARCH = "gfx950"
 
 SOURCES = ["pa_api.cpp", "block_manager.cpp", "store_kvcache.hip", "decode.hip", "prefill.hip",
-           "mixed.hip"]
+           "mixed.hip", "stream_probe.hip"]
 
 # Packed fp32 VALU instructions are disabled: hipcc must not form them.
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -564,4 +564,24 @@ pa_status pa_mixed_batch_fp8(void* out, const void* q, const void* k_cache, cons
   }
 }
 
+pa_status pa_stream_read(const void* buf, size_t bytes, uint32_t* out, size_t* bytes_read,
+                         void* stream) {
+  try {
+    if (!buf || !out || !bytes_read)
+      return fail(PA_ERR_INVALID_ARG, "pa_stream_read: null pointer argument");
+    if (!aligned(buf, 16) || !aligned(out, 4))
+      return fail(PA_ERR_UNSUPPORTED, "pa_stream_read: buf must be 16-byte aligned, out 4-byte");
+    const int64_t need = pa::stream_read_min_bytes();
+    if ((int64_t)bytes < need)
+      return fail(PA_ERR_INVALID_ARG, "pa_stream_read: %zu bytes, at least %lld needed", bytes,
+                  (long long)need);
+    const hipError_t err = pa::launch_stream_read(buf, bytes, out, bytes_read,
+                                                  static_cast<hipStream_t>(stream));
+    if (err != hipSuccess) return fail(PA_ERR_HIP, "stream read launch: %s", hipGetErrorString(err));
+    return ok();
+  } catch (...) {
+    return fail(PA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
 }  // extern "C"

@@ -102,6 +102,14 @@ hipError_t launch_store(const StoreArgs& a, hipStream_t stream);
 hipError_t launch_store_e4m3(const StoreE4M3Args& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+// pa_stream_read (stream_probe.hip): waves it launches on the current
+// device, the smallest buffer it takes, and the launch (bytes_read: the
+// bytes one launch reads, a whole number of per-wave slices).
+int64_t stream_read_waves();
+int64_t stream_read_min_bytes();
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* out, size_t* bytes_read,
+                              hipStream_t stream);
 // a describes the whole batch; its first num_decode sequences are decode
 // tokens (workspace: the balanced decode workspace for num_decode sequences).
 hipError_t launch_mixed(const PrefillArgs& a, int32_t num_decode, void* workspace,

@@ -328,3 +328,14 @@ def test_store_decode_fp8_rejections(lib):
     assert _store_decode_fp8(lib, dtype=0) == PA_ERR_UNSUPPORTED       # bf16 queries only
     assert _store_decode_fp8(lib, ks=500) == PA_ERR_INVALID_ARG        # stride below one row
     assert _store_decode_fp8(lib, P=32) == PA_ERR_WORKSPACE
+
+
+def test_stream_read_rejections(lib):
+    n = ctypes.c_size_t(0)
+    out = ctypes.c_void_p(0x200000)
+    assert lib.pa_stream_read(None, 1 << 30, out, ctypes.byref(n), None) == PA_ERR_INVALID_ARG
+    assert lib.pa_stream_read(FAKE, 1 << 30, None, ctypes.byref(n), None) == PA_ERR_INVALID_ARG
+    assert lib.pa_stream_read(FAKE, 1 << 30, out, None, None) == PA_ERR_INVALID_ARG
+    assert lib.pa_stream_read(ctypes.c_void_p(0x100008), 1 << 30, out, ctypes.byref(n), None) == PA_ERR_UNSUPPORTED
+    assert lib.pa_stream_read(FAKE, 1 << 20, out, ctypes.byref(n), None) == PA_ERR_INVALID_ARG  # below the minimum
+

@@ -111,3 +111,22 @@ def test_store_decode_fp8_in_graph(gpu):
         pa.pa_store_decode_fp8(out, b.q, b.key, b.value, b.k_cache, b.v_cache, b.k_scale, b.v_scale,
                                arrs["slots"], arrs["tables"], arrs["lens"], b.max_context_len, b.scale, P, ws)
     _capture_and_replay(call, out, _other_decode(gpu))
+
+
+def test_store_decode_fp8_pairs_with_shared_lens_in_graph(gpu):
+    """E4M3 at head_dim 64 with one query head per KV head (the balanced
+    split reads KV head pairs), with a shared prefix and its shared_lens."""
+    b = wl.make_batch(wl.spec(wl.B64_MHA_DECODE, kv="e4m3", num_seqs=16, lens=("uniform", 300, 2000),
+                              max_context=2048, share=dict(num_sharers=8, prefix_tokens=256)), device=gpu)
+    arrs = gs.device_arrays(b)
+    shared = gs.shared_lens_arg(b, True)
+    P = pa.PA_PARTITION_BALANCED
+    ws = pa.decode_workspace(b.num_seqs, b.num_heads, b.num_kv_heads, b.head_dim, b.max_context_len, P, gpu)
+    out = torch.empty_like(b.q)
+    gs.say(f"graph store+decode e4m3 pairs shared_lens={b.shared_lens.tolist()}")
+
+    def call():
+        pa.pa_store_decode_fp8(out, b.q, b.key, b.value, b.k_cache, b.v_cache, b.k_scale, b.v_scale,
+                               arrs["slots"], arrs["tables"], arrs["lens"], b.max_context_len, b.scale, P, ws,
+                               shared_lens=shared)
+    _capture_and_replay(call, out, _other_decode(gpu))
