@@ -238,6 +238,9 @@ pa_status pa_prefill_chunk(void* out, const void* q,
  * pa_decode_workspace_size(num_decode_seqs, num_heads, num_kv_heads,
  * head_dim, max_context_len, PA_PARTITION_BALANCED) bytes, 256-byte aligned
  * (may be NULL when num_decode_seqs is 0). At most 2048 decode sequences.
+ * shared_lens: NULL or int32 [num_seqs], the decode rows' load-policy hint
+ * as for pa_decode (entries of prefill sequences are not read); the result
+ * does not depend on it.
  * PA_BF16 only. Other arguments, shapes and errors as for pa_prefill_chunk.
  */
 pa_status pa_mixed_batch(void* out, const void* q,
@@ -245,6 +248,7 @@ pa_status pa_mixed_batch(void* out, const void* q,
                          const int32_t* block_tables,
                          const int32_t* query_start_loc,
                          const int32_t* context_lens,
+                         const int32_t* shared_lens,
                          int32_t num_seqs, int32_t num_decode_seqs,
                          int32_t num_heads, int32_t num_kv_heads,
                          int32_t head_dim, int32_t block_size,
@@ -359,8 +363,8 @@ pa_status pa_prefill_chunk_fp8(void* out, const void* q,
  * pa_mixed_batch_fp8 -- pa_mixed_batch over E4M3 pools: the same batch
  * layout and launch, its decode rows computed as pa_decode_fp8 computes them
  * (balanced split) and its prefill chunks as pa_prefill_chunk_fp8 does.
- * Scales as for pa_decode_fp8; workspace, shapes and errors as for
- * pa_mixed_batch, plus PA_ERR_INVALID_ARG for a null scale array and
+ * Scales as for pa_decode_fp8; workspace, shared_lens, shapes and errors
+ * as for pa_mixed_batch, plus PA_ERR_INVALID_ARG for a null scale array and
  * PA_ERR_UNSUPPORTED for one not 4-byte aligned. PA_BF16 q/out only.
  */
 pa_status pa_mixed_batch_fp8(void* out, const void* q,
@@ -369,6 +373,7 @@ pa_status pa_mixed_batch_fp8(void* out, const void* q,
                              const int32_t* block_tables,
                              const int32_t* query_start_loc,
                              const int32_t* context_lens,
+                             const int32_t* shared_lens,
                              int32_t num_seqs, int32_t num_decode_seqs,
                              int32_t num_heads, int32_t num_kv_heads,
                              int32_t head_dim, int32_t block_size,

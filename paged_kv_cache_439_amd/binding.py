@@ -50,8 +50,8 @@ _SIGNATURES = {
                          _i32, _f32, _i32, _c_void_p, _size, ctypes.c_int, _c_void_p], ctypes.c_int),
     "pa_store_decode_fp8": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _c_void_p,
                              _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
-                             _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _c_void_p, _size,
-                             ctypes.c_int, _c_void_p], ctypes.c_int),
+                             _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                             _c_void_p, _size, ctypes.c_int, _c_void_p], ctypes.c_int),
     "pa_prefill_chunk": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                           _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                           _f32, ctypes.c_int, _c_void_p], ctypes.c_int),
@@ -65,10 +65,10 @@ _SIGNATURES = {
                               _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32,
                               _i32, _i32, _i32, _f32, ctypes.c_int, _c_void_p], ctypes.c_int),
     "pa_mixed_batch": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
-                        _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                        _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                         _c_void_p, _size, ctypes.c_int, _c_void_p], ctypes.c_int),
     "pa_mixed_batch_fp8": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
-                            _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32,
+                            _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32,
                             _i32, _i32, _i32, _i32, _f32, _c_void_p, _size, ctypes.c_int,
                             _c_void_p], ctypes.c_int),
     "pa_stream_read": ([_c_void_p, _size, _c_void_p, ctypes.POINTER(_size), _c_void_p], ctypes.c_int),
@@ -523,10 +523,11 @@ def mixed_workspace(num_decode_seqs, num_heads, num_kv_heads, head_dim, max_cont
 
 def pa_mixed_batch(out, q, k_cache, v_cache, block_tables, query_start_loc, context_lens,
                    num_decode_seqs, max_query_len, max_context_len, scale, workspace=None,
-                   stream=None):
+                   stream=None, shared_lens=None):
     """A continuous batch in one call: the first num_decode_seqs sequences are
     decode tokens (one row each), the rest prefill chunks; out and q are
-    [T][Hq][D] bf16."""
+    [T][Hq][D] bf16. shared_lens (int32 [B] or None): the decode rows'
+    load-policy hint, as for pa_decode."""
     lib = load_library()
     T, Hq, D = q.shape
     _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
@@ -547,8 +548,9 @@ def pa_mixed_batch(out, q, k_cache, v_cache, block_tables, query_start_loc, cont
     if workspace is not None:
         _need(workspace.device == q.device and workspace.is_contiguous(), "bad workspace")
         ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    sl = _shared_lens(shared_lens, B, q.device)
     st = lib.pa_mixed_batch(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-                            _ptr(query_start_loc), _ptr(context_lens), B, int(num_decode_seqs), Hq, Hkv,
+                            _ptr(query_start_loc), _ptr(context_lens), sl, B, int(num_decode_seqs), Hq, Hkv,
                             D, bs, NB, block_tables.shape[1], int(max_query_len), int(max_context_len),
                             float(scale), ws_ptr, ws_bytes, _dtype_code(q), _stream(stream))
     _check("pa_mixed_batch", st)
@@ -556,9 +558,10 @@ def pa_mixed_batch(out, q, k_cache, v_cache, block_tables, query_start_loc, cont
 
 def pa_mixed_batch_fp8(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, query_start_loc,
                        context_lens, num_decode_seqs, max_query_len, max_context_len, scale,
-                       workspace=None, stream=None):
+                       workspace=None, stream=None, shared_lens=None):
     """pa_mixed_batch over E4M3 pools (uint8 codes, fp32 per-head scales);
-    out and q are [T][Hq][D] bf16, the workspace as for pa_mixed_batch."""
+    out and q are [T][Hq][D] bf16, the workspace and shared_lens as for
+    pa_mixed_batch."""
     lib = load_library()
     T, Hq, D = q.shape
     _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
@@ -578,9 +581,10 @@ def pa_mixed_batch_fp8(out, q, k_cache, v_cache, k_scale, v_scale, block_tables,
     if workspace is not None:
         _need(workspace.device == q.device and workspace.is_contiguous(), "bad workspace")
         ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    sl = _shared_lens(shared_lens, B, q.device)
     st = lib.pa_mixed_batch_fp8(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_scale),
                                 _ptr(v_scale), _ptr(block_tables), _ptr(query_start_loc),
-                                _ptr(context_lens), B, int(num_decode_seqs), Hq, Hkv, D, bs, NB,
+                                _ptr(context_lens), sl, B, int(num_decode_seqs), Hq, Hkv, D, bs, NB,
                                 block_tables.shape[1], int(max_query_len), int(max_context_len),
                                 float(scale), ws_ptr, ws_bytes, _dtype_code(q), _stream(stream))
     _check("pa_mixed_batch_fp8", st)

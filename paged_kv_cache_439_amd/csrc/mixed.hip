@@ -123,8 +123,8 @@ static void launch_mixed_kt(const MixedParams& prm, const PrefillArgs& a, int32_
   }
 }
 
-hipError_t launch_mixed(const PrefillArgs& a, int32_t num_decode, void* workspace,
-                        hipStream_t stream) {
+hipError_t launch_mixed(const PrefillArgs& a, int32_t num_decode, const int32_t* shared_lens,
+                        void* workspace, hipStream_t stream) {
   const int32_t Bd = num_decode, Bp = a.num_seqs - num_decode;
   if (Bd == 0) return launch_prefill(a, stream);
   DecodeArgs da{};
@@ -134,6 +134,7 @@ hipError_t launch_mixed(const PrefillArgs& a, int32_t num_decode, void* workspac
   da.v_cache = a.v_cache;
   da.block_tables = a.block_tables;
   da.context_lens = a.context_lens;
+  da.shared_lens = shared_lens;  // the decode rows are sequences 0 .. Bd-1
   da.num_seqs = Bd;
   da.num_heads = a.num_heads;
   da.num_kv_heads = a.num_kv_heads;

@@ -473,7 +473,8 @@ namespace {
 
 pa_status mixed_impl(const char* fn, void* out, const void* q, const void* k_cache,
                      const void* v_cache, const int32_t* block_tables,
-                     const int32_t* query_start_loc, const int32_t* context_lens, int32_t num_seqs,
+                     const int32_t* query_start_loc, const int32_t* context_lens,
+                     const int32_t* shared_lens, int32_t num_seqs,
                      int32_t num_decode_seqs, int32_t num_heads, int32_t num_kv_heads,
                      int32_t head_dim, int32_t block_size, int32_t num_blocks,
                      int32_t max_blocks_per_seq, int32_t max_query_len, int32_t max_context_len,
@@ -518,7 +519,9 @@ pa_status mixed_impl(const char* fn, void* out, const void* q, const void* k_cac
     a.k_scale = e4m3->k_scale;
     a.v_scale = e4m3->v_scale;
   }
-  const hipError_t err = pa::launch_mixed(a, num_decode_seqs, workspace,
+  if (!aligned(shared_lens, 4))
+    return fail(PA_ERR_UNSUPPORTED, "%s: shared_lens must be 4-byte aligned", fn);
+  const hipError_t err = pa::launch_mixed(a, num_decode_seqs, shared_lens, workspace,
                                           static_cast<hipStream_t>(stream));
   if (err != hipSuccess) return fail(PA_ERR_HIP, "%s launch: %s", fn, hipGetErrorString(err));
   return ok();
@@ -528,15 +531,16 @@ pa_status mixed_impl(const char* fn, void* out, const void* q, const void* k_cac
 
 pa_status pa_mixed_batch(void* out, const void* q, const void* k_cache, const void* v_cache,
                          const int32_t* block_tables, const int32_t* query_start_loc,
-                         const int32_t* context_lens, int32_t num_seqs, int32_t num_decode_seqs,
+                         const int32_t* context_lens, const int32_t* shared_lens,
+                         int32_t num_seqs, int32_t num_decode_seqs,
                          int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                          int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                          int32_t max_query_len, int32_t max_context_len, float scale,
                          void* workspace, size_t workspace_bytes, pa_dtype dtype, void* stream) {
   try {
     return mixed_impl("pa_mixed_batch", out, q, k_cache, v_cache, block_tables, query_start_loc,
-                      context_lens, num_seqs, num_decode_seqs, num_heads, num_kv_heads, head_dim,
-                      block_size, num_blocks, max_blocks_per_seq, max_query_len, max_context_len,
+                      context_lens, shared_lens, num_seqs, num_decode_seqs, num_heads, num_kv_heads,
+                      head_dim, block_size, num_blocks, max_blocks_per_seq, max_query_len, max_context_len,
                       scale, workspace, workspace_bytes, dtype, stream, nullptr);
   } catch (...) {
     return fail(PA_ERR_HIP, "unexpected C++ exception");
@@ -546,7 +550,8 @@ pa_status pa_mixed_batch(void* out, const void* q, const void* k_cache, const vo
 pa_status pa_mixed_batch_fp8(void* out, const void* q, const void* k_cache, const void* v_cache,
                              const float* k_scale, const float* v_scale,
                              const int32_t* block_tables, const int32_t* query_start_loc,
-                             const int32_t* context_lens, int32_t num_seqs,
+                             const int32_t* context_lens,
+                             const int32_t* shared_lens, int32_t num_seqs,
                              int32_t num_decode_seqs, int32_t num_heads, int32_t num_kv_heads,
                              int32_t head_dim, int32_t block_size, int32_t num_blocks,
                              int32_t max_blocks_per_seq, int32_t max_query_len,
@@ -555,8 +560,8 @@ pa_status pa_mixed_batch_fp8(void* out, const void* q, const void* k_cache, cons
   try {
     const E4M3Scales sc{k_scale, v_scale};
     return mixed_impl("pa_mixed_batch_fp8", out, q, k_cache, v_cache, block_tables,
-                      query_start_loc, context_lens, num_seqs, num_decode_seqs, num_heads,
-                      num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                      query_start_loc, context_lens, shared_lens, num_seqs, num_decode_seqs,
+                      num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
                       max_query_len, max_context_len, scale, workspace, workspace_bytes, dtype,
                       stream, &sc);
   } catch (...) {

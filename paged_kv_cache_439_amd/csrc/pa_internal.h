@@ -112,7 +112,7 @@ hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* out, size
                               hipStream_t stream);
 // a describes the whole batch; its first num_decode sequences are decode
 // tokens (workspace: the balanced decode workspace for num_decode sequences).
-hipError_t launch_mixed(const PrefillArgs& a, int32_t num_decode, void* workspace,
-                        hipStream_t stream);
+hipError_t launch_mixed(const PrefillArgs& a, int32_t num_decode, const int32_t* shared_lens,
+                        void* workspace, hipStream_t stream);
 
 }  // namespace pa

@@ -152,7 +152,7 @@ def snapshot_pools(batch):
     return batch
 
 
-def gpu_mixed(batch, arrs=None, workspace=None):
+def gpu_mixed(batch, arrs=None, workspace=None, hint=None):
     """pa_mixed_batch over the batch (its first num_decode sequences decode)."""
     arrs = arrs or device_arrays(batch)
     if workspace is None:
@@ -161,7 +161,7 @@ def gpu_mixed(batch, arrs=None, workspace=None):
     out = torch.full_like(batch.q, float("nan"))
     pa.pa_mixed_batch(out, batch.q, batch.k_cache, batch.v_cache, arrs["tables"], arrs["qsl"],
                       arrs["lens"], batch.num_decode, batch.max_query_len, batch.max_context_len,
-                      batch.scale, workspace)
+                      batch.scale, workspace, shared_lens=shared_lens_arg(batch, hint))
     return out
 
 
@@ -277,7 +277,7 @@ def sample_prefill_rows(batch, total_rows, sample_rows, seed):
     return list(zip(toks, heads.tolist()))
 
 
-def gpu_mixed_fp8(batch, arrs=None, workspace=None):
+def gpu_mixed_fp8(batch, arrs=None, workspace=None, hint=None):
     """pa_mixed_batch_fp8 over the batch (its first num_decode sequences decode)."""
     arrs = arrs or device_arrays(batch)
     if workspace is None:
@@ -286,7 +286,8 @@ def gpu_mixed_fp8(batch, arrs=None, workspace=None):
     out = torch.full_like(batch.q, float("nan"))
     pa.pa_mixed_batch_fp8(out, batch.q, batch.k_cache, batch.v_cache, batch.k_scale, batch.v_scale,
                           arrs["tables"], arrs["qsl"], arrs["lens"], batch.num_decode,
-                          batch.max_query_len, batch.max_context_len, batch.scale, workspace)
+                          batch.max_query_len, batch.max_context_len, batch.scale, workspace,
+                          shared_lens=shared_lens_arg(batch, hint))
     return out
 
 

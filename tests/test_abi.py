@@ -264,12 +264,13 @@ def test_store_fp8_rejections(lib):
 
 
 def _mixed(lib, **kw):
-    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, qsl=FAKE, cl=FAKE, B=260, Bd=256, Hq=32, Hkv=8,
-             D=128, bs=256, NB=4000, MB=16, mq=512, maxL=4096, scale=0.088, ws=FAKE, wsb=1 << 30, dtype=1)
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, qsl=FAKE, cl=FAKE, sl=None, B=260, Bd=256, Hq=32,
+             Hkv=8, D=128, bs=256, NB=4000, MB=16, mq=512, maxL=4096, scale=0.088, ws=FAKE, wsb=1 << 30,
+             dtype=1)
     a.update(kw)
-    return lib.pa_mixed_batch(a["out"], a["q"], a["k"], a["v"], a["bt"], a["qsl"], a["cl"], a["B"], a["Bd"],
-                              a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"], a["MB"], a["mq"], a["maxL"],
-                              a["scale"], a["ws"], a["wsb"], a["dtype"], None)
+    return lib.pa_mixed_batch(a["out"], a["q"], a["k"], a["v"], a["bt"], a["qsl"], a["cl"], a["sl"], a["B"],
+                              a["Bd"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"], a["MB"], a["mq"],
+                              a["maxL"], a["scale"], a["ws"], a["wsb"], a["dtype"], None)
 
 
 def test_mixed_rejections(lib):
@@ -283,16 +284,17 @@ def test_mixed_rejections(lib):
     assert _mixed(lib, ws=None) == PA_ERR_WORKSPACE
     assert _mixed(lib, wsb=16) == PA_ERR_WORKSPACE
     assert _mixed(lib, ws=ctypes.c_void_p(0x100010)) == PA_ERR_WORKSPACE   # not 256-byte aligned
+    assert _mixed(lib, sl=ctypes.c_void_p(0x100002)) == PA_ERR_UNSUPPORTED  # shared_lens misaligned
     assert "pa_mixed_batch" in binding.load_library().pa_last_error().decode()
 
 
 def _mixed_fp8(lib, **kw):
-    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, kscale=FAKE, vscale=FAKE, bt=FAKE, qsl=FAKE, cl=FAKE,
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, kscale=FAKE, vscale=FAKE, bt=FAKE, qsl=FAKE, cl=FAKE, sl=None,
              B=260, Bd=256, Hq=32, Hkv=8, D=128, bs=256, NB=4000, MB=16, mq=512, maxL=4096, scale=0.088,
              ws=FAKE, wsb=1 << 30, dtype=1)
     a.update(kw)
     return lib.pa_mixed_batch_fp8(a["out"], a["q"], a["k"], a["v"], a["kscale"], a["vscale"], a["bt"],
-                                  a["qsl"], a["cl"], a["B"], a["Bd"], a["Hq"], a["Hkv"], a["D"], a["bs"],
+                                  a["qsl"], a["cl"], a["sl"], a["B"], a["Bd"], a["Hq"], a["Hkv"], a["D"], a["bs"],
                                   a["NB"], a["MB"], a["mq"], a["maxL"], a["scale"], a["ws"], a["wsb"],
                                   a["dtype"], None)
 

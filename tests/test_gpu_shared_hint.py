@@ -118,3 +118,27 @@ def test_hint_full_shared_prefix_workload(gpu):
     sharers = [i for i in range(b.num_seqs) if b.shared_lens[i] > 0]
     seqs = sorted(set(gs.sample_seqs(b, 4, seed=3)) | set(sharers[:3]))
     gs.decode_parity(b, -1, seqs=seqs, hint=True)
+
+
+@pytest.mark.parametrize("kv", [None, "e4m3"])
+def test_hint_leaves_mixed_batch_bit_identical(gpu, kv):
+    """pa_mixed_batch(_fp8): the decode rows take the hint, the prefill
+    chunks ignore it; every output row bit-identical to the call without."""
+    over = dict(num_seqs=12, num_decode=8, decode_lens=("uniform", 1, 600), cached=("uniform", 0, 300),
+                chunk=[40, 1, 77, 129], block_size=16, max_context=1024)
+    sp = wl.spec(wl.MIXED_BATCH, **over) if kv is None else wl.spec(wl.MIXED_BATCH, kv=kv, **over)
+    b = wl.make_batch(sp, device=gpu, poison=True)
+    arrs = gs.device_arrays(b)
+    if kv is None:
+        gs.gpu_store(b, arrs)
+        run = lambda hint: gs.gpu_mixed(b, arrs, hint=hint)
+    else:
+        gs.gpu_store_fp8(b, arrs)
+        run = lambda hint: gs.gpu_mixed_fp8(b, arrs, hint=hint)
+    gs.say(f"shared hint mixed batch kv={kv} lens={b.context_lens.tolist()}")
+    plain = run(None)
+    for hname, hint in _hints(b, seed=5).items():
+        got = run(hint)
+        torch.cuda.synchronize()
+        assert torch.equal(_bits(got), _bits(plain)), (kv, hname)
+
