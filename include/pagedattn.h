@@ -107,7 +107,11 @@ pa_status pa_store_kvcache(const void* key, const void* value,
  * need more than one partition, i.e. partition_size == 0 or partition_size
  * >= max_context_len), or the balanced split (PA_PARTITION_BALANCED; the
  * size depends on the current device's compute-unit count, 256 assumed when
- * no device is visible). Returns 0 for invalid arguments too.
+ * no device is visible). The same size serves pa_decode_fp8 and
+ * pa_store_decode_fp8: over E4M3 pools at head_dim 64 with one query head
+ * per KV head (and an even KV head count) the balanced split reads pairs of
+ * KV heads and plans twice the workers, and the size returned is the larger
+ * of the two plans. Returns 0 for invalid arguments too.
  */
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
                                 int32_t num_kv_heads, int32_t head_dim,
