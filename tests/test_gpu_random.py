@@ -1,0 +1,63 @@
+"""Seeded random sweep of decode configurations against the oracle.
+
+Each case draws a query type (bf16 or fp32), a pool type (the query's, or
+E4M3), head_dim, KV heads and group size, block size, batch size, context
+lengths, split (whole contexts, fixed slices, balanced) and a shared_lens
+hint (none, the batch's own, random), then runs the store and the decode on
+the GPU and compares every output with the oracle's store and decode of the
+same inputs (tolerances as in every decode test). The cases cover the
+combinations the hand-written tests take one at a time: KV head pairs with
+and without a hint, blocks smaller and larger than a chunk, shared prefixes
+over every split.
+"""
+
+import numpy as np
+import pytest
+
+from paged_kv_cache_439_amd import workloads as wl
+from tests import gpu_support as gs
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 64
+
+
+def draw_case(k):
+    rng = np.random.Generator(np.random.PCG64(4390 + k))
+    dtype = ["bf16", "f32"][int(rng.integers(0, 2))]
+    kv = [None, "e4m3"][int(rng.integers(0, 2))]
+    D = [64, 128][int(rng.integers(0, 2))]
+    Hkv = int(rng.integers(1, 9))
+    G = [1, 1, 2, 3, 4, 8][int(rng.integers(0, 6))]
+    bs = [8, 16, 32, 64, 128, 256][int(rng.integers(0, 6))]
+    B = int(rng.integers(1, 21))
+    maxL = int(rng.integers(16, 1600))
+    lens = ("uniform", 1, maxL)
+    max_context = ((maxL + bs - 1) // bs) * bs
+    P = [0, -1, -1, 16 * int(rng.integers(1, 33))][int(rng.integers(0, 4))]
+    share = None
+    if B >= 4 and maxL > 2 * bs + 1:
+        share = dict(num_sharers=int(rng.integers(2, B + 1)), prefix_tokens=bs * int(rng.integers(1, 3)))
+    hint = [None, True, "random"][int(rng.integers(0, 3))]
+    if k % 4 == 0:  # every fourth case: KV head pairs (E4M3, head_dim 64, MHA, even heads, balanced)
+        kv, D, G, P = "e4m3", 64, 1, -1
+        Hkv = 2 * int(rng.integers(1, 5))
+    return dict(dtype=dtype, kv=kv, head_dim=D, num_kv_heads=Hkv, num_heads=Hkv * G, block_size=bs,
+                num_seqs=B, lens=lens, max_context=max_context, share=share), P, hint, rng
+
+
+@pytest.mark.parametrize("k", range(N_CASES))
+def test_random_decode_case(gpu, k):
+    over, P, hint, rng = draw_case(k)
+    kv = over.pop("kv")
+    sp = wl.spec(wl.B512_LOGNORMAL_DECODE, **over) if kv is None else \
+        wl.spec(wl.B512_LOGNORMAL_DECODE, kv=kv, **over)
+    b = wl.make_batch(sp, device=gpu, poison=True)
+    if hint == "random":
+        hint = rng.integers(-3, int(b.context_lens.max()) + 40, size=b.num_seqs).astype(np.int32)
+    gs.say(f"random case {k}: kv={kv} P={P} hint={'array' if hint is not None and hint is not True else hint} "
+           f"{ {kk: v for kk, v in over.items() if kk != 'lens'} } lens={b.context_lens.tolist()}")
+    if kv is None:
+        gs.decode_parity(b, P, hint=hint)
+    else:
+        gs.decode_fp8_parity(b, P, hint=hint)
