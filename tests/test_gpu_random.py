@@ -61,3 +61,55 @@ def test_random_decode_case(gpu, k):
         gs.decode_parity(b, P, hint=hint)
     else:
         gs.decode_fp8_parity(b, P, hint=hint)
+
+
+N_PREFILL_CASES = 24
+
+
+def draw_prefill_case(k, mixed=False):
+    """A chunked-prefill batch (mixed: decode tokens first, then chunks)."""
+    rng = np.random.Generator(np.random.PCG64(4391000 + 1000 * mixed + k))
+    kv = [None, "e4m3"][int(rng.integers(0, 2))]
+    D = [64, 128][int(rng.integers(0, 2))]
+    Hkv = int(rng.integers(1, 9))
+    G = [1, 2, 3, 4, 8][int(rng.integers(0, 5))]
+    bs = [8, 16, 32, 64, 128, 256, 512][int(rng.integers(0, 7))]
+    nb = int(rng.integers(1, 6))
+    chunks = [int(x) for x in rng.integers(1, 201, size=nb)]
+    cmax = int(rng.integers(0, 801))
+    over = dict(head_dim=D, num_kv_heads=Hkv, num_heads=Hkv * G, block_size=bs, chunk=chunks,
+                cached=("uniform", 0, cmax))
+    longest = cmax + max(chunks)
+    if mixed:
+        nd = int(rng.integers(1, 9))
+        dmax = int(rng.integers(1, 1500))
+        over.update(num_seqs=nd + nb, num_decode=nd, decode_lens=("uniform", 1, dmax))
+        longest = max(longest, dmax)
+    else:
+        over.update(num_seqs=nb)
+    over["max_context"] = ((longest + bs - 1) // bs) * bs
+    return over, kv
+
+
+def _prefill_case(gpu, k, mixed):
+    over, kv = draw_prefill_case(k, mixed)
+    cfg = wl.MIXED_BATCH if mixed else wl.CHUNKED_PREFILL
+    sp = wl.spec(cfg, **over) if kv is None else wl.spec(cfg, kv=kv, **over)
+    b = wl.make_batch(sp, device=gpu, poison=True)
+    gs.say(f"random {'mixed' if mixed else 'prefill'} case {k}: kv={kv} "
+           f"{ {kk: v for kk, v in over.items() if kk not in ('cached', 'decode_lens')} } "
+           f"lens={b.context_lens.tolist()} qsl={b.query_start_loc.tolist()}")
+    if kv is None:
+        gs.prefill_parity(b, runner=gs.gpu_mixed if mixed else None)
+    else:
+        gs.prefill_fp8_parity(b, runner=gs.gpu_mixed_fp8 if mixed else None)
+
+
+@pytest.mark.parametrize("k", range(N_PREFILL_CASES))
+def test_random_prefill_case(gpu, k):
+    _prefill_case(gpu, k, mixed=False)
+
+
+@pytest.mark.parametrize("k", range(N_PREFILL_CASES))
+def test_random_mixed_case(gpu, k):
+    _prefill_case(gpu, k, mixed=True)
