@@ -440,6 +440,15 @@ pa_status pa_bm_free(pa_block_manager* bm, const int32_t* table, int32_t num_tab
 int32_t pa_bm_num_free(const pa_block_manager* bm);
 int32_t pa_bm_ref_count(const pa_block_manager* bm, int32_t block_id);
 
+/* The leading tokens of a sequence (num_tokens long, its table of
+ * num_table_blocks entries) that lie in blocks with more than one reference,
+ * i.e. that other sequences read too: the decode calls' shared_lens entry
+ * for it. Prefix sharing shares leading blocks only (the nano-vllm page,
+ * sections 3.2 and 4.2), so the count stops at the first private block. -1
+ * for a null manager, negative sizes or an invalid block id. */
+int32_t pa_bm_shared_tokens(const pa_block_manager* bm, const int32_t* table,
+                            int32_t num_table_blocks, int32_t num_tokens);
+
 /* Description of the calling thread's last failed block-manager call. */
 const char* pa_bm_last_error(void);
 

@@ -413,6 +413,7 @@ _BM_SIGNATURES = {
     "pa_bm_free": ([_c_void_p, _c_void_p, _i32], ctypes.c_int),
     "pa_bm_num_free": ([_c_void_p], _i32),
     "pa_bm_ref_count": ([_c_void_p, _i32], _i32),
+    "pa_bm_shared_tokens": ([_c_void_p, _c_void_p, _i32, _i32], _i32),
     "pa_bm_last_error": ([], ctypes.c_char_p),
 }
 PA_ERR_OUT_OF_BLOCKS = 5
@@ -511,6 +512,16 @@ class BlockManager:
 
     def ref_count(self, block_id):
         return int(self._lib.pa_bm_ref_count(self._h, int(block_id)))
+
+    def shared_tokens(self, table, num_tokens):
+        """Leading tokens of a sequence that lie in blocks other sequences
+        also hold (its shared_lens entry for the decode calls)."""
+        t = _i32_array(table)
+        n = int(self._lib.pa_bm_shared_tokens(self._h, t.ctypes.data if len(t) else None, len(t),
+                                              int(num_tokens)))
+        if n < 0:
+            raise ValueError("pa_bm_shared_tokens: invalid arguments")
+        return n
 
 
 def mixed_workspace(num_decode_seqs, num_heads, num_kv_heads, head_dim, max_context_len, device):

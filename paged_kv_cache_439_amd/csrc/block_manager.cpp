@@ -128,6 +128,20 @@ int32_t pa_bm_ref_count(const pa_block_manager* bm, int32_t block_id) {
   return bm->blocks[block_id].ref;
 }
 
+int32_t pa_bm_shared_tokens(const pa_block_manager* bm, const int32_t* table, int32_t num_table_blocks,
+                            int32_t num_tokens) {
+  if (!bm || num_table_blocks < 0 || num_tokens < 0 || (num_table_blocks > 0 && !table)) return -1;
+  const int64_t bs = bm->block_size;
+  int64_t k = 0;
+  while (k < num_table_blocks && k * bs < num_tokens) {
+    const int32_t b = table[k];
+    if (b < 0 || b >= (int32_t)bm->blocks.size()) return -1;
+    if (bm->blocks[b].ref <= 1) break;
+    ++k;
+  }
+  return (int32_t)std::min<int64_t>(k * bs, num_tokens);
+}
+
 pa_status pa_bm_allocate(pa_block_manager* bm, const int32_t* token_ids, int32_t num_tokens,
                          int32_t* table, int32_t table_capacity, int32_t* num_table_blocks,
                          int32_t* num_cached_tokens, int32_t* slots) {
