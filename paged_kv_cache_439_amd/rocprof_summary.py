@@ -171,8 +171,11 @@ def counters(counter_csv, out_md, cmd, cus=256, simds_per_cu=4, xcds=8):
         t = med([dur[d] for d in ds])
         cyc = a.get("GRBM_GUI_ACTIVE", 0.0) / xcds
         nan = float("nan")
-        mf = 100 * a["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * cus * simds_per_cu) if cyc and "SQ_VALU_MFMA_BUSY_CYCLES" in a else nan
-        va = 100 * a["SQ_ACTIVE_INST_VALU"] / (cyc * cus) if cyc and "SQ_ACTIVE_INST_VALU" in a else nan
+        mf, va = nan, nan
+        if cyc and "SQ_VALU_MFMA_BUSY_CYCLES" in a:
+            mf = 100 * a["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * cus * simds_per_cu)
+        if cyc and "SQ_ACTIVE_INST_VALU" in a:
+            va = 100 * a["SQ_ACTIVE_INST_VALU"] / (cyc * cus)
         fl = a.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", nan) * 512 / 1e9
         # the counters' window is a few us longer than the dispatch itself,
         # so the clock is only given for dispatches long enough to hide that
