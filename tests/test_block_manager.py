@@ -128,3 +128,19 @@ def test_rejections_change_nothing():
         binding.BlockManager(4, 4, [0, 1, 1, 3])   # not a permutation
     assert (bm.num_free(), [bm.ref_count(b) for b in range(8)]) == before
     assert bm.ref_count(8) == -1
+
+
+def test_workload_shared_lens_equal_block_manager_counts():
+    """The hint the benchmark passes (a batch's shared_lens, derived from its
+    tables and shared blocks) equals what the block manager derives from its
+    reference counts for the same prompts."""
+    sp = wl.spec(wl.B256_SHARED_PREFIX_DECODE, num_seqs=16, lens=("uniform", 300, 1500), max_context=1536,
+                 share=dict(num_sharers=7, prefix_tokens=512))
+    st = wl.draw_structure(sp)
+    b = wl.make_batch(sp, device="cpu")
+    bs = b.block_size
+    bm = binding.BlockManager(int(st["num_blocks"]), bs, st["free_list"].tolist())
+    tables = [bm.allocate(ids)[0] for ids in st["token_ids"]]
+    got = [bm.shared_tokens(t, int(L)) for t, L in zip(tables, b.context_lens)]
+    assert got == b.shared_lens.tolist()
+    assert sum(1 for x in got if x == 512) == 7
