@@ -175,10 +175,11 @@ def test_decode_fp8_peaked_logits(gpu, cfg, over):
         gs.decode_fp8_parity(b, P)
 
 
-def test_decode_fp8_edge_lengths(gpu):
+@pytest.mark.parametrize("cfg", [wl.B512_LOGNORMAL_DECODE, wl.B64_MHA_DECODE])  # MHA D 64: KV head pairs
+def test_decode_fp8_edge_lengths(gpu, cfg):
     """Lengths 1, one block, one partition, partition+1, a full table."""
     lens = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128]
-    sp = wl.spec(wl.B512_LOGNORMAL_DECODE, num_seqs=len(lens), lens=("fixed", lens), block_size=16, max_context=128,
+    sp = wl.spec(cfg, num_seqs=len(lens), lens=("fixed", lens), block_size=16, max_context=128,
                  pool=("factor", 1.5), kv="e4m3")
     for part in (0, 32, 16, 112, -1):
         b = wl.make_batch(sp, device=gpu, poison=True)
@@ -187,8 +188,9 @@ def test_decode_fp8_edge_lengths(gpu):
 
 
 @pytest.mark.parametrize("P", [0, 16, -1])
-def test_decode_fp8_zero_length_gives_zeros(gpu, P):
-    b = wl.make_batch(wl.spec(wl.B512_LOGNORMAL_DECODE, num_seqs=4, lens=("fixed", [5, 40, 9, 70]), block_size=16,
+@pytest.mark.parametrize("cfg", [wl.B512_LOGNORMAL_DECODE, wl.B64_MHA_DECODE])  # MHA D 64: KV head pairs
+def test_decode_fp8_zero_length_gives_zeros(gpu, P, cfg):
+    b = wl.make_batch(wl.spec(cfg, num_seqs=4, lens=("fixed", [5, 40, 9, 70]), block_size=16,
                               max_context=80, kv="e4m3"), device=gpu)
     lens = torch.tensor([5, 0, 9, 0], dtype=torch.int32, device=gpu)
     tables = torch.from_numpy(b.block_tables).to(gpu)
