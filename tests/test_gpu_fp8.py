@@ -319,6 +319,9 @@ FP8_STORE_DECODE_CASES = [
                             share=dict(num_sharers=6, prefix_tokens=256)), [0, 128, -1]),
     ("bs8_len1", 2, dict(num_seqs=6, lens=("fixed", [1, 2, 8, 9, 17, 64]), block_size=8,
                          max_context=64), [0, 16, -1]),
+    # 4096 rows of 8 x 128 codes: two 16-byte granules per thread of the
+    # balanced grid (one staged at start-up, one in the loop after it)
+    ("rows_over_grid", 5, dict(num_seqs=4096, lens=("uniform", 1, 48), max_context=64), [0, -1]),
 ]
 
 

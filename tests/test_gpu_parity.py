@@ -330,6 +330,10 @@ STORE_DECODE_CASES = [
                             share=dict(num_sharers=6, prefix_tokens=256)), [0, 128, -1]),
     ("bs8_len1", 2, dict(num_seqs=6, lens=("fixed", [1, 2, 8, 9, 17, 64]), block_size=8,
                          max_context=64), [0, 16, -1]),
+    # 2048 rows of 8 x 128 bf16: twice as many 16-byte granules as the balanced
+    # grid has threads, so each thread stores one granule after the start-up
+    # and one more in the loop after it
+    ("rows_over_grid", 5, dict(num_seqs=2048, lens=("uniform", 1, 48), max_context=64), [0, -1]),
 ]
 
 
