@@ -121,8 +121,8 @@ class DecodeSet:
                                a["tables"], a["lens"], b.max_context_len, b.scale, self.P, self.ws,
                                shared_lens=a["shared"])
         else:
-            pa.pa_decode(a["out"], b.q, b.k_cache, b.v_cache, a["tables"], a["lens"],
-                         b.max_context_len, b.scale, self.P, self.ws, shared_lens=a["shared"])
+            pa.pa_decode_hinted(a["out"], b.q, b.k_cache, b.v_cache, a["tables"], a["lens"], a["shared"],
+                                b.max_context_len, b.scale, self.P, self.ws)
 
 
 # Untimed calls before each extra decode measurement. The first few dozen

@@ -103,19 +103,27 @@ pa_status pa_store_kvcache(const void* key, const void* value,
 
 /*
  * pa_decode_workspace_size -- bytes of workspace pa_decode needs for the
- * given split: partitions of partition_size tokens (0 when no sequence can
+ * given split, whatever num_kv_heads the call passes (any divisor of
+ * num_heads): partitions of partition_size tokens (0 when no sequence can
  * need more than one partition, i.e. partition_size == 0 or partition_size
  * >= max_context_len), or the balanced split (PA_PARTITION_BALANCED; the
  * size depends on the current device's compute-unit count, 256 assumed when
- * no device is visible). The same size serves pa_decode_fp8 and
- * pa_store_decode_fp8: over E4M3 pools at head_dim 64 with one query head
- * per KV head (and an even KV head count) the balanced split reads pairs of
- * KV heads and plans twice the workers, and the size returned is the larger
- * of the two plans. Returns 0 for invalid arguments too.
+ * no device is visible). The size also serves pa_decode_hinted and the
+ * E4M3 calls. Returns 0 for invalid arguments too.
+ *
+ * pa_decode_workspace_size_kv -- the same for a known num_kv_heads: the
+ * exact size of that call's plan (the balanced split's workers depend on
+ * how many query heads a wave serves). Over E4M3 pools at head_dim 64 with
+ * one query head per KV head (and an even KV head count) the balanced split
+ * reads pairs of KV heads and plans twice the workers; the size returned is
+ * the larger of the paired and unpaired plans, so it serves pa_decode,
+ * pa_decode_hinted, pa_decode_fp8 and the fused calls alike.
  */
-size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
-                                int32_t num_kv_heads, int32_t head_dim,
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
                                 int32_t max_context_len, int32_t partition_size);
+size_t pa_decode_workspace_size_kv(int32_t num_seqs, int32_t num_heads,
+                                   int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t max_context_len, int32_t partition_size);
 
 /*
  * pa_decode -- one query token per sequence.
@@ -138,10 +146,22 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
  *                          merged by a second kernel. At most 4096 sequences.
  * The result does not depend on the split beyond fp32 rounding.
  *
- * workspace: device memory of at least pa_decode_workspace_size(...) bytes,
+ * workspace: device memory of at least pa_decode_workspace_size(...) bytes
+ * (or pa_decode_workspace_size_kv(...) with this call's num_kv_heads),
  * 256-byte aligned; its contents on entry do not matter and are scratch
  * afterwards. Calls sharing a workspace must not overlap in time (same
  * stream, or synchronised). May be NULL when the size is 0.
+ */
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens,
+                    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                    float scale, int32_t partition_size,
+                    void* workspace, size_t workspace_bytes, pa_dtype dtype, void* stream);
+
+/*
+ * pa_decode_hinted -- pa_decode with a load-policy hint for shared prefix
+ * blocks; every other argument is pa_decode's, in the same order.
  *
  * shared_lens: NULL, or int32 [num_seqs] on the device (4-byte aligned):
  * the number of leading context tokens of sequence i that lie in blocks
@@ -149,26 +169,26 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads,
  * page, sections 3.2 and 4.2: full blocks found by their rolling hash, with
  * reference counts) only ever shares a sequence's leading blocks, so one
  * count per sequence describes it; the Sequence's num_cached_tokens
- * (pa_bm_allocate) is such a count. Those tokens are read with a
- * cache-retaining load policy, so that the sequences sharing them find them
- * in L2, while every other K/V byte is streamed past the caches. It is a
- * hint only: the result is bit-identical for any values (or NULL, which
- * streams everything).
+ * (pa_bm_allocate) and pa_bm_shared_tokens give such a count. Those tokens
+ * are read with a cache-retaining load policy, so that the sequences
+ * sharing them find them in L2, while every other K/V byte is streamed past
+ * the caches. It is a hint only: the result is bit-identical to pa_decode's
+ * for any values (NULL streams everything, exactly as pa_decode does).
  */
-pa_status pa_decode(void* out, const void* q,
-                    const void* k_cache, const void* v_cache,
-                    const int32_t* block_tables, const int32_t* context_lens,
-                    const int32_t* shared_lens,
-                    int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                    int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                    int32_t max_blocks_per_seq, int32_t max_context_len,
-                    float scale, int32_t partition_size,
-                    void* workspace, size_t workspace_bytes,
-                    pa_dtype dtype, void* stream);
+pa_status pa_decode_hinted(void* out, const void* q,
+                           const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           const int32_t* shared_lens,
+                           int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                           int32_t max_blocks_per_seq, int32_t max_context_len,
+                           float scale, int32_t partition_size,
+                           void* workspace, size_t workspace_bytes,
+                           pa_dtype dtype, void* stream);
 
 /*
  * pa_store_decode -- pa_store_kvcache of each sequence's newest token fused
- * with pa_decode, in one launch (plus the merge kernel of a split).
+ * with pa_decode_hinted, in one launch (plus the merge kernel of a split).
  *
  * Row i of key/value ([num_seqs][num_kv_heads][head_dim], token strides in
  * elements as for pa_store_kvcache) is sequence i's newest token, at
@@ -181,7 +201,8 @@ pa_status pa_decode(void* out, const void* q,
  * mini-vllm page's engine, whose decode step appends one token's K/V through
  * the block table and attends over the whole cached context). A sequence
  * with a negative slot is not stored and attends over the pool as it is.
- * All other arguments, errors and the workspace are those of pa_decode.
+ * All other arguments, errors and the workspace are those of
+ * pa_decode_hinted (shared_lens may be NULL).
  */
 pa_status pa_store_decode(void* out, const void* q,
                           const void* key, const void* value,
@@ -239,11 +260,11 @@ pa_status pa_prefill_chunk(void* out, const void* q,
  * merge kernel of the decode split.
  *
  * max_query_len: the largest n_i. workspace: at least
- * pa_decode_workspace_size(num_decode_seqs, num_heads, num_kv_heads,
+ * pa_decode_workspace_size_kv(num_decode_seqs, num_heads, num_kv_heads,
  * head_dim, max_context_len, PA_PARTITION_BALANCED) bytes, 256-byte aligned
  * (may be NULL when num_decode_seqs is 0). At most 2048 decode sequences.
  * shared_lens: NULL or int32 [num_seqs], the decode rows' load-policy hint
- * as for pa_decode (entries of prefill sequences are not read); the result
+ * as for pa_decode_hinted (entries of prefill sequences are not read); the result
  * does not depend on it.
  * PA_BF16 only. Other arguments, shapes and errors as for pa_prefill_chunk.
  */
@@ -297,9 +318,10 @@ pa_status pa_store_kvcache_fp8(const void* key, const void* value,
  * K[g] = value(codes) * k_scale[g] and V[g] = value(codes) * v_scale[g].
  * q and out are dtype (PA_BF16: q . K by bf16 dot products of q with the
  * exactly widened codes; PA_F32: fp32), accumulation fp32. Splits,
- * workspace (pa_decode_workspace_size with the same arguments), shapes and
- * errors as for pa_decode, and so is shared_lens (pa_store_decode_fp8 below
- * is the fused-store form).
+ * workspace (pa_decode_workspace_size or pa_decode_workspace_size_kv with
+ * the same arguments), shapes and errors as for pa_decode, and shared_lens
+ * as for pa_decode_hinted (pa_store_decode_fp8 below is the fused-store
+ * form).
  */
 pa_status pa_decode_fp8(void* out, const void* q,
                         const void* k_cache, const void* v_cache,

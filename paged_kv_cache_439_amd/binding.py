@@ -41,10 +41,14 @@ _c_void_p, _i32, _i64, _f32, _size = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_
 _SIGNATURES = {
     "pa_store_kvcache": ([_c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
                           _i32, _i32, _i32, _i32, _i32, ctypes.c_int, _c_void_p], ctypes.c_int),
-    "pa_decode_workspace_size": ([_i32, _i32, _i32, _i32, _i32, _i32], _size),
-    "pa_decode": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+    "pa_decode_workspace_size": ([_i32, _i32, _i32, _i32, _i32], _size),
+    "pa_decode_workspace_size_kv": ([_i32, _i32, _i32, _i32, _i32, _i32], _size),
+    "pa_decode": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                    _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                    _c_void_p, _size, ctypes.c_int, _c_void_p], ctypes.c_int),
+    "pa_decode_hinted": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                          _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                          _c_void_p, _size, ctypes.c_int, _c_void_p], ctypes.c_int),
     "pa_store_decode": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p,
                          _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                          _i32, _f32, _i32, _c_void_p, _size, ctypes.c_int, _c_void_p], ctypes.c_int),
@@ -155,18 +159,25 @@ def pa_store_kvcache(key, value, k_cache, v_cache, slot_mapping, stream=None):
     _check("pa_store_kvcache", st)
 
 
-def pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
-                             partition_size) -> int:
-    return int(load_library().pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim,
-                                                       max_context_len, partition_size))
+def pa_decode_workspace_size(num_seqs, num_heads, head_dim, max_context_len, partition_size) -> int:
+    """Workspace bytes a decode call needs whatever its KV head count."""
+    return int(load_library().pa_decode_workspace_size(num_seqs, num_heads, head_dim, max_context_len,
+                                                       partition_size))
+
+
+def pa_decode_workspace_size_kv(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
+                                partition_size) -> int:
+    """Workspace bytes of a decode call with this KV head count (exact)."""
+    return int(load_library().pa_decode_workspace_size_kv(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                          max_context_len, partition_size))
 
 
 def decode_workspace(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
                      partition_size, device):
-    """A workspace of the size pa_decode needs (None if 0); its contents do
-    not matter."""
-    n = pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
-                                 partition_size)
+    """A workspace of the size the decode calls need (None if 0); its
+    contents do not matter."""
+    n = pa_decode_workspace_size_kv(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
+                                    partition_size)
     if n == 0:
         return None
     return torch.empty(n, dtype=torch.uint8, device=device)
@@ -181,12 +192,9 @@ def _shared_lens(t, num_seqs, device):
     return _ptr(t)
 
 
-def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
-              partition_size=0, workspace=None, stream=None, shared_lens=None):
-    """Single-token decode; out and q are [B][Hq][D]. shared_lens (int32 [B]
-    or None): leading context tokens of each sequence in blocks other
-    sequences also read, a load-policy hint that leaves the result unchanged."""
-    lib = load_library()
+def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, workspace):
+    """Checks shared by pa_decode and pa_decode_hinted; returns
+    (B, Hq, Hkv, D, bs, NB, workspace pointer, workspace bytes)."""
     B, Hq, D = q.shape
     _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
     _need(q.is_contiguous() and out.is_contiguous(), "q and out must be contiguous")
@@ -203,12 +211,36 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_
     if workspace is not None:
         _need(workspace.device == q.device and workspace.is_contiguous(), "bad workspace")
         ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
-    sl = _shared_lens(shared_lens, B, q.device)
+    return B, Hq, Hkv, D, bs, NB, ws_ptr, ws_bytes
+
+
+def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+              partition_size=0, workspace=None, stream=None):
+    """Single-token decode; out and q are [B][Hq][D]."""
+    lib = load_library()
+    B, Hq, Hkv, D, bs, NB, ws_ptr, ws_bytes = _decode_args(out, q, k_cache, v_cache, block_tables,
+                                                           context_lens, workspace)
     st = lib.pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
-                       _ptr(context_lens), sl, B, Hq, Hkv, D, bs, NB, block_tables.shape[1],
+                       _ptr(context_lens), B, Hq, Hkv, D, bs, NB, block_tables.shape[1],
                        int(max_context_len), float(scale), int(partition_size), ws_ptr, ws_bytes,
                        _dtype_code(q), _stream(stream))
     _check("pa_decode", st)
+
+
+def pa_decode_hinted(out, q, k_cache, v_cache, block_tables, context_lens, shared_lens,
+                     max_context_len, scale, partition_size=0, workspace=None, stream=None):
+    """pa_decode with the shared-prefix load hint: shared_lens (int32 [B] or
+    None) gives the leading context tokens of each sequence in blocks other
+    sequences also read; the result is pa_decode's."""
+    lib = load_library()
+    B, Hq, Hkv, D, bs, NB, ws_ptr, ws_bytes = _decode_args(out, q, k_cache, v_cache, block_tables,
+                                                           context_lens, workspace)
+    sl = _shared_lens(shared_lens, B, q.device)
+    st = lib.pa_decode_hinted(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                              _ptr(context_lens), sl, B, Hq, Hkv, D, bs, NB, block_tables.shape[1],
+                              int(max_context_len), float(scale), int(partition_size), ws_ptr,
+                              ws_bytes, _dtype_code(q), _stream(stream))
+    _check("pa_decode_hinted", st)
 
 
 def pa_store_decode(out, q, key, value, k_cache, v_cache, slot_mapping, block_tables, context_lens,
@@ -216,7 +248,7 @@ def pa_store_decode(out, q, key, value, k_cache, v_cache, slot_mapping, block_ta
                     shared_lens=None):
     """Store each sequence's newest K/V row [B][Hkv][D] and decode, in one
     launch; the same as pa_store_kvcache followed by pa_decode (shared_lens
-    as for pa_decode)."""
+    as for pa_decode_hinted)."""
     lib = load_library()
     B, Hq, D = q.shape
     _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
@@ -323,7 +355,8 @@ def pa_decode_fp8(out, q, k_cache, v_cache, k_scale, v_scale, block_tables, cont
                   max_context_len, scale, partition_size=0, workspace=None, stream=None,
                   shared_lens=None):
     """Single-token decode over E4M3 pools; out and q are [B][Hq][D] (bf16 or
-    fp32), the workspace and shared_lens as for pa_decode."""
+    fp32), the workspace as for pa_decode, shared_lens as for
+    pa_decode_hinted."""
     lib = load_library()
     B, Hq, D = q.shape
     _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")
@@ -538,7 +571,7 @@ def pa_mixed_batch(out, q, k_cache, v_cache, block_tables, query_start_loc, cont
     """A continuous batch in one call: the first num_decode_seqs sequences are
     decode tokens (one row each), the rest prefill chunks; out and q are
     [T][Hq][D] bf16. shared_lens (int32 [B] or None): the decode rows'
-    load-policy hint, as for pa_decode."""
+    load-policy hint, as for pa_decode_hinted."""
     lib = load_library()
     T, Hq, D = q.shape
     _need(out.shape == q.shape and out.dtype == q.dtype, "out must match q")

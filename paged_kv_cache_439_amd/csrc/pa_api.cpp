@@ -131,8 +131,9 @@ pa_status pa_store_kvcache(const void* key, const void* value, int64_t key_tok_s
   }
 }
 
-size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                                int32_t head_dim, int32_t max_context_len, int32_t partition_size) {
+size_t pa_decode_workspace_size_kv(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                   int32_t head_dim, int32_t max_context_len,
+                                   int32_t partition_size) {
   if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads ||
       head_dim <= 0 || max_context_len <= 0 ||
       (partition_size < 0 && partition_size != PA_PARTITION_BALANCED))
@@ -145,6 +146,18 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t num
                   pa::plan_decode(num_seqs, num_heads, num_kv_heads, head_dim, max_context_len,
                                   partition_size, true)
                       .total_bytes);
+}
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t num_heads, int32_t head_dim,
+                                int32_t max_context_len, int32_t partition_size) {
+  // every grouping a call may use: the largest plan over the KV head counts
+  // that divide num_heads
+  size_t most = 0;
+  for (int32_t hkv = 1; hkv > 0 && hkv <= num_heads; ++hkv)
+    if (num_heads % hkv == 0)
+      most = std::max(most, pa_decode_workspace_size_kv(num_seqs, num_heads, hkv, head_dim,
+                                                        max_context_len, partition_size));
+  return most;
 }
 
 }  // extern "C"
@@ -254,17 +267,33 @@ pa_status decode_impl(const char* fn, void* out, const void* q, const void* k_ca
 extern "C" {
 
 pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-                    const int32_t* block_tables, const int32_t* context_lens,
-                    const int32_t* shared_lens, int32_t num_seqs,
+                    const int32_t* block_tables, const int32_t* context_lens, int32_t num_seqs,
                     int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                     int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
                     float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
                     pa_dtype dtype, void* stream) {
   try {
-    return decode_impl("pa_decode", out, q, k_cache, v_cache, block_tables, context_lens, shared_lens, num_seqs,
-                       num_heads, num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
-                       max_context_len, scale, partition_size, workspace, workspace_bytes, dtype,
-                       stream, nullptr, nullptr);
+    return decode_impl("pa_decode", out, q, k_cache, v_cache, block_tables, context_lens, nullptr,
+                       num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                       max_blocks_per_seq, max_context_len, scale, partition_size, workspace,
+                       workspace_bytes, dtype, stream, nullptr, nullptr);
+  } catch (...) {
+    return fail(PA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+pa_status pa_decode_hinted(void* out, const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           const int32_t* shared_lens, int32_t num_seqs, int32_t num_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int32_t num_blocks, int32_t max_blocks_per_seq, int32_t max_context_len,
+                           float scale, int32_t partition_size, void* workspace,
+                           size_t workspace_bytes, pa_dtype dtype, void* stream) {
+  try {
+    return decode_impl("pa_decode_hinted", out, q, k_cache, v_cache, block_tables, context_lens,
+                       shared_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
+                       num_blocks, max_blocks_per_seq, max_context_len, scale, partition_size,
+                       workspace, workspace_bytes, dtype, stream, nullptr, nullptr);
   } catch (...) {
     return fail(PA_ERR_HIP, "unexpected C++ exception");
   }

@@ -53,9 +53,13 @@ def gpu_decode(batch, partition_size, arrs=None, workspace=None, hint=None):
         workspace = pa.decode_workspace(batch.num_seqs, batch.num_heads, batch.num_kv_heads,
                                         batch.head_dim, batch.max_context_len, partition_size, dev)
     out = torch.full_like(batch.q, float("nan"))
-    pa.pa_decode(out, batch.q, batch.k_cache, batch.v_cache, arrs["tables"], arrs["lens"],
-                 batch.max_context_len, batch.scale, partition_size, workspace,
-                 shared_lens=shared_lens_arg(batch, hint))
+    sl = shared_lens_arg(batch, hint)
+    if sl is None:  # the plain call
+        pa.pa_decode(out, batch.q, batch.k_cache, batch.v_cache, arrs["tables"], arrs["lens"],
+                     batch.max_context_len, batch.scale, partition_size, workspace)
+    else:
+        pa.pa_decode_hinted(out, batch.q, batch.k_cache, batch.v_cache, arrs["tables"], arrs["lens"], sl,
+                            batch.max_context_len, batch.scale, partition_size, workspace)
     return out
 
 

@@ -36,6 +36,86 @@ def test_header_declares_the_three_calls():
         assert n in names
 
 
+# The boundary's fixed prototypes: the three calls, the workspace query and
+# the status string, each parameter as (type, name) in order. A caller bound
+# to these lists (ctypes, dlsym) must find exactly them in the header.
+FIXED_PROTOTYPES = {
+    "pa_store_kvcache": ("pa_status", [
+        ("const void*", "key"), ("const void*", "value"), ("int64_t", "key_tok_stride"),
+        ("int64_t", "value_tok_stride"), ("void*", "k_cache"), ("void*", "v_cache"),
+        ("const int32_t*", "slot_mapping"), ("int32_t", "num_tokens"), ("int32_t", "num_kv_heads"),
+        ("int32_t", "head_dim"), ("int32_t", "block_size"), ("int32_t", "num_blocks"),
+        ("pa_dtype", "dtype"), ("void*", "stream")]),
+    "pa_decode_workspace_size": ("size_t", [
+        ("int32_t", "num_seqs"), ("int32_t", "num_heads"), ("int32_t", "head_dim"),
+        ("int32_t", "max_context_len"), ("int32_t", "partition_size")]),
+    "pa_decode": ("pa_status", [
+        ("void*", "out"), ("const void*", "q"), ("const void*", "k_cache"), ("const void*", "v_cache"),
+        ("const int32_t*", "block_tables"), ("const int32_t*", "context_lens"),
+        ("int32_t", "num_seqs"), ("int32_t", "num_heads"), ("int32_t", "num_kv_heads"),
+        ("int32_t", "head_dim"), ("int32_t", "block_size"), ("int32_t", "num_blocks"),
+        ("int32_t", "max_blocks_per_seq"), ("int32_t", "max_context_len"), ("float", "scale"),
+        ("int32_t", "partition_size"), ("void*", "workspace"), ("size_t", "workspace_bytes"),
+        ("pa_dtype", "dtype"), ("void*", "stream")]),
+    "pa_prefill_chunk": ("pa_status", [
+        ("void*", "out"), ("const void*", "q"), ("const void*", "k_cache"), ("const void*", "v_cache"),
+        ("const int32_t*", "block_tables"), ("const int32_t*", "query_start_loc"),
+        ("const int32_t*", "context_lens"), ("int32_t", "num_seqs"), ("int32_t", "num_heads"),
+        ("int32_t", "num_kv_heads"), ("int32_t", "head_dim"), ("int32_t", "block_size"),
+        ("int32_t", "num_blocks"), ("int32_t", "max_blocks_per_seq"), ("int32_t", "max_query_len"),
+        ("int32_t", "max_context_len"), ("float", "scale"), ("pa_dtype", "dtype"),
+        ("void*", "stream")]),
+    "pa_status_string": ("const char*", [("pa_status", "s")]),
+}
+
+
+def _norm_type(t):
+    """'const int32_t *' -> 'const int32_t*'."""
+    t = " ".join(t.split())
+    return t.replace(" *", "*")
+
+
+def header_prototypes():
+    """{name: (return type, [(param type, param name), ...])} of every
+    function the header declares (comments and preprocessor lines removed)."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    text = "\n".join(line for line in text.splitlines() if not line.lstrip().startswith("#"))
+    protos = {}
+    for stmt in re.split(r"[;{}]", text):
+        m = re.fullmatch(r"\s*([\w\s\*]+?)\s*\b(pa_\w+)\s*\(([^()]*)\)\s*", stmt)
+        if not m or "typedef" in m.group(1):
+            continue
+        params = []
+        body = " ".join(m.group(3).split())
+        if body and body != "void":
+            for part in body.split(","):
+                pm = re.fullmatch(r"\s*(.*?[\s\*])(\w+)\s*", part)
+                params.append((_norm_type(pm.group(1)), pm.group(2)))
+        protos[m.group(2)] = (_norm_type(m.group(1)), params)
+    return protos
+
+
+def test_fixed_prototypes_verbatim():
+    protos = header_prototypes()
+    for name, (ret, params) in FIXED_PROTOTYPES.items():
+        assert name in protos, name
+        got_ret, got_params = protos[name]
+        assert got_params == params, (name, got_params)
+        assert got_ret == ret, (name, got_ret)
+
+
+def test_hinted_decode_is_pa_decode_plus_shared_lens():
+    """pa_decode_hinted takes pa_decode's parameters with shared_lens after
+    context_lens; pa_decode_workspace_size_kv takes num_kv_heads after
+    num_heads."""
+    protos = header_prototypes()
+    plain = protos["pa_decode"][1]
+    hinted = protos["pa_decode_hinted"][1]
+    assert hinted == plain[:6] + [("const int32_t*", "shared_lens")] + plain[6:]
+    ws = protos["pa_decode_workspace_size"][1]
+    assert protos["pa_decode_workspace_size_kv"][1] == ws[:2] + [("int32_t", "num_kv_heads")] + ws[2:]
+
+
 def test_every_declared_symbol_is_exported(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
@@ -51,12 +131,16 @@ FAKE = ctypes.c_void_p(0x100000)  # 16-byte aligned, never dereferenced on these
 
 
 def _decode(lib, **kw):
-    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, sl=None, B=4, Hq=8, Hkv=8, D=64,
+    """pa_decode, or pa_decode_hinted when shared_lens (sl) is given."""
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, B=4, Hq=8, Hkv=8, D=64,
              bs=16, NB=64, MB=7, maxL=100, scale=0.125, P=0, ws=None, wsb=0, dtype=0)
+    hinted = "sl" in kw
     a.update(kw)
-    return lib.pa_decode(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["sl"], a["B"], a["Hq"],
-                         a["Hkv"], a["D"], a["bs"], a["NB"], a["MB"], a["maxL"], a["scale"], a["P"],
-                         a["ws"], a["wsb"], a["dtype"], None)
+    rest = (a["B"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"], a["MB"], a["maxL"], a["scale"], a["P"],
+            a["ws"], a["wsb"], a["dtype"], None)
+    if hinted:
+        return lib.pa_decode_hinted(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["sl"], *rest)
+    return lib.pa_decode(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], *rest)
 
 
 def test_decode_rejections(lib):
@@ -69,12 +153,15 @@ def test_decode_rejections(lib):
     assert _decode(lib, bs=4) == PA_ERR_UNSUPPORTED
     assert _decode(lib, maxL=113) == PA_ERR_INVALID_ARG   # > 7 blocks x 16
     assert _decode(lib, sl=ctypes.c_void_p(0x100002)) == PA_ERR_UNSUPPORTED  # shared_lens misaligned
+    assert "pa_decode_hinted" in binding.load_library().pa_last_error().decode()
+    assert _decode(lib, sl=None, B=0) == PA_OK                    # hinted, NULL hint: a no-op too
+    assert _decode(lib, sl=None, q=None) == PA_ERR_INVALID_ARG
     assert _decode(lib, P=24) == PA_ERR_INVALID_ARG
     assert _decode(lib, scale=float("nan")) == PA_ERR_INVALID_ARG
     assert _decode(lib, dtype=7) == PA_ERR_INVALID_ARG
     assert _decode(lib, q=ctypes.c_void_p(0x100008)) == PA_ERR_UNSUPPORTED
     assert _decode(lib, P=32) == PA_ERR_WORKSPACE          # split without a workspace
-    need = lib.pa_decode_workspace_size(4, 8, 8, 64, 100, 32)
+    need = lib.pa_decode_workspace_size_kv(4, 8, 8, 64, 100, 32)
     assert _decode(lib, P=32, ws=FAKE, wsb=need - 1) == PA_ERR_WORKSPACE
     assert _decode(lib, P=32, ws=ctypes.c_void_p(0x100010), wsb=need) == PA_ERR_WORKSPACE
     assert "workspace" in binding.load_library().pa_last_error().decode()
@@ -89,14 +176,28 @@ def _gpu_visible():
 
 
 def test_workspace_sizes(lib):
-    assert lib.pa_decode_workspace_size(4, 8, 8, 64, 100, 0) == 0
-    assert lib.pa_decode_workspace_size(4, 8, 8, 64, 100, 112) == 0    # one partition suffices
+    assert lib.pa_decode_workspace_size_kv(4, 8, 8, 64, 100, 0) == 0
+    assert lib.pa_decode_workspace_size_kv(4, 8, 8, 64, 100, 112) == 0    # one partition suffices
     # 4 seqs x 8 heads x 4 partitions: D floats of weighted values, an (m, l) pair
-    n = lib.pa_decode_workspace_size(4, 8, 8, 64, 100, 32)
+    n = lib.pa_decode_workspace_size_kv(4, 8, 8, 64, 100, 32)
     r = lambda x: (x + 255) // 256 * 256
     assert n == r(4 * 8 * 4 * 64 * 4) + r(4 * 8 * 4 * 2 * 4)
-    assert lib.pa_decode_workspace_size(4, 8, 3, 64, 100, 32) == 0      # invalid grouping
-    assert lib.pa_decode_workspace_size(4, 8, 8, 64, 100, -2) == 0      # not a split mode
+    assert lib.pa_decode_workspace_size_kv(4, 8, 3, 64, 100, 32) == 0      # invalid grouping
+    assert lib.pa_decode_workspace_size_kv(4, 8, 8, 64, 100, -2) == 0      # not a split mode
+
+
+def test_workspace_size_without_kv_heads(lib):
+    """pa_decode_workspace_size (no KV head count) returns the largest size
+    over every KV head count that divides num_heads, so it serves any call;
+    fixed slices do not depend on the KV heads at all."""
+    for (B, Hq, D, L, P) in [(4, 8, 64, 100, 32), (512, 32, 128, 4096, 512), (64, 12, 64, 4096, -1),
+                             (512, 32, 128, 4096, -1), (3, 6, 128, 100, -1), (7, 5, 64, 900, 0)]:
+        sizes = [lib.pa_decode_workspace_size_kv(B, Hq, k, D, L, P) for k in range(1, Hq + 1) if Hq % k == 0]
+        assert lib.pa_decode_workspace_size(B, Hq, D, L, P) == max(sizes), (B, Hq, D, L, P)
+        if P > 0:
+            assert len(set(sizes)) == 1
+    assert lib.pa_decode_workspace_size(0, 8, 64, 100, 32) == 0
+    assert lib.pa_decode_workspace_size(4, 8, 64, 100, -2) == 0
 
 
 def test_balanced_workspace_size(lib):
@@ -123,13 +224,13 @@ def test_balanced_workspace_size(lib):
         want = size(B, Hq, units, D)
         if D == 64 and G == 1 and Hkv % 2 == 0:
             want = max(want, size(B, Hq, Hkv // 2, D))
-        assert lib.pa_decode_workspace_size(B, Hq, Hkv, D, 4096, -1) == want, (B, Hq, Hkv, D)
+        assert lib.pa_decode_workspace_size_kv(B, Hq, Hkv, D, 4096, -1) == want, (B, Hq, Hkv, D)
 
 
 def test_balanced_rejections(lib):
     # head_dim 128: no KV-head pairing, so the size is exactly what the call
     # checks, and one byte less is rejected before anything is launched
-    need = lib.pa_decode_workspace_size(4, 8, 8, 128, 100, -1)
+    need = lib.pa_decode_workspace_size_kv(4, 8, 8, 128, 100, -1)
     assert need > 0
     assert _decode(lib, D=128, P=-1) == PA_ERR_WORKSPACE
     assert _decode(lib, D=128, P=-1, ws=FAKE, wsb=need - 1) == PA_ERR_WORKSPACE
@@ -231,7 +332,7 @@ def _decode_fp8(lib, **kw):
 def test_decode_fp8_rejections(lib):
     # E4M3, head_dim 64, 8 KV heads: the balanced split pairs the heads and
     # needs the whole workspace size; one byte less is rejected up front
-    need = lib.pa_decode_workspace_size(4, 8, 8, 64, 100, -1)
+    need = lib.pa_decode_workspace_size_kv(4, 8, 8, 64, 100, -1)
     assert _decode_fp8(lib, P=-1, ws=FAKE, wsb=need - 1) == PA_ERR_WORKSPACE
     assert _decode_fp8(lib, B=0) == PA_OK
     assert _decode_fp8(lib, kscale=None) == PA_ERR_INVALID_ARG
@@ -341,3 +442,15 @@ def test_stream_read_rejections(lib):
     assert lib.pa_stream_read(ctypes.c_void_p(0x100008), 1 << 30, out, ctypes.byref(n), None) == PA_ERR_UNSUPPORTED
     assert lib.pa_stream_read(FAKE, 1 << 20, out, ctypes.byref(n), None) == PA_ERR_INVALID_ARG  # below the minimum
 
+
+
+def test_binding_argument_counts_match_header():
+    """Every ctypes signature of the binding passes as many arguments as the
+    header's prototype declares (a dropped or extra argument would shift
+    every later one)."""
+    protos = header_prototypes()
+    sigs = dict(binding._SIGNATURES)
+    sigs.update(binding._BM_SIGNATURES)
+    for name, (args, _res) in sigs.items():
+        assert name in protos, name
+        assert len(args) == len(protos[name][1]), (name, len(args), len(protos[name][1]))
