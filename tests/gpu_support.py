@@ -350,3 +350,93 @@ def store_decode_fp8_parity(batch, partition_size):
                                    wl.to_numpy(batch.key), wl.to_numpy(batch.value), batch.slot_mapping,
                                    batch.block_size, ks, vs, batch.dtype)
     return res, ek, ev
+
+
+# ---------------------------------------------------------------------------
+# the oracle over whole full-size batches
+# ---------------------------------------------------------------------------
+#
+# Sequences are independent, and row t of a prefill chunk over c cached
+# tokens depends only on keys 0 .. c+t, so the oracle's own functions are
+# applied to groups of sequences (decode) or to pieces of a chunk's rows
+# (prefill: rows t0..t1-1 form a chunk of t1-t0 rows over a context of
+# c+t1 tokens) in a few host threads, and the pieces are put back in place.
+# Nothing of the arithmetic changes: each output row is the oracle's.
+
+ORACLE_THREADS = 4
+
+
+def oracle_decode_all(hb, kp, vp, scale, block_size, dtype, fp8_scales=None, threads=ORACLE_THREADS):
+    """oracle decode (oa.decode, or of8.decode_fp8 with fp8_scales=(ks, vs))
+    of every sequence of the host batch hb over the stored pools kp/vp."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+    import oracle.fp8 as of8
+    B = hb.q.shape[0]
+    groups = [np.arange(k, B, 4 * threads) for k in range(min(B, 4 * threads))]
+
+    def run(idx):
+        if fp8_scales is None:
+            return idx, oa.decode(hb.q[idx], kp, vp, hb.block_tables[idx], hb.context_lens[idx], scale,
+                                  block_size, dtype)
+        ks, vs = fp8_scales
+        return idx, of8.decode_fp8(hb.q[idx], kp, vp, ks, vs, hb.block_tables[idx], hb.context_lens[idx],
+                                   scale, block_size, dtype)
+
+    out = np.zeros(hb.q.shape, dtype=np.float64)
+    with threadpool_limits(limits=1), ThreadPoolExecutor(threads) as ex:
+        for idx, res in ex.map(run, groups):
+            out[idx] = res
+    return out
+
+
+def oracle_prefill_all(hb, kp, vp, scale, block_size, dtype, fp8_scales=None, threads=ORACLE_THREADS,
+                       piece=128):
+    """oracle varlen prefill (oa.prefill, or of8.prefill_fp8) of every row
+    of the host batch hb, in pieces of at most `piece` rows per chunk."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+    import oracle.fp8 as of8
+    qsl, lens = hb.query_start_loc, hb.context_lens
+    tasks = []
+    for i in range(len(lens)):
+        s, e = int(qsl[i]), int(qsl[i + 1])
+        c = int(lens[i]) - (e - s)
+        for t0 in range(0, e - s, piece):
+            t1 = min(e - s, t0 + piece)
+            tasks.append((i, s + t0, s + t1, c + t1))
+    tasks.sort(key=lambda t: -(t[3] * (t[2] - t[1])))   # longest first
+
+    def run(task):
+        i, r0, r1, L = task
+        qs = np.array([0, r1 - r0], dtype=np.int32)
+        ls = np.array([L], dtype=np.int32)
+        if fp8_scales is None:
+            res = oa.prefill(hb.q[r0:r1], kp, vp, hb.block_tables[i:i + 1], qs, ls, scale, block_size, dtype)
+        else:
+            ks, vs = fp8_scales
+            res = of8.prefill_fp8(hb.q[r0:r1], kp, vp, ks, vs, hb.block_tables[i:i + 1], qs, ls, scale,
+                                  block_size, dtype)
+        return r0, r1, res
+
+    out = np.zeros(hb.q.shape, dtype=np.float64)
+    with threadpool_limits(limits=1), ThreadPoolExecutor(threads) as ex:
+        for r0, r1, res in ex.map(run, tasks):
+            out[r0:r1] = res
+    return out
+
+
+def check_pool_after_store(before_k, before_v, batch, kp, vp, hb):
+    """The pools after a (fused) store: the rows every context covers equal
+    the oracle's stored pools kp/vp byte for byte (host_subset renumbers the
+    covered blocks in the same order for both), and no other byte of either
+    pool changed (before_k/before_v: device copies taken before the call)."""
+    after = wl.host_subset(batch)
+    assert np.array_equal(after.k_cache, kp) and np.array_equal(after.v_cache, vp), "stored rows differ"
+    covered = torch.from_numpy(wl.covered_rows(batch)).to(batch.k_cache.device)
+    for name, pb, pa_ in (("k", before_k, batch.k_cache), ("v", before_v, batch.v_cache)):
+        bits = torch.int16 if pa_.element_size() == 2 else torch.int32 if pa_.element_size() == 4 else torch.uint8
+        untouched = torch.equal(pa_.view(bits)[~covered], pb.view(bits)[~covered])
+        assert untouched, f"{name} pool changed outside the contexts"

@@ -76,3 +76,25 @@ def test_host_subset_renumbers_consistently():
     c = oa.decode(part.q, part.k_cache, part.v_cache, part.block_tables, part.context_lens,
                   b.scale, b.block_size, b.dtype)
     assert a[4].tobytes() == c[0].tobytes() and a[1].tobytes() == c[1].tobytes()
+
+
+def test_b512_balanced_split_cuts_most_long_contexts():
+    """The regime the full-size decode comparisons cover: on the b512
+    lognormal workload (GQA 32/8, head_dim 128, bf16) a 256-CU device runs
+    2 waves per SIMD, i.e. 2048 waves, over 8 units (one KV head with its 4
+    query heads each), so 256 workers per unit take equal ranges of the
+    contexts cut into 32-token chunks (8 loads per lane, 4 token rows per
+    wave-wide load). Many sequences are cut by a range boundary, so their
+    outputs come from the merge of partial states."""
+    st = wl.draw_structure(wl.spec(wl.B512_LOGNORMAL_DECODE))
+    lens = st["context_lens"].astype(np.int64)
+    ct, workers = 32, 2 * 4 * 256 // 8
+    nchunks = (lens + ct - 1) // ct
+    pfx = np.concatenate([[0], np.cumsum(nchunks)])
+    C = int(pfx[-1])
+    first = ((pfx[:-1] + 1) * workers - 1) // C
+    last = (pfx[1:] * workers - 1) // C
+    cut = last > first
+    assert cut.sum() >= 200, int(cut.sum())
+    # and a worker's range spans several whole contexts on average
+    assert C / workers > lens.mean() / ct
