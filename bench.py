@@ -7,29 +7,32 @@ writes the new token's K/V row of every sequence into the pool and attends
 over the whole paged context in the same launch (balanced split: equal K/V
 ranges per resident wave, then a merge kernel for the sequences the ranges
 cut).
-The default workload is the bf16 MHA decode batch (64 sequences, 12 heads,
-head_dim 64, block 256, context lengths uniform in [512, 4096]). Several
-independently drawn batches (each with its own pool) are resident in HBM and
-the steps cycle through them, so consecutive steps never find their K/V in the
-256 MB last-level cache.
+The default workload is the largest decode batch that one GPU holds: 512
+sequences of GQA 32/8 heads, head_dim 128, bf16, blocks of 64 tokens,
+context lengths lognormal (median 1500, sigma 1) clipped to [64, 4096],
+about 4 GB of K/V in a shuffled pool. Several independently drawn batches
+(each with its own pool) are resident in HBM and the steps cycle through
+them, so consecutive steps never find their K/V in the 256 MB last-level
+cache.
 
 Prints ONE JSON line. `value` is decode tokens/s (sequences x steps / timed
 seconds). `roofline` covers the decode call (its main and merge kernels):
 algorithmic K+V bytes per launch over its average duration: one pair of HIP
 events on the launch stream around the timed run of launches, divided by the
 number of launches (an event pair around every launch would add GPU time to
-each step). The roofline also gives the device's streaming-read rate measured in the
-same run (pa_stream_read, a measurement aid of the library) and the decode
-rate as a fraction of it. `cpu_baseline` is the
-CPU oracle on a bounded sample of the same workload, single-threaded, and
-under `parallel` the same oracle's decode parallel over sequences in a
-fork-based pool of up to 16 processes (forked before any GPU call). `extra`
-reports the other workloads (GQA decode with shared prefix, GQA decode at 512
-sequences, each with the balanced split and with its fixed-slice split, the
-three decode workloads over 8-bit E4M3 pools, chunked prefill, and a
-continuous batch of decode tokens and prefill chunks in one pa_mixed_batch
-call beside the same work as two calls, the last two also over E4M3 pools)
-measured the same way.
+each step). The roofline also gives the device's streaming-read rate
+measured in the same run (pa_stream_read, a measurement aid of the library)
+and the decode rate as a fraction of it. `cpu_baseline` is the CPU oracle's
+decode of whole sequences of the same workload (a host-drawn batch of the
+same recipe) on one thread, and under `parallel` the same work over
+sequences in a fork-based pool of min(host CPUs, 16) processes (forked
+before any GPU call). `extra` reports the other workloads measured the same
+way (the tiny fp32 decode, the b64 MHA and b256 shared-prefix decodes, each
+decode workload with its fixed-slice split, the three decode workloads over
+8-bit E4M3 pools, chunked prefill, and a continuous batch of decode tokens
+and prefill chunks in one pa_mixed_batch call beside the same work as two
+calls, the last two also over E4M3 pools) and, under `cpu_oracle`, the CPU
+oracle's rate on a bounded sample of each workload.
 """
 
 from __future__ import annotations
@@ -178,11 +181,13 @@ def time_run(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def bench_prefill(steps, warmup, device, kv=None):
+def bench_prefill(steps, warmup, device, kv=None, oracle_rates=None):
     """The chunked-prefill workload: pa_prefill_chunk on bf16 pools, or
     (kv="e4m3") pa_prefill_chunk_fp8 on E4M3 pools with per-head scales."""
     sp = wl.spec(wl.CHUNKED_PREFILL, kv="e4m3") if kv == "e4m3" else wl.spec(wl.CHUNKED_PREFILL)
     b = wl.make_batch(sp, device=device)
+    if oracle_rates is not None:
+        oracle_rates[sp["name"]] = oracle_sample_rate(b)
     slots = torch.from_numpy(b.slot_mapping).to(device)
     tables = torch.from_numpy(b.block_tables).to(device)
     qsl = torch.from_numpy(b.query_start_loc).to(device)
@@ -213,7 +218,7 @@ def bench_prefill(steps, warmup, device, kv=None):
                 kv_cache=kv or "bf16")
 
 
-def bench_mixed(steps, warmup, device, kv=None):
+def bench_mixed(steps, warmup, device, kv=None, oracle_rates=None):
     """The continuous batch (decode tokens + prefill chunks): pa_mixed_batch
     against the same work as two calls (pa_decode on the decode tokens, then
     pa_prefill_chunk on the chunks) and against each call alone; with
@@ -222,6 +227,8 @@ def bench_mixed(steps, warmup, device, kv=None):
     e4 = kv == "e4m3"
     sp = wl.spec(wl.MIXED_BATCH, kv="e4m3") if e4 else wl.spec(wl.MIXED_BATCH)
     b = wl.make_batch(sp, device=device)
+    if oracle_rates is not None:
+        oracle_rates[sp["name"]] = oracle_sample_rate(b)
     Bd = b.num_decode
     a = dict(slots=torch.from_numpy(b.slot_mapping).to(device),
              tables=torch.from_numpy(b.block_tables).to(device),
@@ -321,6 +328,15 @@ def stream_read_probe(dev, nbytes=4 << 30, iters=10):
     return n / (ms * 1e-3) / 1e9
 
 
+def lens_desc(lens):
+    """A workload's context-length recipe as text."""
+    if lens[0] == "uniform":
+        return f"uniform[{lens[1]},{lens[2]}]"
+    if lens[0] == "lognormal":
+        return f"lognormal(median {lens[1]:g}, sigma {lens[2]:g}) clipped to [{lens[3]},{lens[4]}]"
+    return str(list(lens[1]))
+
+
 def split_name(P):
     return "balanced" if P == pa.PA_PARTITION_BALANCED else "fixed"
 
@@ -378,101 +394,158 @@ def copy_probe(nbytes, device, reps=3):
     del x, y
 
 
-def cpu_baseline(ds, budget_s=12.0):
-    """The CPU oracle (store + decode, fp64), single-threaded, on whole
-    sequences of the first batch until about budget_s seconds have passed."""
+# The host batch the CPU oracle is timed on, built before anything touches
+# the GPU (so that the parallel leg's forked workers hold no device state):
+# (host copy, stored K pool, stored V pool, scale, block size, dtype).
+_PAR = None
+
+
+def host_oracle_batch(cfg):
+    """The workload's first batch drawn on the host, and the oracle's store
+    applied to it once (untimed: it copies whole pools)."""
     import oracle.attention as oa
-    from threadpoolctl import threadpool_limits
-    b = ds.batches[0][0]
+    b = wl.make_batch(wl.spec(cfg), device="cpu", seed=wl.SEED_BASE + cfg)
     hb = wl.host_subset(b)
-    done = 0
-    with threadpool_limits(limits=1):
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < budget_s:
-            kp, vp = oa.store_kvcache(hb.k_cache, hb.v_cache, hb.key, hb.value, hb.slot_mapping,
-                                      b.block_size)
-            for i in range(b.num_seqs):
-                oa.decode(hb.q[i:i + 1], kp, vp, hb.block_tables[i:i + 1], hb.context_lens[i:i + 1],
-                          b.scale, b.block_size, b.dtype)
-                done += 1
-                if time.perf_counter() - t0 >= budget_s:
-                    break
-    secs = time.perf_counter() - t0
-    return dict(value=round(done / secs, 2), unit="tokens/s", cores=1, kind="oracle",
-                sample=f"{done} sequences of the first batch (mean context "
-                       f"{float(b.context_lens.mean()):.0f} tokens), store+decode in fp64, "
-                       f"{secs:.1f} s on 1 thread")
+    kp, vp = oa.store_kvcache(hb.k_cache, hb.v_cache, hb.key, hb.value, hb.slot_mapping, b.block_size)
+    return hb, kp, vp, b.scale, b.block_size, b.dtype
 
 
-_PAR = None  # the host batch the parallel oracle's forked workers inherit
-
-
-def _par_worker(task):
-    """One forked worker: decode sequences w, w+n, ... of the inherited batch
-    (wrapping around) until budget_s has passed; returns (sequences, tokens)."""
+def _decode_for(budget_s, first, stride):
+    """Oracle decodes of whole sequences first, first + stride, ... of the
+    host batch (wrapping around) until budget_s has passed, one thread;
+    returns (sequences, context tokens, seconds)."""
     import oracle.attention as oa
     from threadpoolctl import threadpool_limits
-    w, n, budget_s = task
     hb, kp, vp, scale, bs, dtype = _PAR
     B = len(hb.context_lens)
     done = toks = 0
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        i = w % B
+        i = first % B
         while time.perf_counter() - t0 < budget_s:
             oa.decode(hb.q[i:i + 1], kp, vp, hb.block_tables[i:i + 1], hb.context_lens[i:i + 1],
                       scale, bs, dtype)
             done += 1
             toks += int(hb.context_lens[i])
-            i = (i + n) % B
-    return done, toks
+            i = (i + stride) % B
+        secs = time.perf_counter() - t0
+    return done, toks, secs
+
+
+def _par_worker(task):
+    w, n, budget_s = task
+    return _decode_for(budget_s, w, n)
 
 
 def cpu_model():
+    """The host CPU as /proc/cpuinfo names it (model name, family, model,
+    stepping), and the logical CPUs the host has."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as fh:
             for line in fh:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" in line:
+                    k, v = (x.strip() for x in line.split(":", 1))
+                    info.setdefault(k, v)
     except OSError:
         pass
-    return "unknown"
+    name = info.get("model name", "unknown")
+    fam = ", ".join(f"{k} {info[k]}" for k in ("cpu family", "model", "stepping") if k in info)
+    return f"{name} ({fam})" if fam else name
 
 
-def cpu_baseline_parallel(cfg, budget_s=10.0, max_workers=16):
-    """The CPU oracle's decode of whole sequences, parallel over sequences in
-    a fork-based process pool (at most max_workers, the host share of one
-    GPU), on a copy of the workload's first batch built on the host. It runs
-    before anything initialises the GPU, so the workers are forks of a
-    process that holds no device state. The oracle's store runs once per
-    batch, untimed (it copies whole pools)."""
+# The parallel leg's process count: the host share of one GPU on a
+# multi-GPU host is 16 CPUs, whatever the host's own count is.
+CPU_SHARE = 16
+
+
+def cpu_baselines(cfg, budget_1=12.0, budget_par=10.0):
+    """The CPU oracle's decode of whole sequences of the workload's first
+    batch, in fp64: on one thread, and parallel over sequences in a
+    fork-based pool of min(host CPUs, CPU_SHARE) processes (one thread each).
+    Both time the same work (the decode; the store ran once, untimed). Runs
+    before anything initialises the GPU."""
     global _PAR
     import multiprocessing as mp
-    import oracle.attention as oa
-    b = wl.make_batch(wl.spec(cfg), device="cpu", seed=wl.SEED_BASE + cfg)
-    hb = wl.host_subset(b)
-    kp, vp = oa.store_kvcache(hb.k_cache, hb.v_cache, hb.key, hb.value, hb.slot_mapping, b.block_size)
-    _PAR = (hb, kp, vp, b.scale, b.block_size, b.dtype)
-    n = max(1, min(max_workers, os.cpu_count() or 1))
+    _PAR = host_oracle_batch(cfg)
+    hb = _PAR[0]
+    mean_ctx = float(hb.context_lens.mean())
+    model, host_cpus = cpu_model(), os.cpu_count() or 1
+    done, toks, secs = _decode_for(budget_1, 0, 1)
+    single = dict(value=round(done / secs, 2), unit="tokens/s", cores=1, kind="oracle",
+                  cpu_model=model, host_cpus=host_cpus,
+                  sample=f"{done} whole-sequence decodes (fp64 attention of the query over its whole "
+                         f"context; {toks} context tokens) of the first batch (mean context {mean_ctx:.0f}), "
+                         f"{secs:.1f} s on 1 thread; the oracle's store of the batch ran once, untimed")
+    n = max(1, min(CPU_SHARE, host_cpus))
     pool = mp.get_context("fork").Pool(n)
+    par = None
     try:
         t0 = time.perf_counter()
-        res = pool.map_async(_par_worker, [(w, n, budget_s) for w in range(n)])
-        out = res.get(timeout=budget_s + 120)
+        res = pool.map_async(_par_worker, [(w, n, budget_par) for w in range(n)])
+        out = res.get(timeout=budget_par + 120)
         secs = time.perf_counter() - t0
+        done = sum(d for d, _, _ in out)
+        toks = sum(t for _, t, _ in out)
+        par = dict(value=round(done / secs, 2), unit="tokens/s", cores=n, kind="oracle",
+                   cpu_model=model, host_cpus=host_cpus,
+                   sample=f"{done} whole-sequence decodes ({toks} context tokens) of the first batch "
+                          f"(mean context {mean_ctx:.0f}) in fp64, {secs:.1f} s on {n} forked processes, "
+                          f"one thread each ({n} of the host's {host_cpus} CPUs; the host share of one GPU is "
+                          f"{CPU_SHARE}); the store once, untimed")
     except mp.TimeoutError:
         pool.terminate()
-        return None
     finally:
         pool.close()
         pool.join()
         _PAR = None
-    done = sum(d for d, _ in out)
-    return dict(value=round(done / secs, 2), unit="tokens/s", cores=n, cpu_model=cpu_model(),
-                kind="oracle",
-                sample=f"{done} whole-sequence decodes of the first batch (mean context "
-                       f"{float(b.context_lens.mean()):.0f} tokens) in fp64, {secs:.1f} s on {n} "
-                       f"forked processes, one thread each; the store once per batch, untimed")
+    return single, par
+
+
+def oracle_sample_rate(batch, budget_s=3.0, seed=0):
+    """The CPU oracle (one thread, fp64) on a bounded sample of a device
+    batch: decode workloads, whole sequences in seeded random order
+    (tokens/s = sequences per second); prefill and mixed workloads, pieces
+    of up to 32 consecutive rows of random chunks (rows per second; a piece
+    of rows t0..t1-1 is the chunk's definition restricted to those rows).
+    The store of the sampled rows' blocks runs once, untimed."""
+    import oracle.attention as oa
+    from threadpoolctl import threadpool_limits
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if batch.kind == "decode":
+        seqs = sorted(rng.permutation(batch.num_seqs)[:min(batch.num_seqs, 24)].tolist())
+    else:
+        seqs = sorted(rng.permutation(batch.num_seqs)[:min(batch.num_seqs, 6)].tolist())
+    hb = wl.host_subset(batch, seqs)
+    kp, vp = oa.store_kvcache(hb.k_cache, hb.v_cache, hb.key, hb.value, hb.slot_mapping, batch.block_size)
+    units = toks = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        k = 0
+        while time.perf_counter() - t0 < budget_s:
+            r = k % len(seqs)
+            k += 1
+            if batch.kind == "decode":
+                oa.decode(hb.q[r:r + 1], kp, vp, hb.block_tables[r:r + 1], hb.context_lens[r:r + 1],
+                          batch.scale, batch.block_size, batch.dtype)
+                units += 1
+                toks += int(hb.context_lens[r])
+            else:
+                s0, s1 = int(hb.query_start_loc[r]), int(hb.query_start_loc[r + 1])
+                n = s1 - s0
+                t0_ = int(rng.integers(0, n))
+                t1_ = min(n, t0_ + 32)
+                L = int(hb.context_lens[r]) - n + t1_
+                oa.prefill(hb.q[s0 + t0_:s0 + t1_], kp, vp, hb.block_tables[r:r + 1],
+                           np.array([0, t1_ - t0_], dtype=np.int32), np.array([L], dtype=np.int32),
+                           batch.scale, batch.block_size, batch.dtype)
+                units += t1_ - t0_
+        secs = time.perf_counter() - t0
+    what = "sequences" if batch.kind == "decode" else "rows"
+    return dict(value=round(units / secs, 2), unit="tokens/s", cores=1, kind="oracle",
+                sample=f"{units} {what} of {len(seqs)} sampled sequences"
+                       + (f" ({toks} context tokens)" if batch.kind == "decode" else "")
+                       + f", {secs:.1f} s on 1 thread")
 
 
 def main():
@@ -481,7 +554,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=100)
     by_name = {wl.WORKLOADS[w]["name"]: w for w in wl.DECODE_WORKLOADS}
-    ap.add_argument("--workload", default=wl.WORKLOADS[wl.B64_MHA_DECODE]["name"], choices=sorted(by_name))
+    ap.add_argument("--workload", default=wl.WORKLOADS[wl.B512_LOGNORMAL_DECODE]["name"], choices=sorted(by_name))
     ap.add_argument("--rotations", type=int, default=4)
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -496,11 +569,11 @@ def main():
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
-    # the parallel CPU oracle forks worker processes: before any GPU call
-    par = None
+    # the CPU oracle (its parallel leg forks worker processes): before any GPU call
+    single = par = None
     if not args.no_cpu and args.only is None:
-        log("cpu baseline, parallel")
-        par = cpu_baseline_parallel(by_name[args.workload])
+        log("cpu baseline: oracle on the host, 1 thread and parallel")
+        single, par = cpu_baselines(by_name[args.workload])
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
@@ -543,14 +616,14 @@ def main():
             "workload": ds.spec["name"],
             "num_seqs": b0.num_seqs, "num_heads": b0.num_heads, "num_kv_heads": b0.num_kv_heads,
             "head_dim": b0.head_dim, "block_size": b0.block_size,
-            "context_lens": "uniform[512,4096]" if workload == wl.B64_MHA_DECODE else str(ds.spec["lens"]),
+            "context_lens": lens_desc(ds.spec["lens"]),
             "split": split_name(ds.P), "partition_size": ds.P, "rotating_batches": args.rotations,
             "step": "pa_store_decode: store the new rows + decode, one launch (+ merge)",
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": ("pa_decode: paged_decode_balanced_kernel + paged_decode_balanced_merge_kernel"
-                       if ds.P == pa.PA_PARTITION_BALANCED else "pa_decode: paged_decode_kernel (+ merge)"),
+            "kernel": ("pa_store_decode: paged_decode_balanced_kernel + paged_decode_balanced_merge_kernel"
+                       if ds.P == pa.PA_PARTITION_BALANCED else "pa_store_decode: paged_decode_kernel (+ merge)"),
             "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(ds.spec["name"], split_name(ds.P)),
@@ -562,6 +635,23 @@ def main():
     }
     if not args.no_extra:
         extra = {}
+        # the CPU oracle on a bounded sample of every workload (one thread)
+        with_oracle = not args.no_cpu and args.only is None
+        oracle_rates = {}
+        if with_oracle:
+            oracle_rates[ds.spec["name"]] = oracle_sample_rate(b0)
+        log("extra workload tiny_fp32_mha_decode")
+        d = DecodeSet(wl.TINY_FP32_DECODE, 1, dev)
+        s_t, ms_t, nb_t = time_decode(d, 200, 50)
+        bb = d.batches[0][0]
+        extra[bb.spec["name"]] = dict(
+            tokens_per_s=round(bb.num_seqs * 200 / s_t, 1), call_ms=round(ms_t, 4),
+            kv_gbs=round(nb_t / (ms_t * 1e-3) / 1e9, 2), bytes_per_launch=int(nb_t), split="whole contexts",
+            step="pa_store_decode (fp32): store the new rows + decode, one launch",
+            note="4 sequences: launch-latency bound, a correctness workload")
+        if with_oracle:
+            oracle_rates[bb.spec["name"]] = oracle_sample_rate(bb)
+        del d
         for cfg in wl.DECODE_WORKLOADS:
             P_bal = wl.WORKLOADS[cfg]["partition_size"]
             runs = [(P_bal, True, True), (wl.WORKLOADS[cfg]["fixed_partition_size"], True, True)]
@@ -579,6 +669,8 @@ def main():
                 d = DecodeSet(cfg, 2, dev, partition=P, fused=fused, hint=hint)
                 s, ms, nb = time_decode(d, 30, LEG_WARMUP)
                 bb = d.batches[0][0]
+                if with_oracle and bb.spec["name"] not in oracle_rates:
+                    oracle_rates[bb.spec["name"]] = oracle_sample_rate(bb)
                 key = d.spec["name"] + ("" if P == pa.PA_PARTITION_BALANCED else f"_fixed_p{P}")
                 key += "" if fused else "_separate_store"
                 key += "" if hint else "_no_shared_lens"
@@ -610,28 +702,29 @@ def main():
                 step="pa_store_kvcache_fp8 + pa_decode_fp8 (kernel_ms: pa_decode_fp8)",
                 fused_step="pa_store_decode_fp8, one launch (+ merge)",
                 fused_tokens_per_s=round(bb.num_seqs * 30 / s_f, 1), fused_call_ms=round(ms_f, 4),
-                logical_bytes_per_launch=int(np.mean(d.kv_bytes_logical)))
+                logical_bytes_per_launch=int(np.mean(d.kv_bytes_logical)),
+                traffic=measured_traffic(d.spec["name"] + "_e4m3", split_name(P)))
             del d
             torch.cuda.empty_cache()
         if args.only is None:
             log("extra block manager")
             extra["block_manager"] = bench_block_manager()
             log("extra prefill")
-            extra["prefill"] = bench_prefill(20, 10, dev)
+            extra["prefill"] = bench_prefill(20, 10, dev, oracle_rates=oracle_rates if with_oracle else None)
             log("extra prefill e4m3")
             extra["prefill_e4m3"] = bench_prefill(20, 10, dev, kv="e4m3")
             log("extra mixed batch")
-            extra["mixed_batch"] = bench_mixed(20, 10, dev)
+            extra["mixed_batch"] = bench_mixed(20, 10, dev, oracle_rates=oracle_rates if with_oracle else None)
             log("extra mixed batch e4m3")
             extra["mixed_batch_e4m3"] = bench_mixed(20, 10, dev, kv="e4m3")
+        if oracle_rates:
+            extra["cpu_oracle"] = oracle_rates
         line["extra"] = extra
     if args.copy_probe:
         log(f"copy probe {args.copy_probe} bytes")
         copy_probe(args.copy_probe, dev)
-    if not args.no_cpu:
-        log("cpu baseline")
-        line["cpu_baseline"] = cpu_baseline(ds)
-        line["cpu_baseline"]["cpu_model"] = cpu_model()
+    if single is not None:
+        line["cpu_baseline"] = single
         if par is not None:
             line["cpu_baseline"]["parallel"] = par
     print(json.dumps(line), flush=True)

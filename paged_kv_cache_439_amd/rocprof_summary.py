@@ -98,19 +98,29 @@ def traffic(fetch_csv, write_csv, out_json, out_md, copy_bytes, cmd_fetch, cmd_w
     # per workload and split: the balanced split's two kernels, or the
     # fixed-slice split's main and merge kernels
     workloads = {}
+    # Main kernels name the query and pool types (E4M3 pools: unsigned char;
+    # the paired-head kernel of the b64 workload has one head per wave too),
+    # merge kernels only the output type, so a merge kernel's average is
+    # shared by a workload's bf16 and E4M3 calls (a few MB against GBs).
+    merges = {}
     for k, v in kernels.items():
-        # bf16 pools only (main kernels name the query and pool types, merge
-        # kernels the output type)
-        m = re.search(r"paged_decode(_balanced)?(_merge)?_kernel<unsigned short, (?:unsigned short, )?(\d+), (\d+)", k)
+        m = re.search(r"paged_decode(_balanced)?_merge_kernel<unsigned short, (\d+), (\d+)>", k)
+        if m:
+            merges[("balanced" if m.group(1) else "fixed", m.group(2), m.group(3))] = (k, v)
+    for k, v in kernels.items():
+        m = re.search(r"paged_decode(_balanced)?_kernel<unsigned short, unsigned (short|char), (\d+), (\d+)", k)
         if not m:
             continue
         wname = KERNEL_WORKLOAD.get((m.group(3), m.group(4)))
         if not wname:
             continue
+        wname += "_e4m3" if m.group(2) == "char" else ""
         split = "balanced" if m.group(1) else "fixed"
         w = workloads.setdefault(wname, {}).setdefault(split, dict(hbm_bytes_per_launch=0.0, kernels=[]))
-        w["hbm_bytes_per_launch"] += v["fetch_bytes"] + v["write_bytes"]
-        w["kernels"].append(k)
+        for kk, vv in [(k, v)] + ([merges[(split, m.group(3), m.group(4))]]
+                                  if (split, m.group(3), m.group(4)) in merges else []):
+            w["hbm_bytes_per_launch"] += vv["fetch_bytes"] + vv["write_bytes"]
+            w["kernels"].append(kk)
     for ws_ in workloads.values():
         for w in ws_.values():
             w["hbm_bytes_per_launch"] = int(w["hbm_bytes_per_launch"])
