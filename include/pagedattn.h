@@ -187,6 +187,36 @@ pa_status pa_decode_hinted(void* out, const void* q,
                            pa_dtype dtype, void* stream);
 
 /*
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same arguments without the workspace, the same
+ * kernels and result. A split's partial states go to a static scratch
+ * array of PA_NOALLOC_SCRATCH_BYTES in the library, one per GPU, held
+ * until the process ends; the call allocates and frees nothing. Its address
+ * on a GPU is looked up the first time the call runs there (PA_ERR_HIP if
+ * that fails).
+ *
+ * Limit: a split whose workspace (pa_decode_workspace_size_kv with the same
+ * arguments) exceeds PA_NOALLOC_SCRATCH_BYTES returns PA_ERR_WORKSPACE and
+ * enqueues nothing. The balanced split (PA_PARTITION_BALANCED) needs at
+ * most about 8.5 MB on a 256-CU device for any batch the call accepts;
+ * whole contexts (0) need none; fixed slices need num_seqs * num_heads *
+ * partitions * (head_dim + 2) * 4 bytes.
+ *
+ * Every call on one GPU shares that GPU's array, which keeps the last
+ * call's contents (nothing in it needs clearing: every call writes what it
+ * reads). Calls that overlap in time on one GPU (different streams, or
+ * different host threads without ordering) race on it.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                            int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                            int32_t partition_size, pa_dtype dtype, void* stream);
+
+/*
  * pa_store_decode -- pa_store_kvcache of each sequence's newest token fused
  * with pa_decode_hinted, in one launch (plus the merge kernel of a split).
  *

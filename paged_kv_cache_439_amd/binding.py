@@ -46,6 +46,9 @@ _SIGNATURES = {
     "pa_decode": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                    _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                    _c_void_p, _size, ctypes.c_int, _c_void_p], ctypes.c_int),
+    "pa_decode_noalloc": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                           _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                           ctypes.c_int, _c_void_p], ctypes.c_int),
     "pa_decode_hinted": ([_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
                           _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                           _c_void_p, _size, ctypes.c_int, _c_void_p], ctypes.c_int),
@@ -225,6 +228,23 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, context_lens, max_context_
                        int(max_context_len), float(scale), int(partition_size), ws_ptr, ws_bytes,
                        _dtype_code(q), _stream(stream))
     _check("pa_decode", st)
+
+
+PA_NOALLOC_SCRATCH_BYTES = 16 << 20  # the library's static scratch per GPU
+
+
+def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                      partition_size=0, stream=None):
+    """pa_decode without a workspace: a split keeps its partial states in
+    the library's static per-GPU scratch (calls on one GPU must not
+    overlap); nothing is allocated."""
+    lib = load_library()
+    B, Hq, Hkv, D, bs, NB, _, _ = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, None)
+    st = lib.pa_decode_noalloc(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+                               _ptr(context_lens), B, Hq, Hkv, D, bs, NB, block_tables.shape[1],
+                               int(max_context_len), float(scale), int(partition_size), _dtype_code(q),
+                               _stream(stream))
+    _check("pa_decode_noalloc", st)
 
 
 def pa_decode_hinted(out, q, k_cache, v_cache, block_tables, context_lens, shared_lens,

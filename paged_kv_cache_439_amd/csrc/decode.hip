@@ -4,6 +4,7 @@
 #include "decode_device.h"
 
 #include <algorithm>
+#include <mutex>
 
 namespace pa {
 
@@ -191,6 +192,40 @@ DecodeParams make_decode_params(const DecodeArgs& a, const DecodePlan& pl) {
     prm.num_slots = (int64_t)a.num_blocks * a.block_size;
   }
   return prm;
+}
+
+// ---------------------------------------------------------------------------
+// static scratch of pa_decode_noalloc
+// ---------------------------------------------------------------------------
+//
+// The split workspace of callers that cannot allocate device memory: one
+// array per GPU, in the library's code object, held until the process ends.
+// Its address on a device comes from hipGetSymbolAddress with that device
+// current (each GPU holds its own copy at its own address); in host code
+// the array's name is not a device address, so only the looked-up pointer
+// is ever passed on.
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[NOALLOC_MAX_DEVICES] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t stream) {

@@ -186,7 +186,7 @@ pa_status decode_impl(const char* fn, void* out, const void* q, const void* k_ca
                       int32_t block_size, int32_t num_blocks, int32_t max_blocks_per_seq,
                       int32_t max_context_len, float scale, int32_t partition_size, void* workspace,
                       size_t workspace_bytes, pa_dtype dtype, void* stream, const Fusion* fused,
-                      const E4M3Scales* e4m3) {
+                      const E4M3Scales* e4m3, bool noalloc = false) {
   if (pa_status st = check_dtype(dtype)) return st;
   if (num_seqs < 0) return fail(PA_ERR_INVALID_ARG, "%s: num_seqs=%d is negative", fn, num_seqs);
   if (num_seqs == 0) return ok();
@@ -235,6 +235,21 @@ pa_status decode_impl(const char* fn, void* out, const void* q, const void* k_ca
   const pa::DecodePlan plan = pa::plan_decode(num_seqs, num_heads, num_kv_heads, head_dim,
                                               max_context_len, partition_size, e4m3 != nullptr);
   if ((plan.units + 3) / 4 > 65535) return fail(PA_ERR_UNSUPPORTED, "%s: too many heads", fn);
+  if (noalloc) {
+    // pa_decode_noalloc: the library's static scratch is the workspace
+    if (plan.total_bytes > pa::NOALLOC_SCRATCH_BYTES)
+      return fail(PA_ERR_WORKSPACE,
+                  "%s: this split needs %zu bytes of scratch; the static scratch holds %zu (use "
+                  "pa_decode with a workspace, or a larger partition_size)",
+                  fn, plan.total_bytes, pa::NOALLOC_SCRATCH_BYTES);
+    workspace = nullptr;
+    workspace_bytes = 0;
+    if (plan.total_bytes) {
+      const hipError_t err = pa::noalloc_scratch(&workspace);
+      if (err != hipSuccess) return fail(PA_ERR_HIP, "%s: scratch lookup: %s", fn, hipGetErrorString(err));
+      workspace_bytes = pa::NOALLOC_SCRATCH_BYTES;
+    }
+  }
   if (plan.total_bytes) {
     if (!workspace)
       return fail(PA_ERR_WORKSPACE, "%s: this split needs a workspace of %zu bytes", fn,
@@ -294,6 +309,23 @@ pa_status pa_decode_hinted(void* out, const void* q, const void* k_cache, const 
                        shared_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size,
                        num_blocks, max_blocks_per_seq, max_context_len, scale, partition_size,
                        workspace, workspace_bytes, dtype, stream, nullptr, nullptr);
+  } catch (...) {
+    return fail(PA_ERR_HIP, "unexpected C++ exception");
+  }
+}
+
+pa_status pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                            int32_t max_blocks_per_seq, int32_t max_context_len, float scale,
+                            int32_t partition_size, pa_dtype dtype, void* stream) {
+  static_assert(PA_NOALLOC_SCRATCH_BYTES == pa::NOALLOC_SCRATCH_BYTES, "scratch size");
+  try {
+    return decode_impl("pa_decode_noalloc", out, q, k_cache, v_cache, block_tables, context_lens,
+                       nullptr, num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                       max_blocks_per_seq, max_context_len, scale, partition_size, nullptr, 0, dtype,
+                       stream, nullptr, nullptr, /*noalloc=*/true);
   } catch (...) {
     return fail(PA_ERR_HIP, "unexpected C++ exception");
   }

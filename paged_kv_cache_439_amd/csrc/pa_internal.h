@@ -101,6 +101,13 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
 hipError_t launch_store(const StoreArgs& a, hipStream_t stream);
 hipError_t launch_store_e4m3(const StoreE4M3Args& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& plan, hipStream_t stream);
+
+// pa_decode_noalloc: the bytes of the static per-GPU scratch array
+// (decode.hip), the devices it serves, and its address on the current
+// device (looked up once per device with hipGetSymbolAddress, then kept).
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(16) << 20;
+constexpr int NOALLOC_MAX_DEVICES = 64;
+hipError_t noalloc_scratch(void** ptr);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
 // pa_stream_read (stream_probe.hip): waves it launches on the current

@@ -454,3 +454,24 @@ def test_binding_argument_counts_match_header():
     for name, (args, _res) in sigs.items():
         assert name in protos, name
         assert len(args) == len(protos[name][1]), (name, len(args), len(protos[name][1]))
+
+
+def test_noalloc_rejections(lib):
+    """pa_decode_noalloc validates like pa_decode and refuses, before any
+    device call, a split whose workspace exceeds its static scratch."""
+    def call(**kw):
+        a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, cl=FAKE, B=4, Hq=8, Hkv=8, D=64, bs=16, NB=64,
+                 MB=7, maxL=100, scale=0.125, P=0, dtype=0)
+        a.update(kw)
+        return lib.pa_decode_noalloc(a["out"], a["q"], a["k"], a["v"], a["bt"], a["cl"], a["B"], a["Hq"],
+                                     a["Hkv"], a["D"], a["bs"], a["NB"], a["MB"], a["maxL"], a["scale"], a["P"],
+                                     a["dtype"], None)
+    assert call(B=0) == PA_OK
+    assert call(B=-1) == PA_ERR_INVALID_ARG
+    assert call(D=96) == PA_ERR_UNSUPPORTED
+    # 512 x 32 x 8 slices x (128 + 2) floats: 68 MB of split state
+    assert call(B=512, Hq=32, Hkv=8, D=128, bs=64, NB=20000, MB=64, maxL=4096, P=512, dtype=1) == PA_ERR_WORKSPACE
+    assert "static scratch" in binding.load_library().pa_last_error().decode()
+    assert binding.PA_NOALLOC_SCRATCH_BYTES == 16 << 20
+    text = open(HEADER).read()
+    assert "#define PA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)" in text
