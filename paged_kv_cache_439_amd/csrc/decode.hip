@@ -88,7 +88,7 @@ static void launch_balanced_main(const DecodeParams& prm, const DecodePlan& pl, 
 }
 
 template <typename T, typename KT, int D, int GT, int U>
-static void launch_balanced(const DecodeParams& prm, const DecodePlan& pl, dim3 grid, hipStream_t stream) {
+static void launch_balanced(const DecodeParams& prm, const DecodePlan& pl, int32_t num_seqs, hipStream_t stream) {
   if constexpr (sizeof(KT) == 1 && D == 64 && GT == 1) {
     if (pl.pair) launch_balanced_main<T, KT, D, GT, U, true>(prm, pl, stream);
     else launch_balanced_main<T, KT, D, GT, U, false>(prm, pl, stream);
@@ -97,12 +97,19 @@ static void launch_balanced(const DecodeParams& prm, const DecodePlan& pl, dim3 
   }
   // the merge takes one KV head per unit (a pair's two heads separately)
   const unsigned merge_units = (unsigned)(pl.pair ? 2 * pl.units : pl.units);
-  hipLaunchKernelGGL((paged_decode_balanced_merge_kernel<T, D, GT>), dim3(grid.z, (merge_units + 3) / 4),
+  hipLaunchKernelGGL((paged_decode_balanced_merge_kernel<T, D, GT>), dim3(num_seqs, (merge_units + 3) / 4),
                      dim3(256), 0, stream, prm);
 }
 
 template <typename T, typename KT, int D, int GT, int U>
-static void launch_fixed(const DecodeParams& prm, const DecodePlan& pl, dim3 grid, hipStream_t stream) {
+// Fixed slices: grid (unit groups, sequences, partitions), so that every
+// sequence's first partition is dispatched before any second one: the
+// long contexts' later partitions come last, and the waves in flight at any
+// time spread over all sequences (measured on the b512 lognormal workload
+// with 512-token slices: 730 us against 820 us with partitions dispatched
+// sequence by sequence).
+static void launch_fixed(const DecodeParams& prm, const DecodePlan& pl, int32_t num_seqs, hipStream_t stream) {
+  const dim3 grid((unsigned)((pl.units + 3) / 4), (unsigned)num_seqs, (unsigned)pl.max_parts);
   constexpr int TPW = 64 / (D * (int)sizeof(KT) / 16);
   constexpr int CT = U * TPW;
   const bool big_blocks = (1 << prm.bs_log2) >= CT;
@@ -112,7 +119,7 @@ static void launch_fixed(const DecodeParams& prm, const DecodePlan& pl, dim3 gri
   else
     hipLaunchKernelGGL((paged_decode_kernel<T, KT, D, GT, U, false>), grid, dim3(256), 0, stream, prm);
   if (pl.max_parts > 1)
-    hipLaunchKernelGGL((paged_decode_merge_kernel<T, D, GT>), dim3(grid.z, grid.x), dim3(256), 0,
+    hipLaunchKernelGGL((paged_decode_merge_kernel<T, D, GT>), dim3(num_seqs, grid.x), dim3(256), 0,
                        stream, prm);
 }
 
@@ -120,28 +127,28 @@ static void launch_fixed(const DecodeParams& prm, const DecodePlan& pl, dim3 gri
 // E4M3 pools DECODE_U_E4M3 in the balanced split and half of it in the fixed
 // split, whose four-heads-per-wave kernel would otherwise spill registers.
 template <typename T, typename KT, int D, int GT>
-static void launch_split(const DecodeParams& prm, const DecodePlan& pl, dim3 grid, hipStream_t stream) {
+static void launch_split(const DecodeParams& prm, const DecodePlan& pl, int32_t num_seqs, hipStream_t stream) {
   constexpr bool E8 = sizeof(KT) == 1;
   constexpr int UB = E8 ? DECODE_U_E4M3 : DECODE_U;
   constexpr int UF = E8 ? (DECODE_U_E4M3 > 2 ? DECODE_U_E4M3 / 2 : DECODE_U_E4M3) : DECODE_U;
-  if (pl.balanced) launch_balanced<T, KT, D, GT, UB>(prm, pl, grid, stream);
-  else launch_fixed<T, KT, D, GT, UF>(prm, pl, grid, stream);
+  if (pl.balanced) launch_balanced<T, KT, D, GT, UB>(prm, pl, num_seqs, stream);
+  else launch_fixed<T, KT, D, GT, UF>(prm, pl, num_seqs, stream);
 }
 
 template <typename T, typename KT, int D>
-static void launch_gt(const DecodeParams& prm, const DecodePlan& pl, dim3 grid, hipStream_t stream) {
+static void launch_gt(const DecodeParams& prm, const DecodePlan& pl, int32_t num_seqs, hipStream_t stream) {
   switch (pl.heads_per_unit) {
-    case 1: launch_split<T, KT, D, 1>(prm, pl, grid, stream); break;
-    case 2: launch_split<T, KT, D, 2>(prm, pl, grid, stream); break;
-    default: launch_split<T, KT, D, 4>(prm, pl, grid, stream); break;
+    case 1: launch_split<T, KT, D, 1>(prm, pl, num_seqs, stream); break;
+    case 2: launch_split<T, KT, D, 2>(prm, pl, num_seqs, stream); break;
+    default: launch_split<T, KT, D, 4>(prm, pl, num_seqs, stream); break;
   }
 }
 
 template <typename T, typename KT>
-static void launch_d(const DecodeParams& prm, const DecodePlan& pl, int head_dim, dim3 grid,
+static void launch_d(const DecodeParams& prm, const DecodePlan& pl, int head_dim, int32_t num_seqs,
                      hipStream_t stream) {
-  if (head_dim == 64) launch_gt<T, KT, 64>(prm, pl, grid, stream);
-  else launch_gt<T, KT, 128>(prm, pl, grid, stream);
+  if (head_dim == 64) launch_gt<T, KT, 64>(prm, pl, num_seqs, stream);
+  else launch_gt<T, KT, 128>(prm, pl, num_seqs, stream);
 }
 
 DecodeParams make_decode_params(const DecodeArgs& a, const DecodePlan& pl) {
@@ -230,15 +237,12 @@ hipError_t noalloc_scratch(void** ptr) {
 
 hipError_t launch_decode(const DecodeArgs& a, const DecodePlan& pl, hipStream_t stream) {
   const DecodeParams prm = make_decode_params(a, pl);
-  // x: head group (fastest, so one token's rows of all heads are read by
-  // neighbouring workgroups), y: partition, z: sequence.
-  const dim3 grid((unsigned)((pl.units + 3) / 4), (unsigned)pl.max_parts, (unsigned)a.num_seqs);
   if (a.kv_e4m3) {
-    if (a.bf16) launch_d<uint16_t, uint8_t>(prm, pl, a.head_dim, grid, stream);
-    else launch_d<float, uint8_t>(prm, pl, a.head_dim, grid, stream);
+    if (a.bf16) launch_d<uint16_t, uint8_t>(prm, pl, a.head_dim, a.num_seqs, stream);
+    else launch_d<float, uint8_t>(prm, pl, a.head_dim, a.num_seqs, stream);
   } else {
-    if (a.bf16) launch_d<uint16_t, uint16_t>(prm, pl, a.head_dim, grid, stream);
-    else launch_d<float, float>(prm, pl, a.head_dim, grid, stream);
+    if (a.bf16) launch_d<uint16_t, uint16_t>(prm, pl, a.head_dim, a.num_seqs, stream);
+    else launch_d<float, float>(prm, pl, a.head_dim, a.num_seqs, stream);
   }
   return hipGetLastError();
 }

@@ -13,7 +13,7 @@
 //
 // Work decomposition (one wave64 = one unit of work):
 //   unit = (sequence, KV head, group of GT query heads, partition of P tokens)
-//   grid = (max partitions, sequences, ceil(units per (seq, partition) / 4)),
+//   grid = (ceil(units per (seq, partition) / 4), sequences, max partitions),
 //   256 threads = 4 independent waves, no LDS and no barriers.
 // Lane mapping: a K or V row of one head is D*e bytes = LPT lanes x 16 bytes,
 // so a wave-wide 16-byte load covers TPW = 64/LPT token rows; U loads per lane
@@ -748,8 +748,8 @@ __global__ __launch_bounds__(256, (decode_min_wgs<T, KT, GT>())) void paged_deco
 
   const int lane = threadIdx.x & 63;
   const int unit = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int seq = blockIdx.z;
-  const int part = blockIdx.y;
+  const int seq = blockIdx.y;
+  const int part = blockIdx.z;
   if constexpr (fused_store_supported<T, KT>()) {
     if (p.new_k != nullptr && blockIdx.x == 0 && part == 0) {  // fused store of seq's row
       const int64_t cpr = p.row_bytes / 16;

@@ -235,6 +235,9 @@ pa_status decode_impl(const char* fn, void* out, const void* q, const void* k_ca
   const pa::DecodePlan plan = pa::plan_decode(num_seqs, num_heads, num_kv_heads, head_dim,
                                               max_context_len, partition_size, e4m3 != nullptr);
   if ((plan.units + 3) / 4 > 65535) return fail(PA_ERR_UNSUPPORTED, "%s: too many heads", fn);
+  if (plan.max_parts > 65535)  // a grid dimension of the fixed split
+    return fail(PA_ERR_UNSUPPORTED, "%s: %d partitions of %d tokens (at most 65535)", fn, plan.max_parts,
+                partition_size);
   if (noalloc) {
     // pa_decode_noalloc: the library's static scratch is the workspace
     if (plan.total_bytes > pa::NOALLOC_SCRATCH_BYTES)

@@ -161,6 +161,8 @@ def test_decode_rejections(lib):
     assert _decode(lib, dtype=7) == PA_ERR_INVALID_ARG
     assert _decode(lib, q=ctypes.c_void_p(0x100008)) == PA_ERR_UNSUPPORTED
     assert _decode(lib, P=32) == PA_ERR_WORKSPACE          # split without a workspace
+    # more partitions than a grid dimension holds: 16-token slices of 2^20 tokens
+    assert _decode(lib, P=16, MB=1 << 16, maxL=1 << 20, ws=FAKE, wsb=1 << 40) == PA_ERR_UNSUPPORTED
     need = lib.pa_decode_workspace_size_kv(4, 8, 8, 64, 100, 32)
     assert _decode(lib, P=32, ws=FAKE, wsb=need - 1) == PA_ERR_WORKSPACE
     assert _decode(lib, P=32, ws=ctypes.c_void_p(0x100010), wsb=need) == PA_ERR_WORKSPACE
