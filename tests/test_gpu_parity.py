@@ -456,6 +456,53 @@ def test_prefill_variants(gpu, name):
     gs.prefill_parity(b)
 
 
+def _grow_prefill_keys(b, factor):
+    """Scale the K row at context position j of every sequence by
+    1 + factor * j / L (cached rows in the pool, the chunk's own rows in
+    key), so that each row's logits grow along its causal prefix."""
+    bs = b.block_size
+    blocks, rows, scales = [], [], []
+    krow_scale = torch.ones(b.key.shape[0], dtype=torch.float32)
+    for i, L in enumerate(b.context_lens.tolist()):
+        n = int(b.query_start_loc[i + 1] - b.query_start_loc[i])
+        c = L - n
+        for j in range(c):
+            blocks.append(int(b.block_tables[i, j // bs]))
+            rows.append(j % bs)
+            scales.append(1.0 + factor * j / L)
+        for t in range(n):
+            krow_scale[int(b.query_start_loc[i]) + t] = 1.0 + factor * (c + t) / L
+    dev = b.k_cache.device
+    if blocks:
+        bi, ri = torch.tensor(blocks, device=dev), torch.tensor(rows, device=dev)
+        sc = torch.tensor(scales, device=dev, dtype=torch.float32)[:, None, None]
+        b.k_cache[bi, ri] = (b.k_cache[bi, ri].float() * sc).to(b.k_cache.dtype)
+    b.key = (b.key.float() * krow_scale.to(dev)[:, None, None]).to(b.key.dtype)
+    return b
+
+
+@pytest.mark.parametrize("factor", [0.0, 0.5, 4.0])
+@pytest.mark.parametrize("runner", ["prefill", "mixed"])
+def test_prefill_peaked_growing_logits(gpu, factor, runner):
+    """Scale 1.0 (log2-logits spanning about +-40) with keys growing along
+    the context: with factor 4 the later tiles' logits exceed every
+    earlier running maximum by far more than the lazy-rescale threshold,
+    so the maxima are raised and the partial sums rescaled many times per
+    row; with factor 0 and 0.5 the raises are fewer and smaller."""
+    if runner == "prefill":
+        sp = wl.spec(wl.CHUNKED_PREFILL, num_seqs=4, cached=("uniform", 0, 1500), chunk=[200, 77, 33, 130],
+                     max_context=2048, scale=1.0)
+        b = _grow_prefill_keys(wl.make_batch(sp, device=gpu, poison=True), factor)
+        gs.say(f"prefill growing keys factor={factor} lens={b.context_lens.tolist()}")
+        gs.prefill_parity(b)
+    else:
+        sp = wl.spec(wl.MIXED_BATCH, num_seqs=7, num_decode=4, decode_lens=("uniform", 1, 1200),
+                     cached=("uniform", 0, 1200), chunk=[150, 64, 1], max_context=1536, scale=1.0)
+        b = _grow_prefill_keys(wl.make_batch(sp, device=gpu, poison=True), factor)
+        gs.say(f"mixed growing keys factor={factor} lens={b.context_lens.tolist()}")
+        gs.prefill_parity(b, runner=gs.gpu_mixed)
+
+
 def test_prefill_full_config_sampled(gpu):
     b = wl.make_batch(wl.spec(wl.CHUNKED_PREFILL), device=gpu, poison=True)
     gs.say(f"prefill full cfg4 lens={b.context_lens.tolist()}")
