@@ -462,6 +462,130 @@ __device__ __forceinline__ void pv_token_pair(const uint4& vu, const uint4& vu1,
   }
 }
 
+// Fused store: the newest token of sequence seq (KV head kvh), taken from
+// the new row itself (over E4M3 pools, as the codes the store writes), into
+// the state st with the exact max-rescaling update. Token-row group 0 holds
+// it (every lane loads the same row so that the butterfly over the row's
+// lanes stays uniform); lane dc holds the row's slice dc.
+template <typename T, typename KT, int D, int GT>
+__device__ __forceinline__ void attend_new_row(const DecodeParams& p, int seq, int kvh, int dc, int tr,
+                                               const QSlice<T, KT> (&qv)[GT], float sm,
+                                               WaveState<GT, 16 / ElemTraits<KT>::E>& st) {
+  constexpr int E = ElemTraits<KT>::E;
+  constexpr int EPL = 16 / E;
+  constexpr int LPT = D / EPL;
+  uint4 kr, vr;
+  if constexpr (E == 1) {  // E4M3 pools: this lane's 16 elements, quantised
+    const int64_t src = ((int64_t)kvh * D + dc * 16) * (int64_t)sizeof(T);
+    kr = quantize16<T>(p.new_k + seq * p.new_k_stride + src, p.k_scale[kvh]);
+    vr = quantize16<T>(p.new_v + seq * p.new_v_stride + src, p.v_scale[kvh]);
+  } else {
+    const int64_t off = (int64_t)kvh * D * E + dc * 16;
+    kr = *reinterpret_cast<const uint4*>(p.new_k + seq * p.new_k_stride + off);
+    vr = *reinterpret_cast<const uint4*>(p.new_v + seq * p.new_v_stride + off);
+  }
+  float vf[EPL];
+  widen_slice<KT, EPL>(vr, vf);
+#pragma unroll
+  for (int h = 0; h < GT; ++h) {
+    float sc = group_sum<LPT>(qv[h].dot(kr)) * sm;
+    sc = (tr == 0) ? sc : -INFINITY;
+    const float mn = fmaxf(st.m[h], sc);
+    const float alpha = fast_exp2(st.m[h] - mn);
+    const float pr = fast_exp2(sc - mn);
+    st.m[h] = mn;
+    st.l[h] = st.l[h] * alpha + pr;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) st.acc[h][e] = fmaf(pr, vf[e], st.acc[h][e] * alpha);
+  }
+}
+
+// The pool offsets of a streaming loop's chunks: lane (dc, tr) reads the
+// 16-byte slice at lane_off of token rows tr, tr + TPW, ..., tr + (U-1)*TPW
+// of the chunk. The block-table window (lane i holds the physical id of
+// block wbase + i) slides with the chunks. UNIFORM_BLOCK: every chunk lies
+// inside one block (block_size >= U*TPW and the range starts at a multiple
+// of it), so one table lookup serves all lanes; otherwise each lane looks up
+// its own token's block. Rows past tok_end (valid false) re-read the chunk's
+// first row, so that they hold finite pool data.
+//
+// The loads themselves stay in each loop (issue_chunk_loads): behind a
+// function boundary, LLVM sinks the last loads of the two cache-policy
+// branches into one store through a selected pointer, and the chunk's
+// arrays go to scratch memory.
+template <int U, int TPW, bool NT, bool UNIFORM_BLOCK>
+struct ChunkAddresses {
+  static constexpr int CT = U * TPW;
+  const char* k_cache;
+  const char* v_cache;
+  const int32_t* bt;
+  int64_t block_bytes;
+  int num_blocks, bs_log2, bs_mask, row_bytes, lane_off, lane, tr, tok_end, last_blk, wbase, tbl;
+  // Tokens [0, shared_len) lie in blocks that other sequences read too
+  // (prefix sharing shares leading blocks only): they are loaded with the
+  // cache-retaining policy, so that the other readers find them in L2,
+  // while the rest of the context streams past. Only the hint differs.
+  int shared_len;
+
+  __device__ __forceinline__ ChunkAddresses(const DecodeParams& p, int seq, int lane_, int tr_, int lane_off_,
+                                         int tok_begin, int tok_end_)
+      : k_cache(p.k_cache), v_cache(p.v_cache), bt(p.block_tables + (int64_t)seq * p.max_blocks_per_seq),
+        block_bytes(p.block_bytes), num_blocks(p.num_blocks), bs_log2(p.bs_log2),
+        bs_mask((1 << p.bs_log2) - 1), row_bytes(p.row_bytes), lane_off(lane_off_), lane(lane_), tr(tr_),
+        tok_end(tok_end_) {
+    shared_len = (NT && p.shared_lens != nullptr) ? p.shared_lens[seq] : 0;
+    last_blk = (tok_end - 1) >> bs_log2;
+    wbase = tok_begin >> bs_log2;
+    tbl = (wbase + lane <= last_blk) ? clamp_block(bt[wbase + lane], num_blocks) : 0;
+  }
+
+  __device__ __forceinline__ void chunk(int j0, int64_t (&off)[U], bool (&valid)[U]) {
+    const int chunk_last = (min(j0 + CT, tok_end) - 1) >> bs_log2;
+    if (chunk_last >= wbase + 64) {  // uniform: slide the table window
+      wbase = j0 >> bs_log2;
+      tbl = (wbase + lane <= last_blk) ? clamp_block(bt[wbase + lane], num_blocks) : 0;
+    }
+    if constexpr (UNIFORM_BLOCK) {
+      const int phys = __builtin_amdgcn_readlane(tbl, (j0 >> bs_log2) - wbase);
+      const int64_t base = (int64_t)phys * block_bytes;
+      const int row0 = (j0 & bs_mask) + tr;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = j0 + u * TPW + tr;
+        valid[u] = j < tok_end;
+        const int row = valid[u] ? row0 + u * TPW : (j0 & bs_mask);
+        off[u] = base + (row * row_bytes + lane_off);
+      }
+    } else {
+      int phys[U], row[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int j = j0 + u * TPW + tr;
+        valid[u] = j < tok_end;
+        const int jj = valid[u] ? j : j0;  // in-bounds stand-in for tail lanes
+        phys[u] = __shfl(tbl, (jj >> bs_log2) - wbase);
+        row[u] = jj & bs_mask;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < U; ++u) off[u] = (int64_t)phys[u] * block_bytes + (row[u] * row_bytes + lane_off);
+    }
+  }
+};
+
+// Every K and V load of a chunk at the offsets ca.chunk gave, issued before
+// any of them is used (a macro so that the branches stay in the loop body).
+#define PA_ISSUE_CHUNK_LOADS(ca, j0, off, kr, vr, U, NT)                                \
+  do {                                                                                   \
+    if ((j0) < (ca).shared_len) { /* V first: see shared_load */                         \
+      _Pragma("unroll") for (int u_ = 0; u_ < (U); ++u_) (vr)[u_] = shared_load((ca).v_cache + (off)[u_]); \
+      _Pragma("unroll") for (int u_ = 0; u_ < (U); ++u_) (kr)[u_] = shared_load((ca).k_cache + (off)[u_]); \
+    } else {                                                                             \
+      _Pragma("unroll") for (int u_ = 0; u_ < (U); ++u_) (kr)[u_] = stream_load<NT>((ca).k_cache + (off)[u_]); \
+      _Pragma("unroll") for (int u_ = 0; u_ < (U); ++u_) (vr)[u_] = stream_load<NT>((ca).v_cache + (off)[u_]); \
+    }                                                                                    \
+  } while (0)
+
 // Stream tokens [tok_begin, tok_end) of sequence seq (KV head kvh) through
 // the online softmax of st. UNIFORM_BLOCK: every chunk lies inside one block
 // (block_size >= CT and tok_begin a multiple of CT), so one table lookup per
@@ -497,16 +621,6 @@ __device__ __forceinline__ void attend_range(const DecodeParams& p, int seq, int
   static_assert(!PAIR || (GT == 1 && LPR * 16 == 128), "pairs: one head per lane group, whole lines");
   const int dc = lane % LPT;
   const int tr = lane / LPR;
-  const int bs_log2 = p.bs_log2;
-  const int bs_mask = (1 << bs_log2) - 1;
-  const int row_bytes = p.row_bytes;
-  const int lane_off = kvh * D * E + dc * 16;
-  const int32_t* bt = p.block_tables + (int64_t)seq * p.max_blocks_per_seq;
-  // Tokens [0, shared_len) lie in blocks that other sequences read too
-  // (prefix sharing shares leading blocks only): they are loaded with the
-  // cache-retaining policy, so that the other readers find them in L2,
-  // while the rest of the context streams past. Only the hint differs.
-  const int shared_len = (NT && p.shared_lens != nullptr) ? p.shared_lens[seq] : 0;
 
   // Spread softmax (GT >= 2): this lane's head, its running maximum and sum.
   // bf16 outputs take the V product on v_dot2 with the probabilities rounded
@@ -521,58 +635,14 @@ __device__ __forceinline__ void attend_range(const DecodeParams& p, int seq, int
     ll = own_head<GT>(st.l, myh);
   }
 
-  // Block-table window: lane i holds the physical id of block wbase + i.
-  const int last_blk = (tok_end - 1) >> bs_log2;
-  int wbase = tok_begin >> bs_log2;
-  int tbl = (wbase + lane <= last_blk) ? clamp_block(bt[wbase + lane], p.num_blocks) : 0;
-
+  ChunkAddresses<U, TPW, NT, UNIFORM_BLOCK> ca(p, seq, lane, tr, kvh * D * E + dc * 16, tok_begin, tok_end);
   for (int j0 = tok_begin; j0 < tok_end; j0 += CT) {
-    const int chunk_last = (min(j0 + CT, tok_end) - 1) >> bs_log2;
-    if (chunk_last >= wbase + 64) {  // uniform: slide the table window
-      wbase = j0 >> bs_log2;
-      tbl = (wbase + lane <= last_blk) ? clamp_block(bt[wbase + lane], p.num_blocks) : 0;
-    }
-    // Addresses first, then every K and V load of the chunk, then compute:
-    // the whole chunk's bytes are in flight before any of them is waited on.
+    // the whole chunk's bytes are in flight before any of them is waited on
     bool valid[U];
     int64_t off[U];
-    if constexpr (UNIFORM_BLOCK) {
-      const int phys = __builtin_amdgcn_readlane(tbl, (j0 >> bs_log2) - wbase);
-      const int64_t base = (int64_t)phys * p.block_bytes;
-      const int row0 = (j0 & bs_mask) + tr;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = j0 + u * TPW + tr;
-        valid[u] = j < tok_end;
-        const int row = valid[u] ? row0 + u * TPW : (j0 & bs_mask);
-        off[u] = base + (row * row_bytes + lane_off);
-      }
-    } else {
-      int phys[U], row[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = j0 + u * TPW + tr;
-        valid[u] = j < tok_end;
-        const int jj = valid[u] ? j : j0;  // in-bounds stand-in for tail lanes
-        phys[u] = __shfl(tbl, (jj >> bs_log2) - wbase);
-        row[u] = jj & bs_mask;
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < U; ++u) off[u] = (int64_t)phys[u] * p.block_bytes + (row[u] * row_bytes + lane_off);
-    }
+    ca.chunk(j0, off, valid);
     uint4 kr[U], vr[U];
-    if (j0 < shared_len) {  // V first: see shared_load
-#pragma unroll
-      for (int u = 0; u < U; ++u) vr[u] = shared_load(p.v_cache + off[u]);
-#pragma unroll
-      for (int u = 0; u < U; ++u) kr[u] = shared_load(p.k_cache + off[u]);
-    } else {
-#pragma unroll
-      for (int u = 0; u < U; ++u) kr[u] = stream_load<NT>(p.k_cache + off[u]);
-#pragma unroll
-      for (int u = 0; u < U; ++u) vr[u] = stream_load<NT>(p.v_cache + off[u]);
-    }
+    PA_ISSUE_CHUNK_LOADS(ca, j0, off, kr, vr, U, NT);
     __builtin_amdgcn_sched_barrier(0);
 
     if constexpr (SPREAD) {
@@ -671,34 +741,173 @@ __device__ __forceinline__ void attend_range(const DecodeParams& p, int seq, int
   }
 
   if constexpr (FUSABLE) {
-    if (new_row) {
-    // one more token, held by token-row group 0 (every lane loads the same
-    // row so that the butterfly over the row's lanes stays uniform)
-    uint4 kr, vr;
-    if constexpr (E == 1) {  // E4M3 pools: this lane's 16 elements, quantised
-      const int64_t src = ((int64_t)kvh * D + dc * 16) * (int64_t)sizeof(T);
-      kr = quantize16<T>(p.new_k + seq * p.new_k_stride + src, p.k_scale[kvh]);
-      vr = quantize16<T>(p.new_v + seq * p.new_v_stride + src, p.v_scale[kvh]);
-    } else {
-      const int64_t off = (int64_t)kvh * D * E + dc * 16;
-      kr = *reinterpret_cast<const uint4*>(p.new_k + seq * p.new_k_stride + off);
-      vr = *reinterpret_cast<const uint4*>(p.new_v + seq * p.new_v_stride + off);
-    }
-    float vf[EPL];
-    widen_slice<KT, EPL>(vr, vf);
+    if (new_row) attend_new_row<T, KT, D, GT>(p, seq, kvh, dc, tr, qv, sm, st);
+  }
+}
+
+// attend_range with the logits on the matrix cores, for bf16 queries over
+// E4M3 pools (head_dim 128, GT = 2 or 4 query heads of one KV head per
+// wave). Loads and the PV product are attend_range's (lane (dc, tr) holds
+// the 16-byte slices dc of token rows tr, tr + 8, ...; the probabilities of
+// tokens u and u + 8 of a 16-token tile are paired on v_dot2), the rest
+// differs:
+//   * the K slices go through a wave-private LDS tile and come back
+//     transposed: lane 16g + c holds the 32 codes of dims 32g .. 32g+31 of
+//     tile token c, widened to bf16: the B operand (K^T, 32 dims x 16
+//     tokens per step) of v_mfma_f32_16x16x32_bf16. Granule j of row r of
+//     load u is stored at j ^ r ^ (u & 1), so that the row writes and the
+//     transposed reads each touch distinct banks (for 32 and for 64 banks);
+//   * the A operand holds the GT query rows, each repeated 16 / GT times, so
+//     S = Q K^T leaves lane 16g + c with the logit of head g * GT / 4 and
+//     token c in all four of its result registers: one logit, one
+//     exponential per lane and tile, instead of GT dot products reduced
+//     over 8 lanes per token;
+//   * the running maximum is kept per head, equal in all lanes of the head,
+//     and raised lazily past the same margin as the spread softmax, so that
+//     the probabilities of all tokens of a head share it;
+//   * each lane packs its probability with that of token c ^ 8 (DPP) and the
+//     PV lanes fetch the pairs of their row tr from lanes 16g + tr
+//     (ds_bpermute).
+// st is reset here; on return each lane holds, per head, the shared
+// maximum, the probability sum of the tokens of its row group (tokens
+// tr and tr + 8 of every tile) and the weighted V sums of its slice, as
+// attend_range leaves them.
+template <typename T, typename KT, int D, int GT, int U, bool UNIFORM_BLOCK>
+__device__ __forceinline__ void attend_range_mfma(const DecodeParams& p, int seq, int kvh, int h0, int lane,
+                                                  int tok_begin, int tok_end, float sm,
+                                                  WaveState<GT, 16 / ElemTraits<KT>::E>& st) {
+  static_assert(sizeof(T) == 2 && sizeof(KT) == 1 && D == 128 && (GT == 2 || GT == 4) && U % 2 == 0,
+                "bf16 queries, E4M3 pools, head_dim 128, 2 or 4 heads, whole tiles");
+  constexpr int EPL = 16;         // codes per 16-byte slice
+  constexpr int LPT = D / EPL;    // 8 lanes per token row
+  constexpr int TPW = 64 / LPT;   // 8 token rows per load
+  constexpr int CT = U * TPW;     // tokens per chunk
+  constexpr int TILES = U / 2;    // 16-token tiles per chunk
+  constexpr int REP = 16 / GT;    // rows of the A operand per head
+  // K tile: per wave, U loads x 8 rows x 8 granules of 16 bytes
+  __shared__ uint4 ktile[4][U * 64];
+  uint4* const kt = ktile[threadIdx.x >> 6];
+
+  const bool new_row = tok_end > tok_begin && stores_new_row(p, seq) &&
+                       tok_end == min(p.context_lens[seq], p.max_context_len);
+  if (new_row) --tok_end;
+  const int dc = lane % LPT, tr = lane / LPT;  // load and PV layout
+  const int g = lane >> 4, c = lane & 15;      // MFMA layout
+
+  // A operand of step k: Q[h0 + c / REP][32g + 8k .. 32g + 8k + 7]
+  bf16x8 qa[4];
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(static_cast<const char*>(p.q) +
+                                                      (((int64_t)seq * p.num_heads + h0 + c / REP) * D + 32 * g) * 2);
 #pragma unroll
-    for (int h = 0; h < GT; ++h) {
-      float sc = group_sum<LPT>(qv[h].dot(kr)) * sm;
-      sc = (tr == 0) ? sc : -INFINITY;
-      const float mn = fmaxf(st.m[h], sc);
-      const float alpha = fast_exp2(st.m[h] - mn);
-      const float pr = fast_exp2(sc - mn);
-      st.m[h] = mn;
-      st.l[h] = st.l[h] * alpha + pr;
+    for (int k = 0; k < 4; ++k) qa[k] = __builtin_bit_cast(bf16x8, src[k]);
+  }
+  // head h's logits are in lanes 16 * (h * 4 / GT) + c; a PV lane takes
+  // tokens tr and tr + 8 from lane 16 * (h * 4 / GT) + tr
+  int src_addr[GT];
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) st.acc[h][e] = fmaf(pr, vf[e], st.acc[h][e] * alpha);
+  for (int h = 0; h < GT; ++h) src_addr[h] = (16 * (h * 4 / GT) + tr) * 4;
+
+  st.reset();
+  float mm = NEG_BIG, ll = 0.0f;
+  ChunkAddresses<U, TPW, true, UNIFORM_BLOCK> ca(p, seq, lane, tr, kvh * D + dc * 16, tok_begin, tok_end);
+  for (int j0 = tok_begin; j0 < tok_end; j0 += CT) {
+    bool valid[U];  // the PV products need no mask: masked logits give zero probabilities
+    int64_t off[U];
+    ca.chunk(j0, off, valid);
+    uint4 kr[U], vr[U];
+    PA_ISSUE_CHUNK_LOADS(ca, j0, off, kr, vr, U, true);
+    __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+    for (int u = 0; u < U; ++u) kt[u * 64 + tr * 8 + (dc ^ tr ^ (u & 1))] = kr[u];
+
+    float s[TILES];
+    float cm = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+      const int u = 2 * t + (c >> 3), r = c & 7, b = c >> 3;
+      const uint4 k0 = kt[u * 64 + r * 8 + ((2 * g) ^ r ^ b)];
+      const uint4 k1 = kt[u * 64 + r * 8 + ((2 * g + 1) ^ r ^ b)];
+      const uint32_t kw[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+      f32x4 acc4 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint4 bw = make_uint4(e4m3x2_to_bf16x2<false>(kw[2 * k]), e4m3x2_to_bf16x2<true>(kw[2 * k]),
+                                    e4m3x2_to_bf16x2<false>(kw[2 * k + 1]), e4m3x2_to_bf16x2<true>(kw[2 * k + 1]));
+        acc4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[k], __builtin_bit_cast(bf16x8, bw), acc4, 0, 0, 0);
+      }
+      const bool ok = j0 + 16 * t + c < tok_end;
+      s[t] = bit_select(0u - (uint32_t)ok, acc4[0] * sm, -INFINITY);
+      cm = fmaxf(cm, s[t]);
     }
+    if (__any(cm > mm + DECODE_RESCALE_SLACK)) {  // raise the heads' maxima (wave-uniform branch)
+      float rmax = cm;
+      rmax = fmaxf(rmax, dpp_f32<DPP_ROW_ROR8>(rmax));
+      rmax = fmaxf(rmax, dpp_f32<DPP_ROW_ROR4>(rmax));
+      rmax = fmaxf(rmax, dpp_f32<DPP_ROW_ROR2>(rmax));
+      rmax = fmaxf(rmax, dpp_f32<DPP_ROW_ROR1>(rmax));
+      const float mn = fmaxf(mm, rmax);
+      const float alpha = fast_exp2(mm - mn);
+      mm = mn;
+      ll *= alpha;
+      for_heads<GT>([&](auto H) {
+        const float a = __builtin_bit_cast(
+            float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, alpha), 16 * (H.value * 4 / GT)));
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) st.acc[H.value][e] *= a;
+      });
     }
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+      const float pr = fast_exp2(s[t] - mm);
+      const uint32_t pk = pack2_bf16(pr, dpp_f32<DPP_ROW_ROR8>(pr));  // (token c, token c ^ 8)
+      ll = dot2_bf16(pk, 0x3F80u, ll);                                 // + this token's rounded probability
+      uint32_t pp[GT];
+#pragma unroll
+      for (int h = 0; h < GT; ++h) pp[h] = (uint32_t)__builtin_amdgcn_ds_bpermute(src_addr[h], (int)pk);
+      pv_token_pair<KT, GT, EPL>(vr[2 * t], vr[2 * t + 1], pp, st.acc);
+    }
+  }
+
+  // every lane gets each head's maximum and its row group's probability sum
+  const float l2 = ll + dpp_f32<DPP_ROW_ROR8>(ll);  // tokens c and c ^ 8
+  for_heads<GT>([&](auto H) {
+    st.m[H.value] = __builtin_bit_cast(
+        float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mm), 16 * (H.value * 4 / GT)));
+    st.l[H.value] = __builtin_bit_cast(
+        float, __builtin_amdgcn_ds_bpermute(src_addr[H.value], __builtin_bit_cast(int, l2)));
+  });
+
+  if (new_row) {
+    QSlice<T, KT> qv[GT];
+    load_q<T, KT, D, GT>(p, seq, h0, dc, qv);
+    attend_new_row<T, KT, D, GT>(p, seq, kvh, dc, tr, qv, sm, st);
+  }
+}
+
+// Does a wave of this kernel take its logits on the matrix cores? LDS_OK:
+// the kernel can spare the 16 * U KiB of LDS of the K tiles (the mixed
+// prefill + decode kernel cannot: its prefill stages hold that LDS).
+template <typename T, typename KT, int D, int GT, int U, bool PAIR, bool LDS_OK>
+constexpr bool decode_mfma_logits() {
+  return LDS_OK && sizeof(T) == 2 && sizeof(KT) == 1 && D == 128 && (GT == 2 || GT == 4) && U % 2 == 0 && !PAIR;
+}
+
+// One wave's pass over tokens [tok_begin, tok_end) of sequence seq into a
+// fresh state st: attend_range_mfma where it applies, else attend_range
+// with the lane's q slices (dc: the lane's slice).
+template <typename T, typename KT, int D, int GT, int U, bool UNIFORM_BLOCK, bool PAIR = false, bool LDS_OK = true>
+__device__ __forceinline__ void attend(const DecodeParams& p, int seq, int kvh, int h0, int lane, int dc,
+                                       int tok_begin, int tok_end, float sm,
+                                       WaveState<GT, 16 / ElemTraits<KT>::E>& st) {
+  if constexpr (decode_mfma_logits<T, KT, D, GT, U, PAIR, LDS_OK>()) {
+    attend_range_mfma<T, KT, D, GT, U, UNIFORM_BLOCK>(p, seq, kvh, h0, lane, tok_begin, tok_end, sm, st);
+  } else {
+    QSlice<T, KT> qv[GT];
+    load_q<T, KT, D, GT>(p, seq, h0, dc, qv);
+    st.reset();
+    attend_range<T, KT, D, GT, U, UNIFORM_BLOCK, PAIR>(p, seq, kvh, lane, tok_begin, tok_end, qv, sm, st);
   }
 }
 
@@ -774,12 +983,9 @@ __global__ __launch_bounds__(256, (decode_min_wgs<T, KT, GT>())) void paged_deco
 
   const int tok_begin = part * P;
   const int tok_end = min(L, tok_begin + P);
-  QSlice<T, KT> qv[GT];
-  load_q<T, KT, D, GT>(p, seq, h0, dc, qv);
   WaveState<GT, EPL> st;
-  st.reset();
-  attend_range<T, KT, D, GT, U, UNIFORM_BLOCK>(p, seq, kvh, lane, tok_begin, tok_end, qv,
-                                               logit_scale<KT>(p, kvh), st);
+  attend<T, KT, D, GT, U, UNIFORM_BLOCK>(p, seq, kvh, h0, lane, dc, tok_begin, tok_end, logit_scale<KT>(p, kvh),
+                                         st);
   apply_v_scale<KT, GT, EPL>(p, kvh, st.acc);
   merge_row_groups<LPT, GT, EPL>(st.m, st.l, st.acc);
 
@@ -975,9 +1181,9 @@ __device__ __forceinline__ void merge_pieces(const DecodeParams& p, int seq, int
 
 // The balanced split's workers, as workgroup wg of num_wgs (each workgroup
 // holds 4 waves, i.e. 4 (unit, worker) pairs). MAXS bounds num_seqs (the
-// chunk prefix sums live in LDS).
+// chunk prefix sums live in LDS). LDS_OK: see decode_mfma_logits.
 template <typename T, typename KT, int D, int GT, int U, bool UNIFORM_BLOCK, int MAXS,
-          bool PAIR = false>
+          bool PAIR = false, bool LDS_OK = true>
 __device__ __forceinline__ void balanced_body(const DecodeParams& p, int wg, int num_wgs) {
   constexpr int EPL = 16 / ElemTraits<KT>::E;
   constexpr int LPT = D / EPL;
@@ -1027,12 +1233,9 @@ __device__ __forceinline__ void balanced_body(const DecodeParams& p, int wg, int
     const int cb = pfx[i], ce = pfx[i + 1];
     const int ps = max(c0, cb), pe = min(c1, ce);
     const int L = min(p.context_lens[i], p.max_context_len);
-    QSlice<T, KT> qv[GT];
-    load_q<T, KT, D, GT>(p, i, h0, dc, qv);
     WaveState<GT, EPL> st;
-    st.reset();
-    attend_range<T, KT, D, GT, U, UNIFORM_BLOCK, PAIR>(p, i, kvh, lane, (ps - cb) * CT,
-                                                       min((pe - cb) * CT, L), qv, sm, st);
+    attend<T, KT, D, GT, U, UNIFORM_BLOCK, PAIR, LDS_OK>(p, i, kvh, h0, lane, dc, (ps - cb) * CT,
+                                                         min((pe - cb) * CT, L), sm, st);
     apply_v_scale<KT, GT, EPL>(p, kvh, st.acc);
     merge_row_groups<LPR, GT, EPL>(st.m, st.l, st.acc);
     if (tr == 0) {

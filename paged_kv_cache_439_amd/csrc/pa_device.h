@@ -29,6 +29,11 @@ constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1,0,3,2]
 constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
 constexpr int DPP_HALF_MIRROR = 0x141; // lane i <-> 7-i within 8
 constexpr int DPP_MIRROR = 0x140;      // lane i <-> 15-i within 16
+// Rotations within a row of 16 lanes (row_ror:n); ror 8 pairs lane i with i ^ 8.
+constexpr int DPP_ROW_ROR1 = 0x121;
+constexpr int DPP_ROW_ROR2 = 0x122;
+constexpr int DPP_ROW_ROR4 = 0x124;
+constexpr int DPP_ROW_ROR8 = 0x128;
 
 // Sum over aligned groups of N consecutive lanes (N in {1,2,4,8,16,32});
 // every lane of a group receives the group's total.
