@@ -14,7 +14,9 @@
 // Work decomposition (one wave64 = one unit of work):
 //   unit = (sequence, KV head, group of GT query heads, partition of P tokens)
 //   grid = (ceil(units per (seq, partition) / 4), sequences, max partitions),
-//   256 threads = 4 independent waves, no LDS and no barriers.
+//   256 threads = 4 independent waves, no barriers (LDS only for the
+//   balanced split's chunk prefix sums and attend_range_mfma's per-wave K
+//   tiles).
 // Lane mapping: a K or V row of one head is D*e bytes = LPT lanes x 16 bytes,
 // so a wave-wide 16-byte load covers TPW = 64/LPT token rows; U loads per lane
 // give a chunk of CT = U*TPW tokens whose K and V loads are all issued before
@@ -33,6 +35,10 @@
 //   PV:  acc[h][slice] += p * V-slice, all in registers; with GT >= 2 and
 //        bf16 outputs, two tokens at a time on v_dot2_f32_bf16 (the
 //        probabilities rounded to bf16, the values widened exactly).
+//   bf16 queries at head_dim 128 with GT = 2 or 4 take the logits on the
+//        matrix cores instead (attend_range_mfma): K is transposed through
+//        a wave-private LDS tile into the B operand of
+//        v_mfma_f32_16x16x32_bf16, one logit per lane and 16-token tile.
 // Split: each partition writes (m, l, acc) in fp32 to the workspace and a
 //   second, small kernel (paged_decode_merge_kernel) combines them with the
 //   exact max-rescaling merge. The kernel boundary makes the states visible
@@ -746,45 +752,53 @@ __device__ __forceinline__ void attend_range(const DecodeParams& p, int seq, int
 }
 
 // attend_range with the logits on the matrix cores, for bf16 queries over
-// E4M3 pools (head_dim 128, GT = 2 or 4 query heads of one KV head per
-// wave). Loads and the PV product are attend_range's (lane (dc, tr) holds
-// the 16-byte slices dc of token rows tr, tr + 8, ...; the probabilities of
-// tokens u and u + 8 of a 16-token tile are paired on v_dot2), the rest
-// differs:
+// bf16 or E4M3 pools (head_dim 128, GT = 2 or 4 query heads of one KV head
+// per wave). Loads and the PV product are attend_range's: lane (dc, tr)
+// holds the 16-byte slices dc of token rows tr, tr + TPW, ... (TPW = 4 rows
+// of bf16 or 8 of E4M3 per load), and PV pairs the rows of loads u and
+// u + 1 on v_dot2. The rest differs:
+//   * tokens go in 16-token tiles (16 / TPW loads). Load v of a tile, row
+//     tr, is tile column c = tr + 8 (v & 1) + 4 (v >> 1), so that the two
+//     rows every PV pair combines sit in columns c and c ^ 8;
 //   * the K slices go through a wave-private LDS tile and come back
-//     transposed: lane 16g + c holds the 32 codes of dims 32g .. 32g+31 of
-//     tile token c, widened to bf16: the B operand (K^T, 32 dims x 16
-//     tokens per step) of v_mfma_f32_16x16x32_bf16. Granule j of row r of
-//     load u is stored at j ^ r ^ (u & 1), so that the row writes and the
-//     transposed reads each touch distinct banks (for 32 and for 64 banks);
+//     transposed: lane 16g + c holds dims 32g .. 32g+31 of column c's
+//     token, in bf16 (E4M3 codes widened exactly): the B operand (K^T, 32
+//     dims x 16 tokens per step) of v_mfma_f32_16x16x32_bf16. Granule j of
+//     a row is stored at j ^ swz(c) (swz: 3 bits for the 8-granule E4M3
+//     rows, 4 for the 16-granule bf16 rows), so that the row writes and the
+//     transposed reads touch distinct banks (for 32 and for 64 banks);
 //   * the A operand holds the GT query rows, each repeated 16 / GT times, so
 //     S = Q K^T leaves lane 16g + c with the logit of head g * GT / 4 and
-//     token c in all four of its result registers: one logit, one
+//     column c in all four of its result registers: one logit, one
 //     exponential per lane and tile, instead of GT dot products reduced
-//     over 8 lanes per token;
+//     over the lanes of a token row;
 //   * the running maximum is kept per head, equal in all lanes of the head,
 //     and raised lazily past the same margin as the spread softmax, so that
 //     the probabilities of all tokens of a head share it;
-//   * each lane packs its probability with that of token c ^ 8 (DPP) and the
-//     PV lanes fetch the pairs of their row tr from lanes 16g + tr
-//     (ds_bpermute).
+//   * each lane packs its probability with that of column c ^ 8 (DPP) and
+//     the PV lanes fetch the pairs of their row tr from lanes 16g + tr + 4q
+//     (pair q of the tile; ds_bpermute).
 // st is reset here; on return each lane holds, per head, the shared
-// maximum, the probability sum of the tokens of its row group (tokens
-// tr and tr + 8 of every tile) and the weighted V sums of its slice, as
-// attend_range leaves them.
+// maximum, the probability sum of its row group's tokens and the weighted V
+// sums of its slice, as attend_range leaves them.
 template <typename T, typename KT, int D, int GT, int U, bool UNIFORM_BLOCK>
 __device__ __forceinline__ void attend_range_mfma(const DecodeParams& p, int seq, int kvh, int h0, int lane,
                                                   int tok_begin, int tok_end, float sm,
                                                   WaveState<GT, 16 / ElemTraits<KT>::E>& st) {
-  static_assert(sizeof(T) == 2 && sizeof(KT) == 1 && D == 128 && (GT == 2 || GT == 4) && U % 2 == 0,
-                "bf16 queries, E4M3 pools, head_dim 128, 2 or 4 heads, whole tiles");
-  constexpr int EPL = 16;         // codes per 16-byte slice
-  constexpr int LPT = D / EPL;    // 8 lanes per token row
-  constexpr int TPW = 64 / LPT;   // 8 token rows per load
-  constexpr int CT = U * TPW;     // tokens per chunk
-  constexpr int TILES = U / 2;    // 16-token tiles per chunk
-  constexpr int REP = 16 / GT;    // rows of the A operand per head
-  // K tile: per wave, U loads x 8 rows x 8 granules of 16 bytes
+  constexpr int E = ElemTraits<KT>::E;
+  constexpr int EPL = 16 / E;       // elements per 16-byte slice
+  constexpr int LPT = D / EPL;      // lanes per token row = granules per row
+  constexpr int TPW = 64 / LPT;     // token rows per load
+  constexpr int CT = U * TPW;       // tokens per chunk
+  constexpr int LPU = 16 / TPW;     // loads per 16-token tile
+  constexpr int TILES = U / LPU;
+  constexpr int GL = 32 * E / 16;   // granules of a lane's 32 dims
+  constexpr int REP = 16 / GT;      // rows of the A operand per head
+  static_assert(sizeof(T) == 2 && (E == 1 || E == 2) && D == 128 && (GT == 2 || GT == 4) && U % LPU == 0,
+                "bf16 queries, bf16 or E4M3 pools, head_dim 128, 2 or 4 heads, whole tiles");
+  auto column = [](int v, int r) { return r + 8 * (v & 1) + 4 * (v >> 1); };
+  auto swz = [](int c) { return TPW == 8 ? ((c & 7) ^ (c >> 3)) : c; };
+  // K tile: per wave, U loads x 64 lanes x 16 bytes
   __shared__ uint4 ktile[4][U * 64];
   uint4* const kt = ktile[threadIdx.x >> 6];
 
@@ -793,6 +807,11 @@ __device__ __forceinline__ void attend_range_mfma(const DecodeParams& p, int seq
   if (new_row) --tok_end;
   const int dc = lane % LPT, tr = lane / LPT;  // load and PV layout
   const int g = lane >> 4, c = lane & 15;      // MFMA layout
+  // this lane's column as a (load of the tile, row) pair, and its token
+  const int cr = c & (TPW - 1);
+  const int cv = TPW == 8 ? (c >> 3) : (((c >> 3) & 1) | (((c >> 2) & 1) << 1));
+  const int ctok = cv * TPW + cr;
+  const int cswz = swz(c);
 
   // A operand of step k: Q[h0 + c / REP][32g + 8k .. 32g + 8k + 7]
   bf16x8 qa[4];
@@ -802,15 +821,15 @@ __device__ __forceinline__ void attend_range_mfma(const DecodeParams& p, int seq
 #pragma unroll
     for (int k = 0; k < 4; ++k) qa[k] = __builtin_bit_cast(bf16x8, src[k]);
   }
-  // head h's logits are in lanes 16 * (h * 4 / GT) + c; a PV lane takes
-  // tokens tr and tr + 8 from lane 16 * (h * 4 / GT) + tr
+  // head h's logits are in lanes 16 * (h * 4 / GT) + c; a PV lane takes the
+  // pair of columns tr + 4q and tr + 4q + 8 from lane 16 * (h * 4 / GT) + tr + 4q
   int src_addr[GT];
 #pragma unroll
   for (int h = 0; h < GT; ++h) src_addr[h] = (16 * (h * 4 / GT) + tr) * 4;
 
   st.reset();
   float mm = NEG_BIG, ll = 0.0f;
-  ChunkAddresses<U, TPW, true, UNIFORM_BLOCK> ca(p, seq, lane, tr, kvh * D + dc * 16, tok_begin, tok_end);
+  ChunkAddresses<U, TPW, true, UNIFORM_BLOCK> ca(p, seq, lane, tr, kvh * D * E + dc * 16, tok_begin, tok_end);
   for (int j0 = tok_begin; j0 < tok_end; j0 += CT) {
     bool valid[U];  // the PV products need no mask: masked logits give zero probabilities
     int64_t off[U];
@@ -820,24 +839,32 @@ __device__ __forceinline__ void attend_range_mfma(const DecodeParams& p, int seq
     __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll
-    for (int u = 0; u < U; ++u) kt[u * 64 + tr * 8 + (dc ^ tr ^ (u & 1))] = kr[u];
+    for (int u = 0; u < U; ++u) kt[u * 64 + tr * LPT + (dc ^ swz(column(u % LPU, tr)))] = kr[u];
 
     float s[TILES];
     float cm = -INFINITY;
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
-      const int u = 2 * t + (c >> 3), r = c & 7, b = c >> 3;
-      const uint4 k0 = kt[u * 64 + r * 8 + ((2 * g) ^ r ^ b)];
-      const uint4 k1 = kt[u * 64 + r * 8 + ((2 * g + 1) ^ r ^ b)];
-      const uint32_t kw[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+      const uint4* row = kt + (LPU * t + cv) * 64 + cr * LPT;
+      uint32_t kw[4 * GL];
+#pragma unroll
+      for (int j = 0; j < GL; ++j) {
+        const uint4 w = row[(GL * g + j) ^ cswz];
+        kw[4 * j] = w.x; kw[4 * j + 1] = w.y; kw[4 * j + 2] = w.z; kw[4 * j + 3] = w.w;
+      }
       f32x4 acc4 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        const uint4 bw = make_uint4(e4m3x2_to_bf16x2<false>(kw[2 * k]), e4m3x2_to_bf16x2<true>(kw[2 * k]),
-                                    e4m3x2_to_bf16x2<false>(kw[2 * k + 1]), e4m3x2_to_bf16x2<true>(kw[2 * k + 1]));
+        uint4 bw;
+        if constexpr (E == 1) {  // 8 codes -> 8 bf16
+          bw = make_uint4(e4m3x2_to_bf16x2<false>(kw[2 * k]), e4m3x2_to_bf16x2<true>(kw[2 * k]),
+                          e4m3x2_to_bf16x2<false>(kw[2 * k + 1]), e4m3x2_to_bf16x2<true>(kw[2 * k + 1]));
+        } else {
+          bw = make_uint4(kw[4 * k], kw[4 * k + 1], kw[4 * k + 2], kw[4 * k + 3]);
+        }
         acc4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[k], __builtin_bit_cast(bf16x8, bw), acc4, 0, 0, 0);
       }
-      const bool ok = j0 + 16 * t + c < tok_end;
+      const bool ok = j0 + 16 * t + ctok < tok_end;
       s[t] = bit_select(0u - (uint32_t)ok, acc4[0] * sm, -INFINITY);
       cm = fmaxf(cm, s[t]);
     }
@@ -861,22 +888,27 @@ __device__ __forceinline__ void attend_range_mfma(const DecodeParams& p, int seq
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
       const float pr = fast_exp2(s[t] - mm);
-      const uint32_t pk = pack2_bf16(pr, dpp_f32<DPP_ROW_ROR8>(pr));  // (token c, token c ^ 8)
-      ll = dot2_bf16(pk, 0x3F80u, ll);                                 // + this token's rounded probability
-      uint32_t pp[GT];
+      const uint32_t pk = pack2_bf16(pr, dpp_f32<DPP_ROW_ROR8>(pr));  // (column c, column c ^ 8)
+      ll = dot2_bf16(pk, 0x3F80u, ll);                                 // + this column's rounded probability
 #pragma unroll
-      for (int h = 0; h < GT; ++h) pp[h] = (uint32_t)__builtin_amdgcn_ds_bpermute(src_addr[h], (int)pk);
-      pv_token_pair<KT, GT, EPL>(vr[2 * t], vr[2 * t + 1], pp, st.acc);
+      for (int q = 0; q < LPU / 2; ++q) {
+        uint32_t pp[GT];
+#pragma unroll
+        for (int h = 0; h < GT; ++h) pp[h] = (uint32_t)__builtin_amdgcn_ds_bpermute(src_addr[h] + 16 * q, (int)pk);
+        pv_token_pair<KT, GT, EPL>(vr[LPU * t + 2 * q], vr[LPU * t + 2 * q + 1], pp, st.acc);
+      }
     }
   }
 
   // every lane gets each head's maximum and its row group's probability sum
-  const float l2 = ll + dpp_f32<DPP_ROW_ROR8>(ll);  // tokens c and c ^ 8
+  // (columns tr + 4q and tr + 4q + 8 for every pair q)
+  float lsum = ll + dpp_f32<DPP_ROW_ROR8>(ll);
+  if constexpr (LPU == 4) lsum += dpp_f32<DPP_ROW_ROR4>(lsum);  // either direction: lsum(c ^ 8) = lsum(c)
   for_heads<GT>([&](auto H) {
     st.m[H.value] = __builtin_bit_cast(
         float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, mm), 16 * (H.value * 4 / GT)));
     st.l[H.value] = __builtin_bit_cast(
-        float, __builtin_amdgcn_ds_bpermute(src_addr[H.value], __builtin_bit_cast(int, l2)));
+        float, __builtin_amdgcn_ds_bpermute(src_addr[H.value], __builtin_bit_cast(int, lsum)));
   });
 
   if (new_row) {
@@ -886,22 +918,26 @@ __device__ __forceinline__ void attend_range_mfma(const DecodeParams& p, int seq
   }
 }
 
-// Does a wave of this kernel take its logits on the matrix cores? LDS_OK:
-// the kernel can spare the 16 * U KiB of LDS of the K tiles (the mixed
-// prefill + decode kernel cannot: its prefill stages hold that LDS).
-template <typename T, typename KT, int D, int GT, int U, bool PAIR, bool LDS_OK>
+// Does a wave of this kernel take its logits on the matrix cores? MFMA_OK:
+// the kernel can spare what attend_range_mfma needs beyond attend_range:
+// 16 * U KiB of LDS for the K tiles per workgroup (the mixed prefill +
+// decode kernel cannot: its prefill stages hold that LDS) and about 20 more
+// registers (the fixed split over bf16 pools, built for 3 workgroups per
+// CU, would spill).
+template <typename T, typename KT, int D, int GT, int U, bool PAIR, bool MFMA_OK>
 constexpr bool decode_mfma_logits() {
-  return LDS_OK && sizeof(T) == 2 && sizeof(KT) == 1 && D == 128 && (GT == 2 || GT == 4) && U % 2 == 0 && !PAIR;
+  return MFMA_OK && sizeof(T) == 2 && (sizeof(KT) == 1 || sizeof(KT) == 2) && D == 128 && (GT == 2 || GT == 4) &&
+         U % (16 / (64 / (D * (int)sizeof(KT) / 16))) == 0 && !PAIR;
 }
 
 // One wave's pass over tokens [tok_begin, tok_end) of sequence seq into a
 // fresh state st: attend_range_mfma where it applies, else attend_range
 // with the lane's q slices (dc: the lane's slice).
-template <typename T, typename KT, int D, int GT, int U, bool UNIFORM_BLOCK, bool PAIR = false, bool LDS_OK = true>
+template <typename T, typename KT, int D, int GT, int U, bool UNIFORM_BLOCK, bool PAIR = false, bool MFMA_OK = true>
 __device__ __forceinline__ void attend(const DecodeParams& p, int seq, int kvh, int h0, int lane, int dc,
                                        int tok_begin, int tok_end, float sm,
                                        WaveState<GT, 16 / ElemTraits<KT>::E>& st) {
-  if constexpr (decode_mfma_logits<T, KT, D, GT, U, PAIR, LDS_OK>()) {
+  if constexpr (decode_mfma_logits<T, KT, D, GT, U, PAIR, MFMA_OK>()) {
     attend_range_mfma<T, KT, D, GT, U, UNIFORM_BLOCK>(p, seq, kvh, h0, lane, tok_begin, tok_end, sm, st);
   } else {
     QSlice<T, KT> qv[GT];
@@ -984,8 +1020,8 @@ __global__ __launch_bounds__(256, (decode_min_wgs<T, KT, GT>())) void paged_deco
   const int tok_begin = part * P;
   const int tok_end = min(L, tok_begin + P);
   WaveState<GT, EPL> st;
-  attend<T, KT, D, GT, U, UNIFORM_BLOCK>(p, seq, kvh, h0, lane, dc, tok_begin, tok_end, logit_scale<KT>(p, kvh),
-                                         st);
+  attend<T, KT, D, GT, U, UNIFORM_BLOCK, false, (sizeof(KT) == 1)>(p, seq, kvh, h0, lane, dc, tok_begin, tok_end,
+                                                                   logit_scale<KT>(p, kvh), st);
   apply_v_scale<KT, GT, EPL>(p, kvh, st.acc);
   merge_row_groups<LPT, GT, EPL>(st.m, st.l, st.acc);
 
@@ -1181,9 +1217,9 @@ __device__ __forceinline__ void merge_pieces(const DecodeParams& p, int seq, int
 
 // The balanced split's workers, as workgroup wg of num_wgs (each workgroup
 // holds 4 waves, i.e. 4 (unit, worker) pairs). MAXS bounds num_seqs (the
-// chunk prefix sums live in LDS). LDS_OK: see decode_mfma_logits.
+// chunk prefix sums live in LDS). MFMA_OK: see decode_mfma_logits.
 template <typename T, typename KT, int D, int GT, int U, bool UNIFORM_BLOCK, int MAXS,
-          bool PAIR = false, bool LDS_OK = true>
+          bool PAIR = false, bool MFMA_OK = true>
 __device__ __forceinline__ void balanced_body(const DecodeParams& p, int wg, int num_wgs) {
   constexpr int EPL = 16 / ElemTraits<KT>::E;
   constexpr int LPT = D / EPL;
@@ -1234,7 +1270,7 @@ __device__ __forceinline__ void balanced_body(const DecodeParams& p, int wg, int
     const int ps = max(c0, cb), pe = min(c1, ce);
     const int L = min(p.context_lens[i], p.max_context_len);
     WaveState<GT, EPL> st;
-    attend<T, KT, D, GT, U, UNIFORM_BLOCK, PAIR, LDS_OK>(p, i, kvh, h0, lane, dc, (ps - cb) * CT,
+    attend<T, KT, D, GT, U, UNIFORM_BLOCK, PAIR, MFMA_OK>(p, i, kvh, h0, lane, dc, (ps - cb) * CT,
                                                          min((pe - cb) * CT, L), sm, st);
     apply_v_scale<KT, GT, EPL>(p, kvh, st.acc);
     merge_row_groups<LPR, GT, EPL>(st.m, st.l, st.acc);

@@ -91,7 +91,7 @@ __global__ __launch_bounds__(256, 2) void mixed_batch_kernel(MixedParams p) {
     prefill_body<D, G, KT>(p.f, idx - r * p.fx, r % p.fy, r / p.fy);
   } else {
     balanced_body<uint16_t, KT, D, G, mixed_decode_u<KT>(), UNIFORM_BLOCK, MIXED_MAX_DECODE_SEQS,
-                  /*PAIR=*/false, /*LDS_OK=*/false>(
+                  /*PAIR=*/false, /*MFMA_OK=*/false>(
         p.d, idx, p.nd);
   }
 }
