@@ -320,7 +320,7 @@ FP8_STORE_DECODE_CASES = [
     ("bs8_len1", 2, dict(num_seqs=6, lens=("fixed", [1, 2, 8, 9, 17, 64]), block_size=8,
                          max_context=64), [0, 16, -1]),
     # 4096 rows of 8 x 128 codes: two 16-byte granules per thread of the
-    # balanced grid (one staged at start-up, one in the loop after it)
+    # balanced grid, i.e. two passes of the grid-stride store loop per thread
     ("rows_over_grid", 5, dict(num_seqs=4096, lens=("uniform", 1, 48), max_context=64), [0, -1]),
 ]
 

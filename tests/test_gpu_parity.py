@@ -331,8 +331,8 @@ STORE_DECODE_CASES = [
     ("bs8_len1", 2, dict(num_seqs=6, lens=("fixed", [1, 2, 8, 9, 17, 64]), block_size=8,
                          max_context=64), [0, 16, -1]),
     # 2048 rows of 8 x 128 bf16: twice as many 16-byte granules as the balanced
-    # grid has threads, so each thread stores one granule after the start-up
-    # and one more in the loop after it
+    # grid has threads, so every thread makes two passes of the grid-stride
+    # store loop
     ("rows_over_grid", 5, dict(num_seqs=2048, lens=("uniform", 1, 48), max_context=64), [0, -1]),
 ]
 
@@ -505,7 +505,7 @@ def test_prefill_peaked_growing_logits(gpu, factor, runner):
 
 def test_prefill_full_config_sampled(gpu):
     b = wl.make_batch(wl.spec(wl.CHUNKED_PREFILL), device=gpu, poison=True)
-    gs.say(f"prefill full cfg4 lens={b.context_lens.tolist()}")
+    gs.say(f"prefill, full chunked-prefill workload, lens={b.context_lens.tolist()}")
     gs.prefill_parity(b, sample_rows=96, seed=4)
 
 
