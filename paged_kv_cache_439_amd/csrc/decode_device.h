@@ -927,8 +927,10 @@ __device__ __forceinline__ void attend_range_mfma(const DecodeParams& p, int seq
 // CU, would spill).
 template <typename T, typename KT, int D, int GT, int U, bool PAIR, bool MFMA_OK>
 constexpr bool decode_mfma_logits() {
-  return MFMA_OK && sizeof(T) == 2 && (sizeof(KT) == 1 || sizeof(KT) == 2) && D == 128 && (GT == 2 || GT == 4) &&
-         U % (16 / (64 / (D * (int)sizeof(KT) / 16))) == 0 && !PAIR;
+  constexpr int rows_per_load = 64 / (D * (int)sizeof(KT) / 16);  // token rows per wave-wide load
+  constexpr int loads_per_tile = 16 / rows_per_load;              // loads per 16-token tile
+  return MFMA_OK && !PAIR && sizeof(T) == 2 && (sizeof(KT) == 1 || sizeof(KT) == 2) && D == 128 &&
+         (GT == 2 || GT == 4) && U % loads_per_tile == 0;
 }
 
 // One wave's pass over tokens [tok_begin, tok_end) of sequence seq into a
@@ -1119,6 +1121,8 @@ __global__ __launch_bounds__(256, (decode_min_wgs<T, KT, GT>())) void paged_deco
 
   const int tok_begin = part * P;
   const int tok_end = min(L, tok_begin + P);
+  // MFMA logits over E4M3 pools only: over bf16 pools this kernel would
+  // spill at 3 workgroups per CU (see decode_mfma_logits)
   WaveState<GT, EPL> st;
   attend<T, KT, D, GT, U, UNIFORM_BLOCK, false, (sizeof(KT) == 1)>(p, seq, kvh, h0, lane, dc, tok_begin, tok_end,
                                                                    logit_scale<KT>(p, kvh), st);
