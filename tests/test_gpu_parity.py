@@ -291,6 +291,36 @@ def test_fixed_slices_dispatch_order(gpu, name, over, P, empty):
             assert wl.to_numpy(b.v_cache).tobytes() == vp.tobytes()
 
 
+# The same bounds and length buckets through pa_decode alone, every context
+# non-empty: whole multiples of the slice, one-token and nearly whole partial
+# slices, the 64-slice and 4096-sequence bounds and one past each.
+FIXED_ORDER_PLAIN_CASES = [
+    ("edges", dict(num_seqs=21, lens=("fixed", [128, 1, 63, 65, 127, 200, 4, 8, 12, 20, 24, 28, 33, 40, 44, 48,
+                                                52, 56, 60, 320, 5]),
+                   max_context=320), 64),
+    ("64_slices", dict(num_seqs=5, lens=("fixed", [1024, 1023, 17, 512, 1000]), block_size=16, max_context=1024), 16),
+    ("65_slices", dict(num_seqs=5, lens=("fixed", [1040, 1039, 17, 512, 1000]), block_size=16, max_context=1040), 16),
+    ("4096_seqs", dict(num_seqs=4096, lens=("uniform", 1, 48), block_size=16, max_context=48), 16),
+    ("4097_seqs", dict(num_seqs=4097, lens=("uniform", 1, 48), block_size=16, max_context=48), 16),
+]
+
+
+@pytest.mark.parametrize("name,over,P", FIXED_ORDER_PLAIN_CASES, ids=[c[0] for c in FIXED_ORDER_PLAIN_CASES])
+def test_fixed_slices_order_plain_decode(gpu, name, over, P):
+    """Every output of pa_decode with fixed slices against the oracle, at the
+    bounds of the longest-first dispatch order and one past each (grid
+    order)."""
+    b = wl.make_batch(wl.spec(wl.B512_LOGNORMAL_DECODE, **over), device=gpu, poison=True)
+    gs.say(f"fixed slices, plain decode, {name}: P={P}, {b.num_seqs} sequences")
+    hb, kp, vp = gs.oracle_inputs(b)
+    ref = gs.oracle_decode_all(hb, kp, vp, b.scale, b.block_size, b.dtype)
+    arrs = gs.device_arrays(b)
+    gs.gpu_store(b, arrs)
+    out = gs.gpu_decode(b, P, arrs)
+    torch.cuda.synchronize()
+    gs.check_close(gs.as_f64(out), ref, b.dtype, f"fixed slices plain {name}")
+
+
 def test_decode_balanced_few_long(gpu):
     """Two long contexts cut across hundreds of ranges each."""
     sp = wl.spec(wl.B512_LOGNORMAL_DECODE, num_seqs=2, lens=("fixed", [4096, 3001]), max_context=4096)
