@@ -87,7 +87,7 @@ def test_store_fp8_bit_exact_with_specials(gpu, dtype):
 ])
 def test_store_fp8_full_pool(gpu, cfg, over):
     b = wl.make_batch(wl.spec(cfg, kv="e4m3", **over), device=gpu, poison=True)
-    gs.say(f"store e4m3 cfg{cfg} rows={len(b.slot_mapping)}")
+    gs.say(f"store e4m3 {b.spec['name']} rows={len(b.slot_mapping)}")
     kp0, vp0 = wl.to_numpy(b.k_cache), wl.to_numpy(b.v_cache)
     ks, vs = gs.scales_np(b)
     ek, ev = of8.store_kvcache_fp8(kp0, vp0, wl.to_numpy(b.key), wl.to_numpy(b.value), b.slot_mapping,
@@ -171,7 +171,7 @@ def test_decode_fp8_peaked_logits(gpu, cfg, over):
     for P in (0, -1):
         b = wl.make_batch(wl.spec(cfg, kv="e4m3", scale=1.0, **over), device=gpu, poison=True)
         b.k_scale *= 4.0
-        gs.say(f"decode e4m3 peaked cfg{cfg} P={P}")
+        gs.say(f"decode e4m3 peaked {b.spec['name']} P={P}")
         gs.decode_fp8_parity(b, P)
 
 
@@ -243,7 +243,7 @@ def test_decode_fp8_full_config_sampled(gpu, cfg, nseq):
         sharers = [i for i in range(b.num_seqs) if b.block_tables[i, 0] == b.shared_blocks[0]]
         seqs = sorted(set(seqs) | set(sharers[:2]))
     P = gs.full_config_parts(cfg, "balanced")
-    gs.say(f"decode e4m3 full cfg{cfg} seqs={seqs} P={P}")
+    gs.say(f"decode e4m3 full {b.spec['name']} seqs={seqs} P={P}")
     gs.decode_fp8_parity(b, P, seqs=seqs, hint=True)   # the benchmark passes shared_lens
 
 

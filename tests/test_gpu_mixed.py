@@ -121,7 +121,7 @@ def test_mixed_full_config_sampled(gpu):
             rows.append((r0 + t, h))
             full_rows.append((hb.new_rows[r][t], h))
         r0 += n
-    gs.say(f"mixed full cfg6: {len(rows)} sampled rows over {len(seqs)} sequences")
+    gs.say(f"mixed batch, full workload: {len(rows)} sampled rows over {len(seqs)} sequences")
     ref = oa.prefill_rows(hb.q, kp, vp, hb.block_tables, hb.query_start_loc, hb.context_lens, b.scale,
                           b.block_size, b.dtype, rows)
     sel = np.stack([got[t, h] for t, h in full_rows])

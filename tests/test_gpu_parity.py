@@ -31,7 +31,7 @@ pytestmark = pytest.mark.gpu
 ])
 def test_store_bit_exact_whole_pool(gpu, cfg, over):
     b = wl.make_batch(wl.spec(cfg, **over), device=gpu, poison=True)
-    gs.say(f"store cfg{cfg} rows={len(b.slot_mapping)}")
+    gs.say(f"store {b.spec['name']} rows={len(b.slot_mapping)}")
     kp0, vp0 = wl.to_numpy(b.k_cache), wl.to_numpy(b.v_cache)
     key, value = wl.to_numpy(b.key), wl.to_numpy(b.value)
     ek, ev = oa.store_kvcache(kp0, vp0, key, value, b.slot_mapping, b.block_size)
@@ -80,7 +80,7 @@ def test_store_strided_key(gpu):
 @pytest.mark.parametrize("P", [0, 16, 32, 48, 64, -1])
 def test_decode_tiny_fp32(gpu, P):
     b = wl.make_batch(wl.spec(wl.TINY_FP32_DECODE), device=gpu, poison=True)
-    gs.say(f"decode cfg1 P={P}")
+    gs.say(f"decode tiny fp32 P={P}")
     gs.decode_parity(b, P)
 
 
@@ -476,7 +476,7 @@ def test_decode_full_config_sampled(gpu, cfg, nseq, split):
         sharers = [i for i in range(b.num_seqs) if b.block_tables[i, 0] == b.shared_blocks[0]]
         seqs = sorted(set(seqs) | set(sharers[:2]))
     P = gs.full_config_parts(cfg, split)
-    gs.say(f"decode full cfg{cfg} seqs={seqs} P={P}")
+    gs.say(f"decode full {b.spec['name']} seqs={seqs} P={P}")
     gs.decode_parity(b, P, seqs=seqs, hint=True)   # the benchmark passes shared_lens
 
 
