@@ -75,9 +75,8 @@ struct PrefillParams {
 };
 
 // Work items (sequence, row block) are ranked by their number of key tiles
-// when there are at most this many of them; larger launches keep the grid
-// order (row blocks from the end of the chunk first).
-constexpr int RANK_MAX_ITEMS = 512;
+// with a counting sort over this many bins (two per thread).
+constexpr int RANK_BINS = 512;
 
 // Maximum over lanes l, l^16, l^32, l^48 (the four lanes that hold one row
 // of an MFMA C tile): the cross-half and cross-row swaps of gfx950, with
@@ -178,27 +177,65 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int bx, int
   const int n_items = p.num_seqs * R;
   const int k_rank = bz * p.num_seqs + by;
   int seq, rb;
-  if (n_items <= RANK_MAX_ITEMS) {
-    int* cost = reinterpret_cast<int*>(&kv0[0][0]);  // LDS, free until the main loop
-    for (int x = tid; x < n_items; x += 256) cost[x] = item_tiles(x / R, x % R);
-    __syncthreads();
-    for (int x = tid; x < n_items; x += 256) {
-      const int cx = cost[x];
-      int r = 0;
-      for (int y = 0; y < n_items; ++y) {
-        const int cy = cost[y];
-        r += (cy > cx) || (cy == cx && y < x);
+  {
+    // Counting sort of the items by key tiles (descending; equal counts in
+    // item order): a histogram of the counts, the bin holding rank k_rank
+    // from a scan over the bins, then the item of that bin from a scan over
+    // the items. Counts of RANK_BINS - 1 tiles or more share the last bin.
+    int* hist = reinterpret_cast<int*>(&kv0[0][0]);  // LDS, free until the main loop
+    int* wtot = hist + RANK_BINS;                    // per-wave totals
+    int* pick = wtot + 4;                            // bin, index in the bin, item
+    const int per = (n_items + 255) / 256;
+    const int x0 = min(n_items, tid * per), x1 = min(n_items, x0 + per);
+    auto bin_of = [&](int x) { return min(item_tiles(x / R, x % R), RANK_BINS - 1); };
+    auto block_exclusive = [&](int v) {  // exclusive prefix of v over the workgroup's threads
+      int incl = v;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d);
+        if (lane >= d) incl += y;
       }
-      if (r == k_rank) tbl[0] = x;
+      if (lane == 63) wtot[wave] = incl;
+      __syncthreads();
+      int before = incl - v;
+      for (int w = 0; w < wave; ++w) before += wtot[w];
+      return before;
+    };
+    for (int i = tid; i < RANK_BINS; i += 256) hist[i] = 0;
+    __syncthreads();
+    for (int x = x0; x < x1; ++x) atomicAdd(&hist[bin_of(x)], 1);
+    __syncthreads();
+    {
+      const int b0 = RANK_BINS - 1 - 2 * tid, b1 = b0 - 1;  // thread t: bins from the top
+      const int h0 = hist[b0], h1 = hist[b1];
+      const int before = block_exclusive(h0 + h1);  // items in higher bins
+      if (k_rank >= before && k_rank < before + h0) {
+        pick[0] = b0;
+        pick[1] = k_rank - before;
+      } else if (k_rank >= before + h0 && k_rank < before + h0 + h1) {
+        pick[0] = b1;
+        pick[1] = k_rank - before - h0;
+      }
+      __syncthreads();
+    }
+    const int bin = pick[0], idx = pick[1];
+    int local = 0;
+    for (int x = x0; x < x1; ++x) local += bin_of(x) == bin;
+    __syncthreads();  // wtot is reused
+    const int before = block_exclusive(local);
+    if (idx >= before && idx < before + local) {
+      int r = idx - before;
+      for (int x = x0; x < x1; ++x)
+        if (bin_of(x) == bin) {
+          if (r == 0) pick[2] = x;
+          --r;
+        }
     }
     __syncthreads();
-    const int x = tbl[0];
-    __syncthreads();  // tbl is reused for the block table below
+    const int x = pick[2];
+    __syncthreads();  // the stage is reused for K/V below
     seq = x / R;
     rb = x % R;
-  } else {
-    seq = by;
-    rb = R - 1 - bz;
   }
   const int qs = p.query_start_loc[seq];
   const int n = min(p.query_start_loc[seq + 1] - qs, p.max_query_len);

@@ -66,3 +66,52 @@ def test_streaming_and_shared_loads_both_present(decode_asm, kernel):
     # new-row loads, which are plain)
     assert len(nt) == 16, (kernel, len(nt))
     assert len(loads) - len(nt) >= 16, (kernel, len(loads) - len(nt))
+
+
+# The prefill tile loop holds the output accumulators, the query operands and
+# a tile's logits in registers at two workgroups per CU. Register allocation
+# of that loop has been seen to flip between two outcomes on small changes
+# elsewhere in the kernel: accumulators kept in place, or copied between two
+# register sets every tile (about 130 extra 64-bit moves per loop iteration,
+# plus spills). The second costs time, not correctness, so only this test
+# sees it.
+@pytest.fixture(scope="module")
+def prefill_asm(tmp_path_factory):
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not found")
+    text = ""
+    for src in ("prefill.hip", "mixed.hip"):
+        out = tmp_path_factory.mktemp("isa") / (src + ".s")
+        cmd = [hipcc] + pbuild.COMMON + ["-x", "hip", "--cuda-device-only", "-S",
+                                         os.path.join(CSRC, src), "-o", str(out)]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr[-2000:]
+        text += out.read_text()
+    return text
+
+
+def kernel_meta(asm, name):
+    start = asm.index(name + ":")
+    end = asm.index(".end_amdhsa_kernel", start)
+    meta = asm[end:end + 4000]
+    scratch = int(re.search(r"ScratchSize:\s*(\d+)", meta).group(1))
+    return asm[start:asm.index(".Lfunc_end", start)], scratch
+
+
+# head_dim 128, four query heads per workgroup: bf16 and E4M3 pools, and the
+# mixed batch's kernel (prefill body beside the decode workers)
+PREFILL_KERNELS = [
+    "_ZN2pa20prefill_chunk_kernelILi128ELi4EtEEvNS_13PrefillParamsE",
+    "_ZN2pa20prefill_chunk_kernelILi128ELi4EhEEvNS_13PrefillParamsE",
+    "_ZN2pa20prefill_chunk_kernelILi64ELi4EtEEvNS_13PrefillParamsE",
+    "_ZN2pa18mixed_batch_kernelILi128ELi4ELb1EtEEvNS_11MixedParamsE",
+]
+
+
+@pytest.mark.parametrize("kernel", PREFILL_KERNELS)
+def test_prefill_accumulators_stay_in_place(prefill_asm, kernel):
+    body, scratch = kernel_meta(prefill_asm, kernel)
+    moves = len(re.findall(r"\bv_mov_b64", body))
+    assert scratch == 0, (kernel, "scratch bytes", scratch)
+    assert moves <= 64, (kernel, "v_mov_b64", moves)
