@@ -1339,10 +1339,11 @@ __device__ __forceinline__ void balanced_body(const DecodeParams& p, int wg, int
   const int B = p.num_seqs;
   if (wg == 0)
     for (int k = threadIdx.x; k <= B; k += 256) p.ws_pfx[k] = pfx[k];
-  const int C = pfx[B];
+  const int C = __builtin_amdgcn_readfirstlane(pfx[B]);
 
   const int lane = threadIdx.x & 63;
-  const int g = wg * 4 + (threadIdx.x >> 6);
+  // uniform over the wave: kept in scalar registers
+  const int g = __builtin_amdgcn_readfirstlane(wg * 4 + (threadIdx.x >> 6));
   const int unit = g % p.units;  // the waves of a workgroup share a range
   const int w = g / p.units;
   if (w >= p.workers) return;
