@@ -1097,13 +1097,21 @@ __global__ __launch_bounds__(256, (decode_min_wgs<T, KT, GT>())) void paged_deco
     seq = __builtin_amdgcn_readfirstlane(seq);  // uniform over the workgroup: keep it scalar
     part = __builtin_amdgcn_readfirstlane(part);
   }
-  if constexpr (fused_store_supported<T, KT>()) {
-    if (p.new_k != nullptr && blockIdx.x == 0 && part == 0) {  // fused store of seq's row
-      const int64_t cpr = p.row_bytes / 16;
-      store_new_rows<T, KT>(p, (int64_t)seq * cpr + threadIdx.x, 256, (int64_t)(seq + 1) * cpr);
+  // Fused store of seq's row, by the workgroup of its first partition once
+  // its own work is done (the attention reads a sequence's newest row from
+  // the new rows themselves, so the pool copy may land at any time).
+  auto fused_store = [&]() {
+    if constexpr (fused_store_supported<T, KT>()) {
+      if (p.new_k != nullptr && blockIdx.x == 0 && part == 0) {
+        const int64_t cpr = p.row_bytes / 16;
+        store_new_rows<T, KT>(p, (int64_t)seq * cpr + threadIdx.x, 256, (int64_t)(seq + 1) * cpr);
+      }
     }
+  };
+  if (unit >= p.units) {
+    fused_store();
+    return;
   }
-  if (unit >= p.units) return;
   const int L = min(p.context_lens[seq], p.max_context_len);
   const int P = p.partition;
   const int nparts = L > 0 ? (L + P - 1) / P : 0;
@@ -1115,9 +1123,13 @@ __global__ __launch_bounds__(256, (decode_min_wgs<T, KT, GT>())) void paged_deco
 
   if (nparts == 0) {  // empty context: defined output of zeros
     if (part == 0 && tr == 0) store_zeros<T, D, GT, EPL>(p, seq, h0, dc);
+    fused_store();
     return;
   }
-  if (part >= nparts) return;
+  if (part >= nparts) {
+    fused_store();
+    return;
+  }
 
   const int tok_begin = part * P;
   const int tok_end = min(L, tok_begin + P);
@@ -1131,6 +1143,7 @@ __global__ __launch_bounds__(256, (decode_min_wgs<T, KT, GT>())) void paged_deco
 
   if (nparts == 1) {
     if (tr == 0) store_output<T, D, GT, EPL>(p, seq, h0, dc, st);
+    fused_store();
     return;
   }
 
@@ -1148,6 +1161,7 @@ __global__ __launch_bounds__(256, (decode_min_wgs<T, KT, GT>())) void paged_deco
       if (dc == 0) *reinterpret_cast<float2*>(p.ws_ml + (sh * mp + part) * 2) = make_float2(st.m[h], st.l[h]);
     }
   }
+  fused_store();
 }
 
 // Merge the partition states of every (sequence, unit) whose context was
@@ -1331,10 +1345,15 @@ __device__ __forceinline__ void balanced_body(const DecodeParams& p, int wg, int
   constexpr int TPW = 64 / LPR;
   constexpr int CT = U * TPW;
   __shared__ int32_t pfx[MAXS + 1];
-  if constexpr (fused_store_supported<T, KT>()) {
-    if (p.new_k != nullptr)  // fused store: every thread of the grid writes a share of the rows
-      store_new_rows<T, KT>(p, (int64_t)wg * 256 + threadIdx.x, (int64_t)num_wgs * 256, INT64_MAX);
-  }
+  // Fused store: every thread of the grid writes a share of the rows, once
+  // its own work is done (the attention reads a sequence's newest row from
+  // the new rows themselves, so the pool copy may land at any time).
+  auto fused_store = [&]() {
+    if constexpr (fused_store_supported<T, KT>()) {
+      if (p.new_k != nullptr)
+        store_new_rows<T, KT>(p, (int64_t)wg * 256 + threadIdx.x, (int64_t)num_wgs * 256, INT64_MAX);
+    }
+  };
   chunk_prefix<CT>(p, pfx);
   const int B = p.num_seqs;
   if (wg == 0)
@@ -1346,10 +1365,16 @@ __device__ __forceinline__ void balanced_body(const DecodeParams& p, int wg, int
   const int g = __builtin_amdgcn_readfirstlane(wg * 4 + (threadIdx.x >> 6));
   const int unit = g % p.units;  // the waves of a workgroup share a range
   const int w = g / p.units;
-  if (w >= p.workers) return;
+  if (w >= p.workers) {
+    fused_store();
+    return;
+  }
   const int c0 = (int)((int64_t)w * C / p.workers);
   const int c1 = (int)((int64_t)(w + 1) * C / p.workers);
-  if (c0 >= c1) return;
+  if (c0 >= c1) {
+    fused_store();
+    return;
+  }
   // this lane's KV head (a pair's first or second) and first query head
   const int kvh = PAIR ? 2 * unit + (lane % LPR) / LPT : unit / p.n_sub;
   const int h0 = PAIR ? kvh : kvh * p.group + (unit - kvh * p.n_sub) * GT;
@@ -1402,6 +1427,7 @@ __device__ __forceinline__ void balanced_body(const DecodeParams& p, int wg, int
       --i;
     } while (pfx[i] == pfx[i + 1]);  // skip empty contexts
   }
+  fused_store();
 }
 
 template <typename T, typename KT, int D, int GT, int U, bool UNIFORM_BLOCK, bool PAIR = false>
