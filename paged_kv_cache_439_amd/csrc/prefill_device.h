@@ -107,6 +107,17 @@ __device__ __forceinline__ void load_lds16(const void* gptr, void* lds_base) {
                                    (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
 }
 
+// A buffer resource over the bytes from base on (record limit 2^31 - 1, raw
+// 32-bit data format for untyped loads), and a 16-byte load from it straight
+// into LDS: lane l reads at its own offset voff and writes lds_base + 16*l
+// (lds_base the same for every lane).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const char* base) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7FFFFFFF, 0x00020000);
+}
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, voff, 0, 0, 0);
+}
+
 // Two E4M3 codes (byte pair HI of w: 0 = bytes 0-1, 1 = bytes 2-3) as two
 // bf16 (exact: every E4M3 value is a bf16 value).
 template <bool HI>
@@ -274,11 +285,36 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int bx, int
   // Issue the global->LDS loads of tile kt0 into a stage. Keys past the
   // workgroup's range read the last needed row instead (finite data whose
   // probability is zero), so no NaN from outside the context reaches V.
+  // A whole tile inside one block is copied through buffer loads: the tile's
+  // first row is the base of a buffer resource in scalar registers, and each
+  // lane's offsets from it (NIW K and NIW V copies) are fixed for the kernel.
+  uint32_t koff[NIW], voff[NIW];
+#pragma unroll
+  for (int i = 0; i < NIW; ++i) {
+    const int key = (wave * NIW + i) * KPI + lane / GPR;
+    const int gl = lane % GPR;
+    koff[i] = (uint32_t)(key * row_bytes + head_off + (gl ^ swz_k(key)) * 16);
+    voff[i] = (uint32_t)(key * row_bytes + head_off + (gl ^ swz_v(key)) * 16);
+  }
   auto issue = [&](int kt0, uint16_t (&stage)[2][TE]) {
     // When the tile lies inside one block (block_size >= KT) one table entry
     // serves every lane.
     const bool one_block = KT <= (1 << bs_log2);
     const int phys0 = __builtin_amdgcn_readfirstlane(tbl[(kt0 >> bs_log2) - wb]);
+    if (__builtin_amdgcn_readfirstlane((int)(one_block && kt0 + KT <= kv_end))) {  // a whole tile of one block
+      const int64_t t64 = (((int64_t)phys0 << bs_log2) + (kt0 & bs_mask)) * row_bytes;
+      const int64_t tile = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(t64 >> 32)) << 32) |
+                                     (uint32_t)__builtin_amdgcn_readfirstlane((int)t64));
+      const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(p.k_cache + tile);
+      const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(p.v_cache + tile);
+#pragma unroll
+      for (int i = 0; i < NIW; ++i) {
+        const int ins = wave * NIW + i;
+        buffer_load_lds16(rk, koff[i], &stage[0][ins * KPI * D]);
+        buffer_load_lds16(rv, voff[i], &stage[1][ins * KPI * D]);
+      }
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < NIW; ++i) {
       const int ins = wave * NIW + i;
