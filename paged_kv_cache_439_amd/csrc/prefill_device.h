@@ -478,7 +478,10 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int bx, int
     bf16x8 pb[2][2];
     auto softmax = [&](auto masked_tag) {
       constexpr bool MASKED = decltype(masked_tag)::value;
-      float mt[2];
+      // Each lane's maximum over its own logits of a row; the maximum over
+      // the row's four lanes is only needed when some lane's exceeds the
+      // row's running maximum by more than the slack.
+      float lm[2];
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
         const int tpos = c + wrow0 + rt * 16 + lrow;  // absolute position of the row
@@ -497,19 +500,19 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int bx, int
               }
               mx = __builtin_elementwise_maximum(mx, v);
             }
-        mx = max_over_row_groups(mx);
-        mt[rt] = (MASKED && mx == -INFINITY) ? -INFINITY : mx * sl2;
+        lm[rt] = mx;
       }
       // Raise a row's running maximum only when the tile's maximum exceeds it
       // by more than the slack. The wave takes the branch when any of its
       // rows needs it; rows that keep their maximum scale by exp2(0) = 1
       // exactly.
-      const bool raise0 = mt[0] > m[0] + RESCALE_SLACK;
-      const bool raise1 = mt[1] > m[1] + RESCALE_SLACK;
-      if (__builtin_amdgcn_ballot_w64(raise0 || raise1) != 0) {
+      if (__builtin_amdgcn_ballot_w64(lm[0] * sl2 > m[0] + RESCALE_SLACK ||
+                                      lm[1] * sl2 > m[1] + RESCALE_SLACK) != 0) {
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-          const float nm = (rt == 0 ? raise0 : raise1) ? mt[rt] : m[rt];
+          const float mx = max_over_row_groups(lm[rt]);
+          const float mt = (MASKED && mx == -INFINITY) ? -INFINITY : mx * sl2;
+          const float nm = mt > m[rt] + RESCALE_SLACK ? mt : m[rt];
           const float alpha = fast_exp2(m[rt] - nm);
           m[rt] = nm;
           lsum[rt] *= alpha;
