@@ -128,10 +128,10 @@ class DecodeSet:
                                 b.max_context_len, b.scale, self.P, self.ws)
 
 
-# Untimed calls before each extra decode measurement. The first few dozen
-# calls over freshly built large batches run slower than later ones (an E4M3
-# batch of 512 sequences: about 420 us per call over the first 30, 364 us
-# after), so each leg warms up over this many calls first.
+# Untimed calls before each extra measurement. The first few dozen calls over
+# freshly built large batches run slower than later ones (an E4M3 batch of 512
+# sequences: about 420 us per call over the first 30, 364 us after), so each
+# leg (decode, prefill and mixed alike) warms up over this many calls first.
 LEG_WARMUP = 40
 
 
@@ -710,13 +710,13 @@ def main():
             log("extra block manager")
             extra["block_manager"] = bench_block_manager()
             log("extra prefill")
-            extra["prefill"] = bench_prefill(20, 10, dev, oracle_rates=oracle_rates if with_oracle else None)
+            extra["prefill"] = bench_prefill(40, LEG_WARMUP, dev, oracle_rates=oracle_rates if with_oracle else None)
             log("extra prefill e4m3")
-            extra["prefill_e4m3"] = bench_prefill(20, 10, dev, kv="e4m3")
+            extra["prefill_e4m3"] = bench_prefill(40, LEG_WARMUP, dev, kv="e4m3")
             log("extra mixed batch")
-            extra["mixed_batch"] = bench_mixed(20, 10, dev, oracle_rates=oracle_rates if with_oracle else None)
+            extra["mixed_batch"] = bench_mixed(40, LEG_WARMUP, dev, oracle_rates=oracle_rates if with_oracle else None)
             log("extra mixed batch e4m3")
-            extra["mixed_batch_e4m3"] = bench_mixed(20, 10, dev, kv="e4m3")
+            extra["mixed_batch_e4m3"] = bench_mixed(40, LEG_WARMUP, dev, kv="e4m3")
         if oracle_rates:
             extra["cpu_oracle"] = oracle_rates
         line["extra"] = extra
