@@ -1,11 +1,13 @@
 """Summaries of rocprofv3 output for the profiles/ folder.
 
-    python -m paged_kv_cache_439_amd.rocprof_summary trace STATS_CSV OUT_MD --cmd "..."
+    python -m paged_kv_cache_439_amd.rocprof_summary trace STATS_CSV OUT_MD --cmd "..." \
+        [--kernel-trace TRACE_CSV --last N]
     python -m paged_kv_cache_439_amd.rocprof_summary traffic FETCH_CSV WRITE_CSV OUT_JSON OUT_MD \
         --copy-bytes N --cmd-fetch "..." --cmd-write "..."
     python -m paged_kv_cache_439_amd.rocprof_summary counters COUNTER_CSV OUT_MD --cmd "..."
 
-trace:   kernel-trace statistics of this library's kernels as a table.
+trace:   kernel-trace statistics of this library's kernels as a table
+         (with --last N, also the mean of each kernel's last N dispatches).
 traffic: HBM bytes per dispatch from the FETCH_SIZE and WRITE_SIZE counter
          passes (KiB per dispatch), each scaled by what the same counter
          reads for a plain device copy of a known size in the same run (the
@@ -52,13 +54,37 @@ def _short(name):
     return re.sub(r"\(char const\*.*$", "", name)
 
 
-def trace(stats_csv, out_md, cmd):
+def _last_means(trace_csv, last):
+    """Mean duration (us) of each kernel's last `last` dispatches in a
+    kernel-trace CSV: the calls a benchmark times after its warm-up."""
+    per = collections.defaultdict(list)
+    for r in csv.DictReader(open(trace_csv)):
+        if _ours(r["Kernel_Name"]):
+            t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+            per[_short(r["Kernel_Name"])].append((t0, (t1 - t0) / 1e3))
+    return {k: sum(d for _, d in sorted(v)[-last:]) / len(sorted(v)[-last:]) for k, v in per.items()}
+
+
+def trace(stats_csv, out_md, cmd, trace_csv=None, last=0):
     rows = [r for r in csv.DictReader(open(stats_csv)) if _ours(r["Name"])]
-    lines = ["# Kernel trace: libpagedattn kernels", "", "Command:", "", "```", cmd, "```", "",
-             "| kernel | calls | avg us | min us | max us |", "|---|---|---|---|---|"]
+    tail = _last_means(trace_csv, last) if trace_csv and last > 0 else None
+    head = "| kernel | calls | avg us | min us | max us |"
+    rule = "|---|---|---|---|---|"
+    if tail is not None:
+        head += f" avg of last {last} us |"
+        rule += "---|"
+    lines = ["# Kernel trace: libpagedattn kernels", "", "Command:", "", "```", cmd, "```", ""]
+    if tail is not None:
+        lines += [f"The last column averages each kernel's last {last} dispatches (in start order), the calls a "
+                  "benchmark leg times after its warm-up.", ""]
+    lines += [head, rule]
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
-        lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
-                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+        line = (f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} |")
+        if tail is not None:
+            t = tail.get(_short(r["Name"]))
+            line += f" {t:.2f} |" if t is not None else " - |"
+        lines.append(line)
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
@@ -206,6 +232,8 @@ def main():
     t.add_argument("stats_csv")
     t.add_argument("out_md")
     t.add_argument("--cmd", required=True)
+    t.add_argument("--kernel-trace", default=None, help="kernel-trace CSV of the same run")
+    t.add_argument("--last", type=int, default=0, help="also average each kernel's last N dispatches")
     f = sub.add_parser("traffic")
     f.add_argument("fetch_csv")
     f.add_argument("write_csv")
@@ -222,7 +250,7 @@ def main():
     if a.mode == "counters":
         counters(a.counter_csv, a.out_md, a.cmd)
     elif a.mode == "trace":
-        trace(a.stats_csv, a.out_md, a.cmd)
+        trace(a.stats_csv, a.out_md, a.cmd, a.kernel_trace, a.last)
     else:
         traffic(a.fetch_csv, a.write_csv, a.out_json, a.out_md, a.copy_bytes, a.cmd_fetch, a.cmd_write)
 
