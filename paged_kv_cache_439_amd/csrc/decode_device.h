@@ -593,6 +593,20 @@ struct ChunkAddresses {
     }                                                                                    \
   } while (0)
 
+// Issue priority of a balanced-split wave from the share of its own range
+// still to do (rest of total tokens, in quarters): a wave that has fallen
+// behind the other wave of its SIMD wins the issue slots until it has
+// caught up. Waves with equal chunk counts otherwise end far apart: the
+// older workgroup of a CU wins the arbitration, and some XCDs stream more
+// slowly than others.
+__device__ __forceinline__ void set_progress_prio(int rest, int total) {
+  const int lvl = __builtin_amdgcn_readfirstlane((int)(((int64_t)rest * 4) / (total + 1)));
+  if (lvl >= 3) __builtin_amdgcn_s_setprio(3);
+  else if (lvl == 2) __builtin_amdgcn_s_setprio(2);
+  else if (lvl == 1) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // Stream tokens [tok_begin, tok_end) of sequence seq (KV head kvh) through
 // the online softmax of st. UNIFORM_BLOCK: every chunk lies inside one block
 // (block_size >= CT and tok_begin a multiple of CT), so one table lookup per
@@ -610,7 +624,8 @@ template <typename T, typename KT, int D, int GT, int U, bool UNIFORM_BLOCK, boo
 __device__ __forceinline__ void attend_range(const DecodeParams& p, int seq, int kvh, int lane,
                                              int tok_begin, int tok_end,
                                              const QSlice<T, KT> (&qv)[GT], float sm,
-                                             WaveState<GT, 16 / ElemTraits<KT>::E>& st) {
+                                             WaveState<GT, 16 / ElemTraits<KT>::E>& st,
+                                             int prio_rest = 0, int prio_total = 0) {
   // With a fused store, the newest token (position L-1, L = the context
   // length) comes from the new row itself, not from the pool slot this same
   // launch is writing (over E4M3 pools, as the codes the store writes).
@@ -644,6 +659,9 @@ __device__ __forceinline__ void attend_range(const DecodeParams& p, int seq, int
 
   ChunkAddresses<U, TPW, NT, UNIFORM_BLOCK> ca(p, seq, lane, tr, kvh * D * E + dc * 16, tok_begin, tok_end);
   for (int j0 = tok_begin; j0 < tok_end; j0 += CT) {
+    // priority from the work left (prio_total > 0: a balanced-split wave, every 4 chunks)
+    if (prio_total > 0 && ((j0 - tok_begin) & (4 * CT - 1)) == 0)
+      set_progress_prio(prio_rest + tok_end - j0, prio_total);
     // the whole chunk's bytes are in flight before any of them is waited on
     bool valid[U];
     int64_t off[U];
@@ -785,7 +803,8 @@ __device__ __forceinline__ void attend_range(const DecodeParams& p, int seq, int
 template <typename T, typename KT, int D, int GT, int U, bool UNIFORM_BLOCK>
 __device__ __forceinline__ void attend_range_mfma(const DecodeParams& p, int seq, int kvh, int h0, int lane,
                                                   int tok_begin, int tok_end, float sm,
-                                                  WaveState<GT, 16 / ElemTraits<KT>::E>& st) {
+                                                  WaveState<GT, 16 / ElemTraits<KT>::E>& st,
+                                                  int prio_rest = 0, int prio_total = 0) {
   constexpr int E = ElemTraits<KT>::E;
   constexpr int EPL = 16 / E;       // elements per 16-byte slice
   constexpr int LPT = D / EPL;      // lanes per token row = granules per row
@@ -832,6 +851,9 @@ __device__ __forceinline__ void attend_range_mfma(const DecodeParams& p, int seq
   float mm = NEG_BIG, ll = 0.0f;
   ChunkAddresses<U, TPW, true, UNIFORM_BLOCK> ca(p, seq, lane, tr, kvh * D * E + dc * 16, tok_begin, tok_end);
   for (int j0 = tok_begin; j0 < tok_end; j0 += CT) {
+    // priority from the work left (prio_total > 0: a balanced-split wave, every 4 chunks)
+    if (prio_total > 0 && ((j0 - tok_begin) & (4 * CT - 1)) == 0)
+      set_progress_prio(prio_rest + tok_end - j0, prio_total);
     bool valid[U];  // the PV products need no mask: masked logits give zero probabilities
     int64_t off[U];
     ca.chunk(j0, off, valid);
@@ -939,14 +961,17 @@ constexpr bool decode_mfma_logits() {
 template <typename T, typename KT, int D, int GT, int U, bool UNIFORM_BLOCK, bool PAIR = false, bool MFMA_OK = true>
 __device__ __forceinline__ void attend(const DecodeParams& p, int seq, int kvh, int h0, int lane, int dc,
                                        int tok_begin, int tok_end, float sm,
-                                       WaveState<GT, 16 / ElemTraits<KT>::E>& st) {
+                                       WaveState<GT, 16 / ElemTraits<KT>::E>& st,
+                                       int prio_rest = 0, int prio_total = 0) {
   if constexpr (decode_mfma_logits<T, KT, D, GT, U, PAIR, MFMA_OK>()) {
-    attend_range_mfma<T, KT, D, GT, U, UNIFORM_BLOCK>(p, seq, kvh, h0, lane, tok_begin, tok_end, sm, st);
+    attend_range_mfma<T, KT, D, GT, U, UNIFORM_BLOCK>(p, seq, kvh, h0, lane, tok_begin, tok_end, sm, st,
+                                                      prio_rest, prio_total);
   } else {
     QSlice<T, KT> qv[GT];
     load_q<T, KT, D, GT>(p, seq, h0, dc, qv);
     st.reset();
-    attend_range<T, KT, D, GT, U, UNIFORM_BLOCK, PAIR>(p, seq, kvh, lane, tok_begin, tok_end, qv, sm, st);
+    attend_range<T, KT, D, GT, U, UNIFORM_BLOCK, PAIR>(p, seq, kvh, lane, tok_begin, tok_end, qv, sm, st,
+                                                       prio_rest, prio_total);
   }
 }
 
@@ -1336,8 +1361,10 @@ __device__ __forceinline__ void merge_pieces(const DecodeParams& p, int seq, int
 // The balanced split's workers, as workgroup wg of num_wgs (each workgroup
 // holds 4 waves, i.e. 4 (unit, worker) pairs). MAXS bounds num_seqs (the
 // chunk prefix sums live in LDS). MFMA_OK: see decode_mfma_logits.
+// PRIO: waves set their issue priority from the work they have left
+// (set_progress_prio); off where they share CUs with other work.
 template <typename T, typename KT, int D, int GT, int U, bool UNIFORM_BLOCK, int MAXS,
-          bool PAIR = false, bool MFMA_OK = true>
+          bool PAIR = false, bool MFMA_OK = true, bool PRIO = false>
 __device__ __forceinline__ void balanced_body(const DecodeParams& p, int wg, int num_wgs) {
   constexpr int EPL = 16 / ElemTraits<KT>::E;
   constexpr int LPT = D / EPL;
@@ -1401,7 +1428,8 @@ __device__ __forceinline__ void balanced_body(const DecodeParams& p, int wg, int
     const int L = min(p.context_lens[i], p.max_context_len);
     WaveState<GT, EPL> st;
     attend<T, KT, D, GT, U, UNIFORM_BLOCK, PAIR, MFMA_OK>(p, i, kvh, h0, lane, dc, (ps - cb) * CT,
-                                                         min((pe - cb) * CT, L), sm, st);
+                                                         min((pe - cb) * CT, L), sm, st,
+                                                         PRIO ? (ps - c0) * CT : 0, PRIO ? (c1 - c0) * CT : 0);
     apply_v_scale<KT, GT, EPL>(p, kvh, st.acc);
     merge_row_groups<LPR, GT, EPL>(st.m, st.l, st.acc);
     if (tr == 0) {
@@ -1432,7 +1460,7 @@ __device__ __forceinline__ void balanced_body(const DecodeParams& p, int wg, int
 
 template <typename T, typename KT, int D, int GT, int U, bool UNIFORM_BLOCK, bool PAIR = false>
 __global__ __launch_bounds__(256, DECODE_BAL_WAVES_PER_SIMD) void paged_decode_balanced_kernel(DecodeParams p) {
-  balanced_body<T, KT, D, GT, U, UNIFORM_BLOCK, BAL_MAX_SEQS, PAIR>(p, blockIdx.x, gridDim.x);
+  balanced_body<T, KT, D, GT, U, UNIFORM_BLOCK, BAL_MAX_SEQS, PAIR, true, true>(p, blockIdx.x, gridDim.x);
 }
 
 // One wave per (sequence, unit): combine the partial states the workers
