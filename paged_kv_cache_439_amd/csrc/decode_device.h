@@ -594,13 +594,14 @@ struct ChunkAddresses {
   } while (0)
 
 // Issue priority of a balanced-split wave from the share of its own range
-// still to do (rest of total tokens, in quarters): a wave that has fallen
-// behind the other wave of its SIMD wins the issue slots until it has
-// caught up. Waves with equal chunk counts otherwise end far apart: the
-// older workgroup of a CU wins the arbitration, and some XCDs stream more
-// slowly than others.
+// still to do (rest of total tokens: above 1/2, 1/4, 1/8, or less): a wave
+// that has fallen behind the other wave of its SIMD wins the issue slots
+// until it has caught up. Waves with equal chunk counts otherwise end far
+// apart: the older workgroup of a CU wins the arbitration, and some XCDs
+// stream more slowly than others.
 __device__ __forceinline__ void set_progress_prio(int rest, int total) {
-  const int lvl = __builtin_amdgcn_readfirstlane((int)(((int64_t)rest * 4) / (total + 1)));
+  const int r = __builtin_amdgcn_readfirstlane(rest), t = __builtin_amdgcn_readfirstlane(total);
+  const int lvl = 2 * r > t ? 3 : 4 * r > t ? 2 : 8 * r > t ? 1 : 0;
   if (lvl >= 3) __builtin_amdgcn_s_setprio(3);
   else if (lvl == 2) __builtin_amdgcn_s_setprio(2);
   else if (lvl == 1) __builtin_amdgcn_s_setprio(1);
