@@ -115,3 +115,28 @@ def test_prefill_accumulators_stay_in_place(prefill_asm, kernel):
     moves = len(re.findall(r"\bv_mov_b64", body))
     assert scratch == 0, (kernel, "scratch bytes", scratch)
     assert moves <= 64, (kernel, "v_mov_b64", moves)
+
+
+# The balanced decode waves set their issue priority from the share of their
+# own range still to do (the four levels of s_setprio); the mixed batch's
+# decode waves share their SIMDs with prefill waves and keep the default.
+BALANCED = [k for k in STREAMING if k.startswith("paged_decode_balanced_kernel")]
+
+
+@pytest.mark.parametrize("kernel", BALANCED)
+def test_balanced_decode_sets_progress_priority(decode_asm, kernel):
+    body = kernel_body(decode_asm, kernel)
+    levels = set(re.findall(r"s_setprio (\d)", body))
+    assert levels == {"0", "1", "2", "3"}, (kernel, levels)
+
+
+def test_mixed_batch_keeps_default_priority(prefill_asm):
+    body, _ = kernel_meta(prefill_asm, "_ZN2pa18mixed_batch_kernelILi128ELi4ELb1EtEEvNS_11MixedParamsE")
+    assert "s_setprio" not in body
+
+
+def test_decode_kernels_use_no_scratch(decode_asm):
+    names = re.findall(r"^(_ZN2pa\w*paged_decode\w*kernel\w*):", decode_asm, re.M)
+    assert len(names) >= 20, len(names)
+    spilled = [n for n in names if kernel_meta(decode_asm, n)[1] != 0]
+    assert not spilled, spilled
