@@ -154,15 +154,14 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int bx, int
   constexpr int TBL = 512;        // block-table window (entries)
   static_assert(NIW >= 1, "tile shape");
 
-  // bf16 pools: two stages, each [0 = K, 1 = V][key][granule] with granules
+  // Two stages, each [0 = K, 1 = V][key][granule] of bf16 with granules
   // XOR-swizzled per key. Separate arrays, so the compiler can tell that a
-  // load into one stage does not feed the reads of the other.
-  // E4M3 pools: the codes of two tiles, f8[stage][K/V][key][D bytes] in pool
-  // order, and one bf16 stage (kv0) in the layout above that the workgroup
-  // widens each tile's codes into.
+  // load into one stage does not feed the reads of the other. bf16 pools:
+  // the rows are copied from global memory straight into a stage; E4M3
+  // pools: each thread loads its share of a tile's codes into registers one
+  // tile ahead and widens them into the stage at the start of that tile.
   __shared__ __attribute__((aligned(16))) uint16_t kv0[2][TE];
-  __shared__ __attribute__((aligned(16))) uint16_t kv1[2][E4 ? 8 : TE];
-  __shared__ __attribute__((aligned(16))) uint8_t f8[E4 ? 2 : 1][2][E4 ? TE : 16];
+  __shared__ __attribute__((aligned(16))) uint16_t kv1[2][TE];
   __shared__ int32_t tbl[TBL];
 
   const int tid = threadIdx.x;
@@ -328,45 +327,42 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int bx, int
     }
   };
 
-  // E4M3: issue the global->LDS loads of tile kt0's codes into code stage
-  // st (a wave-wide 16-byte load covers KPL keys of D codes), clamped to the
-  // last needed key like the bf16 loads.
-  constexpr int CPR = D / 16;   // 16-byte code chunks per row of one head
-  constexpr int KPL = 64 / CPR;  // keys one wave-wide load covers
-  auto issue_codes = [&](int kt0, int st) {
-    constexpr int NIW8 = KT / KPL / 4;
+  // E4M3: the codes of tile kt0 into registers, each thread 16 codes of a
+  // key row per tensor and chunk (CPR chunks per row of one head), clamped
+  // to the last needed key like the bf16 loads; widen_store later widens
+  // them exactly to bf16 into a stage, in the swizzled layout above.
+  constexpr int CPR = D / 16;
+  constexpr int PER = E4 ? KT * CPR / 256 : 1;
+  uint4 kcode[PER], vcode[PER];
+  auto load_codes = [&](int kt0) {
     const bool one_block = KT <= (1 << bs_log2);
-    const int phys0 = __builtin_amdgcn_readfirstlane(tbl[(kt0 >> bs_log2) - wb]);
+    const int phys0 = one_block ? __builtin_amdgcn_readfirstlane(tbl[(kt0 >> bs_log2) - wb]) : 0;
 #pragma unroll
-    for (int i = 0; i < NIW8; ++i) {
-      const int ins = wave * NIW8 + i;
-      const int key = ins * KPL + lane / CPR;
+    for (int x = 0; x < PER; ++x) {
+      const int ci = tid + 256 * x;
+      const int key = ci / CPR, part = ci % CPR;
       const int j = min(kt0 + key, kv_end - 1);
       const int phys = one_block ? phys0 : tbl[(j >> bs_log2) - wb];
-      const int64_t row =
-          (((int64_t)phys << bs_log2) + (j & bs_mask)) * row_bytes + head_off + (lane % CPR) * 16;
-      load_lds16(p.k_cache + row, &f8[st][0][ins * KPL * D]);
-      load_lds16(p.v_cache + row, &f8[st][1][ins * KPL * D]);
+      const int64_t row = (((int64_t)phys << bs_log2) + (j & bs_mask)) * row_bytes + head_off + part * 16;
+      kcode[x] = *reinterpret_cast<const uint4*>(p.k_cache + row);
+      vcode[x] = *reinterpret_cast<const uint4*>(p.v_cache + row);
     }
   };
-  // E4M3: widen code stage st into the bf16 stage kv0; each thread takes
-  // 16 codes (two bf16 granules) of a key row per tensor and chunk.
-  auto widen_codes = [&](int st) {
-    constexpr int PER = KT * CPR / 256;
+  auto widen_store = [&](uint16_t (&stage)[2][TE]) {
 #pragma unroll
     for (int x = 0; x < PER; ++x) {
       const int ci = tid + 256 * x;
       const int key = ci / CPR, part = ci % CPR;
 #pragma unroll
       for (int tsr = 0; tsr < 2; ++tsr) {
-        const uint4 w = *reinterpret_cast<const uint4*>(&f8[st][tsr][ci * 16]);
+        const uint4 w = tsr == 0 ? kcode[x] : vcode[x];
         const uint4 lo = make_uint4(widen_e4m3x2<false>(w.x), widen_e4m3x2<true>(w.x),
                                     widen_e4m3x2<false>(w.y), widen_e4m3x2<true>(w.y));
         const uint4 hi = make_uint4(widen_e4m3x2<false>(w.z), widen_e4m3x2<true>(w.z),
                                     widen_e4m3x2<false>(w.w), widen_e4m3x2<true>(w.w));
         const int sw = tsr == 0 ? swz_k(key) : swz_v(key);
-        *reinterpret_cast<uint4*>(&kv0[tsr][key * D + (((2 * part) ^ sw) * 8)]) = lo;
-        *reinterpret_cast<uint4*>(&kv0[tsr][key * D + (((2 * part + 1) ^ sw) * 8)]) = hi;
+        *reinterpret_cast<uint4*>(&stage[tsr][key * D + (((2 * part) ^ sw) * 8)]) = lo;
+        *reinterpret_cast<uint4*>(&stage[tsr][key * D + (((2 * part + 1) ^ sw) * 8)]) = hi;
       }
     }
   };
@@ -409,7 +405,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int bx, int
   }
 
   __syncthreads();  // table window visible
-  if constexpr (E4) issue_codes(0, 0);
+  if constexpr (E4) load_codes(0);
   else issue(0, kv0);
 
   // One 64-key tile: wait for its loads, start the next tile's loads into
@@ -419,6 +415,10 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int bx, int
   // the codes (code stage st, the next tile's into st ^ 1), widened into kv0
   // (cur) before the products.
   auto step = [&](int kt0, uint16_t (&cur)[2][TE], uint16_t (&nxt_stage)[2][TE], int st) {
+    // E4M3: widen tile kt0's codes (loaded during the previous tile) into
+    // this stage, which every wave finished reading before the previous
+    // tile's barrier
+    if constexpr (E4) widen_store(cur);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's part of tile kt0 landed
     __syncthreads();  // the whole tile is in LDS; every wave is done with the other stage
     const int nxt = kt0 + KT;
@@ -429,12 +429,8 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int bx, int
         load_window(wb);
         __syncthreads();
       }
-      if constexpr (E4) issue_codes(nxt, st ^ 1);
+      if constexpr (E4) load_codes(nxt);  // in registers while this tile is computed
       else issue(nxt, nxt_stage);  // in flight while this tile is computed
-    }
-    if constexpr (E4) {
-      widen_codes(st);
-      __syncthreads();  // kv0 holds tile kt0 as bf16
     }
     if (kt0 > wave_last_key) return;  // every key of this tile is masked for this wave
     const uint16_t* Kt = cur[0];
@@ -585,13 +581,8 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p, int bx, int
   };
 
   for (int kt0 = 0; kt0 < kv_end; kt0 += 2 * KT) {
-    if constexpr (E4) {
-      step(kt0, kv0, kv0, 0);
-      if (kt0 + KT < kv_end) step(kt0 + KT, kv0, kv0, 1);
-    } else {
-      step(kt0, kv0, kv1, 0);
-      if (kt0 + KT < kv_end) step(kt0 + KT, kv1, kv0, 1);
-    }
+    step(kt0, kv0, kv1, 0);
+    if (kt0 + KT < kv_end) step(kt0 + KT, kv1, kv0, 1);
   }
 
   // ---- normalise and write: lane holds O[row][16*dt + 4*qgrp + 0..3] ----
