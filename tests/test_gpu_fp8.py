@@ -271,6 +271,12 @@ FP8_PREFILL_VARIANTS = {
                            cached=("uniform", 0, 300), chunk=[45, 70], max_context=512, scale=-0.125),
     "bs1024_gqa4": dict(num_seqs=2, block_size=1024, cached=("fixed", [1000, 3]), chunk=[100, 64],
                         max_context=2048),
+    # eight query heads per KV head: two workgroups read each KV head's codes
+    "group8": dict(num_seqs=2, num_heads=32, num_kv_heads=4, block_size=32,
+                   cached=("uniform", 0, 500), chunk=[96, 33], max_context=640),
+    # a 64-key tile always inside one block, chunks crossing block edges
+    "bs512_gqa4": dict(num_seqs=2, block_size=512, cached=("uniform", 0, 1500), chunk=[300, 129],
+                       max_context=2048),
 }
 
 

@@ -132,7 +132,7 @@ def test_mixed_full_config_sampled(gpu):
 # the same calls over E4M3 pools (pa_mixed_batch_fp8) against the oracle's
 # E4M3 prefill, whose decode tokens are chunks of one row
 
-FP8_MIXED_VARIANTS = ["gqa4_bs16", "mha_d64", "edges", "all_decode", "all_prefill", "bs512"]
+FP8_MIXED_VARIANTS = sorted(MIXED_VARIANTS)
 
 
 @pytest.mark.parametrize("name", FP8_MIXED_VARIANTS)
