@@ -187,6 +187,19 @@ def time_run(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
+def prefill_flops(b, first=0):
+    """Algorithmic flops of the chunks of sequences first.. of a batch: each
+    visible (query row, key) pair costs one D-long dot product for the logit
+    and one D-long multiply-add into the output, 2 * 2 * D flops per query
+    head. Row t of a chunk of n over c cached tokens sees c + t + 1 keys."""
+    flops = 0
+    for i in range(first, b.num_seqs):
+        n = int(b.query_start_loc[i + 1] - b.query_start_loc[i])
+        c = int(b.context_lens[i]) - n
+        flops += 4 * b.head_dim * b.num_heads * (n * c + n * (n + 1) // 2)
+    return flops
+
+
 def bench_prefill(steps, warmup, device, kv=None, oracle_rates=None):
     """The chunked-prefill workload: pa_prefill_chunk on bf16 pools, or
     (kv="e4m3") pa_prefill_chunk_fp8 on E4M3 pools with per-head scales."""
@@ -199,11 +212,7 @@ def bench_prefill(steps, warmup, device, kv=None, oracle_rates=None):
     qsl = torch.from_numpy(b.query_start_loc).to(device)
     lens = torch.from_numpy(b.context_lens).to(device)
     out = torch.empty_like(b.q)
-    flops = 0
-    for i in range(b.num_seqs):
-        n = int(b.query_start_loc[i + 1] - b.query_start_loc[i])
-        c = int(b.context_lens[i]) - n
-        flops += 4 * b.head_dim * b.num_heads * (n * c + n * (n + 1) // 2)
+    flops = prefill_flops(b)
     if kv == "e4m3":
         pa.pa_store_kvcache_fp8(b.key, b.value, b.k_cache, b.v_cache, slots, b.k_scale, b.v_scale)
 
@@ -284,11 +293,7 @@ def bench_mixed(steps, warmup, device, kv=None, oracle_rates=None):
                                            ("decode_only", decode_only), ("prefill_only", prefill_only))}
     rows = int(b.query_start_loc[-1])
     kv_dec = int(sum(int(L) for L in b.context_lens[:Bd])) * b.num_kv_heads * b.head_dim * 2 * (1 if e4 else 2)
-    flops = 0
-    for i in range(Bd, b.num_seqs):
-        n = int(b.query_start_loc[i + 1] - b.query_start_loc[i])
-        c = int(b.context_lens[i]) - n
-        flops += 4 * b.head_dim * b.num_heads * (n * c + n * (n + 1) // 2)
+    flops = prefill_flops(b, first=Bd)
     return dict(workload=sp["name"], decode_tokens=Bd, prefill_rows=rows - Bd,
                 mixed_ms=round(ms["mixed"], 4), separate_ms=round(ms["separate"], 4),
                 decode_only_ms=round(ms["decode_only"], 4), prefill_only_ms=round(ms["prefill_only"], 4),
