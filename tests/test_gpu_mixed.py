@@ -50,6 +50,10 @@ MIXED_VARIANTS = {
     # blocks of 512 tokens
     "bs512": dict(num_seqs=5, num_decode=3, block_size=512, decode_lens=("uniform", 1, 1500),
                   cached=("uniform", 0, 800), chunk=[100, 33], max_context=2048),
+    # 2048 decode tokens, the most one launch takes (their chunk prefix sums live in LDS)
+    "max_decode": dict(num_seqs=2050, num_decode=2048, num_heads=8, num_kv_heads=2, head_dim=64,
+                       block_size=16, decode_lens=("uniform", 1, 48), cached=("fixed", [30, 0]),
+                       chunk=[40, 17], max_context=128),
 }
 
 
