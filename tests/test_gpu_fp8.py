@@ -277,6 +277,11 @@ FP8_PREFILL_VARIANTS = {
     # a 64-key tile always inside one block, chunks crossing block edges
     "bs512_gqa4": dict(num_seqs=2, block_size=512, cached=("uniform", 0, 1500), chunk=[300, 129],
                        max_context=2048),
+    # contexts of 626 and 517 key tiles: past the ranking's 511-tile bins (they share the last one), and a
+    # block-table window that slides five times over 2504 blocks of 16
+    "long_contexts_rank_bins": dict(num_seqs=3, num_heads=8, num_kv_heads=2, block_size=16,
+                                    cached=("fixed", [40000, 33000, 100]), chunk=[64, 40, 200],
+                                    max_context=40064),
 }
 
 
