@@ -282,6 +282,9 @@ FP8_PREFILL_VARIANTS = {
     "long_contexts_rank_bins": dict(num_seqs=3, num_heads=8, num_kv_heads=2, block_size=16,
                                     cached=("fixed", [40000, 33000, 100]), chunk=[64, 40, 200],
                                     max_context=40064),
+    # one chunk of 2048 new rows over an empty cache: 64 row blocks of one sequence, causal throughout
+    "one_long_chunk": dict(num_seqs=1, num_heads=8, num_kv_heads=2, cached=("fixed", [0]), chunk=[2048],
+                           max_context=2048),
 }
 
 
